@@ -1,0 +1,232 @@
+/*
+ * bi.h -- batch-invariant, run-to-run deterministic reductions of an LLM forward
+ * pass on AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [DN]  "Defeating nondeterminism in LLM inference" (Chinese translation):
+ *         sections on floating-point non-associativity, atomic adds, batch
+ *         invariance, batch-invariant RMSNorm, matrix multiplication and attention.
+ *   [GPU] "Does the same LLM give different outputs on different GPUs? Why?":
+ *         sections on the experiment set-up (greedy decoding, token probabilities).
+ *   [XV]  arXiv abstract "cross-vendor mismatch of language models" (FP32 upcast,
+ *         MLPs kept in BF16).
+ *   [SM]  "Same model, same input, different answer": section on sampling (near-tie
+ *         argmax flips).
+ *   [VER] "How to verify GPU program correctness before deployment": sections on
+ *         validation data (bad shapes, illegal types) and error thresholds.
+ *
+ * The contract every entry point keeps ([DN], batch invariance): identical input
+ * bytes give identical output bits for every batch size M, every position of a row
+ * in the batch, every set of co-batched rows, every stream and every call history.
+ * No entry point uses atomics ([DN], atomic adds), no reduction order depends on M.
+ *
+ * Conventions shared by every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or keeps device memory and holds no mutable global state, so
+ *     calls may be issued from several threads.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue work on it
+ *     and return without waiting.
+ *   - Arguments are validated before anything is launched.  On a validation error
+ *     the call returns a negative bi_status and writes nothing.  A failed launch
+ *     returns BI_ERR_HIP.  No exception or abort crosses the ABI.
+ *   - Outputs must not alias inputs unless a call says otherwise.
+ *   - bf16 is IEEE binary32's upper 16 bits; every rounding to bf16 is
+ *     round-to-nearest-even (a NaN stays a quiet NaN).  fp32 denormals are kept.
+ *   - A dimension of 0 is valid and launches nothing (returns BI_OK).
+ */
+#ifndef BI_H_
+#define BI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BI_OK = 0,
+  BI_ERR_NULL = -1,        /* a required pointer is NULL                              */
+  BI_ERR_SHAPE = -2,       /* a size or leading dimension is negative or inconsistent  */
+  BI_ERR_DTYPE = -3,       /* unknown dtype / layout code                              */
+  BI_ERR_ALIGN = -4,       /* pointer or leading dimension breaks the stated alignment */
+  BI_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required               */
+  BI_ERR_UNSUPPORTED = -6, /* a valid request this build does not implement            */
+  BI_ERR_HIP = -7          /* the HIP runtime reported an error at launch              */
+} bi_status;
+
+enum { BI_BF16 = 1, BI_F32 = 2 };
+enum { BI_B_KN = 0, BI_B_NK = 1 };
+
+/* Compile-time constants of the reduction strategy.  They never vary at run time,
+ * because a run-time choice would be a way to break invariance. */
+typedef struct bi_config {
+  int32_t version;          /* layout of this struct                                   */
+  int32_t tree_max_lanes;   /* 256: lanes of the RMSNorm / log-softmax tree            */
+  int32_t wave_size;        /* 64                                                      */
+  int32_t gemm_tile_m;      /* output tile rows per workgroup                          */
+  int32_t gemm_tile_n;      /* output tile columns per workgroup                       */
+  int32_t gemm_tile_k;      /* K step of the main loop (ascending)                     */
+  int32_t gemm_mfma_m, gemm_mfma_n, gemm_mfma_k; /* the one matrix instruction shape     */
+  int32_t attn_chunk;       /* 256: split-KV chunk, at absolute positions 256c          */
+  int32_t attn_max_group;   /* largest supported q heads per kv head                   */
+} bi_config;
+
+/* Fills *out.  Returns BI_ERR_NULL if out is NULL. */
+int bi_get_config(bi_config* out);
+
+/* Static text for a status code ("BI_OK", "BI_ERR_SHAPE", ...). */
+const char* bi_status_string(int status);
+
+/* ------------------------------------------------------------------ RMSNorm
+ * [DN] batch-invariant RMSNorm: y = x * rsqrt(mean(x^2)) * weight, one row per
+ * workgroup, reduction order fixed per row whatever M is.  Readings: eps inside the
+ * square root; rsqrt is a correctly rounded sqrt followed by a correctly rounded
+ * divide; y = bf16((x * r) * gamma) multiplied in that order.
+ *
+ *   x      [M, D] row-major, row stride ldx elements, dtype x_dtype (BI_BF16|BI_F32)
+ *   gamma  [D] bf16
+ *   y      [M, D] row stride ldy, dtype y_dtype (BI_BF16|BI_F32)
+ *   eps    added to mean(x^2) in fp32
+ * Sum of squares: fixed fp32 tree, a function of D only:
+ *   T = min(256, ceil(D / w)) lanes (w = 8 for bf16 x, 4 for fp32 x); lane t owns the
+ *   w-element vectors t, t+T, ...; each lane adds its squares in ascending order
+ *   starting from +0; a wave64 butterfly with offsets 1,2,4,8,16,32; waves combined
+ *   as (w0 + w1) + (w2 + w3).  No fused multiply-add anywhere.
+ * Errors: NULL pointers (when M*D > 0) -> BI_ERR_NULL; M < 0, D < 1 with M > 0,
+ * ldx < D or ldy < D -> BI_ERR_SHAPE; bad dtype -> BI_ERR_DTYPE.
+ */
+int bi_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t D, int64_t ldx,
+               int64_t ldy, float eps, int x_dtype, int y_dtype, void* stream);
+
+/* ------------------------------------------------------------------ GEMM
+ * [DN] introduction (torch.mm of bf16 matrices) and batch-invariant matrix
+ * multiplication: data-parallel over output tiles, every dot product inside one
+ * workgroup, ONE kernel configuration for every shape, no split-K, no stream-K.
+ *
+ *   C[M, N] = A[M, K] . op(B)   fp32 accumulation
+ *   A     dtype a_dtype: BI_BF16, or BI_F32 (each fp32 value is split exactly into
+ *         three bf16 terms hi + mid + lo and the three products are accumulated in the
+ *         same fp32 accumulator: fp32-operand products at three times the work, the
+ *         upcast of [XV]); row stride lda
+ *   B     bf16; b_layout BI_B_NK: B is [N, K] (a Linear weight, C = A . B^T), row
+ *         stride ldb;  BI_B_KN: B is [K, N] (torch.mm orientation), row stride ldb
+ *   C     dtype c_dtype (BI_BF16: one RNE rounding of the fp32 sum; BI_F32), stride ldc
+ * Every output element is produced by the same sequence of matrix instructions over
+ * K in ascending order, whatever M is and wherever its row sits.
+ * Alignment: A and B 16-byte aligned; lda, ldb multiples of 8 elements (4 for fp32 A).
+ * Errors: BI_ERR_NULL, BI_ERR_SHAPE (negative sizes, K < 1 with M*N > 0, strides too
+ * small), BI_ERR_DTYPE, BI_ERR_ALIGN.
+ */
+int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
+            int64_t ldb, int64_t ldc, int b_layout, int a_dtype, int c_dtype, void* stream);
+
+/* Comparison variant, NOT batch-invariant ([DN], split-K matmul): same arguments as
+ * bi_gemm with bf16 A and B_NK, but K is split into a number of slices that grows as
+ * M shrinks (so that small batches fill the GPU), each slice's fp32 partial goes to
+ * `workspace` and a second kernel adds the slices.  The result of a row therefore
+ * depends on M.  workspace >= bi_gemm_splitk_workspace_bytes(M, N, K) bytes. */
+size_t bi_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                   int64_t lda, int64_t ldb, int64_t ldc, int c_dtype, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ attention
+ * [DN] batch-invariant attention: the K/V cache and page table are updated BEFORE
+ * the attention kernel runs, so that a query token reduces over the same keys in the
+ * same order whether it arrives in a prefill (0 cached tokens) or a decode (p cached
+ * tokens); a consistent block size; split-KV (FlashDecoding) for decode.  The split
+ * is one fixed chunk of 256 keys at absolute positions [256c, 256c + 256) that never
+ * depends on the batch or on the number of query tokens.
+ *
+ * Batch: `batch` sequences; sequence b has seq_lens[b] tokens after this call, of which
+ * the last q_b = query_start_loc[b+1] - query_start_loc[b] are new (0 <= q_b <=
+ * seq_lens[b]).  New token i of sequence b (row query_start_loc[b] + i of q/k_new/v_new/
+ * out) sits at absolute position p = seq_lens[b] - q_b + i.
+ *   q        [num_tokens, Hq, D] bf16, contiguous
+ *   k_new    [num_tokens, Hkv, D] bf16 (keys already rotated), contiguous
+ *   v_new    [num_tokens, Hkv, D] bf16, contiguous
+ *   k_cache  [num_pages, Hkv, page_size, D] bf16: page-major, then kv head, then slot
+ *   v_cache  [num_pages, Hkv, D, page_size] bf16: like k_cache but each page stores V
+ *            transposed (slot fastest), the operand order of the P.V matrix product
+ *   block_table [batch, max_pages_per_seq] int32: physical page of logical page j
+ *            (entries at j >= ceil(seq_lens[b] / page_size) are never read)
+ *   seq_lens [batch] int32, query_start_loc [batch + 1] int32 (device)
+ *   out      [num_tokens, Hq, D], dtype out_dtype (BI_BF16 | BI_F32)
+ *   scale    softmax scale (1/sqrt(D) for the standard reading)
+ * Step 1 writes k_new/v_new into their pages.  Step 2: token at position p of q head
+ * h (kv head h / (Hq/Hkv)) computes, for each chunk c <= p/256, the partial
+ * (m_c, l_c, o_c) over keys [256c, min(256c + 256, p + 1)) with fp32 scores, P kept
+ * as an exact bf16 hi + lo pair, fp32 accumulation; step 3 merges c = 0, 1, ... in
+ * that order: m' = max(m, m_c), a = 2^(m - m'), b = 2^(m_c - m'), l' = a l + b l_c,
+ * o' = a o + b o_c;  out = o / l.  Decode-sized calls compute the chunks in parallel
+ * and merge in a second kernel, longer calls walk the chunks in registers; both use
+ * the same arithmetic, so the bits never depend on which is used.
+ * Supported: D = 128, Hq/Hkv in {1, 2, 4, 8, 16}, page_size a multiple of 16 dividing
+ * 256.  max_seq_len is an upper bound of seq_lens (sizes the grid); every seq_len must
+ * be <= max_pages_per_seq * page_size.
+ * workspace >= bi_attention_workspace_bytes(num_tokens, Hq, D, max_seq_len).
+ * Errors: BI_ERR_NULL, BI_ERR_SHAPE, BI_ERR_UNSUPPORTED, BI_ERR_WORKSPACE,
+ * BI_ERR_ALIGN (16-byte alignment of every tensor).
+ */
+size_t bi_attention_workspace_bytes(int64_t num_tokens, int32_t num_q_heads, int32_t head_dim,
+                                    int64_t max_seq_len);
+int bi_attention(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                 void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                 const int32_t* query_start_loc, int32_t batch, int64_t num_tokens,
+                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                 int32_t max_pages_per_seq, int64_t max_seq_len, float scale, void* out,
+                 int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ log-softmax + argmax
+ * [GPU] greedy decoding and token probabilities from normalised scores; [DN]
+ * temperature 0 = always the most likely token; [SM] near ties decide the token.
+ * Per row of fp32 logits x: a = lowest index of the maximum (a NaN counts as the
+ * maximum, -0 == +0); m = x[a]; d_i = x_i - m; s = tree sum of EXP(d_i) with the fixed
+ * tree of bi_rmsnorm over 4-element vectors; logprob_i = d_i - LOG(s).  EXP is a
+ * Cody-Waite reduction with the degree-7 Taylor polynomial, LOG the atanh series to
+ * z^15, both with separately rounded fp32 operations, so the result is reproducible
+ * bit for bit on any IEEE machine.
+ *   logits   [M, V] fp32, row stride ld
+ *   logprobs [M, V] fp32, row stride ld, or NULL to skip
+ *   argmax   [M] int32
+ * Errors: BI_ERR_NULL, BI_ERR_SHAPE (V < 1 with M > 0, ld < V).
+ */
+int bi_logsoftmax_argmax(const float* logits, int64_t M, int64_t V, int64_t ld, float* logprobs,
+                         int32_t* argmax, void* stream);
+
+/* ------------------------------------------------------------------ pointwise glue
+ * [DN] section on making kernels batch-invariant: pointwise operations are invariant
+ * as long as every element runs the same code.  All of these compute in fp32 and
+ * round once to the output dtype.
+ *
+ * bi_embedding: out[t, :] = table[ids[t], :].  table [vocab, D] bf16, out [T, D] of
+ *   out_dtype (exact widening for BI_F32).  ids outside [0, vocab) produce zeros.
+ */
+int bi_embedding(const int32_t* ids, const void* table, void* out, int64_t T, int64_t D,
+                 int64_t vocab, int out_dtype, void* stream);
+
+/* bi_rope_qkv: splits a fused projection qkv [T, (Hq + 2 Hkv) * D] (row stride ldqkv,
+ *   dtype qkv_dtype) into q [T, Hq, D], k [T, Hkv, D], v [T, Hkv, D] (bf16, contiguous)
+ *   and rotates q and k by position ("rotate half": pairs (i, i + D/2), angle
+ *   pos * base^(-2i/D), angle, cos and sin evaluated in fp64 and rounded to fp32).
+ *   positions [T] int32. */
+int bi_rope_qkv(const void* qkv, int64_t ldqkv, int qkv_dtype, const int32_t* positions,
+                void* q, void* k, void* v, int64_t T, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, double base, void* stream);
+
+/* bi_swiglu: out[t, j] = silu(g) * u with g = gu[t, j], u = gu[t, F + j];
+ *   silu(g) = g / (1 + 2^(-g log2 e)) in fp32 with the hardware base-2 exponential
+ *   (graded against fp64 within tolerance, the same code for every element).
+ *   gu [T, 2F] bf16 (row stride ldgu, a multiple of 8), out [T, F] bf16. */
+int bi_swiglu(const void* gu, int64_t ldgu, void* out, int64_t T, int64_t F, void* stream);
+
+/* bi_residual_add: out = a + b elementwise over n elements, each operand of its own
+ *   dtype (BI_BF16 | BI_F32); out may alias a or b. */
+int bi_residual_add(const void* a, int a_dtype, const void* b, int b_dtype, void* out,
+                    int out_dtype, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BI_H_ */

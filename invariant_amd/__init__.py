@@ -1,0 +1,223 @@
+"""Python binding of libbi (batch-invariant LLM-forward reductions, MI355X / gfx950).
+
+Argument marshalling only: every function below turns torch tensors into device
+pointers, sizes and the current HIP stream, calls the C entry point of the same name
+(declared in include/bi.h) and raises BIError on a negative status.  torch provides
+device memory and streams; all arithmetic runs in the library's HIP kernels.  There is
+no fallback: if libbi.so is missing, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbi.so")
+
+BI_BF16, BI_F32 = 1, 2
+BI_B_KN, BI_B_NK = 0, 1
+
+_c = ctypes
+_P, _I64, _I32, _F32, _F64, _SZ = _c.c_void_p, _c.c_int64, _c.c_int32, _c.c_float, _c.c_double, _c.c_size_t
+
+_SIGS = {
+    "bi_get_config": (_c.c_int, [_P]),
+    "bi_status_string": (_c.c_char_p, [_c.c_int]),
+    "bi_rmsnorm": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _F32, _c.c_int, _c.c_int, _P]),
+    "bi_gemm": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _c.c_int, _c.c_int, _c.c_int, _P]),
+    "bi_gemm_splitk_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "bi_gemm_splitk": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _c.c_int, _P, _SZ, _P]),
+    "bi_attention_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I64]),
+    "bi_attention": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
+                                _I32, _I64, _F32, _P, _c.c_int, _P, _SZ, _P]),
+    "bi_logsoftmax_argmax": (_c.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "bi_embedding": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _c.c_int, _P]),
+    "bi_rope_qkv": (_c.c_int, [_P, _I64, _c.c_int, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F64, _P]),
+    "bi_swiglu": (_c.c_int, [_P, _I64, _P, _I64, _I64, _P]),
+    "bi_residual_add": (_c.c_int, [_P, _c.c_int, _P, _c.c_int, _P, _c.c_int, _I64, _P]),
+}
+EXPORTS = tuple(_SIGS)
+
+
+class BIConfig(ctypes.Structure):
+    _fields_ = [(n, _I32) for n in (
+        "version", "tree_max_lanes", "wave_size", "gemm_tile_m", "gemm_tile_n", "gemm_tile_k",
+        "gemm_mfma_m", "gemm_mfma_n", "gemm_mfma_k", "attn_chunk", "attn_max_group")]
+
+
+class BIError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} returned {status} ({status_string(status)})")
+
+
+_LIB = None
+
+
+def load(path: str | None = None):
+    """Open libbi.so (built by ``python -m invariant_amd.build``); raise if absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built: run `python -m invariant_amd.build` first")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGS.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().bi_status_string(int(status)).decode()
+
+
+def get_config() -> dict:
+    cfg = BIConfig()
+    st = load().bi_get_config(ctypes.byref(cfg))
+    if st:
+        raise BIError("bi_get_config", st)
+    return {n: getattr(cfg, n) for n, _ in BIConfig._fields_}
+
+
+def _check(fn, st):
+    if st != 0:
+        raise BIError(fn, st)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _code(dtype):
+    if dtype == torch.bfloat16:
+        return BI_BF16
+    if dtype == torch.float32:
+        return BI_F32
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def _ld(t):
+    if t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+# ----------------------------------------------------------------------------- calls
+def bi_rmsnorm(x, gamma, eps: float, out=None, out_dtype=torch.bfloat16):
+    M, D = x.shape
+    if out is None:
+        out = torch.empty((M, D), dtype=out_dtype, device=x.device)
+    _check("bi_rmsnorm", load().bi_rmsnorm(_ptr(x), _ptr(gamma), _ptr(out), M, D, _ld(x), _ld(out),
+                                            float(eps), _code(x.dtype), _code(out.dtype), _stream(x)))
+    return out
+
+
+def bi_gemm(a, b, out=None, b_layout: int = BI_B_NK, out_dtype=torch.bfloat16):
+    """C = a @ b^T for b_layout BI_B_NK (b is [N, K]), C = a @ b for BI_B_KN (b is [K, N])."""
+    M, K = a.shape
+    N = b.shape[0] if b_layout == BI_B_NK else b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check("bi_gemm", load().bi_gemm(_ptr(a), _ptr(b), _ptr(out), M, N, K, _ld(a), _ld(b), _ld(out),
+                                      b_layout, _code(a.dtype), _code(out.dtype), _stream(a)))
+    return out
+
+
+def bi_gemm_splitk(a, b, out=None, out_dtype=torch.bfloat16, workspace=None):
+    M, K = a.shape
+    N = b.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    need = load().bi_gemm_splitk_workspace_bytes(M, N, K)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    _check("bi_gemm_splitk", load().bi_gemm_splitk(
+        _ptr(a), _ptr(b), _ptr(out), M, N, K, _ld(a), _ld(b), _ld(out), _code(out.dtype),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(a)))
+    return out
+
+
+def bi_attention_workspace_bytes(num_tokens, num_q_heads, head_dim, max_seq_len) -> int:
+    return int(load().bi_attention_workspace_bytes(num_tokens, num_q_heads, head_dim, max_seq_len))
+
+
+def bi_attention(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start_loc,
+                 max_seq_len: int, scale: float, out=None, out_dtype=torch.bfloat16, workspace=None):
+    """q [T, Hq, D], k_new/v_new [T, Hkv, D] bf16; k_cache [P, Hkv, page, D];
+    v_cache [P, Hkv, D, page]; block_table [B, max_pages] int32; seq_lens [B] int32;
+    query_start_loc [B + 1] int32 (all on the device)."""
+    T, Hq, D = q.shape
+    Hkv = k_new.shape[1]
+    page = k_cache.shape[2]
+    B, max_pages = block_table.shape
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=out_dtype, device=q.device)
+    need = bi_attention_workspace_bytes(T, Hq, D, max_seq_len)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bi_attention", load().bi_attention(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(query_start_loc), B, T, Hq, Hkv, D, page, max_pages, int(max_seq_len),
+        float(scale), _ptr(out), _code(out.dtype), _ptr(workspace), wsz, _stream(q)))
+    return out
+
+
+def bi_logsoftmax_argmax(logits, logprobs=None, argmax=None, want_logprobs: bool = True):
+    M, V = logits.shape
+    if argmax is None:
+        argmax = torch.empty((M,), dtype=torch.int32, device=logits.device)
+    if logprobs is None and want_logprobs:
+        logprobs = torch.empty_like(logits)
+    _check("bi_logsoftmax_argmax", load().bi_logsoftmax_argmax(
+        _ptr(logits), M, V, _ld(logits), _ptr(logprobs), _ptr(argmax), _stream(logits)))
+    return logprobs, argmax
+
+
+def bi_embedding(ids, table, out=None, out_dtype=torch.bfloat16):
+    T = ids.shape[0]
+    V, D = table.shape
+    if out is None:
+        out = torch.empty((T, D), dtype=out_dtype, device=table.device)
+    _check("bi_embedding", load().bi_embedding(_ptr(ids), _ptr(table), _ptr(out), T, D, V,
+                                                _code(out.dtype), _stream(table)))
+    return out
+
+
+def bi_rope_qkv(qkv, positions, num_q_heads, num_kv_heads, head_dim, base=10000.0,
+                q=None, k=None, v=None):
+    T = qkv.shape[0]
+    dev = qkv.device
+    q = q if q is not None else torch.empty((T, num_q_heads, head_dim), dtype=torch.bfloat16, device=dev)
+    k = k if k is not None else torch.empty((T, num_kv_heads, head_dim), dtype=torch.bfloat16, device=dev)
+    v = v if v is not None else torch.empty((T, num_kv_heads, head_dim), dtype=torch.bfloat16, device=dev)
+    _check("bi_rope_qkv", load().bi_rope_qkv(_ptr(qkv), _ld(qkv), _code(qkv.dtype), _ptr(positions),
+                                              _ptr(q), _ptr(k), _ptr(v), T, num_q_heads,
+                                              num_kv_heads, head_dim, float(base), _stream(qkv)))
+    return q, k, v
+
+
+def bi_swiglu(gu, out=None):
+    T, F2 = gu.shape
+    F = F2 // 2
+    if out is None:
+        out = torch.empty((T, F), dtype=torch.bfloat16, device=gu.device)
+    _check("bi_swiglu", load().bi_swiglu(_ptr(gu), _ld(gu), _ptr(out), T, F, _stream(gu)))
+    return out
+
+
+def bi_residual_add(a, b, out=None, out_dtype=None):
+    if out is None:
+        out = torch.empty(a.shape, dtype=out_dtype or a.dtype, device=a.device)
+    _check("bi_residual_add", load().bi_residual_add(_ptr(a), _code(a.dtype), _ptr(b), _code(b.dtype),
+                                                      _ptr(out), _code(out.dtype), a.numel(), _stream(a)))
+    return out

@@ -1,0 +1,455 @@
+// bi_attention: causal GQA attention over a paged KV cache, batch- and
+// prefill/decode-invariant.
+//
+// "Defeating nondeterminism in LLM inference", section on batch-invariant attention:
+//  * the K/V cache and the page table are updated BEFORE the attention kernel, so a
+//    query token sees its keys laid out the same way however many tokens are in
+//    flight (step 1 below runs first, on the same stream);
+//  * the reduction order of a token may not depend on how many other tokens of its
+//    sequence are processed with it: here the keys of every query are split into
+//    chunks of 256 at ABSOLUTE positions [256c, 256c + 256), each chunk is reduced by
+//    one wave with one fixed instruction sequence (chunk_partial), and the chunk
+//    partials are merged in ascending c (merge_step).  Split-KV decode and the prefill
+//    walk call exactly these two routines, so a token's bits never depend on the path,
+//    the batch, its neighbours or the physical pages.
+//
+// Per chunk (one wave, 16 query columns, GQA: every column of a wave reads the same kv
+// head):
+//   S^T = K . Q^T   16 tiles of v_mfma_f32_16x16x32_bf16 (keys x columns), d-sum over
+//                   4 instructions in ascending order;
+//   t = S * (scale * log2 e), masked to -inf beyond the query position;
+//   m_c = max t;  P = 2^(t - m_c) (v_exp_f32);  l_c = sum P (per-lane ascending, then
+//   lanes (g0 + g1) + (g2 + g3));
+//   O^T = V^T . P^T with P split exactly-enough into bf16 hi + lo (two instructions per
+//   32-key slice, hi first), fp32 accumulation.  Rounding P itself to bf16 would cost
+//   tens of bf16 ulps in the output; hi + lo keeps 16 bits.
+// Merge (ascending c, first chunk copied):  m' = max(m, m_c); a = 2^(m - m');
+//   b = 2^(m_c - m');  l' = a l + b l_c;  o' = a o + b o_c;  out = o / l.
+//
+// Cache layout (chosen so every matrix operand is a 16-byte load):
+//   k_cache [page][kv head][slot][128]      v_cache [page][kv head][128][slot]
+#include "bi_common.h"
+
+namespace bi {
+namespace {
+
+constexpr int CHUNK = 256;
+constexpr int HD = 128;
+constexpr int SPLIT_MAX_TOKENS = 1024;  // calls with more tokens walk chunks in registers
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u16x8 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ floatx4 mfma16(u16x8 a, u16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int find_seq(const int32_t* qsl, int batch, int t) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (qsl[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct Seq {
+  const uint16_t* kc;   // k_cache base
+  const uint16_t* vc;   // v_cache base
+  const int32_t* bt;    // block-table row of the sequence
+  int ps;               // page size
+  int hkv, kvh;
+  int seq_len;
+};
+
+// One 256-key chunk for the wave's 16 columns.  pcol: absolute position of this lane's
+// column (-1: unused column).  Returns the partial in the MFMA output layout: lane l
+// holds column l % 16 and o[db][r] = d 16 db + 4 (l / 16) + r.
+__device__ __forceinline__ void chunk_partial(const Seq& sq, int c, const u16x8 (&qop)[4], int pcol,
+                                              float sl2, float& m_c, float& l_c, floatx4 (&o)[8]) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int kr0 = 8 * (i >> 2) + (i & 3);           // key of MFMA row i in the first tile of a pair
+  const int64_t page_k = static_cast<int64_t>(sq.ps) * HD;
+  const int c0 = c * CHUNK;
+
+  floatx4 s[8][2];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int key = c0 + 32 * u + kr0 + 4 * h2;
+      u16x8 kop[4];
+      if (key < sq.seq_len) {
+        const int phys = sq.bt[key / sq.ps];
+        const uint16_t* kp = sq.kc + (static_cast<int64_t>(phys) * sq.hkv + sq.kvh) * page_k +
+                             static_cast<int64_t>(key % sq.ps) * HD + 32 * g;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kop[t] = *reinterpret_cast<const u16x8*>(kp + 8 * t);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kop[t] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc = mfma16(kop[t], qop[t], acc);
+      s[u][h2] = acc;
+    }
+  }
+
+  // scale, causal mask, chunk maximum
+  float mx = -__builtin_huge_valf();
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kp = c0 + 32 * u + 8 * g + 4 * h2 + r;
+        const float t = s[u][h2][r] * sl2;
+        s[u][h2][r] = (kp <= pcol) ? t : -__builtin_huge_valf();
+        mx = fmaxf(mx, s[u][h2][r]);
+      }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  m_c = mx;
+
+  float lsum = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kp = c0 + 32 * u + 8 * g + 4 * h2 + r;
+        const float p = (kp <= pcol) ? exp2_hw(s[u][h2][r] - mx) : 0.f;
+        s[u][h2][r] = p;
+        lsum = lsum + p;
+      }
+  lsum = lsum + __shfl_xor(lsum, 16, 64);
+  lsum = lsum + __shfl_xor(lsum, 32, 64);
+  l_c = lsum;
+
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    u16x8 phi, plo;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = s[u][h2][r];
+        const uint16_t h = f32_to_bf16(p);
+        phi[4 * h2 + r] = h;
+        plo[4 * h2 + r] = f32_to_bf16(p - bf16_to_f32(h));
+      }
+    const int kp0 = c0 + 32 * u + 8 * g;               // first of this lane's 8 keys
+    const bool any = kp0 < sq.seq_len;
+    const int nvalid = sq.seq_len - kp0;                // keys kp0 + e valid for e < nvalid
+    const uint16_t* vbase = nullptr;
+    if (any) {
+      const int phys = sq.bt[kp0 / sq.ps];
+      vbase = sq.vc + (static_cast<int64_t>(phys) * sq.hkv + sq.kvh) * page_k + (kp0 % sq.ps);
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      u16x8 vop = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (any) {
+        vop = *reinterpret_cast<const u16x8*>(vbase + static_cast<int64_t>(16 * db + i) * sq.ps);
+        if (nvalid < 8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e >= nvalid) vop[e] = 0;
+        }
+      }
+      o[db] = mfma16(vop, phi, o[db]);
+      o[db] = mfma16(vop, plo, o[db]);
+    }
+  }
+}
+
+__device__ __forceinline__ void merge_step(float& m, float& l, float mc, float lc, float& a,
+                                           float& b) {
+  const float mn = fmaxf(m, mc);
+  a = exp2_hw(m - mn);
+  b = exp2_hw(mc - mn);
+  l = a * l + b * lc;
+  m = mn;
+}
+
+__device__ __forceinline__ float mix(float o, float oc, float a, float b) { return a * o + b * oc; }
+
+// Q operand of one column: q[token][head][32 g + 8 t .. + 7] for t = 0..3.
+__device__ __forceinline__ void load_q(const uint16_t* q, int64_t token, int head, int hq, bool ok,
+                                       u16x8 (&qop)[4]) {
+  const int g = (threadIdx.x & 63) >> 4;
+  if (ok) {
+    const uint16_t* p = q + (token * hq + head) * HD + 32 * g;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qop[t] = *reinterpret_cast<const u16x8*>(p + 8 * t);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qop[t] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+}
+
+// ---------------------------------------------------------------- step 1: cache write
+__global__ __launch_bounds__(256) void kv_write_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch,
+    int max_pages, int hkv, int ps) {
+  const int t = blockIdx.x;
+  const int b = find_seq(qsl, batch, t);
+  const int pos = seq_lens[b] - (qsl[b + 1] - qsl[b]) + (t - qsl[b]);
+  const int phys = bt[static_cast<int64_t>(b) * max_pages + pos / ps];
+  const int slot = pos % ps;
+  const int nvec = hkv * HD / 8;
+  for (int v = threadIdx.x; v < 2 * nvec; v += blockDim.x) {
+    const bool is_v = v >= nvec;
+    const int vv = is_v ? v - nvec : v;
+    const int head = vv / (HD / 8), d0 = (vv % (HD / 8)) * 8;
+    const int64_t src = (static_cast<int64_t>(t) * hkv + head) * HD + d0;
+    const int64_t pg = (static_cast<int64_t>(phys) * hkv + head) * ps * HD;
+    if (!is_v) {
+      *reinterpret_cast<u16x8*>(kc + pg + static_cast<int64_t>(slot) * HD + d0) =
+          *reinterpret_cast<const u16x8*>(k_new + src);
+    } else {
+      const u16x8 x = *reinterpret_cast<const u16x8*>(v_new + src);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vc[pg + static_cast<int64_t>(d0 + e) * ps + slot] = x[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- step 2a: split-KV chunks
+// grid.x = num_tokens * ceil(max_chunks / 4), grid.y = kv heads; wave w of a workgroup
+// takes chunk 4 * (blockIdx.x % cpb) + w of its token.
+__global__ __launch_bounds__(256) void attn_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch,
+    int max_pages, int hq, int hkv, int ps, int max_chunks, float sl2, float* __restrict__ ws_ml,
+    float* __restrict__ ws_o) {
+  const int cpb = (max_chunks + 3) / 4;
+  const int t = blockIdx.x / cpb;
+  const int c = 4 * (blockIdx.x % cpb) + (threadIdx.x >> 6);
+  const int kvh = blockIdx.y;
+  const int b = find_seq(qsl, batch, t);
+  const int L = seq_lens[b];
+  const int pos = L - (qsl[b + 1] - qsl[b]) + (t - qsl[b]);
+  if (c * CHUNK > pos) return;
+  const int G = hq / hkv;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const bool used = col < G;
+  u16x8 qop[4];
+  load_q(q, t, kvh * G + col, hq, used, qop);
+  Seq sq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, kvh, L};
+  float m_c, l_c;
+  floatx4 o[8];
+  chunk_partial(sq, c, qop, used ? pos : -1, sl2, m_c, l_c, o);
+  if (!used) return;
+  const int64_t slot = (static_cast<int64_t>(t) * hq + kvh * G + col) * max_chunks + c;
+  float* po = ws_o + slot * HD + 4 * (lane >> 4);
+#pragma unroll
+  for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4*>(po + 16 * db) = o[db];
+  if ((lane >> 4) == 0) {
+    ws_ml[2 * slot] = m_c;
+    ws_ml[2 * slot + 1] = l_c;
+  }
+}
+
+// ---------------------------------------------------------------- step 3a: merge chunks
+// one wave per (token, q head); lane holds d = 2 lane, 2 lane + 1.
+__global__ __launch_bounds__(256) void attn_combine_kernel(
+    const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch, int hq,
+    int max_chunks, int64_t n_rows, void* __restrict__ out, int out_f32) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  const int t = static_cast<int>(row / hq);
+  const int lane = threadIdx.x & 63;
+  const int b = find_seq(qsl, batch, t);
+  const int pos = seq_lens[b] - (qsl[b + 1] - qsl[b]) + (t - qsl[b]);
+  const int nc = pos / CHUNK + 1;
+  const float* ml = ws_ml + row * max_chunks * 2;
+  const float* po = ws_o + row * max_chunks * HD + 2 * lane;
+  float m = ml[0], l = ml[1];
+  float o0 = po[0], o1 = po[1];
+  for (int c = 1; c < nc; ++c) {
+    float a, bb;
+    merge_step(m, l, ml[2 * c], ml[2 * c + 1], a, bb);
+    o0 = mix(o0, po[c * HD], a, bb);
+    o1 = mix(o1, po[c * HD + 1], a, bb);
+  }
+  const float r0 = o0 / l, r1 = o1 / l;
+  if (out_f32) {
+    float* p = static_cast<float*>(out) + row * HD + 2 * lane;
+    p[0] = r0;
+    p[1] = r1;
+  } else {
+    uint16_t* p = static_cast<uint16_t*>(out) + row * HD + 2 * lane;
+    p[0] = f32_to_bf16(r0);
+    p[1] = f32_to_bf16(r1);
+  }
+}
+
+// ---------------------------------------------------------------- step 2b: prefill walk
+// Each wave owns 16 / G consecutive tokens (a block aligned to the global token index)
+// and one kv head, i.e. 16 columns; it walks chunks 0.. in order and merges in
+// registers.  A block that straddles two sequences is processed once per sequence with
+// the other sequence's columns switched off.
+__global__ __launch_bounds__(256) void attn_walk_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch,
+    int max_pages, int hq, int hkv, int ps, int64_t num_tokens, float sl2, void* __restrict__ out,
+    int out_f32) {
+  const int G = hq / hkv;
+  const int NT = 16 / G;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int kvh = blockIdx.y;
+  const int64_t tok0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * NT;
+  if (tok0 >= num_tokens) return;
+  const int64_t my_tok = tok0 + col / G;
+  const bool tok_ok = my_tok < num_tokens;
+  const int head = kvh * G + col % G;
+  const int my_b = tok_ok ? find_seq(qsl, batch, static_cast<int>(my_tok)) : -1;
+  const int my_pos = tok_ok ? seq_lens[my_b] - (qsl[my_b + 1] - qsl[my_b]) +
+                                  (static_cast<int>(my_tok) - qsl[my_b])
+                            : -1;
+  int b = find_seq(qsl, batch, static_cast<int>(tok0));
+  const int64_t tok_last = (tok0 + NT < num_tokens ? tok0 + NT : num_tokens) - 1;
+  const int b_last = find_seq(qsl, batch, static_cast<int>(tok_last));
+  for (; b <= b_last; ++b) {
+    if (qsl[b + 1] == qsl[b]) continue;
+    const bool mine = my_b == b;
+    const int pcol = mine ? my_pos : -1;
+    u16x8 qop[4];
+    load_q(q, mine ? my_tok : 0, head, hq, mine, qop);
+    const int L = seq_lens[b];
+    Seq sq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, kvh, L};
+    // highest position among this sequence's columns in the block
+    int pmax = pcol;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) pmax = max(pmax, __shfl_xor(pmax, off, 64));
+    float m = 0.f, l = 0.f;
+    floatx4 o[8];
+    for (int c = 0; c * CHUNK <= pmax; ++c) {
+      float m_c, l_c;
+      floatx4 oc[8];
+      chunk_partial(sq, c, qop, pcol, sl2, m_c, l_c, oc);
+      if (c * CHUNK > pcol) continue;
+      if (c == 0) {
+        m = m_c;
+        l = l_c;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db] = oc[db];
+      } else {
+        float a, bb;
+        merge_step(m, l, m_c, l_c, a, bb);
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[db][r] = mix(o[db][r], oc[db][r], a, bb);
+      }
+    }
+    if (!mine) continue;
+    const int64_t orow = my_tok * hq + head;
+    const int d0 = 4 * (lane >> 4);
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = o[db][r] / l;
+        const int64_t idx = orow * HD + 16 * db + d0 + r;
+        if (out_f32) static_cast<float*>(out)[idx] = v;
+        else static_cast<uint16_t*>(out)[idx] = f32_to_bf16(v);
+      }
+  }
+}
+
+int64_t chunks_for(int64_t max_seq_len) { return max_seq_len <= 0 ? 1 : (max_seq_len + CHUNK - 1) / CHUNK; }
+
+// (m, l) pairs first, padded so the partial outputs start on a 16-byte boundary.
+int64_t ml_floats(int64_t rows) { return (2 * rows + 3) / 4 * 4; }
+
+}  // namespace
+}  // namespace bi
+
+using namespace bi;
+
+extern "C" size_t bi_attention_workspace_bytes(int64_t num_tokens, int32_t num_q_heads,
+                                               int32_t head_dim, int64_t max_seq_len) {
+  if (num_tokens <= 0 || num_tokens > SPLIT_MAX_TOKENS || num_q_heads <= 0 || head_dim <= 0)
+    return 0;
+  const int64_t rows = num_tokens * num_q_heads * chunks_for(max_seq_len);
+  return static_cast<size_t>(ml_floats(rows) + rows * head_dim) * sizeof(float);
+}
+
+extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                            void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, int32_t batch, int64_t num_tokens,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t page_size, int32_t max_pages_per_seq, int64_t max_seq_len,
+                            float scale, void* out, int out_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (out_dtype != BI_BF16 && out_dtype != BI_F32) return BI_ERR_DTYPE;
+  if (batch < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+      page_size < 1 || max_pages_per_seq < 1 || max_seq_len < 0)
+    return BI_ERR_SHAPE;
+  if (head_dim != HD) return BI_ERR_UNSUPPORTED;
+  if (num_q_heads % num_kv_heads) return BI_ERR_SHAPE;
+  const int G = num_q_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return BI_ERR_UNSUPPORTED;
+  if (page_size % 16 || CHUNK % page_size) return BI_ERR_UNSUPPORTED;
+  if (max_seq_len > static_cast<int64_t>(max_pages_per_seq) * page_size || num_tokens > (1 << 30) ||
+      max_seq_len > (1 << 30))
+    return BI_ERR_SHAPE;
+  if (num_tokens == 0 || batch == 0) return BI_OK;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !block_table || !seq_lens ||
+      !query_start_loc || !out)
+    return BI_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(out))
+    return BI_ERR_ALIGN;
+  const bool split = num_tokens <= SPLIT_MAX_TOKENS;
+  const size_t need = bi_attention_workspace_bytes(num_tokens, num_q_heads, head_dim, max_seq_len);
+  if (split && (!workspace || workspace_bytes < need)) return BI_ERR_WORKSPACE;
+
+  hipStream_t s = as_stream(stream);
+  const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  kv_write_kernel<<<dim3(static_cast<unsigned>(num_tokens)), dim3(256), 0, s>>>(
+      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+      static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_table, seq_lens,
+      query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size);
+  const int of = out_dtype == BI_F32;
+  if (split) {
+    const int64_t maxc = chunks_for(max_seq_len);
+    float* ws_ml = static_cast<float*>(workspace);
+    float* ws_o = ws_ml + ml_floats(num_tokens * num_q_heads * maxc);
+    const int64_t cpb = (maxc + 3) / 4;
+    attn_split_kernel<<<dim3(static_cast<unsigned>(num_tokens * cpb), num_kv_heads), dim3(256), 0, s>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+        static_cast<const uint16_t*>(v_cache), block_table, seq_lens, query_start_loc, batch,
+        max_pages_per_seq, num_q_heads, num_kv_heads, page_size, static_cast<int>(maxc), sl2,
+        ws_ml, ws_o);
+    const int64_t rows = num_tokens * num_q_heads;
+    attn_combine_kernel<<<dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s>>>(
+        ws_ml, ws_o, seq_lens, query_start_loc, batch, num_q_heads, static_cast<int>(maxc), rows,
+        out, of);
+  } else {
+    const int NT = 16 / G;
+    const int64_t waves = (num_tokens + NT - 1) / NT;
+    attn_walk_kernel<<<dim3(static_cast<unsigned>((waves + 3) / 4), num_kv_heads), dim3(256), 0, s>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+        static_cast<const uint16_t*>(v_cache), block_table, seq_lens, query_start_loc, batch,
+        max_pages_per_seq, num_q_heads, num_kv_heads, page_size, num_tokens, sl2, out, of);
+  }
+  return launch_status();
+}

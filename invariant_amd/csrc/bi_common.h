@@ -1,0 +1,53 @@
+// Device helpers shared by the HIP kernels of libbi (gfx950, wave64).
+// Every file of the library is compiled with -ffp-contract=off: each fp32 multiply and
+// add is rounded on its own unless a kernel asks for a fused multiply-add by name.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bi.h"
+
+namespace bi {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even; a NaN keeps its sign and payload top bits and gets the
+// quiet bit.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float wave_xor(float v, int off) { return __shfl_xor(v, off, kWave); }
+
+// Butterfly over the 64 lanes with offsets 1, 2, 4, 8, 16, 32.  fp32 addition is
+// commutative, so every lane ends with the index-order pairwise tree sum.
+__device__ __forceinline__ float wave_tree_sum(float v) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) v = v + wave_xor(v, off);
+  return v;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
+}  // namespace bi

@@ -1,0 +1,296 @@
+// bi_gemm: batch-invariant bf16 GEMM on the gfx950 matrix cores.
+//
+// "Defeating nondeterminism in LLM inference", section on batch-invariant matrix
+// multiplication: parallelise over output tiles so every dot product stays inside one
+// workgroup; do not split K (split-K changes the order with the batch) and do not use
+// stream-K (it even loses batch-position invariance); compile ONE kernel configuration
+// and use it for every shape.  Here that configuration is:
+//   workgroup tile 128 x 128, K step 64, 4 waves (2 x 2), each wave 64 x 64 made of
+//   2 x 2 v_mfma_f32_32x32x16_bf16, fp32 accumulators starting at +0, K walked in
+//   ascending 16-wide steps from 0 to K.  Rows past M and K past K read as zeros and
+//   are never stored.
+// Output element (i, j) is therefore the result of the same instruction sequence for
+// every M and every position of row i inside its tile.
+//
+// A may be fp32 ("FP32 upcast" of the cross-vendor mismatch abstract): each value is
+// split exactly into bf16 hi + mid + lo (truncations, so hi + mid + lo == a for normal
+// numbers) and the three products are accumulated into the same fp32 accumulator in
+// the order hi, mid, lo for every 16-wide K step.
+#include "bi_common.h"
+
+namespace bi {
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int kThreads = 256;
+constexpr int LDS_LD = BK + 8;  // bf16 per LDS row: 144 bytes keeps 16-byte reads conflict-free
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u16x8 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint16_t bf16_trunc(float f) {
+  return static_cast<uint16_t>(__float_as_uint(f) >> 16);
+}
+
+// Global -> register staging of one K step.  A tile: 128 rows x 64 k; each thread owns
+// rows (tid / 8) + 32 i and the 8-wide k vector tid % 8.
+template <bool AF32>
+struct Stage {
+  u16x8 a[AF32 ? 3 : 1][4];
+  u16x8 b[4];
+};
+
+__device__ __forceinline__ u16x8 load_bf16x8(const uint16_t* p, int64_t k, int64_t K, bool row_ok) {
+  u16x8 r = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (!row_ok) return r;
+  if (k + 8 <= K) return *reinterpret_cast<const u16x8*>(p + k);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (k + e < K) r[e] = p[k + e];
+  return r;
+}
+
+__device__ __forceinline__ void split3(const float* p, int64_t k, int64_t K, bool row_ok,
+                                       u16x8& hi, u16x8& mid, u16x8& lo) {
+  float v[8];
+  if (row_ok && k + 8 <= K) {
+    floatx4 q0 = *reinterpret_cast<const floatx4*>(p + k);
+    floatx4 q1 = *reinterpret_cast<const floatx4*>(p + k + 4);
+    v[0] = q0[0]; v[1] = q0[1]; v[2] = q0[2]; v[3] = q0[3];
+    v[4] = q1[0]; v[5] = q1[1]; v[6] = q1[2]; v[7] = q1[3];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (row_ok && k + e < K) ? p[k + e] : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint16_t h = bf16_trunc(v[e]);
+    const float r1 = v[e] - bf16_to_f32(h);
+    const uint16_t m = bf16_trunc(r1);
+    const float r2 = r1 - bf16_to_f32(m);
+    hi[e] = h;
+    mid[e] = m;
+    lo[e] = bf16_trunc(r2);
+  }
+}
+
+template <bool AF32>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(
+    const void* __restrict__ Ap, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
+    int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int tiles_m, int tiles_n,
+    int k_begin, int k_end, int64_t split_stride) {
+  constexpr int NA = AF32 ? 3 : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][NA][BM * LDS_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDS_LD];
+
+  // Tile order: consecutive workgroup ids land on different XCDs (round robin over 8),
+  // so regroup them to give each XCD a contiguous band of tiles, then walk tiles
+  // column-major inside bands of 8 tile-rows to share A rows and B columns in L2.
+  const int nwg = tiles_m * tiles_n;
+  int id = blockIdx.x;
+  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+  const int group = 8;
+  const int per_group = group * tiles_n;
+  const int g = id / per_group;
+  const int first_m = g * group;
+  const int gm = min(tiles_m - first_m, group);
+  const int tm = first_m + (id % per_group) % gm;
+  const int tn = (id % per_group) / gm;
+
+  C = static_cast<char*>(C) + static_cast<int64_t>(blockIdx.y) * split_stride;
+  const int kb = k_begin + static_cast<int>(blockIdx.y) * (k_end - k_begin);
+  const int ke = min(K, kb + (k_end - k_begin));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // staging coordinates
+  const int st_row = tid >> 3;      // 0..31, +32 i
+  const int st_k = (tid & 7) * 8;   // 0..56
+  const uint16_t* Ab = static_cast<const uint16_t*>(Ap);
+  const float* Af = static_cast<const float*>(Ap);
+  bool a_ok[4], b_ok[4];
+  int64_t a_off[4], b_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = tm * BM + st_row + 32 * i;
+    const int rb = tn * BN + st_row + 32 * i;
+    a_ok[i] = ra < M;
+    b_ok[i] = rb < N;
+    a_off[i] = static_cast<int64_t>(a_ok[i] ? ra : 0) * lda;
+    b_off[i] = static_cast<int64_t>(b_ok[i] ? rb : 0) * ldb;
+  }
+
+  auto load_stage = [&](Stage<AF32>& s, int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (AF32) split3(Af + a_off[i], k0 + st_k, ke, a_ok[i], s.a[0][i], s.a[NA > 1 ? 1 : 0][i], s.a[NA - 1][i]);
+      else s.a[0][i] = load_bf16x8(Ab + a_off[i], k0 + st_k, ke, a_ok[i]);
+      s.b[i] = load_bf16x8(B + b_off[i], k0 + st_k, ke, b_ok[i]);
+    }
+  };
+  auto store_stage = [&](const Stage<AF32>& s, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = (st_row + 32 * i) * LDS_LD + st_k;
+#pragma unroll
+      for (int t = 0; t < NA; ++t) *reinterpret_cast<u16x8*>(&sA[buf][t][o]) = s.a[t][i];
+      *reinterpret_cast<u16x8*>(&sB[buf][o]) = s.b[i];
+    }
+  };
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+  Stage<AF32> st;
+  if (nk > 0) {
+    load_stage(st, kb);
+    store_stage(st, 0);
+  }
+  __syncthreads();
+
+  // operand read coordinates: lane holds row (lane % 32) and k (lane / 32) * 8 .. +7
+  const int orow = lane & 31;
+  const int okk = (lane >> 5) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_stage(st, kb + (kt + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 bv[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bv[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(
+            &sB[cur][(wn * 64 + j * 32 + orow) * LDS_LD + kk + okk]));
+#pragma unroll
+      for (int t = 0; t < NA; ++t) {
+        bf16x8 av[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          av[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(
+              &sA[cur][t][(wm * 64 + i * 32 + orow) * LDS_LD + kk + okk]));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) store_stage(st, cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: register r of block (i, j) is row 8(r/4) + 4(lane/32) + r%4, column lane%32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = tn * BN + wn * 64 + j * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = tm * BM + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row >= M) continue;
+        if (c_f32)
+          static_cast<float*>(C)[static_cast<int64_t>(row) * ldc + col] = acc[i][j][r];
+        else
+          static_cast<uint16_t*>(C)[static_cast<int64_t>(row) * ldc + col] = f32_to_bf16(acc[i][j][r]);
+      }
+    }
+}
+
+// Fixed-order sum of the split-K partials (comparison variant only).
+__global__ void splitk_reduce_kernel(const float* __restrict__ ws, void* __restrict__ C, int M,
+                                     int N, int64_t ldc, int c_f32, int splits) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(M) * N) return;
+  const int row = static_cast<int>(idx / N), col = static_cast<int>(idx % N);
+  float s = 0.f;
+  for (int k = 0; k < splits; ++k) s = s + ws[static_cast<int64_t>(k) * M * N + idx];
+  if (c_f32) static_cast<float*>(C)[row * ldc + col] = s;
+  else static_cast<uint16_t*>(C)[row * ldc + col] = f32_to_bf16(s);
+}
+
+int splitk_count(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t nk = (K + BK - 1) / BK;
+  int64_t s = (2 * 256) / (tiles > 0 ? tiles : 1);
+  if (s < 1) s = 1;
+  if (s > 16) s = 16;
+  if (s > nk) s = nk;
+  return static_cast<int>(s);
+}
+
+}  // namespace
+}  // namespace bi
+
+using namespace bi;
+
+extern "C" int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldb, int64_t ldc, int b_layout, int a_dtype,
+                       int c_dtype, void* stream) {
+  if ((a_dtype != BI_BF16 && a_dtype != BI_F32) || (c_dtype != BI_BF16 && c_dtype != BI_F32) ||
+      (b_layout != BI_B_NK && b_layout != BI_B_KN))
+    return BI_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0) return BI_ERR_SHAPE;
+  if (M == 0 || N == 0) return BI_OK;
+  if (K < 1 || lda < K || ldc < N || M > (1 << 30) || N > (1 << 30) || K > (1 << 30))
+    return BI_ERR_SHAPE;
+  if (b_layout == BI_B_NK ? ldb < K : ldb < N) return BI_ERR_SHAPE;
+  if (!A || !B || !C) return BI_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || (lda % (a_dtype == BI_F32 ? 4 : 8)) || (ldb % 8))
+    return BI_ERR_ALIGN;
+  if (b_layout == BI_B_KN) return BI_ERR_UNSUPPORTED;
+  const int tm = static_cast<int>((M + BM - 1) / BM), tn = static_cast<int>((N + BN - 1) / BN);
+  const int64_t nwg = static_cast<int64_t>(tm) * tn;
+  if (nwg > 0x7fffffffLL) return BI_ERR_SHAPE;
+  hipStream_t s = as_stream(stream);
+  const int cf = c_dtype == BI_F32;
+  if (a_dtype == BI_F32)
+    gemm_kernel<true><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
+        A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
+        0, int(K), 0);
+  else
+    gemm_kernel<false><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
+        A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
+        0, int(K), 0);
+  return launch_status();
+}
+
+extern "C" size_t bi_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return static_cast<size_t>(splitk_count(M, N, K)) * M * N * sizeof(float);
+}
+
+extern "C" int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                              int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int c_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (c_dtype != BI_BF16 && c_dtype != BI_F32) return BI_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0) return BI_ERR_SHAPE;
+  if (M == 0 || N == 0) return BI_OK;
+  if (K < 1 || lda < K || ldb < K || ldc < N || M > (1 << 30) || N > (1 << 30) || K > (1 << 30))
+    return BI_ERR_SHAPE;
+  if (!A || !B || !C) return BI_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || (lda % 8) || (ldb % 8)) return BI_ERR_ALIGN;
+  const int splits = splitk_count(M, N, K);
+  if (!workspace || workspace_bytes < bi_gemm_splitk_workspace_bytes(M, N, K))
+    return BI_ERR_WORKSPACE;
+  const int tm = static_cast<int>((M + BM - 1) / BM), tn = static_cast<int>((N + BN - 1) / BN);
+  const int64_t nk = (K + BK - 1) / BK;
+  const int per = static_cast<int>((nk + splits - 1) / splits) * BK;
+  hipStream_t s = as_stream(stream);
+  gemm_kernel<false><<<dim3(static_cast<unsigned>(tm * tn), splits), dim3(kThreads), 0, s>>>(
+      A, static_cast<const uint16_t*>(B), workspace, int(M), int(N), int(K), lda, ldb, N, 1, tm,
+      tn, 0, per, static_cast<int64_t>(M) * N * sizeof(float));
+  const int64_t total = M * N;
+  splitk_reduce_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(
+      static_cast<const float*>(workspace), C, int(M), int(N), ldc, c_dtype == BI_F32, splits);
+  return launch_status();
+}

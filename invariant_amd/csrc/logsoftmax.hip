@@ -1,0 +1,202 @@
+// bi_logsoftmax_argmax: greedy-decoding head, one row per workgroup.
+//
+// Greedy decoding takes the most likely token ("Does the same LLM give different
+// outputs on different GPUs? Why?", experiment set-up; "Defeating nondeterminism in
+// LLM inference", introduction: temperature 0); token probabilities come from the
+// normalised scores.  A near tie decides the token ("Same model, same input,
+// different answer", sampling), so the argmax rule is exact: lowest index of the
+// maximum, a NaN counting as the maximum and -0 == +0.  That is a selection under a
+// total order, so any combination order gives the same index.
+//
+// The sum of exponentials uses the fixed tree of bi_rmsnorm over 4-element vectors
+// (T = min(256, ceil(V/4)) lanes, ascending per lane, wave64 butterfly 1..32, waves
+// (w0 + w1) + (w2 + w3)).  EXP and LOG are evaluated with separately rounded fp32
+// operations from published methods, so every bit is reproducible:
+//   EXP(d), d <= 0 or NaN: Cody & Waite (1980) reduction d = k ln2 + r with ln2 split
+//     into a 16-significant-bit head (k * head is exact) and a rounded tail; exp(r) by
+//     the Taylor polynomial of degree 7 (coefficients 1/n! rounded to binary32) in
+//     Horner form; result p * 2^k from exponent bits; k < -125 gives +0.
+//   LOG(s), s >= 1: s = 2^e f, f moved into [sqrt(1/2), sqrt(2)); log f =
+//     z (2 + 2/3 z^2 + ... + 2/15 z^14), z = (f - 1)/(f + 1) (J.-M. Muller, Elementary
+//     Functions, range reduction and the atanh series); e ln2 added head then tail.
+// Constants (binary32 bit patterns): 1/ln2 = 0x3fb8aa3b; ln2 head = 0x3f317200 (ln 2
+// rounded to 16 significant bits), ln2 tail = 0x35bfbe8e; sqrt 2 = 0x3fb504f3;
+// 1/n! for n = 0..7 and 2/(2i+1) for i = 0..7 rounded to nearest.
+#include "bi_common.h"
+
+namespace bi {
+
+__device__ __forceinline__ float f32c(uint32_t b) { return __uint_as_float(b); }
+
+__device__ float exp_cw(float d) {
+  if (d != d) return d;
+  const float t = d * f32c(0x3fb8aa3bu);
+  const float k = __builtin_rintf(t);
+  if (!(k >= -125.0f)) return 0.0f;
+  float r = d - k * f32c(0x3f317200u);
+  r = r - k * f32c(0x35bfbe8eu);
+  float p = f32c(0x39500d01u);       // 1/5040
+  p = p * r + f32c(0x3ab60b61u);     // 1/720
+  p = p * r + f32c(0x3c088889u);     // 1/120
+  p = p * r + f32c(0x3d2aaaabu);     // 1/24
+  p = p * r + f32c(0x3e2aaaabu);     // 1/6
+  p = p * r + f32c(0x3f000000u);     // 1/2
+  p = p * r + f32c(0x3f800000u);     // 1
+  p = p * r + f32c(0x3f800000u);     // 1
+  const int ki = static_cast<int>(k);
+  return p * __int_as_float((ki + 127) << 23);
+}
+
+__device__ float log_at(float s) {
+  if (!__builtin_isfinite(s)) return s;
+  const uint32_t b = __float_as_uint(s);
+  int e = static_cast<int>(b >> 23) - 127;
+  float f = __uint_as_float((b & 0x7fffffu) | 0x3f800000u);
+  if (f > f32c(0x3fb504f3u)) {
+    f = f * 0.5f;
+    e += 1;
+  }
+  const float z = (f - 1.0f) / (f + 1.0f);
+  const float w = z * z;
+  float q = f32c(0x3e088889u);       // 2/15
+  q = q * w + f32c(0x3e1d89d9u);     // 2/13
+  q = q * w + f32c(0x3e3a2e8cu);     // 2/11
+  q = q * w + f32c(0x3e638e39u);     // 2/9
+  q = q * w + f32c(0x3e924925u);     // 2/7
+  q = q * w + f32c(0x3ecccccdu);     // 2/5
+  q = q * w + f32c(0x3f2aaaabu);     // 2/3
+  q = q * w + f32c(0x40000000u);     // 2
+  const float lf = z * q;
+  const float ef = static_cast<float>(e);
+  return ef * f32c(0x3f317200u) + (ef * f32c(0x35bfbe8eu) + lf);
+}
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// (value, index) selection: larger value wins, NaN beats numbers, equal -> lower index.
+__device__ __forceinline__ void pick(float& bv, int& bi, float v, int i) {
+  const bool bn = bv != bv, vn = v != v;
+  bool take;
+  if (bn && vn) take = i < bi;
+  else if (vn) take = true;
+  else if (bn) take = false;
+  else if (v > bv) take = true;
+  else if (bv > v) take = false;
+  else take = i < bi;
+  if (take) {
+    bv = v;
+    bi = i;
+  }
+}
+
+__device__ __forceinline__ void load4(const float* row, int v, int V, bool vec, float (&e)[4]) {
+  const float* p = row + static_cast<int64_t>(v) * 4;
+  if (vec && v * 4 + 4 <= V) {
+    floatx4 q = *reinterpret_cast<const floatx4*>(p);
+    e[0] = q[0]; e[1] = q[1]; e[2] = q[2]; e[3] = q[3];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = (v * 4 + i < V) ? p[i] : 0.f;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void logsoftmax_argmax_kernel(
+    const float* __restrict__ logits, int V, int64_t ld, float* __restrict__ logprobs,
+    int32_t* __restrict__ argmax, int vec_in, int vec_out) {
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nvec = (V + 3) / 4;
+  const int T = nvec < kThreads ? nvec : kThreads;
+  const float* x = logits + row * ld;
+  __shared__ float sv[kThreads / kWave];
+  __shared__ int si[kThreads / kWave];
+  __shared__ float ss[kThreads / kWave];
+
+  // pass 1: maximum and lowest index attaining it
+  float bv = -__builtin_huge_valf();
+  int bidx = 0x7fffffff;
+  if (tid < T) {
+    for (int v = tid; v < nvec; v += T) {
+      float e[4];
+      load4(x, v, V, vec_in, e);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (v * 4 + i < V) pick(bv, bidx, e[i], v * 4 + i);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float ov = __shfl_xor(bv, off, kWave);
+    const int oi = __shfl_xor(bidx, off, kWave);
+    pick(bv, bidx, ov, oi);
+  }
+  if ((tid & (kWave - 1)) == 0) {
+    sv[tid / kWave] = bv;
+    si[tid / kWave] = bidx;
+  }
+  __syncthreads();
+  float mv = sv[0];
+  int mi = si[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / kWave; ++w) pick(mv, mi, sv[w], si[w]);
+  const float m = mv;
+
+  // pass 2: s = tree sum of EXP(x - m)
+  float acc = 0.f;
+  if (tid < T) {
+    for (int v = tid; v < nvec; v += T) {
+      float e[4];
+      load4(x, v, V, vec_in, e);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (v * 4 + i < V) acc = acc + exp_cw(e[i] - m);
+    }
+  }
+  const float wsum = wave_tree_sum(acc);
+  if ((tid & (kWave - 1)) == 0) ss[tid / kWave] = wsum;
+  __syncthreads();
+  const float s = (ss[0] + ss[1]) + (ss[2] + ss[3]);
+  const float L = log_at(s);
+
+  if (tid == 0) argmax[row] = mi;
+  if (logprobs == nullptr || tid >= T) return;
+  float* out = logprobs + row * ld;
+  for (int v = tid; v < nvec; v += T) {
+    float e[4];
+    load4(x, v, V, vec_in, e);
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (e[i] - m) - L;
+    if (vec_out && v * 4 + 4 <= V) {
+      floatx4 q;
+      q[0] = o[0]; q[1] = o[1]; q[2] = o[2]; q[3] = o[3];
+      *reinterpret_cast<floatx4*>(out + static_cast<int64_t>(v) * 4) = q;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (v * 4 + i < V) out[static_cast<int64_t>(v) * 4 + i] = o[i];
+    }
+  }
+}
+
+}  // namespace
+}  // namespace bi
+
+using namespace bi;
+
+extern "C" int bi_logsoftmax_argmax(const float* logits, int64_t M, int64_t V, int64_t ld,
+                                    float* logprobs, int32_t* argmax, void* stream) {
+  if (M < 0 || V < 0) return BI_ERR_SHAPE;
+  if (M == 0) return BI_OK;
+  if (V < 1 || ld < V || V > 0x7ffffff0LL || M > 0x7fffffffLL) return BI_ERR_SHAPE;
+  if (!logits || !argmax) return BI_ERR_NULL;
+  // 16-byte vector accesses where rows allow them; element accesses otherwise (same math)
+  const int vec_in = aligned16(logits) && (ld % 4) == 0;
+  const int vec_out = logprobs && aligned16(logprobs) && (ld % 4) == 0;
+  logsoftmax_argmax_kernel<<<dim3(static_cast<unsigned>(M)), dim3(kThreads), 0,
+                             as_stream(stream)>>>(logits, static_cast<int>(V), ld, logprobs,
+                                                  argmax, vec_in, vec_out);
+  return launch_status();
+}

@@ -1,0 +1,191 @@
+// bi_rmsnorm: one row per workgroup, fixed fp32 reduction tree (a function of D only).
+//
+// "Defeating nondeterminism in LLM inference", section on batch-invariant RMSNorm:
+// y = x * rsqrt(mean(x^2)) * weight with a reduction order per row that no batch size
+// can change.  Each row is reduced entirely inside one workgroup of 256 lanes; nothing
+// is split across workgroups and there are no atomics.
+//
+// Tree (w = 8 bf16 or 4 fp32 elements per 16-byte vector, T = min(256, ceil(D/w))):
+//   lane t owns vectors t, t+T, ...; adds its squares in ascending order from +0;
+//   wave64 butterfly with offsets 1..32; waves combined as (w0 + w1) + (w2 + w3).
+// Lanes t >= T hold +0.  Because every partial sum is >= +0, adding those +0 lanes or
+// waves leaves each partial unchanged bit for bit, so one 256-lane shape serves every D.
+#include "bi_common.h"
+
+namespace bi {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <bool F32>
+struct Vec;
+template <>
+struct Vec<false> {  // 8 bf16
+  static constexpr int W = 8;
+  __device__ static void load(const void* row, int v, int D, bool vec_ok, float (&e)[8]) {
+    const uint16_t* p = static_cast<const uint16_t*>(row) + static_cast<int64_t>(v) * 8;
+    if (vec_ok && v * 8 + 8 <= D) {
+      u16x8 q = *reinterpret_cast<const u16x8*>(p);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = bf16_to_f32(q[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = (v * 8 + i < D) ? bf16_to_f32(p[i]) : 0.f;
+    }
+  }
+};
+template <>
+struct Vec<true> {  // 4 fp32
+  static constexpr int W = 4;
+  __device__ static void load(const void* row, int v, int D, bool vec_ok, float (&e)[4]) {
+    const float* p = static_cast<const float*>(row) + static_cast<int64_t>(v) * 4;
+    if (vec_ok && v * 4 + 4 <= D) {
+      floatx4 q = *reinterpret_cast<const floatx4*>(p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = q[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = (v * 4 + i < D) ? p[i] : 0.f;
+    }
+  }
+};
+
+template <bool YF32, int W>
+__device__ __forceinline__ void store_out(void* yrow, int v, int D, bool vec_ok, const float (&o)[W]) {
+  if (YF32) {
+    float* p = static_cast<float*>(yrow) + static_cast<int64_t>(v) * W;
+    if (vec_ok && v * W + W <= D && W == 4) {
+      floatx4 q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = o[i];
+      *reinterpret_cast<floatx4*>(p) = q;
+    } else {
+#pragma unroll
+      for (int i = 0; i < W; ++i)
+        if (v * W + i < D) p[i] = o[i];
+    }
+  } else {
+    uint16_t* p = static_cast<uint16_t*>(yrow) + static_cast<int64_t>(v) * W;
+    if (vec_ok && v * W + W <= D && W == 8) {
+      u16x8 q;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = f32_to_bf16(o[i]);
+      *reinterpret_cast<u16x8*>(p) = q;
+    } else {
+#pragma unroll
+      for (int i = 0; i < W; ++i)
+        if (v * W + i < D) p[i] = f32_to_bf16(o[i]);
+    }
+  }
+}
+
+// NV vectors per lane stay in registers between the two passes; longer rows re-read.
+template <bool XF32, bool YF32>
+__global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restrict__ x,
+                                                           const uint16_t* __restrict__ gamma,
+                                                           void* __restrict__ y, int D,
+                                                           int64_t ldx, int64_t ldy, float eps,
+                                                           int vec_x, int vec_y, int vec_g) {
+  using V = Vec<XF32>;
+  constexpr int W = V::W;
+  constexpr int NV = XF32 ? 8 : 4;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nvec = (D + W - 1) / W;
+  const int T = nvec < kThreads ? nvec : kThreads;
+  const char* xrow = static_cast<const char*>(x) + row * ldx * (XF32 ? 4 : 2);
+  char* yrow = static_cast<char*>(y) + row * ldy * (YF32 ? 4 : 2);
+
+  float cache[NV][W];
+  float acc = 0.f;
+  if (tid < T) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int v = tid + j * T;
+      if (v < nvec) {
+        V::load(xrow, v, D, vec_x, cache[j]);
+#pragma unroll
+        for (int i = 0; i < W; ++i)
+          if (v * W + i < D) acc = acc + cache[j][i] * cache[j][i];
+      }
+    }
+    for (int v = tid + NV * T; v < nvec; v += T) {
+      float e[W];
+      V::load(xrow, v, D, vec_x, e);
+#pragma unroll
+      for (int i = 0; i < W; ++i)
+        if (v * W + i < D) acc = acc + e[i] * e[i];
+    }
+  }
+
+  __shared__ float wave_part[kThreads / kWave];
+  const float wsum = wave_tree_sum(acc);
+  if ((tid & (kWave - 1)) == 0) wave_part[tid / kWave] = wsum;
+  __syncthreads();
+  const float ssum = (wave_part[0] + wave_part[1]) + (wave_part[2] + wave_part[3]);
+  const float mean = ssum / static_cast<float>(D);
+  const float var = mean + eps;
+  const float r = 1.0f / __builtin_sqrtf(var);
+
+  if (tid >= T) return;
+  for (int j = 0, v = tid; v < nvec; ++j, v += T) {
+    float e[W];
+    if (j < NV) {
+#pragma unroll
+      for (int jj = 0; jj < NV; ++jj)
+        if (jj == j) {
+#pragma unroll
+          for (int i = 0; i < W; ++i) e[i] = cache[jj][i];
+        }
+    } else {
+      V::load(xrow, v, D, vec_x, e);
+    }
+    float g[W];
+    const uint16_t* gp = gamma + static_cast<int64_t>(v) * W;
+    if (vec_g && v * W + W <= D && W == 8) {
+      u16x8 q = *reinterpret_cast<const u16x8*>(gp);
+#pragma unroll
+      for (int i = 0; i < W; ++i) g[i] = bf16_to_f32(q[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < W; ++i) g[i] = (v * W + i < D) ? bf16_to_f32(gp[i]) : 0.f;
+    }
+    float o[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) o[i] = (e[i] * r) * g[i];
+    store_out<YF32, W>(yrow, v, D, vec_y, o);
+  }
+}
+
+}  // namespace
+}  // namespace bi
+
+using namespace bi;
+
+extern "C" int bi_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t D,
+                          int64_t ldx, int64_t ldy, float eps, int x_dtype, int y_dtype,
+                          void* stream) {
+  if ((x_dtype != BI_BF16 && x_dtype != BI_F32) || (y_dtype != BI_BF16 && y_dtype != BI_F32))
+    return BI_ERR_DTYPE;
+  if (M < 0 || D < 0) return BI_ERR_SHAPE;
+  if (M == 0) return BI_OK;
+  if (D < 1 || ldx < D || ldy < D || D > (int64_t(1) << 24) || M > 0x7fffffffLL)
+    return BI_ERR_SHAPE;
+  if (!x || !gamma || !y) return BI_ERR_NULL;
+  const bool xf = x_dtype == BI_F32, yf = y_dtype == BI_F32;
+  const int wx = xf ? 4 : 8;
+  const int vec_x = aligned16(x) && (ldx % wx == 0);
+  const int vec_y = aligned16(y) && (ldy % (yf ? 4 : 8) == 0) && (yf ? wx == 4 : wx == 8);
+  const int vec_g = aligned16(gamma);
+  dim3 grid(static_cast<unsigned>(M)), block(kThreads);
+  hipStream_t s = as_stream(stream);
+  if (!xf && !yf)
+    rmsnorm_kernel<false, false><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, vec_y, vec_g);
+  else if (!xf && yf)
+    rmsnorm_kernel<false, true><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, 0, vec_g);
+  else if (xf && !yf)
+    rmsnorm_kernel<true, false><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, 0, vec_g);
+  else
+    rmsnorm_kernel<true, true><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, vec_y, vec_g);
+  return launch_status();
+}

@@ -52,6 +52,6 @@ def attention_case_f64(case, which=None) -> list:
     for b, (L, ql) in enumerate(zip(case["seq_lens"], case["q_lens"])):
         idx = list(range(ql)) if which is None else list(which.get(b, []))
         pos = [L - ql + i for i in idx]
-        qb = case["q"][b][L - ql:][idx] if idx else case["q"][b][:0]
+        qb = case["q"][b][idx] if idx else case["q"][b][:0]
         outs.append(attention_rows_f64(qb, case["k"][b][:L], case["v"][b][:L], pos))
     return outs

@@ -105,18 +105,24 @@ def paged_layout(seq_lens, page_size: int, cfg: int, tensor: int, extra_pages: i
 
 def attention_case(seq_lens, q_lens, n_q_heads=32, n_kv_heads=8, head_dim=128,
                    cfg: int = 4, salt: int = 0, sd: float = 1.0):
-    """Logical per-sequence K/V and the new tokens' q/k/v for one attention call.
+    """Logical per-sequence K/V and the new tokens' q for one attention call.
 
     Sequence b holds seq_lens[b] tokens after the call; its last q_lens[b] tokens are
-    new.  K/V of every position are drawn once, so the same logical sequence can be
-    replayed as prefill (all tokens new) or decode (one new token)."""
+    new.  K/V of a sequence are drawn in one stream (a longer draw extends a shorter
+    one) and q is drawn per absolute position, so the same token has the same inputs
+    whether it arrives in a prefill (all tokens new) or a decode (one token new).
+    Returns k[b], v[b]: [L, Hkv, D] and q[b]: [q_b, Hq, D] as bf16 bits."""
     seq_lens = [int(s) for s in seq_lens]
     q_lens = [int(q) for q in q_lens]
     ks, vs, qs = [], [], []
-    for b, L in enumerate(seq_lens):
+    for b, (L, ql) in enumerate(zip(seq_lens, q_lens)):
         ks.append(normal_bf16((L, n_kv_heads, head_dim), 0.0, sd, cfg, 100 + 3 * b, salt))
         vs.append(normal_bf16((L, n_kv_heads, head_dim), 0.0, sd, cfg, 101 + 3 * b, salt))
-        qs.append(normal_bf16((L, n_q_heads, head_dim), 0.0, sd, cfg, 102 + 3 * b, salt))
+        if ql:
+            qs.append(np.stack([normal_bf16((n_q_heads, head_dim), 0.0, sd, cfg, 102 + 3 * b,
+                                            (salt << 20) + p) for p in range(L - ql, L)]))
+        else:
+            qs.append(np.zeros((0, n_q_heads, head_dim), dtype=np.uint16))
     return dict(seq_lens=seq_lens, q_lens=q_lens, k=ks, v=vs, q=qs)
 
 

@@ -1,0 +1,125 @@
+"""bi_attention on the GPU: within 1 bf16 ulp of the fp64 oracle at the scale of each
+(token, head) output, and bitwise invariant to the batch, the path (split-KV decode or
+prefill walk), the physical pages and the position of a sequence in the batch.
+
+Cited: "Defeating nondeterminism in LLM inference", section on batch-invariant attention
+(update the KV cache and page table before the kernel; a token must reduce in the same
+order whether 0 or p tokens are cached; split-KV for decode).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import attention_case_f64
+from oracle.check import bf16_within_1ulp, f32_within_rel
+from synth import attention_case, ragged_lengths
+from tests._attn import make_cache, run
+from tests._gpu import bits, host, same_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_vs_oracle(case, out, qsl, which=None):
+    ref = attention_case_f64(case, which)
+    o = bits(out)
+    for b, r in enumerate(ref):
+        idx = range(case["q_lens"][b]) if which is None else which.get(b, [])
+        for j, i in enumerate(idx):
+            got = o[qsl[b] + i]
+            res = bf16_within_1ulp(got, r[j])
+            assert res["ok"], (b, i, res)
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 8), (16, 1), (8, 4)])
+def test_prefill_small_vs_oracle(lib, hq, hkv):
+    say("attention prefill", hq, hkv)
+    L = [1, 37, 256, 300]
+    case = attention_case(L, L, hq, hkv, 128, cfg=40, salt=hq)
+    kc, vc, bt = make_cache(case, 16, [0] * len(L))
+    out, qsl = run(lib, case, kc, vc, bt)
+    _check_vs_oracle(case, out, qsl)
+
+
+def test_decode_vs_oracle_and_prefill_bitwise(lib):
+    L = [255, 256, 257, 513, 1400, 3000]
+    pre = attention_case(L, L, cfg=41)                       # 5681 tokens: prefill walk
+    kc, vc, bt = make_cache(pre, 16, [0] * len(L))
+    out_p, qsl_p = run(lib, pre, kc, vc, bt)
+    dec = attention_case(L, [1] * len(L), cfg=41)            # same sequences, last token new
+    kc2, vc2, bt2 = make_cache(dec, 16, [l - 1 for l in L], cfg=78)
+    out_d, qsl_d = run(lib, dec, kc2, vc2, bt2)
+    for b, l in enumerate(L):
+        assert same_bits(out_d[b], out_p[qsl_p[b] + l - 1]), b
+    _check_vs_oracle(dec, out_d, qsl_d)
+    _check_vs_oracle(pre, out_p, qsl_p, which={b: [0, l // 2, l - 1] for b, l in enumerate(L)})
+    # the K/V the prefill wrote into its pages are the logical sequence
+    pages = torch.from_numpy(bt[5, :3].astype(np.int64)).cuda()
+    got = kc[pages].permute(0, 2, 1, 3).reshape(48, 8, 128)
+    assert np.array_equal(bits(got), pre["k"][5][:48])
+    gotv = vc[pages].permute(0, 3, 1, 2).reshape(48, 8, 128)
+    assert np.array_equal(bits(gotv), pre["v"][5][:48])
+
+
+def test_batch_position_page_invariance(lib):
+    L = ragged_lengths(8, 300, 2500, 42, 0)
+    case = attention_case(L, [1] * 8, cfg=42)
+    kc, vc, bt = make_cache(case, 16, [l - 1 for l in L])
+    out, _ = run(lib, case, kc, vc, bt)
+    for b in (0, 5):
+        one = {k: [case[k][b]] for k in ("seq_lens", "q_lens", "k", "v", "q")}
+        for cfg in (79, 80):                                  # two different page permutations
+            kc1, vc1, bt1 = make_cache(one, 16, [L[b] - 1], cfg=cfg)
+            o1, _ = run(lib, one, kc1, vc1, bt1)
+            assert same_bits(o1[0], out[b])
+    rev = {k: case[k][::-1] for k in ("seq_lens", "q_lens", "k", "v", "q")}
+    kcr, vcr, btr = make_cache(rev, 16, [l - 1 for l in rev["seq_lens"]], cfg=81)
+    outr, _ = run(lib, rev, kcr, vcr, btr)
+    assert same_bits(outr.flip(0), out)
+    # page size 32 and 256 give the same bits (chunks are logical)
+    for ps in (32, 256):
+        kcp, vcp, btp = make_cache(case, ps, [l - 1 for l in L], cfg=82)
+        op, _ = run(lib, case, kcp, vcp, btp)
+        assert same_bits(op, out), ps
+
+
+def test_chunked_prefill_matches_full_prefill(lib):
+    L = 1100
+    full = attention_case([L], [L], cfg=43)
+    kc, vc, bt = make_cache(full, 16, [0])
+    out_full, _ = run(lib, full, kc, vc, bt)
+    # the same prompt in pieces of 300, 1, 512, 287 new tokens
+    kc2, vc2, bt2 = make_cache(full, 16, [0], cfg=83)
+    start = 0
+    for piece in (300, 1, 512, 287):
+        part = attention_case([start + piece], [piece], cfg=43)
+        o, _ = run(lib, part, kc2, vc2, bt2)
+        assert same_bits(o, out_full[start:start + piece]), piece
+        start += piece
+
+
+def test_cfg4_decode_batch64(lib):
+    B = 64
+    L = ragged_lengths(B, 1400, 32768, 4, 0)
+    case = attention_case(L, [1] * B, cfg=4)
+    kc, vc, bt = make_cache(case, 16, [l - 1 for l in L])
+    out, qsl = run(lib, case, kc, vc, bt)
+    _check_vs_oracle(case, out, qsl, which={b: [0] for b in range(0, B, 9)})
+    for m in (1, 7, 33):
+        sub = {k: case[k][:m] for k in ("seq_lens", "q_lens", "k", "v", "q")}
+        o, _ = run(lib, sub, kc, vc, bt[:m].copy())
+        assert same_bits(o, out[:m]), m
+    of, _ = run(lib, case, kc, vc, bt, out_dtype=torch.float32)
+    ref = attention_case_f64(case, {0: [0]})[0][0]
+    assert f32_within_rel(host(of[0]), ref)["ok"]
+
+
+def test_cfg4_decode_equals_prefill_long(lib):
+    L = [4000, 9000]
+    pre = attention_case(L, L, cfg=44)
+    kc, vc, bt = make_cache(pre, 16, [0, 0])
+    out_p, qsl_p = run(lib, pre, kc, vc, bt)
+    dec = attention_case(L, [1, 1], cfg=44)
+    kc2, vc2, bt2 = make_cache(dec, 16, [l - 1 for l in L], cfg=84)
+    out_d, _ = run(lib, dec, kc2, vc2, bt2)
+    for b, l in enumerate(L):
+        assert same_bits(out_d[b], out_p[qsl_p[b] + l - 1])

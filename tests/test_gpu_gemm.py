@@ -1,0 +1,143 @@
+"""bi_gemm on the GPU: within 1 bf16 ulp (at output scale) of the fp64 oracle, bit-exact
+when every order is exact, and bitwise batch- and position-invariant.
+
+Cited: "Defeating nondeterminism in LLM inference": introduction (repeated torch.mm is
+bitwise equal), sections on batch invariance (the linspace example: row 0 of a
+[1, D] product vs of a [2048, D] product) and batch-invariant matrix multiplication.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp
+from oracle.check import bf16_within_1ulp, f32_within_rel
+from oracle.gemm import gemm_f64
+from oracle.rmsnorm import rmsnorm_tree
+from synth import gemm_inputs, normal_bf16, rmsnorm_linear_inputs
+from tests._gpu import bf16, bits, f32, host, same_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _nk(b_kn):
+    return np.ascontiguousarray(b_kn.T)
+
+
+def test_identity_b_gives_a(lib):
+    a = normal_bf16((70, 96), 0, 1, 30, 0)
+    eye = fp.f32_to_bf16(np.eye(96, dtype=np.float32))
+    c = lib.bi_gemm(bf16(a), bf16(eye))
+    assert np.array_equal(bits(c), a)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 512, 512), (33, 200, 72), (128, 128, 64), (130, 260, 1000),
+                                   (257, 384, 4096), (512, 1024, 14336), (7, 6144, 4096)])
+def test_vs_oracle(lib, m, n, k):
+    say("gemm", m, n, k)
+    a, b = gemm_inputs(m, n, k, cfg=31)
+    c = lib.bi_gemm(bf16(a), bf16(_nk(b)))
+    r = bf16_within_1ulp(bits(c), gemm_f64(a, b))
+    assert r["ok"], r
+    cf = lib.bi_gemm(bf16(a), bf16(_nk(b)), out_dtype=torch.float32)
+    r = f32_within_rel(host(cf), gemm_f64(a, b))
+    assert r["ok"], r
+
+
+def test_integer_inputs_bit_exact(lib):
+    rng = np.random.default_rng(0)
+    a = fp.f32_to_bf16(rng.integers(-8, 9, (300, 1000)).astype(np.float32))
+    b = fp.f32_to_bf16(rng.integers(-8, 9, (1000, 200)).astype(np.float32))
+    ref = gemm_f64(a, b)
+    assert np.abs(ref).max() < 2 ** 24
+    c = lib.bi_gemm(bf16(a), bf16(_nk(b)), out_dtype=torch.float32)
+    assert np.array_equal(host(c).astype(np.float64), ref)
+
+
+def test_cfg1_rmsnorm_then_linear(lib):
+    x, gamma, w = rmsnorm_linear_inputs(32, 512, 512)
+    X, G, W = bf16(x), bf16(gamma), bf16(w)
+    row0 = None
+    for m in range(1, 33):
+        y = lib.bi_rmsnorm(X[:m], G, 1e-6)
+        z = lib.bi_gemm(y, W)
+        yr = rmsnorm_tree(x[:m], gamma, 1e-6)
+        ref = gemm_f64(yr, w, "nk")
+        r = bf16_within_1ulp(bits(z), ref)
+        assert r["ok"], (m, r)
+        row0 = z[0].clone() if row0 is None else row0
+        assert same_bits(z[0], row0), m
+
+
+def test_cfg2_repeats_prefixes_permutation(lib):
+    a, b = gemm_inputs(2048, 2048, 2048, cfg=2)
+    A, B = bf16(a), bf16(_nk(b))
+    ref = lib.bi_gemm(A, B)
+    torch.cuda.synchronize()
+    r = bf16_within_1ulp(bits(ref[:64]), gemm_f64(a[:64], b))
+    assert r["ok"], r
+    for _ in range(1000):
+        c = lib.bi_gemm(A, B)
+        assert (c.float() - ref.float()).abs().max().item() == 0
+    for m in (1, 3, 17, 128, 511, 2048):
+        assert same_bits(lib.bi_gemm(A[:m], B), ref[:m]), m
+    perm = torch.randperm(2048, generator=torch.Generator().manual_seed(0)).cuda()
+    assert same_bits(lib.bi_gemm(A[perm].contiguous(), B), ref[perm])
+    # rows placed mid-batch among other rows
+    mix = torch.cat([A[100:101], torch.randn(40, 2048, device="cuda").to(torch.bfloat16), A[5:6]])
+    cm = lib.bi_gemm(mix, B)
+    assert same_bits(cm[0], ref[100]) and same_bits(cm[41], ref[5])
+
+
+def test_splitk_variant_is_not_invariant(lib):
+    # the page's linspace example: row 0 of a [1, D] product vs of a [2048, D] product
+    Bn, D = 2048, 4096
+    a = torch.linspace(-1000, 1000, Bn * D, device="cuda").reshape(Bn, D).to(torch.bfloat16)
+    b = torch.linspace(-1000, 1000, D * D, device="cuda").reshape(D, D).to(torch.bfloat16)
+    bt = b.t().contiguous()
+    inv1 = lib.bi_gemm(a[:1], bt, out_dtype=torch.float32)
+    inv2 = lib.bi_gemm(a, bt, out_dtype=torch.float32)[:1]
+    assert (inv1 - inv2).abs().max().item() == 0
+    s1 = lib.bi_gemm_splitk(a[:1], bt, out_dtype=torch.float32)
+    s2 = lib.bi_gemm_splitk(a, bt, out_dtype=torch.float32)[:1]
+    say("split-K row-0 max diff", (s1 - s2).abs().max().item())
+    assert (s1 - s2).abs().max().item() > 0
+    # on well-conditioned data the split-K variant is still a correct GEMM
+    a2, b2 = gemm_inputs(64, 512, 4096, cfg=34)
+    sk = lib.bi_gemm_splitk(bf16(a2), bf16(_nk(b2)))
+    assert bf16_within_1ulp(bits(sk), gemm_f64(a2, b2))["ok"]
+
+
+def test_fp32_operand_variant(lib):
+    rng = np.random.default_rng(2)
+    af = rng.standard_normal((100, 4096)).astype(np.float32)
+    w = normal_bf16((300, 4096), 0, 0.02, 32, 0)
+    c = lib.bi_gemm(f32(af), bf16(w), out_dtype=torch.float32)
+    ref = gemm_f64(af, w, "nk", a_dtype="f32")
+    r = f32_within_rel(host(c), ref)
+    assert r["ok"], r
+    # the fp32-operand path is far closer than rounding the operand to bf16 first
+    ab = lib.bi_gemm(f32(af).to(torch.bfloat16), bf16(w), out_dtype=torch.float32)
+    err32 = np.abs(host(c) - ref).max()
+    err16 = np.abs(host(ab) - ref).max()
+    say("fp32-operand max err", err32, "bf16-operand max err", err16)
+    assert err32 * 8 < err16
+    # exact split: a value with all 24 mantissa bits times 1.0 comes back exactly
+    a1 = np.float32([[1.0 + 2 ** -23 + 2 ** -10, -3.1415927]] + [[0.0, 0.0]] * 7)
+    e = fp.f32_to_bf16(np.eye(2, 8, dtype=np.float32)[:2, :2])
+    a8 = np.zeros((8, 8), dtype=np.float32); a8[:, :2] = a1
+    w8 = np.zeros((2, 8), dtype=np.uint16); w8[:, :2] = e
+    c1 = lib.bi_gemm(f32(a8), bf16(w8), out_dtype=torch.float32)
+    assert np.array_equal(host(c1)[0], a1[0])
+    # batch invariance of the fp32 path
+    A = f32(af)
+    full = lib.bi_gemm(A, bf16(w), out_dtype=torch.float32)
+    assert same_bits(lib.bi_gemm(A[:1], bf16(w), out_dtype=torch.float32)[0], full[0])
+
+
+def test_empty_and_ragged(lib):
+    A = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
+    assert lib.bi_gemm(A, W).shape == (0, 16)
+    a, b = gemm_inputs(1, 1, 8, cfg=33)
+    c = lib.bi_gemm(bf16(a), bf16(_nk(b)), out_dtype=torch.float32)
+    assert f32_within_rel(host(c), gemm_f64(a, b))["ok"]

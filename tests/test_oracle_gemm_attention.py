@@ -41,7 +41,7 @@ def test_attention_matches_scalar_brute_force():
         v = fp.bf16_to_f64(case["v"][b]).tolist()
         for i in range(ql):
             p = L - ql + i
-            ref = np.array(S.attention_scalar(q[p], k, v, p, 2))
+            ref = np.array(S.attention_scalar(q[i], k, v, p, 2))
             assert np.max(np.abs(outs[b][i] - ref)) < 1e-12
 
 
