@@ -184,6 +184,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gemm-sweep", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (to scale rocprof byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no collectives and every box has "
@@ -200,6 +202,13 @@ def main():
         gemm_sweep(torch, bi)
         return
 
+    if args.copy_calibration:
+        src = torch.ones((1 << 29,), dtype=torch.bfloat16, device="cuda:0")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log("building inputs")
     inp = build_inputs(torch, bi)
     ops = step_ops(bi, inp)
