@@ -52,7 +52,7 @@ def build_inputs(torch, bi):
     L = synth.ragged_lengths(B, 1400, 32768, 4, 0)
     bt, total = synth.paged_layout(L, ps, 4, 7, 0)
     inp["L"] = L
-    inp["k_cache"] = torch.randn((total, hkv, ps, hd), generator=g, device=dev).to(torch.bfloat16)
+    inp["k_cache"] = torch.randn((total, hkv, hd // 8, ps, 8), generator=g, device=dev).to(torch.bfloat16)
     inp["v_cache"] = torch.randn((total, hkv, hd, ps), generator=g, device=dev).to(torch.bfloat16)
     inp["bt"] = torch.from_numpy(bt).to(dev)
     inp["seq_lens"] = torch.from_numpy(L.astype(np.int32)).to(dev)
@@ -123,12 +123,15 @@ def cpu_baseline(inp, torch, work_d, t_peak_step):
     a = bits(inp["A"][:256]); b = bits(inp["B_nk"])
     t0 = time.perf_counter(); gemm_f64(a, b, "nk"); est["gemm"] = (time.perf_counter() - t0) * 8
     # a3: 4 of 64 sequences, gathered from the pages into logical order
-    L = inp["L"]; bt = inp["bt"].cpu().numpy(); ps = inp["k_cache"].shape[2]
+    L = inp["L"]; bt = inp["bt"].cpu().numpy(); ps = inp["v_cache"].shape[3]
     sample = [0, 16, 32, 48]
     t_att = 0.0
     for bb in sample:
         n = int(L[bb]); pages = torch.from_numpy(bt[bb, :(n + ps - 1) // ps].astype(np.int64)).cuda()
-        k = bits(inp["k_cache"][pages].permute(0, 2, 1, 3).reshape(-1, 8, 128)[:n])
+        pos = np.arange(n)
+        kslot = (pos % ps & ~12) | ((pos % ps & 4) << 1) | ((pos % ps & 8) >> 1)
+        k = bits(inp["k_cache"][torch.from_numpy(bt[bb, pos // ps].astype(np.int64)).cuda(), :, :,
+                                torch.from_numpy(kslot.astype(np.int64)).cuda(), :].reshape(n, 8, 128))
         v = bits(inp["v_cache"][pages].permute(0, 3, 1, 2).reshape(-1, 8, 128)[:n])
         q = bits(inp["q"][bb:bb + 1])
         t0 = time.perf_counter(); attention_rows_f64(q, k, v, [n - 1]); t_att += time.perf_counter() - t0

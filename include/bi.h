@@ -146,9 +146,13 @@ int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  *   q        [num_tokens, Hq, D] bf16, contiguous
  *   k_new    [num_tokens, Hkv, D] bf16 (keys already rotated), contiguous
  *   v_new    [num_tokens, Hkv, D] bf16, contiguous
- *   k_cache  [num_pages, Hkv, page_size, D] bf16: page-major, then kv head, then slot
- *   v_cache  [num_pages, Hkv, D, page_size] bf16: like k_cache but each page stores V
- *            transposed (slot fastest), the operand order of the P.V matrix product
+ *   k_cache  [num_pages, Hkv, D/8, page_size, 8] bf16: per page and kv head, D is cut
+ *            into 8-element groups; group j holds d = 8j..8j+7 of every slot.  Inside each
+ *            aligned block of 16 slots the slot order is permuted by swapping bits 2 and 3
+ *            of the slot index (0-3, 8-11, 4-7, 12-15), so that the 8 keys one matrix
+ *            instruction reads from a page are adjacent (whole 128-byte lines per load)
+ *   v_cache  [num_pages, Hkv, D, page_size] bf16: each page stores V transposed (slot
+ *            fastest, natural slot order), the operand order of the P.V product
  *   block_table [batch, max_pages_per_seq] int32: physical page of logical page j
  *            (entries at j >= ceil(seq_lens[b] / page_size) are never read)
  *   seq_lens [batch] int32, query_start_loc [batch + 1] int32 (device)

@@ -152,12 +152,12 @@ def bi_attention_workspace_bytes(num_tokens, num_q_heads, head_dim, max_seq_len)
 
 def bi_attention(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start_loc,
                  max_seq_len: int, scale: float, out=None, out_dtype=torch.bfloat16, workspace=None):
-    """q [T, Hq, D], k_new/v_new [T, Hkv, D] bf16; k_cache [P, Hkv, page, D];
+    """q [T, Hq, D], k_new/v_new [T, Hkv, D] bf16; k_cache [P, Hkv, D/8, page, 8];
     v_cache [P, Hkv, D, page]; block_table [B, max_pages] int32; seq_lens [B] int32;
     query_start_loc [B + 1] int32 (all on the device)."""
     T, Hq, D = q.shape
     Hkv = k_new.shape[1]
-    page = k_cache.shape[2]
+    page = v_cache.shape[3]
     B, max_pages = block_table.shape
     if out is None:
         out = torch.empty((T, Hq, D), dtype=out_dtype, device=q.device)

@@ -8,26 +8,33 @@
 //  * the reduction order of a token may not depend on how many other tokens of its
 //    sequence are processed with it: here the keys of every query are split into
 //    chunks of 256 at ABSOLUTE positions [256c, 256c + 256), each chunk is reduced by
-//    one wave with one fixed instruction sequence (chunk_partial), and the chunk
+//    one workgroup with one fixed instruction sequence (chunk_partial), and the chunk
 //    partials are merged in ascending c (merge_step).  Split-KV decode and the prefill
 //    walk call exactly these two routines, so a token's bits never depend on the path,
 //    the batch, its neighbours or the physical pages.
 //
-// Per chunk (one wave, 16 query columns, GQA: every column of a wave reads the same kv
-// head):
-//   S^T = K . Q^T   16 tiles of v_mfma_f32_16x16x32_bf16 (keys x columns), d-sum over
-//                   4 instructions in ascending order;
+// Per chunk (one workgroup of 4 waves, 16 query columns; GQA: every column of a
+// workgroup reads the same kv head; wave w owns the 64 keys [64w, 64w + 64)):
+//   S^T = K . Q^T   4 tiles of v_mfma_f32_16x16x32_bf16 per wave (keys x columns), the
+//                   d-sum over 4 instructions in ascending order;
 //   t = S * (scale * log2 e), masked to -inf beyond the query position;
-//   m_c = max t;  P = 2^(t - m_c) (v_exp_f32);  l_c = sum P (per-lane ascending, then
-//   lanes (g0 + g1) + (g2 + g3));
-//   O^T = V^T . P^T with P split exactly-enough into bf16 hi + lo (two instructions per
-//   32-key slice, hi first), fp32 accumulation.  Rounding P itself to bf16 would cost
-//   tens of bf16 ulps in the output; hi + lo keeps 16 bits.
+//   m_c = max t over the chunk (the 4 wave maxima exchanged through LDS);
+//   P = 2^(t - m_c) (v_exp_f32);  per wave: l_w = sum P (per-lane ascending, then lanes
+//   (g0 + g1) + (g2 + g3)) and O_w^T = V^T . P^T over its two 32-key slices, P split into
+//   bf16 hi + lo (two instructions per slice, hi first, one fp32 accumulation chain);
+//   l_c = (l_0 + l_1) + (l_2 + l_3),  o_c = (O_0 + O_1) + (O_2 + O_3).
+//   Rounding P itself to bf16 would cost tens of bf16 ulps in the output; hi + lo keeps
+//   16 bits.
 // Merge (ascending c, first chunk copied):  m' = max(m, m_c); a = 2^(m - m');
 //   b = 2^(m_c - m');  l' = a l + b l_c;  o' = a o + b o_c;  out = o / l.
 //
-// Cache layout (chosen so every matrix operand is a 16-byte load):
-//   k_cache [page][kv head][slot][128]      v_cache [page][kv head][128][slot]
+// Cache layout, chosen so every matrix-operand load of a wave covers whole 128-byte
+// lines:
+//   k_cache [page][kv head][16 d-groups][slot'][8]: d-group j holds d = 8j .. 8j+7 of
+//           every slot; inside each aligned block of 16 slots the slot order is
+//           s' = s with bits 2 and 3 swapped (0-3, 8-11, 4-7, 12-15), which puts the 8
+//           keys one matrix instruction reads from a page next to each other;
+//   v_cache [page][kv head][128 d][slot]  (V transposed, slots in order).
 #include "bi_common.h"
 
 namespace bi {
@@ -44,6 +51,27 @@ __device__ __forceinline__ floatx4 mfma16(u16x8 a, u16x8 b, floatx4 c) {
 }
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Largest b < batch with qsl[b] <= t, by a 64-way search (one probe per lane and a
+// ballot per step).  Wave-uniform t required; qsl is non-decreasing with qsl[0] = 0.
+__device__ __forceinline__ int find_seq_wave(const int32_t* qsl, int batch, int t) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, n = batch;
+  while (n > 1) {
+    const int step = (n + 63) / 64;
+    const bool ok = lane * step < n && qsl[lo + lane * step] <= t;
+    const unsigned long long m = __ballot(ok);
+    const int k = 63 - __clzll(m);
+    lo += k * step;
+    n = min(step, n - k * step);
+  }
+  return lo;
+}
+
+// Physical slot of logical slot s inside a K page: bits 2 and 3 swapped.
+__device__ __forceinline__ int k_slot(int s) {
+  return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1);
+}
 
 __device__ __forceinline__ int find_seq(const int32_t* qsl, int batch, int t) {
   int lo = 0, hi = batch - 1;
@@ -64,30 +92,68 @@ struct Seq {
   int seq_len;
 };
 
-// One 256-key chunk for the wave's 16 columns.  pcol: absolute position of this lane's
-// column (-1: unused column).  Returns the partial in the MFMA output layout: lane l
-// holds column l % 16 and o[db][r] = d 16 db + 4 (l / 16) + r.
+// Exchange area of one workgroup for one chunk.
+struct ChunkLDS {
+  float mx[4][16];
+  float l[4][16];
+  floatx4 o[4][8][64];
+};
+
+// One 256-key chunk for the workgroup's 16 columns (all 4 waves call it together).
+// pcol: absolute position of this lane's column (-1: unused column).  Returns, in every
+// wave, m_c and l_c of column lane % 16 and, in wave w, o_c for d-blocks 2w and 2w + 1 in
+// the MFMA output layout (oc[j][r] is d = 16 (2w + j) + 4 (lane / 16) + r).
 __device__ __forceinline__ void chunk_partial(const Seq& sq, int c, const u16x8 (&qop)[4], int pcol,
-                                              float sl2, float& m_c, float& l_c, floatx4 (&o)[8]) {
-  const int lane = threadIdx.x & 63;
+                                              float sl2, ChunkLDS& sh, float& m_c, float& l_c,
+                                              floatx4 (&oc)[2]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int kr0 = 8 * (i >> 2) + (i & 3);           // key of MFMA row i in the first tile of a pair
-  const int64_t page_k = static_cast<int64_t>(sq.ps) * HD;
+  const int64_t page_elems = static_cast<int64_t>(sq.ps) * HD;
   const int c0 = c * CHUNK;
+  const int ppc = CHUNK / sq.ps;                    // pages per chunk
+  // physical page of chunk page l, held by lane l (read once, then shuffled)
+  int pg = 0;
+  if (lane < ppc && (c0 + lane * sq.ps) < sq.seq_len) pg = sq.bt[c * ppc + lane];
 
-  floatx4 s[8][2];
+  // V^T operands of this wave's two 32-key slices (independent of P: issued first)
+  u16x8 vop[2][8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int uu = 0; uu < 2; ++uu) {
+    const int kk0 = 32 * (2 * w + uu) + 8 * g;      // first of this lane's 8 keys
+    const int nvalid = sq.seq_len - (c0 + kk0);     // keys kk0 + e valid for e < nvalid
+    const int phys = __shfl(pg, kk0 / sq.ps, 64);
+    const uint16_t* vbase =
+        sq.vc + (static_cast<int64_t>(phys) * sq.hkv + sq.kvh) * page_elems + (kk0 % sq.ps);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (nvalid > 0) {
+        v = *reinterpret_cast<const u16x8*>(vbase + static_cast<int64_t>(16 * db + i) * sq.ps);
+        if (nvalid < 8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e >= nvalid) v[e] = 0;
+        }
+      }
+      vop[uu][db] = v;
+    }
+  }
+
+  floatx4 s[2][2];
+#pragma unroll
+  for (int uu = 0; uu < 2; ++uu) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int key = c0 + 32 * u + kr0 + 4 * h2;
+      const int kk = 32 * (2 * w + uu) + kr0 + 4 * h2;   // chunk-relative key of this lane's row
+      const int phys = __shfl(pg, kk / sq.ps, 64);
       u16x8 kop[4];
-      if (key < sq.seq_len) {
-        const int phys = sq.bt[key / sq.ps];
-        const uint16_t* kp = sq.kc + (static_cast<int64_t>(phys) * sq.hkv + sq.kvh) * page_k +
-                             static_cast<int64_t>(key % sq.ps) * HD + 32 * g;
+      if (c0 + kk < sq.seq_len) {
+        const uint16_t* kp = sq.kc + (static_cast<int64_t>(phys) * sq.hkv + sq.kvh) * page_elems +
+                             (static_cast<int64_t>(4 * g) * sq.ps + k_slot(kk % sq.ps)) * 8;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) kop[t] = *reinterpret_cast<const u16x8*>(kp + 8 * t);
+        for (int t = 0; t < 4; ++t)
+          kop[t] = *reinterpret_cast<const u16x8*>(kp + static_cast<int64_t>(t) * sq.ps * 8);
       } else {
 #pragma unroll
         for (int t = 0; t < 4; ++t) kop[t] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -95,80 +161,76 @@ __device__ __forceinline__ void chunk_partial(const Seq& sq, int c, const u16x8 
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc = mfma16(kop[t], qop[t], acc);
-      s[u][h2] = acc;
+      s[uu][h2] = acc;
     }
   }
 
   // scale, causal mask, chunk maximum
   float mx = -__builtin_huge_valf();
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
+  for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int kp = c0 + 32 * u + 8 * g + 4 * h2 + r;
-        const float t = s[u][h2][r] * sl2;
-        s[u][h2][r] = (kp <= pcol) ? t : -__builtin_huge_valf();
-        mx = fmaxf(mx, s[u][h2][r]);
+        const int kp = c0 + 32 * (2 * w + uu) + 8 * g + 4 * h2 + r;
+        const float t = s[uu][h2][r] * sl2;
+        s[uu][h2][r] = (kp <= pcol) ? t : -__builtin_huge_valf();
+        mx = fmaxf(mx, s[uu][h2][r]);
       }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  m_c = mx;
+  if (g == 0) sh.mx[w][i] = mx;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(sh.mx[0][i], sh.mx[1][i]), fmaxf(sh.mx[2][i], sh.mx[3][i]));
 
   float lsum = 0.f;
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
+  for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int kp = c0 + 32 * u + 8 * g + 4 * h2 + r;
-        const float p = (kp <= pcol) ? exp2_hw(s[u][h2][r] - mx) : 0.f;
-        s[u][h2][r] = p;
+        const int kp = c0 + 32 * (2 * w + uu) + 8 * g + 4 * h2 + r;
+        const float p = (kp <= pcol) ? exp2_hw(s[uu][h2][r] - m) : 0.f;
+        s[uu][h2][r] = p;
         lsum = lsum + p;
       }
   lsum = lsum + __shfl_xor(lsum, 16, 64);
   lsum = lsum + __shfl_xor(lsum, 32, 64);
-  l_c = lsum;
 
+  floatx4 o[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) o[db] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int uu = 0; uu < 2; ++uu) {
     u16x8 phi, plo;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = s[u][h2][r];
+        const float p = s[uu][h2][r];
         const uint16_t h = f32_to_bf16(p);
         phi[4 * h2 + r] = h;
         plo[4 * h2 + r] = f32_to_bf16(p - bf16_to_f32(h));
       }
-    const int kp0 = c0 + 32 * u + 8 * g;               // first of this lane's 8 keys
-    const bool any = kp0 < sq.seq_len;
-    const int nvalid = sq.seq_len - kp0;                // keys kp0 + e valid for e < nvalid
-    const uint16_t* vbase = nullptr;
-    if (any) {
-      const int phys = sq.bt[kp0 / sq.ps];
-      vbase = sq.vc + (static_cast<int64_t>(phys) * sq.hkv + sq.kvh) * page_k + (kp0 % sq.ps);
-    }
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      u16x8 vop = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (any) {
-        vop = *reinterpret_cast<const u16x8*>(vbase + static_cast<int64_t>(16 * db + i) * sq.ps);
-        if (nvalid < 8) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e >= nvalid) vop[e] = 0;
-        }
-      }
-      o[db] = mfma16(vop, phi, o[db]);
-      o[db] = mfma16(vop, plo, o[db]);
+      o[db] = mfma16(vop[uu][db], phi, o[db]);
+      o[db] = mfma16(vop[uu][db], plo, o[db]);
     }
   }
+  if (g == 0) sh.l[w][i] = lsum;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) sh.o[w][db][lane] = o[db];
+  __syncthreads();
+  l_c = (sh.l[0][i] + sh.l[1][i]) + (sh.l[2][i] + sh.l[3][i]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int db = 2 * w + j;
+    oc[j] = (sh.o[0][db][lane] + sh.o[1][db][lane]) + (sh.o[2][db][lane] + sh.o[3][db][lane]);
+  }
+  m_c = m;
 }
 
 __device__ __forceinline__ void merge_step(float& m, float& l, float mc, float lc, float& a,
@@ -203,7 +265,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch,
     int max_pages, int hkv, int ps) {
   const int t = blockIdx.x;
-  const int b = find_seq(qsl, batch, t);
+  const int b = find_seq_wave(qsl, batch, t);
   const int pos = seq_lens[b] - (qsl[b + 1] - qsl[b]) + (t - qsl[b]);
   const int phys = bt[static_cast<int64_t>(b) * max_pages + pos / ps];
   const int slot = pos % ps;
@@ -215,7 +277,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
     const int64_t src = (static_cast<int64_t>(t) * hkv + head) * HD + d0;
     const int64_t pg = (static_cast<int64_t>(phys) * hkv + head) * ps * HD;
     if (!is_v) {
-      *reinterpret_cast<u16x8*>(kc + pg + static_cast<int64_t>(slot) * HD + d0) =
+      *reinterpret_cast<u16x8*>(kc + pg + (static_cast<int64_t>(d0 / 8) * ps + k_slot(slot)) * 8) =
           *reinterpret_cast<const u16x8*>(k_new + src);
     } else {
       const u16x8 x = *reinterpret_cast<const u16x8*>(v_new + src);
@@ -226,38 +288,38 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 }
 
 // ---------------------------------------------------------------- step 2a: split-KV chunks
-// grid.x = num_tokens * ceil(max_chunks / 4), grid.y = kv heads; wave w of a workgroup
-// takes chunk 4 * (blockIdx.x % cpb) + w of its token.
+// grid.x = num_tokens * max_chunks, grid.y = kv heads; one workgroup per (token, chunk,
+// kv head), its 16 columns are the token's G q heads (the rest unused).
 __global__ __launch_bounds__(256) void attn_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch,
     int max_pages, int hq, int hkv, int ps, int max_chunks, float sl2, float* __restrict__ ws_ml,
     float* __restrict__ ws_o) {
-  const int cpb = (max_chunks + 3) / 4;
-  const int t = blockIdx.x / cpb;
-  const int c = 4 * (blockIdx.x % cpb) + (threadIdx.x >> 6);
+  __shared__ ChunkLDS sh;
+  const int t = blockIdx.x / max_chunks;
+  const int c = blockIdx.x % max_chunks;
   const int kvh = blockIdx.y;
-  const int b = find_seq(qsl, batch, t);
+  const int b = find_seq_wave(qsl, batch, t);
   const int L = seq_lens[b];
   const int pos = L - (qsl[b + 1] - qsl[b]) + (t - qsl[b]);
   if (c * CHUNK > pos) return;
   const int G = hq / hkv;
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15;
   const bool used = col < G;
   u16x8 qop[4];
   load_q(q, t, kvh * G + col, hq, used, qop);
   Seq sq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, kvh, L};
   float m_c, l_c;
-  floatx4 o[8];
-  chunk_partial(sq, c, qop, used ? pos : -1, sl2, m_c, l_c, o);
+  floatx4 oc[2];
+  chunk_partial(sq, c, qop, used ? pos : -1, sl2, sh, m_c, l_c, oc);
   if (!used) return;
   const int64_t slot = (static_cast<int64_t>(t) * hq + kvh * G + col) * max_chunks + c;
   float* po = ws_o + slot * HD + 4 * (lane >> 4);
 #pragma unroll
-  for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4*>(po + 16 * db) = o[db];
-  if ((lane >> 4) == 0) {
+  for (int j = 0; j < 2; ++j) *reinterpret_cast<floatx4*>(po + 16 * (2 * w + j)) = oc[j];
+  if (w == 0 && (lane >> 4) == 0) {
     ws_ml[2 * slot] = m_c;
     ws_ml[2 * slot + 1] = l_c;
   }
@@ -273,18 +335,39 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   if (row >= n_rows) return;
   const int t = static_cast<int>(row / hq);
   const int lane = threadIdx.x & 63;
-  const int b = find_seq(qsl, batch, t);
+  const int b = find_seq_wave(qsl, batch, t);
   const int pos = seq_lens[b] - (qsl[b + 1] - qsl[b]) + (t - qsl[b]);
   const int nc = pos / CHUNK + 1;
   const float* ml = ws_ml + row * max_chunks * 2;
   const float* po = ws_o + row * max_chunks * HD + 2 * lane;
-  float m = ml[0], l = ml[1];
-  float o0 = po[0], o1 = po[1];
-  for (int c = 1; c < nc; ++c) {
-    float a, bb;
-    merge_step(m, l, ml[2 * c], ml[2 * c + 1], a, bb);
-    o0 = mix(o0, po[c * HD], a, bb);
-    o1 = mix(o1, po[c * HD + 1], a, bb);
+  float m = 0.f, l = 0.f, o0 = 0.f, o1 = 0.f;
+  // chunks in groups of 64: lane c holds (m_c, l_c) of chunk base + c; 8 o loads in flight
+  for (int base = 0; base < nc; base += 64) {
+    const int cl = base + lane;
+    const float mc_l = cl < nc ? ml[2 * cl] : 0.f;
+    const float lc_l = cl < nc ? ml[2 * cl + 1] : 0.f;
+    const int n = min(64, nc - base);
+    for (int j0 = 0; j0 < n; j0 += 8) {
+      float2 ov[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j0 + j < n) ov[j] = *reinterpret_cast<const float2*>(po + static_cast<int64_t>(base + j0 + j) * HD);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j0 + j >= n) break;
+        const int c = base + j0 + j;
+        const float mc = __shfl(mc_l, j0 + j, 64);
+        const float lc = __shfl(lc_l, j0 + j, 64);
+        if (c == 0) {
+          m = mc; l = lc; o0 = ov[j].x; o1 = ov[j].y;
+        } else {
+          float a, bb;
+          merge_step(m, l, mc, lc, a, bb);
+          o0 = mix(o0, ov[j].x, a, bb);
+          o1 = mix(o1, ov[j].y, a, bb);
+        }
+      }
+    }
   }
   const float r0 = o0 / l, r1 = o1 / l;
   if (out_f32) {
@@ -299,22 +382,23 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 }
 
 // ---------------------------------------------------------------- step 2b: prefill walk
-// Each wave owns 16 / G consecutive tokens (a block aligned to the global token index)
-// and one kv head, i.e. 16 columns; it walks chunks 0.. in order and merges in
-// registers.  A block that straddles two sequences is processed once per sequence with
-// the other sequence's columns switched off.
+// One workgroup per 16 / G consecutive tokens (a block aligned to the global token index)
+// and kv head, i.e. 16 columns; it walks chunks 0.. in order and merges in registers (wave
+// w keeps d-blocks 2w, 2w + 1).  A block that straddles two sequences is processed once
+// per sequence with the other sequence's columns switched off.
 __global__ __launch_bounds__(256) void attn_walk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch,
     int max_pages, int hq, int hkv, int ps, int64_t num_tokens, float sl2, void* __restrict__ out,
     int out_f32) {
+  __shared__ ChunkLDS sh;
   const int G = hq / hkv;
   const int NT = 16 / G;
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15;
   const int kvh = blockIdx.y;
-  const int64_t tok0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * NT;
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * NT;
   if (tok0 >= num_tokens) return;
   const int64_t my_tok = tok0 + col / G;
   const bool tok_ok = my_tok < num_tokens;
@@ -334,40 +418,40 @@ __global__ __launch_bounds__(256) void attn_walk_kernel(
     load_q(q, mine ? my_tok : 0, head, hq, mine, qop);
     const int L = seq_lens[b];
     Seq sq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, kvh, L};
-    // highest position among this sequence's columns in the block
+    // highest position among this sequence's columns (the same in every wave)
     int pmax = pcol;
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) pmax = max(pmax, __shfl_xor(pmax, off, 64));
     float m = 0.f, l = 0.f;
-    floatx4 o[8];
+    floatx4 o[2];
     for (int c = 0; c * CHUNK <= pmax; ++c) {
       float m_c, l_c;
-      floatx4 oc[8];
-      chunk_partial(sq, c, qop, pcol, sl2, m_c, l_c, oc);
+      floatx4 oc[2];
+      chunk_partial(sq, c, qop, pcol, sl2, sh, m_c, l_c, oc);
       if (c * CHUNK > pcol) continue;
       if (c == 0) {
         m = m_c;
         l = l_c;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) o[db] = oc[db];
+        o[0] = oc[0];
+        o[1] = oc[1];
       } else {
         float a, bb;
         merge_step(m, l, m_c, l_c, a, bb);
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[db][r] = mix(o[db][r], oc[db][r], a, bb);
+          for (int r = 0; r < 4; ++r) o[j][r] = mix(o[j][r], oc[j][r], a, bb);
       }
     }
     if (!mine) continue;
     const int64_t orow = my_tok * hq + head;
     const int d0 = 4 * (lane >> 4);
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float v = o[db][r] / l;
-        const int64_t idx = orow * HD + 16 * db + d0 + r;
+        const float v = o[j][r] / l;
+        const int64_t idx = orow * HD + 16 * (2 * w + j) + d0 + r;
         if (out_f32) static_cast<float*>(out)[idx] = v;
         else static_cast<uint16_t*>(out)[idx] = f32_to_bf16(v);
       }
@@ -433,8 +517,7 @@ extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new,
     const int64_t maxc = chunks_for(max_seq_len);
     float* ws_ml = static_cast<float*>(workspace);
     float* ws_o = ws_ml + ml_floats(num_tokens * num_q_heads * maxc);
-    const int64_t cpb = (maxc + 3) / 4;
-    attn_split_kernel<<<dim3(static_cast<unsigned>(num_tokens * cpb), num_kv_heads), dim3(256), 0, s>>>(
+    attn_split_kernel<<<dim3(static_cast<unsigned>(num_tokens * maxc), num_kv_heads), dim3(256), 0, s>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
         static_cast<const uint16_t*>(v_cache), block_table, seq_lens, query_start_loc, batch,
         max_pages_per_seq, num_q_heads, num_kv_heads, page_size, static_cast<int>(maxc), sl2,
@@ -445,8 +528,8 @@ extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new,
         out, of);
   } else {
     const int NT = 16 / G;
-    const int64_t waves = (num_tokens + NT - 1) / NT;
-    attn_walk_kernel<<<dim3(static_cast<unsigned>((waves + 3) / 4), num_kv_heads), dim3(256), 0, s>>>(
+    const int64_t blocks = (num_tokens + NT - 1) / NT;
+    attn_walk_kernel<<<dim3(static_cast<unsigned>(blocks), num_kv_heads), dim3(256), 0, s>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
         static_cast<const uint16_t*>(v_cache), block_table, seq_lens, query_start_loc, batch,
         max_pages_per_seq, num_q_heads, num_kv_heads, page_size, num_tokens, sl2, out, of);

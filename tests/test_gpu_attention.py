@@ -13,7 +13,7 @@ import torch
 from oracle.attention import attention_case_f64
 from oracle.check import bf16_within_1ulp, f32_within_rel
 from synth import attention_case, ragged_lengths
-from tests._attn import make_cache, run
+from tests._attn import k_logical, make_cache, run
 from tests._gpu import bits, host, same_bits, say
 
 pytestmark = pytest.mark.gpu
@@ -54,7 +54,7 @@ def test_decode_vs_oracle_and_prefill_bitwise(lib):
     _check_vs_oracle(pre, out_p, qsl_p, which={b: [0, l // 2, l - 1] for b, l in enumerate(L)})
     # the K/V the prefill wrote into its pages are the logical sequence
     pages = torch.from_numpy(bt[5, :3].astype(np.int64)).cuda()
-    got = kc[pages].permute(0, 2, 1, 3).reshape(48, 8, 128)
+    got = k_logical(kc, bt[5], 48)
     assert np.array_equal(bits(got), pre["k"][5][:48])
     gotv = vc[pages].permute(0, 3, 1, 2).reshape(48, 8, 128)
     assert np.array_equal(bits(gotv), pre["v"][5][:48])
