@@ -29,12 +29,13 @@ namespace bi {
 __device__ __forceinline__ float f32c(uint32_t b) { return __uint_as_float(b); }
 
 __device__ float exp_cw(float d) {
-  if (d != d) return d;
+  // branch-free form of the same steps: k outside [-125, 0] and NaN are selected away at
+  // the end, after computing with a clamped k
   const float t = d * f32c(0x3fb8aa3bu);
   const float k = __builtin_rintf(t);
-  if (!(k >= -125.0f)) return 0.0f;
-  float r = d - k * f32c(0x3f317200u);
-  r = r - k * f32c(0x35bfbe8eu);
+  const float kc = fmaxf(k, -126.0f);
+  float r = d - kc * f32c(0x3f317200u);
+  r = r - kc * f32c(0x35bfbe8eu);
   float p = f32c(0x39500d01u);       // 1/5040
   p = p * r + f32c(0x3ab60b61u);     // 1/720
   p = p * r + f32c(0x3c088889u);     // 1/120
@@ -43,8 +44,10 @@ __device__ float exp_cw(float d) {
   p = p * r + f32c(0x3f000000u);     // 1/2
   p = p * r + f32c(0x3f800000u);     // 1
   p = p * r + f32c(0x3f800000u);     // 1
-  const int ki = static_cast<int>(k);
-  return p * __int_as_float((ki + 127) << 23);
+  const int ki = static_cast<int>(kc);
+  const float res = p * __int_as_float((ki + 127) << 23);
+  const float live = (k >= -125.0f) ? res : 0.0f;
+  return (d != d) ? d : live;
 }
 
 __device__ float log_at(float s) {
@@ -78,22 +81,16 @@ constexpr int kThreads = 256;
 // (value, index) selection: larger value wins, NaN beats numbers, equal -> lower index.
 __device__ __forceinline__ void pick(float& bv, int& bi, float v, int i) {
   const bool bn = bv != bv, vn = v != v;
-  bool take;
-  if (bn && vn) take = i < bi;
-  else if (vn) take = true;
-  else if (bn) take = false;
-  else if (v > bv) take = true;
-  else if (bv > v) take = false;
-  else take = i < bi;
-  if (take) {
-    bv = v;
-    bi = i;
-  }
+  const bool gt = v > bv, lt = v < bv, lower = i < bi;
+  const bool take = (vn && !bn) || (!vn && !bn && (gt || (!lt && lower))) || (vn && bn && lower);
+  bv = take ? v : bv;
+  bi = take ? i : bi;
 }
 
+template <bool FULL>
 __device__ __forceinline__ void load4(const float* row, int v, int V, bool vec, float (&e)[4]) {
   const float* p = row + static_cast<int64_t>(v) * 4;
-  if (vec && v * 4 + 4 <= V) {
+  if (FULL || (vec && v * 4 + 4 <= V)) {
     floatx4 q = *reinterpret_cast<const floatx4*>(p);
     e[0] = q[0]; e[1] = q[1]; e[2] = q[2]; e[3] = q[3];
   } else {
@@ -102,6 +99,14 @@ __device__ __forceinline__ void load4(const float* row, int v, int V, bool vec, 
   }
 }
 
+// The first NVC vectors of every lane stay in registers across the three passes (all of
+// a 32768-wide row); longer rows re-read the rest.  Only where the values live changes, not
+// the order in which they are combined.
+constexpr int NVC = 32;
+
+// FULL: every 4-element vector lies inside the row and rows are 16-byte aligned, so no
+// element needs a bounds check (V % 4 == 0, aligned pointers and ld).
+template <bool FULL>
 __global__ __launch_bounds__(kThreads) void logsoftmax_argmax_kernel(
     const float* __restrict__ logits, int V, int64_t ld, float* __restrict__ logprobs,
     int32_t* __restrict__ argmax, int vec_in, int vec_out) {
@@ -114,16 +119,34 @@ __global__ __launch_bounds__(kThreads) void logsoftmax_argmax_kernel(
   __shared__ int si[kThreads / kWave];
   __shared__ float ss[kThreads / kWave];
 
+  float cache[NVC][4];
+  if (tid < T) {
+#pragma unroll
+    for (int j = 0; j < NVC; ++j) {
+      const int v = tid + j * T;
+      if (v < nvec) load4<FULL>(x, v, V, vec_in, cache[j]);
+    }
+  }
+
   // pass 1: maximum and lowest index attaining it
   float bv = -__builtin_huge_valf();
   int bidx = 0x7fffffff;
   if (tid < T) {
-    for (int v = tid; v < nvec; v += T) {
+#pragma unroll
+    for (int j = 0; j < NVC; ++j) {
+      const int v = tid + j * T;
+      if (v < nvec) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (FULL || v * 4 + i < V) pick(bv, bidx, cache[j][i], v * 4 + i);
+      }
+    }
+    for (int v = tid + NVC * T; v < nvec; v += T) {
       float e[4];
-      load4(x, v, V, vec_in, e);
+      load4<FULL>(x, v, V, vec_in, e);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (v * 4 + i < V) pick(bv, bidx, e[i], v * 4 + i);
+        if (FULL || v * 4 + i < V) pick(bv, bidx, e[i], v * 4 + i);
     }
   }
 #pragma unroll
@@ -143,15 +166,24 @@ __global__ __launch_bounds__(kThreads) void logsoftmax_argmax_kernel(
   for (int w = 1; w < kThreads / kWave; ++w) pick(mv, mi, sv[w], si[w]);
   const float m = mv;
 
-  // pass 2: s = tree sum of EXP(x - m)
+  // pass 2: s = tree sum of EXP(x - m), each lane in ascending element order
   float acc = 0.f;
   if (tid < T) {
-    for (int v = tid; v < nvec; v += T) {
+#pragma unroll
+    for (int j = 0; j < NVC; ++j) {
+      const int v = tid + j * T;
+      if (v < nvec) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (FULL || v * 4 + i < V) acc = acc + exp_cw(cache[j][i] - m);
+      }
+    }
+    for (int v = tid + NVC * T; v < nvec; v += T) {
       float e[4];
-      load4(x, v, V, vec_in, e);
+      load4<FULL>(x, v, V, vec_in, e);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (v * 4 + i < V) acc = acc + exp_cw(e[i] - m);
+        if (FULL || v * 4 + i < V) acc = acc + exp_cw(e[i] - m);
     }
   }
   const float wsum = wave_tree_sum(acc);
@@ -163,13 +195,11 @@ __global__ __launch_bounds__(kThreads) void logsoftmax_argmax_kernel(
   if (tid == 0) argmax[row] = mi;
   if (logprobs == nullptr || tid >= T) return;
   float* out = logprobs + row * ld;
-  for (int v = tid; v < nvec; v += T) {
-    float e[4];
-    load4(x, v, V, vec_in, e);
+  auto emit = [&](int v, const float (&e)[4]) {
     float o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = (e[i] - m) - L;
-    if (vec_out && v * 4 + 4 <= V) {
+    if ((FULL && vec_out) || (vec_out && v * 4 + 4 <= V)) {
       floatx4 q;
       q[0] = o[0]; q[1] = o[1]; q[2] = o[2]; q[3] = o[3];
       *reinterpret_cast<floatx4*>(out + static_cast<int64_t>(v) * 4) = q;
@@ -178,6 +208,16 @@ __global__ __launch_bounds__(kThreads) void logsoftmax_argmax_kernel(
       for (int i = 0; i < 4; ++i)
         if (v * 4 + i < V) out[static_cast<int64_t>(v) * 4 + i] = o[i];
     }
+  };
+#pragma unroll
+  for (int j = 0; j < NVC; ++j) {
+    const int v = tid + j * T;
+    if (v < nvec) emit(v, cache[j]);
+  }
+  for (int v = tid + NVC * T; v < nvec; v += T) {
+    float e[4];
+    load4<FULL>(x, v, V, vec_in, e);
+    emit(v, e);
   }
 }
 
@@ -195,8 +235,14 @@ extern "C" int bi_logsoftmax_argmax(const float* logits, int64_t M, int64_t V, i
   // 16-byte vector accesses where rows allow them; element accesses otherwise (same math)
   const int vec_in = aligned16(logits) && (ld % 4) == 0;
   const int vec_out = logprobs && aligned16(logprobs) && (ld % 4) == 0;
-  logsoftmax_argmax_kernel<<<dim3(static_cast<unsigned>(M)), dim3(kThreads), 0,
-                             as_stream(stream)>>>(logits, static_cast<int>(V), ld, logprobs,
-                                                  argmax, vec_in, vec_out);
+  const bool full = vec_in && (V % 4) == 0 && (!logprobs || vec_out);
+  if (full)
+    logsoftmax_argmax_kernel<true><<<dim3(static_cast<unsigned>(M)), dim3(kThreads), 0,
+                                     as_stream(stream)>>>(logits, static_cast<int>(V), ld,
+                                                          logprobs, argmax, vec_in, vec_out);
+  else
+    logsoftmax_argmax_kernel<false><<<dim3(static_cast<unsigned>(M)), dim3(kThreads), 0,
+                                      as_stream(stream)>>>(logits, static_cast<int>(V), ld,
+                                                           logprobs, argmax, vec_in, vec_out);
   return launch_status();
 }

@@ -50,11 +50,11 @@ struct Vec<true> {  // 4 fp32
   }
 };
 
-template <bool YF32, int W>
+template <bool YF32, int W, bool FULL>
 __device__ __forceinline__ void store_out(void* yrow, int v, int D, bool vec_ok, const float (&o)[W]) {
   if (YF32) {
     float* p = static_cast<float*>(yrow) + static_cast<int64_t>(v) * W;
-    if (vec_ok && v * W + W <= D && W == 4) {
+    if (vec_ok && (FULL || v * W + W <= D) && W == 4) {
       floatx4 q;
 #pragma unroll
       for (int i = 0; i < 4; ++i) q[i] = o[i];
@@ -66,7 +66,7 @@ __device__ __forceinline__ void store_out(void* yrow, int v, int D, bool vec_ok,
     }
   } else {
     uint16_t* p = static_cast<uint16_t*>(yrow) + static_cast<int64_t>(v) * W;
-    if (vec_ok && v * W + W <= D && W == 8) {
+    if (vec_ok && (FULL || v * W + W <= D) && W == 8) {
       u16x8 q;
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[i] = f32_to_bf16(o[i]);
@@ -80,7 +80,9 @@ __device__ __forceinline__ void store_out(void* yrow, int v, int D, bool vec_ok,
 }
 
 // NV vectors per lane stay in registers between the two passes; longer rows re-read.
-template <bool XF32, bool YF32>
+// FULL: D is a multiple of the vector width and every row is 16-byte aligned, so no
+// element needs a bounds check.
+template <bool XF32, bool YF32, bool FULL>
 __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restrict__ x,
                                                            const uint16_t* __restrict__ gamma,
                                                            void* __restrict__ y, int D,
@@ -103,18 +105,18 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restric
     for (int j = 0; j < NV; ++j) {
       const int v = tid + j * T;
       if (v < nvec) {
-        V::load(xrow, v, D, vec_x, cache[j]);
+        V::load(xrow, v, D, FULL || vec_x, cache[j]);
 #pragma unroll
         for (int i = 0; i < W; ++i)
-          if (v * W + i < D) acc = acc + cache[j][i] * cache[j][i];
+          if (FULL || v * W + i < D) acc = acc + cache[j][i] * cache[j][i];
       }
     }
     for (int v = tid + NV * T; v < nvec; v += T) {
       float e[W];
-      V::load(xrow, v, D, vec_x, e);
+      V::load(xrow, v, D, FULL || vec_x, e);
 #pragma unroll
       for (int i = 0; i < W; ++i)
-        if (v * W + i < D) acc = acc + e[i] * e[i];
+        if (FULL || v * W + i < D) acc = acc + e[i] * e[i];
     }
   }
 
@@ -138,11 +140,11 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restric
           for (int i = 0; i < W; ++i) e[i] = cache[jj][i];
         }
     } else {
-      V::load(xrow, v, D, vec_x, e);
+      V::load(xrow, v, D, FULL || vec_x, e);
     }
     float g[W];
     const uint16_t* gp = gamma + static_cast<int64_t>(v) * W;
-    if (vec_g && v * W + W <= D && W == 8) {
+    if ((FULL || (vec_g && v * W + W <= D)) && W == 8) {
       u16x8 q = *reinterpret_cast<const u16x8*>(gp);
 #pragma unroll
       for (int i = 0; i < W; ++i) g[i] = bf16_to_f32(q[i]);
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restric
     float o[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) o[i] = (e[i] * r) * g[i];
-    store_out<YF32, W>(yrow, v, D, vec_y, o);
+    store_out<YF32, W, FULL>(yrow, v, D, vec_y, o);
   }
 }
 
@@ -179,13 +181,16 @@ extern "C" int bi_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, 
   const int vec_g = aligned16(gamma);
   dim3 grid(static_cast<unsigned>(M)), block(kThreads);
   hipStream_t s = as_stream(stream);
-  if (!xf && !yf)
-    rmsnorm_kernel<false, false><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, vec_y, vec_g);
+  const bool full_bf16 = !xf && !yf && vec_x && vec_y && vec_g && (D % 8) == 0;
+  if (full_bf16)
+    rmsnorm_kernel<false, false, true><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, vec_y, vec_g);
+  else if (!xf && !yf)
+    rmsnorm_kernel<false, false, false><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, vec_y, vec_g);
   else if (!xf && yf)
-    rmsnorm_kernel<false, true><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, 0, vec_g);
+    rmsnorm_kernel<false, true, false><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, 0, vec_g);
   else if (xf && !yf)
-    rmsnorm_kernel<true, false><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, 0, vec_g);
+    rmsnorm_kernel<true, false, false><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, 0, vec_g);
   else
-    rmsnorm_kernel<true, true><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, vec_y, vec_g);
+    rmsnorm_kernel<true, true, false><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, vec_y, vec_g);
   return launch_status();
 }
