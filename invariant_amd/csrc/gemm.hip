@@ -7,10 +7,17 @@
 // and use it for every shape.  Here that configuration is:
 //   workgroup tile 128 x 128, K step 64, 4 waves (2 x 2), each wave 64 x 64 made of
 //   2 x 2 v_mfma_f32_32x32x16_bf16, fp32 accumulators starting at +0, K walked in
-//   ascending 16-wide steps from 0 to K.  Rows past M and K past K read as zeros and
-//   are never stored.
+//   ascending 16-wide steps from 0 to K.  Products past K are exact zeros; rows past M
+//   (columns past N) are never stored.
 // Output element (i, j) is therefore the result of the same instruction sequence for
 // every M and every position of row i inside its tile.
+//
+// Main kernel (bf16 A, B as [N, K]): tiles stream into LDS by direct-to-LDS 16-byte
+// loads through a 4-stage ring (three K steps in flight while one is multiplied); the
+// 16-byte k-chunks of row r sit at chunk position c ^ swz(r) so that the 16-byte operand
+// reads of 8 (or 16) consecutive rows hit distinct banks.  The fp32-A path and the
+// split-K comparison variant stage through registers instead; they share the tile shape,
+// the instruction and the K order.
 //
 // A may be fp32 ("FP32 upcast" of the cross-vendor mismatch abstract): each value is
 // split exactly into bf16 hi + mid + lo (truncations, so hi + mid + lo == a for normal
@@ -206,6 +213,160 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
 }
 
+constexpr int STAGES = 4;
+constexpr int TILE = BM * BK;  // bf16 elements of one operand tile (128 rows x 64 k)
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.  Written in
+// asm so that the compiler does not order every later LDS read behind it; m0 is saved
+// and restored.  No register is written by the load.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(g)
+      : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding and all
+// its LDS operations are done, then meet the other waves.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
+}
+
+__global__ __launch_bounds__(kThreads) void gemm_dma_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
+    int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sA[STAGES][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB[STAGES][TILE];
+
+  const int nwg = tiles_m * tiles_n;
+  int id = blockIdx.x;
+  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+  const int group = 8;
+  const int per_group = group * tiles_n;
+  const int gi = id / per_group;
+  const int first_m = gi * group;
+  const int gm = min(tiles_m - first_m, group);
+  const int tm = first_m + (id % per_group) % gm;
+  const int tn = (id % per_group) / gm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // DMA assignment: instruction j of wave w fills tile rows 32w + 8j .. +7; lane l writes
+  // LDS chunk position l % 8 of row 32w + 8j + l / 8 with k-chunk (l % 8) ^ swz(row).
+  const uint16_t* asrc[4];
+  const uint16_t* bsrc[4];
+  int kc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int R = 32 * wave + 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ swz(R);
+    const int ra = min(tm * BM + R, M - 1);
+    const int rb = min(tn * BN + R, N - 1);
+    asrc[j] = A + static_cast<int64_t>(ra) * lda + c * 8;
+    bsrc[j] = B + static_cast<int64_t>(rb) * ldb + c * 8;
+    kc[j] = c * 8;
+  }
+  auto issue = [&](int buf, int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = k0 + kc[j] < K;   // a chunk wholly past K re-reads chunk 0 (zeroed below)
+      dma16(in ? asrc[j] + k0 : asrc[j], lds_u32(&sA[buf][(32 * wave + 8 * j) * BK]));
+      dma16(in ? bsrc[j] + k0 : bsrc[j], lds_u32(&sB[buf][(32 * wave + 8 * j) * BK]));
+    }
+  };
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (K + BK - 1) / BK;
+  const bool ktail = (K % BK) != 0;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  if (nk > 2) issue(2, 2);
+
+  const int orow = lane & 31;
+  const int okc = lane >> 5;   // which 8-wide half of a 16-wide K step
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & (STAGES - 1);
+    if (kt + 2 < nk) wait_and_barrier<16>();
+    else if (kt + 1 < nk) wait_and_barrier<8>();
+    else wait_and_barrier<0>();
+    if (ktail && kt == nk - 1) {
+      // zero every element at k >= K in the pieces this lane's own loads wrote
+      const int k0 = kt * BK;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int pos = (32 * wave + 8 * j + (lane >> 3)) * BK + (lane & 7) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (k0 + kc[j] + e >= K) {
+            sA[buf][pos + e] = 0;
+            sB[buf][pos + e] = 0;
+          }
+      }
+      wait_and_barrier<0>();
+    }
+    if (kt + 3 < nk) issue((kt + 3) & (STAGES - 1), kt + 3);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 av[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + orow;
+        av[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(&sA[buf][r * BK + (((2 * ks + okc) ^ swz(r)) * 8)]));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn * 64 + j * 32 + orow;
+        bv[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(&sB[buf][r * BK + (((2 * ks + okc) ^ swz(r)) * 8)]));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = tn * BN + wn * 64 + j * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = tm * BM + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row >= M) continue;
+        if (c_f32)
+          static_cast<float*>(C)[static_cast<int64_t>(row) * ldc + col] = acc[i][j][r];
+        else
+          static_cast<uint16_t*>(C)[static_cast<int64_t>(row) * ldc + col] = f32_to_bf16(acc[i][j][r]);
+      }
+    }
+}
+
 // Fixed-order sum of the split-K partials (comparison variant only).
 __global__ void splitk_reduce_kernel(const float* __restrict__ ws, void* __restrict__ C, int M,
                                      int N, int64_t ldc, int c_f32, int splits) {
@@ -258,9 +419,9 @@ extern "C" int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t
         A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
         0, int(K), 0);
   else
-    gemm_kernel<false><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
-        A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
-        0, int(K), 0);
+    gemm_dma_kernel<<<dim3(static_cast<unsigned>(nwg)), dim3(kThreads), 0, s>>>(
+        static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, int(M), int(N),
+        int(K), lda, ldb, ldc, cf, tm, tn);
   return launch_status();
 }
 

@@ -134,6 +134,21 @@ def test_fp32_operand_variant(lib):
     assert same_bits(lib.bi_gemm(A[:1], bf16(w), out_dtype=torch.float32)[0], full[0])
 
 
+def test_k_tail_with_garbage_past_k(lib):
+    # rows padded to a multiple of 8 elements, the padding filled with NaN: every product
+    # past K must be an exact zero
+    for m, n, k in [(65, 70, 1003), (3, 130, 77), (200, 33, 9)]:
+        a, b = gemm_inputs(m, n, k, cfg=35)
+        kp = (k + 7) // 8 * 8 + 8
+        A = torch.full((m, kp), float("nan"), device="cuda").to(torch.bfloat16)
+        W = torch.full((n, kp), float("nan"), device="cuda").to(torch.bfloat16)
+        A[:, :k] = bf16(a)
+        W[:, :k] = bf16(_nk(b))
+        c = lib.bi_gemm(A[:, :k], W[:, :k])
+        r = bf16_within_1ulp(bits(c), gemm_f64(a, b))
+        assert r["ok"], (m, n, k, r)
+
+
 def test_empty_and_ragged(lib):
     A = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
     W = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
