@@ -12,10 +12,11 @@
 // Output element (i, j) is therefore the result of the same instruction sequence for
 // every M and every position of row i inside its tile.
 //
-// Main kernel (bf16 A, B as [N, K]): tiles stream into LDS by direct-to-LDS 16-byte
-// loads through a 4-stage ring (three K steps in flight while one is multiplied); the
-// 16-byte k-chunks of row r sit at chunk position c ^ swz(r) so that the 16-byte operand
-// reads of 8 (or 16) consecutive rows hit distinct banks.  The fp32-A path and the
+// Main kernel (bf16 A, B as [N, K]): 32-wide K slices of both tiles stream into LDS by
+// direct-to-LDS 16-byte loads through a 4-stage ring (three slices in flight while one is
+// multiplied, 64 KB of LDS, two workgroups per CU); the 16-byte k-chunks of row r sit at
+// chunk position c ^ swz(r) so that the 16-byte operand reads of consecutive rows hit
+// distinct banks.  How K is staged does not change the instruction sequence per element.  The fp32-A path and the
 // split-K comparison variant stage through registers instead; they share the tile shape,
 // the instruction and the K order.
 //
@@ -214,22 +215,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 }
 
 constexpr int STAGES = 4;
-constexpr int TILE = BM * BK;  // bf16 elements of one operand tile (128 rows x 64 k)
+constexpr int DBK = 32;             // K step of one LDS stage in the main kernel
+constexpr int DTILE = BM * DBK;     // bf16 elements of one operand tile per stage (8 KB)
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// 64-byte LDS rows of 4 chunks; chunk c of row r sits at position c ^ swz(r), which puts
+// the 16-byte reads of 8 (or 16) consecutive rows into distinct banks.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.  Written in
-// asm so that the compiler does not order every later LDS read behind it; m0 is saved
-// and restored.  No register is written by the load.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane, addressed as
+// a wave-uniform 64-bit base plus a per-lane 32-bit byte offset.  Written in asm so that
+// the compiler does not order every later LDS read behind it; m0 is saved and restored
+// and no register is written by the load.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds_addr), "v"(g)
+      : "s"(lds_addr), "v"(off), "s"(base)
       : "memory");
 }
 
@@ -244,11 +249,19 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
 }
 
-__global__ __launch_bounds__(kThreads) void gemm_dma_kernel(
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// A and B must each span less than 4 GiB (byte offsets are 32-bit); the host checks.
+__global__ __launch_bounds__(kThreads, 2) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
     int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint16_t sA[STAGES][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB[STAGES][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA[STAGES][DTILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB[STAGES][DTILE];
 
   const int nwg = tiles_m * tiles_n;
   int id = blockIdx.x;
@@ -266,28 +279,42 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // DMA assignment: instruction j of wave w fills tile rows 32w + 8j .. +7; lane l writes
-  // LDS chunk position l % 8 of row 32w + 8j + l / 8 with k-chunk (l % 8) ^ swz(row).
-  const uint16_t* asrc[4];
-  const uint16_t* bsrc[4];
-  int kc[4];
+  // DMA assignment: instruction j of wave w fills tile rows 32w + 16j .. +15; lane l writes
+  // chunk position l % 4 of row 32w + 16j + l / 4 with k-chunk (l % 4) ^ swz(row).
+  uint32_t aoff[2], boff[2];
+  int kc[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int R = 32 * wave + 8 * j + (lane >> 3);
-    const int c = (lane & 7) ^ swz(R);
+  for (int j = 0; j < 2; ++j) {
+    const int R = 32 * wave + 16 * j + (lane >> 2);
+    const int c = (lane & 3) ^ swz(R);
     const int ra = min(tm * BM + R, M - 1);
     const int rb = min(tn * BN + R, N - 1);
-    asrc[j] = A + static_cast<int64_t>(ra) * lda + c * 8;
-    bsrc[j] = B + static_cast<int64_t>(rb) * ldb + c * 8;
+    aoff[j] = static_cast<uint32_t>((static_cast<int64_t>(ra) * lda + c * 8) * 2);
+    boff[j] = static_cast<uint32_t>((static_cast<int64_t>(rb) * ldb + c * 8) * 2);
     kc[j] = c * 8;
   }
+  const int nk = (K + DBK - 1) / DBK;
+  const bool ktail = (K % DBK) != 0;
   auto issue = [&](int buf, int kt) {
-    const int k0 = kt * BK;
+    const int k0 = kt * DBK;
+    if (ktail && kt == nk - 1) {
+      // last, partial step: a chunk wholly past K re-reads chunk 0 (zeroed after landing)
+      const void* ab = uniform_ptr(A);
+      const void* bb = uniform_ptr(B);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool in = k0 + kc[j] < K;   // a chunk wholly past K re-reads chunk 0 (zeroed below)
-      dma16(in ? asrc[j] + k0 : asrc[j], lds_u32(&sA[buf][(32 * wave + 8 * j) * BK]));
-      dma16(in ? bsrc[j] + k0 : bsrc[j], lds_u32(&sB[buf][(32 * wave + 8 * j) * BK]));
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t adv = (k0 + kc[j] < K) ? static_cast<uint32_t>(k0) * 2 : 0u;
+        dma16(ab, aoff[j] + adv, lds_u32(&sA[buf][(32 * wave + 16 * j) * DBK]));
+        dma16(bb, boff[j] + adv, lds_u32(&sB[buf][(32 * wave + 16 * j) * DBK]));
+      }
+    } else {
+      const void* ab = uniform_ptr(A + k0);
+      const void* bb = uniform_ptr(B + k0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        dma16(ab, aoff[j], lds_u32(&sA[buf][(32 * wave + 16 * j) * DBK]));
+        dma16(bb, boff[j], lds_u32(&sB[buf][(32 * wave + 16 * j) * DBK]));
+      }
     }
   };
 
@@ -299,8 +326,6 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (K + BK - 1) / BK;
-  const bool ktail = (K % BK) != 0;
   issue(0, 0);
   if (nk > 1) issue(1, 1);
   if (nk > 2) issue(2, 2);
@@ -309,15 +334,15 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(
   const int okc = lane >> 5;   // which 8-wide half of a 16-wide K step
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & (STAGES - 1);
-    if (kt + 2 < nk) wait_and_barrier<16>();
-    else if (kt + 1 < nk) wait_and_barrier<8>();
+    if (kt + 2 < nk) wait_and_barrier<8>();
+    else if (kt + 1 < nk) wait_and_barrier<4>();
     else wait_and_barrier<0>();
     if (ktail && kt == nk - 1) {
       // zero every element at k >= K in the pieces this lane's own loads wrote
-      const int k0 = kt * BK;
+      const int k0 = kt * DBK;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int pos = (32 * wave + 8 * j + (lane >> 3)) * BK + (lane & 7) * 8;
+      for (int j = 0; j < 2; ++j) {
+        const int pos = (32 * wave + 16 * j + (lane >> 2)) * DBK + (lane & 3) * 8;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (k0 + kc[j] + e >= K) {
@@ -329,17 +354,17 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(
     }
     if (kt + 3 < nk) issue((kt + 3) & (STAGES - 1), kt + 3);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < DBK / 16; ++ks) {
       bf16x8 av[2], bv[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = wm * 64 + i * 32 + orow;
-        av[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(&sA[buf][r * BK + (((2 * ks + okc) ^ swz(r)) * 8)]));
+        av[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(&sA[buf][r * DBK + (((2 * ks + okc) ^ swz(r)) * 8)]));
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r = wn * 64 + j * 32 + orow;
-        bv[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(&sB[buf][r * BK + (((2 * ks + okc) ^ swz(r)) * 8)]));
+        bv[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(&sB[buf][r * DBK + (((2 * ks + okc) ^ swz(r)) * 8)]));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -418,10 +443,14 @@ extern "C" int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t
     gemm_kernel<true><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
         A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
         0, int(K), 0);
-  else
+  else if (M * lda * 2 < (int64_t(1) << 32) && N * ldb * 2 < (int64_t(1) << 32))
     gemm_dma_kernel<<<dim3(static_cast<unsigned>(nwg)), dim3(kThreads), 0, s>>>(
         static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, int(M), int(N),
         int(K), lda, ldb, ldc, cf, tm, tn);
+  else  // operands of 4 GiB or more: register-staged kernel (same tile, instruction, K order)
+    gemm_kernel<false><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
+        A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
+        0, int(K), 0);
   return launch_status();
 }
 
