@@ -204,11 +204,13 @@ int bi_logsoftmax_argmax(const float* logits, int64_t M, int64_t V, int64_t ld, 
  * as long as every element runs the same code.  All of these compute in fp32 and
  * round once to the output dtype.
  *
- * bi_embedding: out[t, :] = table[ids[t], :].  table [vocab, D] bf16, out [T, D] of
- *   out_dtype (exact widening for BI_F32).  ids outside [0, vocab) produce zeros.
+ * bi_embedding: out[t, :] = table[ids[t], :] (a row gather: the embedding lookup, and
+ *   the pick of each sequence's last hidden row before the LM head).  table [vocab, D]
+ *   of table_dtype, out [T, D] of out_dtype (exact when widening; one RNE rounding for
+ *   fp32 -> bf16).  ids outside [0, vocab) produce zeros.
  */
-int bi_embedding(const int32_t* ids, const void* table, void* out, int64_t T, int64_t D,
-                 int64_t vocab, int out_dtype, void* stream);
+int bi_embedding(const int32_t* ids, const void* table, int table_dtype, void* out, int64_t T,
+                 int64_t D, int64_t vocab, int out_dtype, void* stream);
 
 /* bi_rope_qkv: splits a fused projection qkv [T, (Hq + 2 Hkv) * D] (row stride ldqkv,
  *   dtype qkv_dtype) into q [T, Hq, D], k [T, Hkv, D], v [T, Hkv, D] (bf16, contiguous)

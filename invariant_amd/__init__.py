@@ -33,7 +33,7 @@ _SIGS = {
     "bi_attention": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
                                 _I32, _I64, _F32, _P, _c.c_int, _P, _SZ, _P]),
     "bi_logsoftmax_argmax": (_c.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
-    "bi_embedding": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _c.c_int, _P]),
+    "bi_embedding": (_c.c_int, [_P, _P, _c.c_int, _P, _I64, _I64, _I64, _c.c_int, _P]),
     "bi_rope_qkv": (_c.c_int, [_P, _I64, _c.c_int, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F64, _P]),
     "bi_swiglu": (_c.c_int, [_P, _I64, _P, _I64, _I64, _P]),
     "bi_residual_add": (_c.c_int, [_P, _c.c_int, _P, _c.c_int, _P, _c.c_int, _I64, _P]),
@@ -184,12 +184,13 @@ def bi_logsoftmax_argmax(logits, logprobs=None, argmax=None, want_logprobs: bool
 
 
 def bi_embedding(ids, table, out=None, out_dtype=torch.bfloat16):
+    """out[t] = table[ids[t]] (rows of a bf16 or fp32 table, ids int32 on the device)."""
     T = ids.shape[0]
     V, D = table.shape
     if out is None:
         out = torch.empty((T, D), dtype=out_dtype, device=table.device)
-    _check("bi_embedding", load().bi_embedding(_ptr(ids), _ptr(table), _ptr(out), T, D, V,
-                                                _code(out.dtype), _stream(table)))
+    _check("bi_embedding", load().bi_embedding(_ptr(ids), _ptr(table), _code(table.dtype), _ptr(out),
+                                                T, D, V, _code(out.dtype), _stream(table)))
     return out
 
 

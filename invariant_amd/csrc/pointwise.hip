@@ -19,14 +19,14 @@ __device__ __forceinline__ void store_from_f32(void* p, int64_t i, float v, bool
   else static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
 }
 
-__global__ void embedding_kernel(const int32_t* __restrict__ ids, const uint16_t* __restrict__ table,
-                                 void* __restrict__ out, int64_t T, int64_t D, int64_t vocab,
-                                 int out_f32) {
+__global__ void embedding_kernel(const int32_t* __restrict__ ids, const void* __restrict__ table,
+                                 int table_f32, void* __restrict__ out, int64_t T, int64_t D,
+                                 int64_t vocab, int out_f32) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= T * D) return;
   const int64_t t = i / D, d = i % D;
   const int32_t id = ids[t];
-  const float v = (id >= 0 && id < vocab) ? bf16_to_f32(table[static_cast<int64_t>(id) * D + d]) : 0.f;
+  const float v = (id >= 0 && id < vocab) ? load_as_f32(table, static_cast<int64_t>(id) * D + d, table_f32) : 0.f;
   store_from_f32(out, i, v, out_f32);
 }
 
@@ -89,15 +89,16 @@ unsigned blocks_for(int64_t n, int per) { return static_cast<unsigned>((n + per 
 
 using namespace bi;
 
-extern "C" int bi_embedding(const int32_t* ids, const void* table, void* out, int64_t T, int64_t D,
-                            int64_t vocab, int out_dtype, void* stream) {
-  if (out_dtype != BI_BF16 && out_dtype != BI_F32) return BI_ERR_DTYPE;
+extern "C" int bi_embedding(const int32_t* ids, const void* table, int table_dtype, void* out,
+                            int64_t T, int64_t D, int64_t vocab, int out_dtype, void* stream) {
+  if ((out_dtype != BI_BF16 && out_dtype != BI_F32) || (table_dtype != BI_BF16 && table_dtype != BI_F32))
+    return BI_ERR_DTYPE;
   if (T < 0 || D < 0 || vocab < 0) return BI_ERR_SHAPE;
   if (T == 0 || D == 0) return BI_OK;
   if (T * D > (int64_t(1) << 40)) return BI_ERR_SHAPE;
   if (!ids || !table || !out) return BI_ERR_NULL;
   embedding_kernel<<<blocks_for(T * D, 256), 256, 0, as_stream(stream)>>>(
-      ids, static_cast<const uint16_t*>(table), out, T, D, vocab, out_dtype == BI_F32);
+      ids, table, table_dtype == BI_F32, out, T, D, vocab, out_dtype == BI_F32);
   return launch_status();
 }
 

@@ -78,3 +78,48 @@ def bits_equal(a: np.ndarray, b: np.ndarray) -> dict:
     ub = b.view(np.uint8).reshape(b.shape + (-1,))
     diff = np.any(ua != ub, axis=-1)
     return dict(ok=not bool(diff.any()), n_diff=int(diff.sum()))
+
+
+def residual_sum_within(got_bits, ref64, terms, n_ulp: float = 2.0, axis=-1) -> dict:
+    """A bf16 output that ends in a sum out = t_1 + t_2 + ... of stored bf16 terms (a
+    residual add).  Two correct evaluations may round each stored term differently (by
+    one ulp of that term), and the sum can cancel, so the band is set by the terms:
+        |got - bf16_rne(ref)| <= n_ulp * ulp_bf16(max_k |t_k|) + ulp_bf16(max(|ref|, floor))
+    with floor = rms(ref row) / 64 as in bf16_within_1ulp."""
+    got = bf16_to_f64(np.asarray(got_bits, dtype=np.uint16))
+    ref64 = np.asarray(ref64, dtype=np.float64)
+    if got.shape != ref64.shape:
+        return dict(ok=False, reason=f"shape {got.shape} != {ref64.shape}")
+    if not np.all(np.isfinite(got)):
+        return dict(ok=False, reason="non-finite output")
+    big = np.max(np.stack([np.abs(np.asarray(t, dtype=np.float64)) for t in terms]), axis=0)
+    floor = _row_floor(ref64, axis=axis)
+    tol = n_ulp * ulp_bf16(big) + ulp_bf16(np.maximum(np.abs(ref64), floor))
+    err = np.abs(got - bf16_to_f64(f64_to_bf16(ref64)))
+    bad = err > tol
+    return dict(ok=not bool(bad.any()), n_bad=int(bad.sum()), max_of_tol=float((err / tol).max()),
+                frac_exact=float(np.mean(err == 0.0)))
+
+
+def composed_drift(got_bits, ref64, axis=-1) -> dict:
+    """Drift of a composed bf16 computation (a whole decoder layer) from its oracle chain.
+
+    Two correct bf16 chains round their stored intermediates differently at about one
+    element in several hundred per operation; wide later sums (a 4096- or 14336-long dot
+    product) add those one-ulp differences up, so after a layer about a third of the
+    outputs differ by an ulp or two and the largest differences reach a few percent of
+    the row rms.  A wrong weight, rotation or mask moves outputs by the order of the rms
+    itself, so the gate is:
+        max |err| <= rms / 8,  mean |err| <= rms / 256,  >= 2/3 within one own-ulp."""
+    got = bf16_to_f64(np.asarray(got_bits, dtype=np.uint16))
+    ref64 = np.asarray(ref64, dtype=np.float64)
+    if got.shape != ref64.shape or not np.all(np.isfinite(got)):
+        return dict(ok=False, reason="shape or non-finite")
+    rms = np.sqrt(np.mean(ref64 ** 2, axis=axis, keepdims=True))
+    err = np.abs(got - ref64)
+    rb = bf16_to_f64(f64_to_bf16(ref64))
+    within1 = np.abs(got - rb) <= ulp_bf16(np.maximum(np.abs(ref64), 1e-30))
+    mx, mean = float((err / rms).max()), float((err / rms).mean())
+    f1 = float(within1.mean())
+    return dict(ok=mx <= 1 / 8 and mean <= 1 / 256 and f1 >= 2 / 3, max_over_rms=mx, mean_over_rms=mean,
+                frac_within_1ulp=f1, frac_exact=float(np.mean(got == rb)))

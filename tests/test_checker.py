@@ -58,3 +58,22 @@ def test_bits_equal():
     assert bits_equal(a, a.copy())["ok"] and not bits_equal(a, b)["ok"]
     z = np.float32([0.0]); nz = np.float32([-0.0])
     assert not bits_equal(z, nz)["ok"]
+
+
+def test_composed_drift_rejects_gross_errors():
+    from oracle.check import composed_drift
+    rng = np.random.default_rng(1)
+    ref = rng.standard_normal((1, 4096)) * 2.5
+    good = fp.f64_to_bf16(ref)
+    assert composed_drift(good, ref)["ok"]
+    # an ulp of noise on a third of the elements still passes
+    noisy = fp.bf16_to_f64(good).copy()
+    sel = rng.random((1, 4096)) < 0.33
+    noisy[sel] += fp.ulp_bf16(noisy[sel]) * rng.choice([-1, 1], int(sel.sum()))
+    assert composed_drift(fp.f64_to_bf16(noisy), ref)["ok"]
+    # a missing residual term, a sign flip or zeros fail
+    assert not composed_drift(fp.f64_to_bf16(ref * 0.7), ref)["ok"]
+    assert not composed_drift(fp.f64_to_bf16(-ref), ref)["ok"]
+    assert not composed_drift(np.zeros_like(good), ref)["ok"]
+    wrong = ref.copy(); wrong[0, :300] += 0.5
+    assert not composed_drift(fp.f64_to_bf16(wrong), ref)["ok"]
