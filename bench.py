@@ -267,6 +267,31 @@ def main():
                      "traffic": None},
         "kernel_time_ms": round(kernel_sum * 1e3, 4),
     }
+    # non-invariant comparison variants on the same inputs (the cost of invariance)
+    L = inp["L"]
+    total_chunks = int(sum((int(l) - 1) // 256 + 1 for l in L))
+    variants = [
+        ("gemm", "bi_gemm_splitk", lambda: bi.bi_gemm_splitk(inp["A"], inp["B_nk"], out=inp["C"])),
+        ("attention_decode", "bi_attention_batchdep_split", lambda: bi.bi_attention_batchdep_split(
+            inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["bt"],
+            inp["seq_lens"], inp["qsl"], int(L.max()), total_chunks, 1.0 / np.sqrt(128.0),
+            out=inp["attn_out"], workspace=inp["ws"])),
+    ]
+    comp = {}
+    for name, vname, fn in variants:
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / K * 1e-3
+        comp[name] = dict(variant=vname, ms=round(t * 1e3, 5),
+                          invariant_ms=round(per[name] * 1e3, 5),
+                          invariant_slowdown=round(per[name] / t, 4))
+    res["nonbi_comparison"] = comp
     if not args.no_cpu_baseline:
         log("timing the oracle on a sample")
         res["cpu_baseline"] = cpu_baseline(inp, torch, wk, t_peak)

@@ -182,6 +182,22 @@ int bi_attention(const void* q, const void* k_new, const void* v_new, void* k_ca
                  int32_t max_pages_per_seq, int64_t max_seq_len, float scale, void* out,
                  int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Comparison variant, NOT batch-invariant (split-KV / FlashDecoding with a number of
+ * splits chosen from the batch, as [DN] describes for decode kernels): same arguments and
+ * layouts as bi_attention (at most 1024 tokens per call) plus total_chunks = sum over
+ * tokens of (position / 256 + 1).  Each workgroup walks a group of consecutive 256-key
+ * chunks, merging in registers; the group size is about total_chunks * Hkv / 1024, so the
+ * association of a token's merges -- and its bits -- depends on the rest of the batch.
+ * workspace >= bi_attention_workspace_bytes(num_tokens, Hq, D, max_seq_len). */
+int bi_attention_batchdep_split(const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* query_start_loc,
+                                int32_t batch, int64_t num_tokens, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                int32_t max_pages_per_seq, int64_t max_seq_len,
+                                int64_t total_chunks, float scale, void* out, int out_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ log-softmax + argmax
  * [GPU] greedy decoding and token probabilities from normalised scores; [DN]
  * temperature 0 = always the most likely token; [SM] near ties decide the token.

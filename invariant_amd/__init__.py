@@ -32,6 +32,9 @@ _SIGS = {
     "bi_attention_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I64]),
     "bi_attention": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
                                 _I32, _I64, _F32, _P, _c.c_int, _P, _SZ, _P]),
+    "bi_attention_batchdep_split": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32,
+                                               _I32, _I32, _I32, _I64, _I64, _F32, _P, _c.c_int, _P,
+                                               _SZ, _P]),
     "bi_logsoftmax_argmax": (_c.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "bi_embedding": (_c.c_int, [_P, _P, _c.c_int, _P, _I64, _I64, _I64, _c.c_int, _P]),
     "bi_rope_qkv": (_c.c_int, [_P, _I64, _c.c_int, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F64, _P]),
@@ -169,6 +172,27 @@ def bi_attention(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(seq_lens), _ptr(query_start_loc), B, T, Hq, Hkv, D, page, max_pages, int(max_seq_len),
         float(scale), _ptr(out), _code(out.dtype), _ptr(workspace), wsz, _stream(q)))
+    return out
+
+
+def bi_attention_batchdep_split(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+                                query_start_loc, max_seq_len: int, total_chunks: int, scale: float,
+                                out=None, out_dtype=torch.bfloat16, workspace=None):
+    """Comparison variant (not batch-invariant), same layouts as bi_attention."""
+    T, Hq, D = q.shape
+    Hkv = k_new.shape[1]
+    page = v_cache.shape[3]
+    B, max_pages = block_table.shape
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=out_dtype, device=q.device)
+    need = bi_attention_workspace_bytes(T, Hq, D, max_seq_len)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("bi_attention_batchdep_split", load().bi_attention_batchdep_split(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(query_start_loc), B, T, Hq, Hkv, D, page, max_pages, int(max_seq_len),
+        int(total_chunks), float(scale), _ptr(out), _code(out.dtype), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q)))
     return out
 
 

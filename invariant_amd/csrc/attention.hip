@@ -330,14 +330,14 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch, int hq,
-    int max_chunks, int64_t n_rows, void* __restrict__ out, int out_f32) {
+    int max_chunks, int64_t n_rows, void* __restrict__ out, int out_f32, int group) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= n_rows) return;
   const int t = static_cast<int>(row / hq);
   const int lane = threadIdx.x & 63;
   const int b = find_seq_wave(qsl, batch, t);
   const int pos = seq_lens[b] - (qsl[b + 1] - qsl[b]) + (t - qsl[b]);
-  const int nc = pos / CHUNK + 1;
+  const int nc = (pos / CHUNK) / group + 1;   // partials to merge (chunks, or groups of them)
   const float* ml = ws_ml + row * max_chunks * 2;
   const float* po = ws_o + row * max_chunks * HD + 2 * lane;
   float m = 0.f, l = 0.f, o0 = 0.f, o1 = 0.f;
@@ -378,6 +378,62 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     uint16_t* p = static_cast<uint16_t*>(out) + row * HD + 2 * lane;
     p[0] = f32_to_bf16(r0);
     p[1] = f32_to_bf16(r1);
+  }
+}
+
+// ---------------------------------------------------------------- comparison variant
+// NOT batch-invariant: one workgroup per (token, group of `group` consecutive chunks, kv
+// head) walks its chunks and merges them in registers, then the groups are merged.  The
+// group size is chosen from the whole batch's work, so the association of the merges of
+// a token -- and its bits -- change with the batch.
+__global__ __launch_bounds__(256) void attn_group_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch,
+    int max_pages, int hq, int hkv, int ps, int max_groups, int group, float sl2,
+    float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+  __shared__ ChunkLDS sh;
+  const int t = blockIdx.x / max_groups;
+  const int gi = blockIdx.x % max_groups;
+  const int kvh = blockIdx.y;
+  const int b = find_seq_wave(qsl, batch, t);
+  const int L = seq_lens[b];
+  const int pos = L - (qsl[b + 1] - qsl[b]) + (t - qsl[b]);
+  const int c_first = gi * group;
+  if (c_first * CHUNK > pos) return;
+  const int c_last = min(pos / CHUNK, c_first + group - 1);
+  const int G = hq / hkv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const bool used = col < G;
+  u16x8 qop[4];
+  load_q(q, t, kvh * G + col, hq, used, qop);
+  Seq sq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, kvh, L};
+  float m = 0.f, l = 0.f;
+  floatx4 o[2];
+  for (int c = c_first; c <= c_last; ++c) {
+    float m_c, l_c;
+    floatx4 oc[2];
+    chunk_partial(sq, c, qop, used ? pos : -1, sl2, sh, m_c, l_c, oc);
+    if (c == c_first) {
+      m = m_c; l = l_c; o[0] = oc[0]; o[1] = oc[1];
+    } else {
+      float a, bb;
+      merge_step(m, l, m_c, l_c, a, bb);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[j][r] = mix(o[j][r], oc[j][r], a, bb);
+    }
+  }
+  if (!used) return;
+  const int64_t slot = (static_cast<int64_t>(t) * hq + kvh * G + col) * max_groups + gi;
+  float* po = ws_o + slot * HD + 4 * (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) *reinterpret_cast<floatx4*>(po + 16 * (2 * w + j)) = o[j];
+  if (w == 0 && (lane >> 4) == 0) {
+    ws_ml[2 * slot] = m;
+    ws_ml[2 * slot + 1] = l;
   }
 }
 
@@ -525,7 +581,7 @@ extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new,
     const int64_t rows = num_tokens * num_q_heads;
     attn_combine_kernel<<<dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s>>>(
         ws_ml, ws_o, seq_lens, query_start_loc, batch, num_q_heads, static_cast<int>(maxc), rows,
-        out, of);
+        out, of, 1);
   } else {
     const int NT = 16 / G;
     const int64_t blocks = (num_tokens + NT - 1) / NT;
@@ -534,5 +590,58 @@ extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new,
         static_cast<const uint16_t*>(v_cache), block_table, seq_lens, query_start_loc, batch,
         max_pages_per_seq, num_q_heads, num_kv_heads, page_size, num_tokens, sl2, out, of);
   }
+  return launch_status();
+}
+
+extern "C" int bi_attention_batchdep_split(
+    const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    const int32_t* block_table, const int32_t* seq_lens, const int32_t* query_start_loc,
+    int32_t batch, int64_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t page_size, int32_t max_pages_per_seq, int64_t max_seq_len, int64_t total_chunks,
+    float scale, void* out, int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (out_dtype != BI_BF16 && out_dtype != BI_F32) return BI_ERR_DTYPE;
+  if (batch < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || page_size < 1 ||
+      max_pages_per_seq < 1 || max_seq_len < 0 || total_chunks < 0)
+    return BI_ERR_SHAPE;
+  if (head_dim != HD) return BI_ERR_UNSUPPORTED;
+  if (num_q_heads % num_kv_heads) return BI_ERR_SHAPE;
+  const int G = num_q_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return BI_ERR_UNSUPPORTED;
+  if (page_size % 16 || CHUNK % page_size) return BI_ERR_UNSUPPORTED;
+  if (max_seq_len > static_cast<int64_t>(max_pages_per_seq) * page_size) return BI_ERR_SHAPE;
+  if (num_tokens == 0 || batch == 0) return BI_OK;
+  if (num_tokens > SPLIT_MAX_TOKENS) return BI_ERR_UNSUPPORTED;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !block_table || !seq_lens ||
+      !query_start_loc || !out)
+    return BI_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(out))
+    return BI_ERR_ALIGN;
+  const size_t need = bi_attention_workspace_bytes(num_tokens, num_q_heads, head_dim, max_seq_len);
+  if (!workspace || workspace_bytes < need) return BI_ERR_WORKSPACE;
+  // occupancy heuristic: about four workgroups per CU over the whole batch
+  const int64_t work = (total_chunks > 0 ? total_chunks : num_tokens) * num_kv_heads;
+  int64_t group = (work + 1023) / 1024;
+  if (group < 1) group = 1;
+  const int64_t maxc = chunks_for(max_seq_len);
+  if (group > maxc) group = maxc;
+  const int64_t maxg = (maxc + group - 1) / group;
+  hipStream_t s = as_stream(stream);
+  const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  kv_write_kernel<<<dim3(static_cast<unsigned>(num_tokens)), dim3(256), 0, s>>>(
+      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+      static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_table, seq_lens,
+      query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size);
+  float* ws_ml = static_cast<float*>(workspace);
+  float* ws_o = ws_ml + ml_floats(num_tokens * num_q_heads * maxg);
+  attn_group_kernel<<<dim3(static_cast<unsigned>(num_tokens * maxg), num_kv_heads), dim3(256), 0, s>>>(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+      static_cast<const uint16_t*>(v_cache), block_table, seq_lens, query_start_loc, batch,
+      max_pages_per_seq, num_q_heads, num_kv_heads, page_size, static_cast<int>(maxg),
+      static_cast<int>(group), sl2, ws_ml, ws_o);
+  const int64_t rows = num_tokens * num_q_heads;
+  attn_combine_kernel<<<dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s>>>(
+      ws_ml, ws_o, seq_lens, query_start_loc, batch, num_q_heads, static_cast<int>(maxg), rows, out,
+      out_dtype == BI_F32, static_cast<int>(group));
   return launch_status();
 }

@@ -123,3 +123,31 @@ def test_cfg4_decode_equals_prefill_long(lib):
     out_d, _ = run(lib, dec, kc2, vc2, bt2)
     for b, l in enumerate(L):
         assert same_bits(out_d[b], out_p[qsl_p[b] + l - 1])
+
+
+def test_batchdep_split_variant_correct_but_not_invariant(lib):
+    B = 32
+    L = ragged_lengths(B, 1400, 8000, 46, 0)
+    case = attention_case(L, [1] * B, cfg=46)
+    kc, vc, bt = make_cache(case, 16, [l - 1 for l in L])
+    inv, qsl = run(lib, case, kc, vc, bt)
+    q = np.concatenate(case["q"])
+    kn = np.concatenate([case["k"][b][L[b] - 1:L[b]] for b in range(B)])
+    vn = np.concatenate([case["v"][b][L[b] - 1:L[b]] for b in range(B)])
+    total = int(sum((int(l) - 1) // 256 + 1 for l in L))
+    from tests._gpu import bf16, i32
+    var = lib.bi_attention_batchdep_split(bf16(q), bf16(kn), bf16(vn), kc, vc, i32(bt), i32(L),
+                                          i32(np.arange(B + 1)), int(max(L)), total,
+                                          1.0 / np.sqrt(128))
+    _check_vs_oracle(case, var, qsl, which={b: [0] for b in (0, 7, 31)})
+    # alone, a sequence gets one chunk per split (the invariant association) ...
+    one = {k: [case[k][0]] for k in ("seq_lens", "q_lens", "k", "v", "q")}
+    kc1, vc1, bt1 = make_cache(one, 16, [int(L[0]) - 1], cfg=85)
+    alone = lib.bi_attention_batchdep_split(bf16(q[:1]), bf16(kn[:1]), bf16(vn[:1]), kc1, vc1,
+                                            i32(bt1), i32(L[:1]), i32(np.arange(2)), int(L[0]),
+                                            (int(L[0]) - 1) // 256 + 1, 1.0 / np.sqrt(128))
+    assert same_bits(alone[0], inv[0])
+    # ... inside the batch its chunks are grouped, so its bits move with the batch
+    n_diff = sum(int(not same_bits(var[b], inv[b])) for b in range(B))
+    say("batch-dependent split: sequences whose bits changed", n_diff, "of", B)
+    assert n_diff > 0
