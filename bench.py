@@ -150,6 +150,20 @@ def cpu_baseline(inp, torch, work_d, t_peak_step):
     }
 
 
+def measured_traffic(root):
+    """HBM bytes per call of the dominant kernel from the committed rocprofv3 counter summary
+    (profiles/attention_decode_traffic.json), or None if the kernel source changed since."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(root, "profiles", "attention_decode_traffic.json")))
+        src = open(os.path.join(root, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return int(rec["traffic_bytes"])
+
+
 def gemm_sweep(torch, bi):
     """Mistral-shaped GEMMs (N, K) x M, TFLOP/s of bi_gemm and of the split-K variant."""
     dev = "cuda:0"
@@ -264,7 +278,8 @@ def main():
                      "bound": "hbm", "achieved": round(att["bytes"] / per["attention_decode"] / 1e9, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(att["bytes"] / per["attention_decode"] / HBM_PEAK, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),
+                     "algorithmic_bytes": att["bytes"]},
         "kernel_time_ms": round(kernel_sum * 1e3, 4),
     }
     # non-invariant comparison variants on the same inputs (the cost of invariance)
