@@ -64,12 +64,14 @@ typedef struct bi_config {
   int32_t version;          /* layout of this struct                                   */
   int32_t tree_max_lanes;   /* 256: lanes of the RMSNorm / log-softmax tree            */
   int32_t wave_size;        /* 64                                                      */
-  int32_t gemm_tile_m;      /* output tile rows per workgroup                          */
-  int32_t gemm_tile_n;      /* output tile columns per workgroup                       */
-  int32_t gemm_tile_k;      /* K step of the main loop (ascending)                     */
+  int32_t gemm_tile_m;      /* output tile rows per workgroup (small tile)             */
+  int32_t gemm_tile_n;      /* output tile columns per workgroup (small tile)          */
+  int32_t gemm_tile_k;      /* K depth of one staged step of the main kernel           */
   int32_t gemm_mfma_m, gemm_mfma_n, gemm_mfma_k; /* the one matrix instruction shape     */
   int32_t attn_chunk;       /* 256: split-KV chunk, at absolute positions 256c          */
   int32_t attn_max_group;   /* largest supported q heads per kv head                   */
+  int32_t gemm_big_tile_m;  /* rows of the large workgroup tile (same bits, see bi_gemm) */
+  int32_t gemm_big_tile_n;  /* columns of the large workgroup tile                     */
 } bi_config;
 
 /* Fills *out.  Returns BI_ERR_NULL if out is NULL. */
@@ -112,14 +114,27 @@ int bi_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t D, 
  *   B     bf16; b_layout BI_B_NK: B is [N, K] (a Linear weight, C = A . B^T), row
  *         stride ldb;  BI_B_KN: B is [K, N] (torch.mm orientation), row stride ldb
  *   C     dtype c_dtype (BI_BF16: one RNE rounding of the fp32 sum; BI_F32), stride ldc
- * Every output element is produced by the same sequence of matrix instructions over
- * K in ascending order, whatever M is and wherever its row sits.
+ * Every output element is produced by the same sequence of matrix instructions
+ * (v_mfma_f32_32x32x16_bf16, one fp32 accumulator from +0, K in ascending 16-wide steps)
+ * whatever M is, wherever its row sits and whichever workgroup tile computes it; the
+ * workgroup tile (bi_gemm_tile) follows the size of the output grid and changes no bit.
  * Alignment: A and B 16-byte aligned; lda, ldb multiples of 8 elements (4 for fp32 A).
+ * Rows are read in 16-byte pieces: row i of A (of B) must be readable up to element
+ * round_up(K, 8) (round_up(K, 4) for fp32 A), which lda (ldb) >= that guarantees for
+ * every row but the last.
  * Errors: BI_ERR_NULL, BI_ERR_SHAPE (negative sizes, K < 1 with M*N > 0, strides too
- * small), BI_ERR_DTYPE, BI_ERR_ALIGN.
+ * small), BI_ERR_DTYPE, BI_ERR_ALIGN; BI_B_KN is not implemented yet and returns
+ * BI_ERR_UNSUPPORTED.
  */
 int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
             int64_t ldb, int64_t ldc, int b_layout, int a_dtype, int c_dtype, void* stream);
+
+/* The workgroup tile bi_gemm uses for an M x N output with A of dtype a_dtype on the
+ * current device: 256 x 256 when the grid of 256 x 256 tiles finishes in fewer rounds of
+ * the CU array than the 128 x 128 grid, else 128 x 128 (always 128 x 128 for fp32 A).
+ * Informational: the bits of C do not depend on it.  Errors: BI_ERR_NULL, BI_ERR_SHAPE
+ * (negative sizes), BI_ERR_DTYPE. */
+int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_t* tile_m, int32_t* tile_n);
 
 /* Comparison variant, NOT batch-invariant ([DN], split-K matmul): same arguments as
  * bi_gemm with bf16 A and B_NK, but K is split into a number of slices that grows as

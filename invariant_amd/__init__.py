@@ -24,6 +24,7 @@ _P, _I64, _I32, _F32, _F64, _SZ = _c.c_void_p, _c.c_int64, _c.c_int32, _c.c_floa
 
 _SIGS = {
     "bi_get_config": (_c.c_int, [_P]),
+    "bi_gemm_tile": (_c.c_int, [_I64, _I64, _I64, _c.c_int, _P, _P]),
     "bi_status_string": (_c.c_char_p, [_c.c_int]),
     "bi_rmsnorm": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _F32, _c.c_int, _c.c_int, _P]),
     "bi_gemm": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _c.c_int, _c.c_int, _c.c_int, _P]),
@@ -47,7 +48,8 @@ EXPORTS = tuple(_SIGS)
 class BIConfig(ctypes.Structure):
     _fields_ = [(n, _I32) for n in (
         "version", "tree_max_lanes", "wave_size", "gemm_tile_m", "gemm_tile_n", "gemm_tile_k",
-        "gemm_mfma_m", "gemm_mfma_n", "gemm_mfma_k", "attn_chunk", "attn_max_group")]
+        "gemm_mfma_m", "gemm_mfma_n", "gemm_mfma_k", "attn_chunk", "attn_max_group",
+        "gemm_big_tile_m", "gemm_big_tile_n")]
 
 
 class BIError(RuntimeError):
@@ -133,6 +135,14 @@ def bi_gemm(a, b, out=None, b_layout: int = BI_B_NK, out_dtype=torch.bfloat16):
     _check("bi_gemm", load().bi_gemm(_ptr(a), _ptr(b), _ptr(out), M, N, K, _ld(a), _ld(b), _ld(out),
                                       b_layout, _code(a.dtype), _code(out.dtype), _stream(a)))
     return out
+
+
+def bi_gemm_tile(M: int, N: int, K: int, a_dtype=torch.bfloat16) -> tuple:
+    """(rows, columns) of the workgroup tile bi_gemm uses for an M x N output."""
+    tm, tn = ctypes.c_int32(), ctypes.c_int32()
+    _check("bi_gemm_tile", load().bi_gemm_tile(M, N, K, _code(a_dtype), ctypes.byref(tm),
+                                                ctypes.byref(tn)))
+    return tm.value, tn.value
 
 
 def bi_gemm_splitk(a, b, out=None, out_dtype=torch.bfloat16, workspace=None):

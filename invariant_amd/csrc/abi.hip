@@ -3,17 +3,19 @@
 
 extern "C" int bi_get_config(bi_config* out) {
   if (!out) return BI_ERR_NULL;
-  out->version = 1;
+  out->version = 2;
   out->tree_max_lanes = 256;
   out->wave_size = 64;
   out->gemm_tile_m = 128;
   out->gemm_tile_n = 128;
-  out->gemm_tile_k = 64;
+  out->gemm_tile_k = 32;
   out->gemm_mfma_m = 32;
   out->gemm_mfma_n = 32;
   out->gemm_mfma_k = 16;
   out->attn_chunk = 256;
   out->attn_max_group = 16;
+  out->gemm_big_tile_m = 256;
+  out->gemm_big_tile_n = 256;
   return BI_OK;
 }
 

@@ -3,27 +3,34 @@
 // "Defeating nondeterminism in LLM inference", section on batch-invariant matrix
 // multiplication: parallelise over output tiles so every dot product stays inside one
 // workgroup; do not split K (split-K changes the order with the batch) and do not use
-// stream-K (it even loses batch-position invariance); compile ONE kernel configuration
-// and use it for every shape.  Here that configuration is:
-//   workgroup tile 128 x 128, K step 64, 4 waves (2 x 2), each wave 64 x 64 made of
-//   2 x 2 v_mfma_f32_32x32x16_bf16, fp32 accumulators starting at +0, K walked in
-//   ascending 16-wide steps from 0 to K.  Products past K are exact zeros; rows past M
+// stream-K (it even loses batch-position invariance); use one kernel configuration, so
+// that no shape switches to another reduction order.  Here the configuration that fixes
+// the order is:
+//   one instruction, v_mfma_f32_32x32x16_bf16; fp32 accumulators starting at +0; K walked
+//   in ascending 16-wide steps from 0 to K, lane l of the instruction holding k offsets
+//   8 (l / 32) .. + 7 of each step.  Products past K are exact zeros; rows past M
 //   (columns past N) are never stored.
 // Output element (i, j) is therefore the result of the same instruction sequence for
-// every M and every position of row i inside its tile.
+// every M, every position of row i inside its tile and every workgroup tile.  The
+// workgroup tile only decides which workgroup computes which outputs: 128 x 128 (4 waves
+// of 64 x 64, two workgroups per CU) or 256 x 256 (8 waves of 128 x 64, one per CU), picked
+// from the size of the output grid; the two give identical bits, which the tests check
+// across the switch.
 //
 // Main kernel (bf16 A, B as [N, K]): 32-wide K slices of both tiles stream into LDS by
 // direct-to-LDS 16-byte loads through a 4-stage ring (three slices in flight while one is
-// multiplied, 64 KB of LDS, two workgroups per CU); the 16-byte k-chunks of row r sit at
-// chunk position c ^ swz(r) so that the 16-byte operand reads of consecutive rows hit
-// distinct banks.  How K is staged does not change the instruction sequence per element.  The fp32-A path and the
-// split-K comparison variant stage through registers instead; they share the tile shape,
-// the instruction and the K order.
+// multiplied); the 16-byte k-chunks of row r sit at chunk position c ^ swz(r) so that the
+// 16-byte operand reads of consecutive rows hit distinct banks.  How K is staged does not
+// change the instruction sequence per element.  The fp32-A path, operands of 4 GiB or more
+// and the split-K comparison variant stage through registers instead (128 x 128 tile);
+// they share the instruction and the K order.
 //
 // A may be fp32 ("FP32 upcast" of the cross-vendor mismatch abstract): each value is
 // split exactly into bf16 hi + mid + lo (truncations, so hi + mid + lo == a for normal
 // numbers) and the three products are accumulated into the same fp32 accumulator in
 // the order hi, mid, lo for every 16-wide K step.
+#include <atomic>
+
 #include "bi_common.h"
 
 namespace bi {
@@ -214,12 +221,38 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
 }
 
-constexpr int STAGES = 4;
-constexpr int DBK = 32;             // K step of one LDS stage in the main kernel
-constexpr int DTILE = BM * DBK;     // bf16 elements of one operand tile per stage (8 KB)
+#ifndef BI_GEMM_STAGES
+#define BI_GEMM_STAGES 4
+#endif
+constexpr int STAGES = BI_GEMM_STAGES;   // LDS ring depth of the main kernel
+constexpr int DBK = 32;                  // K step of one LDS stage in the main kernel
+constexpr int CPR = DBK / 8;             // 16-byte chunks per LDS row
+constexpr int RPI = 64 / CPR;            // tile rows filled by one 1 KB wave-wide load
+static_assert(STAGES >= 2, "unsupported staging");
 
-// 64-byte LDS rows of 4 chunks; chunk c of row r sits at position c ^ swz(r), which puts
-// the 16-byte reads of 8 (or 16) consecutive rows into distinct banks.
+// Workgroup tile: WAVES_M x WAVES_N waves, each wave BLK_M x BLK_N blocks of the one
+// 32 x 32 x 16 matrix instruction.  Every configuration computes each output element with
+// the same instruction sequence (one fp32 chain from +0 over ascending 16-wide K steps,
+// lane l holding k = 8 (l / 32) .. + 7 of each step), so they give identical bits; the tile
+// only decides which workgroup computes which outputs.
+template <int WAVES_M_, int WAVES_N_, int BLK_M_, int BLK_N_>
+struct Tile {
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BLK_M = BLK_M_, BLK_N = BLK_N_;
+  static constexpr int NW = WAVES_M * WAVES_N;
+  static constexpr int THREADS = NW * 64;
+  static constexpr int TM = WAVES_M * BLK_M * 32;
+  static constexpr int TN = WAVES_N * BLK_N * 32;
+  static constexpr int NJA = TM / NW / RPI;  // A loads per wave per stage
+  static constexpr int NJB = TN / NW / RPI;  // B loads per wave per stage
+  static constexpr int PER = NJA + NJB;
+  static constexpr int SA = TM * DBK, SB = TN * DBK;  // bf16 elements per stage
+  static_assert(TM % (NW * RPI) == 0 && TN % (NW * RPI) == 0, "tile rows per wave");
+};
+using Tile128 = Tile<2, 2, 2, 2>;   // 128 x 128, 4 waves of 64 x 64, two workgroups per CU
+using Tile256 = Tile<2, 4, 4, 2>;   // 256 x 256, 8 waves of 128 x 64
+
+// Chunk c of LDS row r sits at position c ^ swz(r): the 16-byte reads of 8 (or 16)
+// consecutive rows at one chunk index then fall into distinct banks.
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 // 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane, addressed as
@@ -245,24 +278,110 @@ __device__ __forceinline__ void wait_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
-}
-
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+// Wait for the oldest stage: `ahead` later stages (0..S) may stay in flight.
+template <int PER, int S>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  if constexpr (S == 0) {
+    wait_and_barrier<0>();
+  } else {
+    if (ahead >= S) wait_and_barrier<S * PER>();
+    else wait_stage<PER, S - 1>(ahead);
+  }
 }
 
 // A and B must each span less than 4 GiB (byte offsets are 32-bit); the host checks.
-__global__ __launch_bounds__(kThreads, 2) void gemm_dma_kernel(
+template <class T>
+struct DmaCtx {
+  const uint16_t* A;
+  const uint16_t* B;
+  uint32_t aoff[T::NJA], boff[T::NJB];   // per-lane byte offsets of this lane's chunks
+  int kca[T::NJA], kcb[T::NJB];          // k offset of each chunk inside a stage
+  uint32_t lds_a, lds_b;                 // LDS byte address of this wave's rows in stage 0
+  int K, nk;
+  bool ktail;
+};
+
+// Stage kt into ring buffer `buf` (a template constant in the steady loop, a run-time
+// value in the prologue and the tail, where it only moves the LDS base).
+template <class T>
+__device__ __forceinline__ void dma_stage_at(const DmaCtx<T>& d, uint32_t buf, int kt) {
+  constexpr uint32_t sa_bytes = T::SA * 2, sb_bytes = T::SB * 2;
+  const int k0 = kt * DBK;
+  const uint32_t la = d.lds_a + buf * sa_bytes, lb = d.lds_b + buf * sb_bytes;
+  if (d.ktail && kt == d.nk - 1) {
+    // last, partial step: a chunk wholly past K re-reads chunk 0 (zeroed after landing)
+#pragma unroll
+    for (int j = 0; j < T::NJA; ++j) {
+      const uint32_t adv = (k0 + d.kca[j] < d.K) ? static_cast<uint32_t>(k0) * 2 : 0u;
+      dma16(d.A, d.aoff[j] + adv, la + j * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < T::NJB; ++j) {
+      const uint32_t adv = (k0 + d.kcb[j] < d.K) ? static_cast<uint32_t>(k0) * 2 : 0u;
+      dma16(d.B, d.boff[j] + adv, lb + j * 1024);
+    }
+  } else {
+    const uint16_t* ab = d.A + k0;
+    const uint16_t* bb = d.B + k0;
+#pragma unroll
+    for (int j = 0; j < T::NJA; ++j) dma16(ab, d.aoff[j], la + j * 1024);
+#pragma unroll
+    for (int j = 0; j < T::NJB; ++j) dma16(bb, d.boff[j], lb + j * 1024);
+  }
+}
+
+template <class T>
+struct Frag {
+  uint32_t ao[T::BLK_M][DBK / 16], bo[T::BLK_N][DBK / 16];   // per-lane LDS byte offsets
+};
+
+// One stage of MFMAs on ring buffer `buf`: the per-lane LDS byte offsets of the operand
+// reads are precomputed; a template-constant buffer becomes an immediate offset.
+template <class T>
+__device__ __forceinline__ void mma_stage_at(const uint16_t* sA, const uint16_t* sB, uint32_t buf,
+                                             const Frag<T>& f, floatx16 (&acc)[T::BLK_M][T::BLK_N]) {
+  const char* a = reinterpret_cast<const char*>(sA) + buf * (T::SA * 2);
+  const char* b = reinterpret_cast<const char*>(sB) + buf * (T::SB * 2);
+#pragma unroll
+  for (int ks = 0; ks < DBK / 16; ++ks) {
+    bf16x8 av[T::BLK_M], bv[T::BLK_N];
+#pragma unroll
+    for (int i = 0; i < T::BLK_M; ++i) av[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(a + f.ao[i][ks]));
+#pragma unroll
+    for (int j = 0; j < T::BLK_N; ++j) bv[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(b + f.bo[j][ks]));
+#pragma unroll
+    for (int i = 0; i < T::BLK_M; ++i)
+#pragma unroll
+      for (int j = 0; j < T::BLK_N; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// Steady-state steps, unrolled by the ring depth so every buffer offset is static: wait for
+// stage kt (STAGES - 2 later stages stay in flight), refill the buffer freed by stage
+// kt - 1 with stage kt + STAGES - 1, multiply stage kt.
+template <class T, int BUF>
+__device__ __forceinline__ void unrolled_steps(const DmaCtx<T>& d, const uint16_t* sA,
+                                               const uint16_t* sB, int kt, const Frag<T>& f,
+                                               floatx16 (&acc)[T::BLK_M][T::BLK_N]) {
+  if constexpr (BUF < STAGES) {
+    wait_and_barrier<(STAGES - 2) * T::PER>();
+    dma_stage_at<T>(d, (BUF + STAGES - 1) % STAGES, kt + BUF + STAGES - 1);
+    mma_stage_at<T>(sA, sB, BUF, f, acc);
+    unrolled_steps<T, BUF + 1>(d, sA, sB, kt, f, acc);
+  }
+}
+
+template <class T>
+__global__ __launch_bounds__(T::THREADS, 2) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
     int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint16_t sA[STAGES][DTILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB[STAGES][DTILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA[STAGES * T::SA];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB[STAGES * T::SB];
 
+  // Tile order: consecutive workgroup ids land on different XCDs (round robin over 8), so
+  // give each XCD a contiguous band of tiles, walked column-major inside bands of 8
+  // tile-rows (A rows and B columns then stay in that XCD's L2).
   const int nwg = tiles_m * tiles_n;
   int id = blockIdx.x;
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
@@ -274,115 +393,114 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_dma_kernel(
   const int tm = first_m + (id % per_group) % gm;
   const int tn = (id % per_group) / gm;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
 
-  // DMA assignment: instruction j of wave w fills tile rows 32w + 16j .. +15; lane l writes
-  // chunk position l % 4 of row 32w + 16j + l / 4 with k-chunk (l % 4) ^ swz(row).
-  uint32_t aoff[2], boff[2];
-  int kc[2];
+  // DMA assignment: load j of wave w fills the wave's tile rows RPI j .. RPI j + RPI - 1
+  // (A rows w TM/NW .., B rows w TN/NW ..); lane l writes chunk position l % CPR of its
+  // row with k-chunk (l % CPR) ^ swz(row).
+  DmaCtx<T> d;
+  d.A = A;
+  d.B = B;
+  d.K = K;
+  d.nk = (K + DBK - 1) / DBK;
+  d.ktail = (K % DBK) != 0;
+  d.lds_a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sA)) + (T::TM / T::NW) * wave * DBK * 2;
+  d.lds_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sB)) + (T::TN / T::NW) * wave * DBK * 2;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int R = 32 * wave + 16 * j + (lane >> 2);
-    const int c = (lane & 3) ^ swz(R);
-    const int ra = min(tm * BM + R, M - 1);
-    const int rb = min(tn * BN + R, N - 1);
-    aoff[j] = static_cast<uint32_t>((static_cast<int64_t>(ra) * lda + c * 8) * 2);
-    boff[j] = static_cast<uint32_t>((static_cast<int64_t>(rb) * ldb + c * 8) * 2);
-    kc[j] = c * 8;
+  for (int j = 0; j < T::NJA; ++j) {
+    const int R = (T::TM / T::NW) * wave + RPI * j + lane / CPR;
+    const int c = (lane % CPR) ^ swz(R);
+    const int ra = min(tm * T::TM + R, M - 1);
+    d.aoff[j] = static_cast<uint32_t>((static_cast<int64_t>(ra) * lda + c * 8) * 2);
+    d.kca[j] = c * 8;
   }
-  const int nk = (K + DBK - 1) / DBK;
-  const bool ktail = (K % DBK) != 0;
-  auto issue = [&](int buf, int kt) {
-    const int k0 = kt * DBK;
-    if (ktail && kt == nk - 1) {
-      // last, partial step: a chunk wholly past K re-reads chunk 0 (zeroed after landing)
-      const void* ab = uniform_ptr(A);
-      const void* bb = uniform_ptr(B);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint32_t adv = (k0 + kc[j] < K) ? static_cast<uint32_t>(k0) * 2 : 0u;
-        dma16(ab, aoff[j] + adv, lds_u32(&sA[buf][(32 * wave + 16 * j) * DBK]));
-        dma16(bb, boff[j] + adv, lds_u32(&sB[buf][(32 * wave + 16 * j) * DBK]));
-      }
-    } else {
-      const void* ab = uniform_ptr(A + k0);
-      const void* bb = uniform_ptr(B + k0);
+  for (int j = 0; j < T::NJB; ++j) {
+    const int R = (T::TN / T::NW) * wave + RPI * j + lane / CPR;
+    const int c = (lane % CPR) ^ swz(R);
+    const int rb = min(tn * T::TN + R, N - 1);
+    d.boff[j] = static_cast<uint32_t>((static_cast<int64_t>(rb) * ldb + c * 8) * 2);
+    d.kcb[j] = c * 8;
+  }
+  // operand reads: lane holds row (lane % 32) of each 32-row block and k-chunk
+  // 2 ks + lane / 32 of each 16-wide K step
+  Frag<T> f;
+  const int orow = lane & 31, okc = lane >> 5;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        dma16(ab, aoff[j], lds_u32(&sA[buf][(32 * wave + 16 * j) * DBK]));
-        dma16(bb, boff[j], lds_u32(&sB[buf][(32 * wave + 16 * j) * DBK]));
-      }
+  for (int ks = 0; ks < DBK / 16; ++ks) {
+#pragma unroll
+    for (int i = 0; i < T::BLK_M; ++i) {
+      const int r = (wm * T::BLK_M + i) * 32 + orow;
+      f.ao[i][ks] = static_cast<uint32_t>((r * DBK + (((2 * ks + okc) ^ swz(r)) * 8)) * 2);
     }
-  };
+#pragma unroll
+    for (int j = 0; j < T::BLK_N; ++j) {
+      const int r = (wn * T::BLK_N + j) * 32 + orow;
+      f.bo[j][ks] = static_cast<uint32_t>((r * DBK + (((2 * ks + okc) ^ swz(r)) * 8)) * 2);
+    }
+  }
 
-  floatx16 acc[2][2];
+  floatx16 acc[T::BLK_M][T::BLK_N];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < T::BLK_M; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < T::BLK_N; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  issue(0, 0);
-  if (nk > 1) issue(1, 1);
-  if (nk > 2) issue(2, 2);
+  const int nk = d.nk;
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) dma_stage_at<T>(d, st, st);
 
-  const int orow = lane & 31;
-  const int okc = lane >> 5;   // which 8-wide half of a 16-wide K step
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & (STAGES - 1);
-    if (kt + 2 < nk) wait_and_barrier<8>();
-    else if (kt + 1 < nk) wait_and_barrier<4>();
-    else wait_and_barrier<0>();
-    if (ktail && kt == nk - 1) {
+  // steady state: stages kt <= nk - STAGES
+  const int full = nk - STAGES + 1 > 0 ? nk - STAGES + 1 : 0;
+  int kt = 0;
+  for (; kt + STAGES <= full; kt += STAGES) unrolled_steps<T, 0>(d, sA, sB, kt, f, acc);
+  for (; kt < full; ++kt) {
+    wait_and_barrier<(STAGES - 2) * T::PER>();
+    dma_stage_at<T>(d, (kt + STAGES - 1) % STAGES, kt + STAGES - 1);
+    mma_stage_at<T>(sA, sB, kt % STAGES, f, acc);
+  }
+  // drain: the last STAGES - 1 stages (fewer if nk is small)
+  for (; kt < nk; ++kt) {
+    const int buf = kt % STAGES;
+    wait_stage<T::PER, STAGES - 2>(min(STAGES - 2, nk - 1 - kt));
+    if (d.ktail && kt == nk - 1) {
       // zero every element at k >= K in the pieces this lane's own loads wrote
       const int k0 = kt * DBK;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int pos = (32 * wave + 16 * j + (lane >> 2)) * DBK + (lane & 3) * 8;
+      for (int j = 0; j < T::NJA; ++j) {
+        const int pos = buf * T::SA + ((T::TM / T::NW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (k0 + kc[j] + e >= K) {
-            sA[buf][pos + e] = 0;
-            sB[buf][pos + e] = 0;
-          }
+          if (k0 + d.kca[j] + e >= K) sA[pos + e] = 0;
+      }
+#pragma unroll
+      for (int j = 0; j < T::NJB; ++j) {
+        const int pos = buf * T::SB + ((T::TN / T::NW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (k0 + d.kcb[j] + e >= K) sB[pos + e] = 0;
       }
       wait_and_barrier<0>();
     }
-    if (kt + 3 < nk) issue((kt + 3) & (STAGES - 1), kt + 3);
-#pragma unroll
-    for (int ks = 0; ks < DBK / 16; ++ks) {
-      bf16x8 av[2], bv[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + orow;
-        av[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(&sA[buf][r * DBK + (((2 * ks + okc) ^ swz(r)) * 8)]));
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wn * 64 + j * 32 + orow;
-        bv[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(&sB[buf][r * DBK + (((2 * ks + okc) ^ swz(r)) * 8)]));
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-    }
+    mma_stage_at<T>(sA, sB, buf, f, acc);
   }
 
+  // epilogue: register r of block (i, j) is row 8 (r / 4) + 4 (lane / 32) + r % 4 and
+  // column lane % 32 of that block
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < T::BLK_M; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = tn * BN + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < T::BLK_N; ++j) {
+      const int col = tn * T::TN + (wn * T::BLK_N + j) * 32 + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = tm * BM + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int row = tm * T::TM + (wm * T::BLK_M + i) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row >= M) continue;
         if (c_f32)
           static_cast<float*>(C)[static_cast<int64_t>(row) * ldc + col] = acc[i][j][r];
@@ -390,6 +508,42 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_dma_kernel(
           static_cast<uint16_t*>(C)[static_cast<int64_t>(row) * ldc + col] = f32_to_bf16(acc[i][j][r]);
       }
     }
+}
+
+// Workgroup tile of the main kernel for an M x N output.  Both tiles give every output
+// element the same bits (same instruction, same K order), so this choice changes only the
+// time: the 256 x 256 tile streams half the operand bytes per flop but runs one workgroup
+// per CU, so it wins once there are enough tiles to fill the CUs.  The cost below counts
+// rounds of the CU array with round times measured on MI355X at K = 4096 (both scale
+// with K): 256 x 256, one per CU: 120; 128 x 128, two per CU: 82, one per CU: 48.
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+    v = 256;
+  cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+bool big_tile(int64_t M, int64_t N, int cus) {
+  const int64_t n256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t n128 = ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t cost256 = 120 * ((n256 + cus - 1) / cus);
+  const int64_t rem = n128 % (2 * cus);
+  const int64_t cost128 = 82 * (n128 / (2 * cus)) + (rem == 0 ? 0 : rem <= cus ? 48 : 82);
+  return cost256 < cost128;
+}
+
+template <class T>
+void launch_dma(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
+                int64_t ldb, int64_t ldc, int cf, hipStream_t s) {
+  const int tm = static_cast<int>((M + T::TM - 1) / T::TM), tn = static_cast<int>((N + T::TN - 1) / T::TN);
+  gemm_dma_kernel<T><<<dim3(static_cast<unsigned>(static_cast<int64_t>(tm) * tn)), dim3(T::THREADS), 0, s>>>(
+      static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, int(M), int(N), int(K),
+      lda, ldb, ldc, cf, tm, tn);
 }
 
 // Fixed-order sum of the split-K partials (comparison variant only).
@@ -443,15 +597,26 @@ extern "C" int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t
     gemm_kernel<true><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
         A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
         0, int(K), 0);
-  else if (M * lda * 2 < (int64_t(1) << 32) && N * ldb * 2 < (int64_t(1) << 32))
-    gemm_dma_kernel<<<dim3(static_cast<unsigned>(nwg)), dim3(kThreads), 0, s>>>(
-        static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, int(M), int(N),
-        int(K), lda, ldb, ldc, cf, tm, tn);
+  else if (M * lda * 2 < (int64_t(1) << 32) && N * ldb * 2 < (int64_t(1) << 32)) {
+    if (big_tile(M, N, cu_count())) launch_dma<Tile256>(A, B, C, M, N, K, lda, ldb, ldc, cf, s);
+    else launch_dma<Tile128>(A, B, C, M, N, K, lda, ldb, ldc, cf, s);
+  }
   else  // operands of 4 GiB or more: register-staged kernel (same tile, instruction, K order)
     gemm_kernel<false><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
         A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
         0, int(K), 0);
   return launch_status();
+}
+
+extern "C" int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_t* tile_m,
+                            int32_t* tile_n) {
+  if (!tile_m || !tile_n) return BI_ERR_NULL;
+  if (M < 0 || N < 0 || K < 0) return BI_ERR_SHAPE;
+  if (a_dtype != BI_BF16 && a_dtype != BI_F32) return BI_ERR_DTYPE;
+  const bool big = a_dtype == BI_BF16 && M > 0 && N > 0 && big_tile(M, N, cu_count());
+  *tile_m = big ? Tile256::TM : Tile128::TM;
+  *tile_n = big ? Tile256::TN : Tile128::TN;
+  return BI_OK;
 }
 
 extern "C" size_t bi_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
