@@ -130,11 +130,14 @@ int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
             int64_t ldb, int64_t ldc, int b_layout, int a_dtype, int c_dtype, void* stream);
 
 /* The workgroup tile bi_gemm uses for an M x N output with A of dtype a_dtype on the
- * current device: 256 x 256 when the grid of 256 x 256 tiles finishes in fewer rounds of
- * the CU array than the 128 x 128 grid, else 128 x 128 (always 128 x 128 for fp32 A).
+ * current device: *tile_m x *tile_n outputs per workgroup and *stages K slices in its LDS
+ * ring.  256 x 256 (2 stages) when that grid finishes in fewer rounds of the CU array;
+ * else 128 x 128, with a 3-stage ring when the grid has no more tiles than CUs and a
+ * 2-stage ring (two workgroups per CU) otherwise; fp32 A: 128 x 128, register staged.
  * Informational: the bits of C do not depend on it.  Errors: BI_ERR_NULL, BI_ERR_SHAPE
  * (negative sizes), BI_ERR_DTYPE. */
-int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_t* tile_m, int32_t* tile_n);
+int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_t* tile_m, int32_t* tile_n,
+                 int32_t* stages);
 
 /* Comparison variant, NOT batch-invariant ([DN], split-K matmul): same arguments as
  * bi_gemm with bf16 A and B_NK, but K is split into a number of slices that grows as

@@ -24,7 +24,7 @@ _P, _I64, _I32, _F32, _F64, _SZ = _c.c_void_p, _c.c_int64, _c.c_int32, _c.c_floa
 
 _SIGS = {
     "bi_get_config": (_c.c_int, [_P]),
-    "bi_gemm_tile": (_c.c_int, [_I64, _I64, _I64, _c.c_int, _P, _P]),
+    "bi_gemm_tile": (_c.c_int, [_I64, _I64, _I64, _c.c_int, _P, _P, _P]),
     "bi_status_string": (_c.c_char_p, [_c.c_int]),
     "bi_rmsnorm": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _F32, _c.c_int, _c.c_int, _P]),
     "bi_gemm": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _c.c_int, _c.c_int, _c.c_int, _P]),
@@ -138,11 +138,11 @@ def bi_gemm(a, b, out=None, b_layout: int = BI_B_NK, out_dtype=torch.bfloat16):
 
 
 def bi_gemm_tile(M: int, N: int, K: int, a_dtype=torch.bfloat16) -> tuple:
-    """(rows, columns) of the workgroup tile bi_gemm uses for an M x N output."""
-    tm, tn = ctypes.c_int32(), ctypes.c_int32()
+    """(rows, columns, LDS ring stages) of the workgroup tile bi_gemm uses for M x N."""
+    tm, tn, st = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     _check("bi_gemm_tile", load().bi_gemm_tile(M, N, K, _code(a_dtype), ctypes.byref(tm),
-                                                ctypes.byref(tn)))
-    return tm.value, tn.value
+                                                ctypes.byref(tn), ctypes.byref(st)))
+    return tm.value, tn.value, st.value
 
 
 def bi_gemm_splitk(a, b, out=None, out_dtype=torch.bfloat16, workspace=None):

@@ -221,23 +221,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
 }
 
-#ifndef BI_GEMM_STAGES
-#define BI_GEMM_STAGES 4
+#ifndef BI_GEMM_DBK
+#define BI_GEMM_DBK 64
 #endif
-constexpr int STAGES = BI_GEMM_STAGES;   // LDS ring depth of the main kernel
-constexpr int DBK = 32;                  // K step of one LDS stage in the main kernel
+constexpr int DBK = BI_GEMM_DBK;         // K depth of one LDS stage in the main kernel
+constexpr int KS = DBK / 16;             // 16-wide K steps per stage
 constexpr int CPR = DBK / 8;             // 16-byte chunks per LDS row
 constexpr int RPI = 64 / CPR;            // tile rows filled by one 1 KB wave-wide load
-static_assert(STAGES >= 2, "unsupported staging");
+static_assert(DBK == 32 || DBK == 64, "the main loop takes an even number of 16-wide K steps");
 
 // Workgroup tile: WAVES_M x WAVES_N waves, each wave BLK_M x BLK_N blocks of the one
 // 32 x 32 x 16 matrix instruction.  Every configuration computes each output element with
 // the same instruction sequence (one fp32 chain from +0 over ascending 16-wide K steps,
 // lane l holding k = 8 (l / 32) .. + 7 of each step), so they give identical bits; the tile
 // only decides which workgroup computes which outputs.
-template <int WAVES_M_, int WAVES_N_, int BLK_M_, int BLK_N_>
+template <int WAVES_M_, int WAVES_N_, int BLK_M_, int BLK_N_, int STAGES_, int WAVES_PER_SIMD_ = 2>
 struct Tile {
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BLK_M = BLK_M_, BLK_N = BLK_N_;
+  static constexpr int STAGES = STAGES_;   // LDS ring depth
+  static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;   // register budget: 512 / this
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int THREADS = NW * 64;
   static constexpr int TM = WAVES_M * BLK_M * 32;
@@ -247,13 +249,25 @@ struct Tile {
   static constexpr int PER = NJA + NJB;
   static constexpr int SA = TM * DBK, SB = TN * DBK;  // bf16 elements per stage
   static_assert(TM % (NW * RPI) == 0 && TN % (NW * RPI) == 0, "tile rows per wave");
+  static_assert(STAGES >= 2, "unsupported staging");
 };
-using Tile128 = Tile<2, 2, 2, 2>;   // 128 x 128, 4 waves of 64 x 64, two workgroups per CU
-using Tile256 = Tile<2, 4, 4, 2>;   // 256 x 256, 8 waves of 128 x 64
+// 128 x 128, 4 waves of 64 x 64: a 2-stage ring (64 KB, two workgroups per CU), or a
+// 3-stage ring (96 KB, one per CU) for grids with no more tiles than CUs; 256 x 256, 8 waves
+// of 128 x 64, 2-stage ring (128 KB, one per CU).
+using Tile128 = Tile<2, 2, 2, 2, 2>;
+using Tile128Deep = Tile<2, 2, 2, 2, 3>;
+using Tile256 = Tile<2, 4, 4, 2, 2>;
 
 // Chunk c of LDS row r sits at position c ^ swz(r): the 16-byte reads of 8 (or 16)
 // consecutive rows at one chunk index then fall into distinct banks.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+#ifndef BI_GEMM_SWZ
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 4) return ((r >> 1) ^ (r >> 3)) & 3;
+  else return ((r >> 1) ^ (r >> 4)) & 7;
+}
+#else
+__device__ __forceinline__ int swz(int r) { return BI_GEMM_SWZ; }
+#endif
 
 // 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane, addressed as
 // a wave-uniform 64-bit base plus a per-lane 32-bit byte offset.  Written in asm so that
@@ -309,15 +323,18 @@ __device__ __forceinline__ void dma_stage_at(const DmaCtx<T>& d, uint32_t buf, i
   const int k0 = kt * DBK;
   const uint32_t la = d.lds_a + buf * sa_bytes, lb = d.lds_b + buf * sb_bytes;
   if (d.ktail && kt == d.nk - 1) {
-    // last, partial step: a chunk wholly past K re-reads chunk 0 (zeroed after landing)
+    // last, partial step: a chunk wholly past K re-reads the first 8 elements of its row
+    // (always inside the row; zeroed after landing)
 #pragma unroll
     for (int j = 0; j < T::NJA; ++j) {
-      const uint32_t adv = (k0 + d.kca[j] < d.K) ? static_cast<uint32_t>(k0) * 2 : 0u;
+      const uint32_t adv = (k0 + d.kca[j] < d.K) ? static_cast<uint32_t>(k0) * 2
+                                                 : static_cast<uint32_t>(-2 * d.kca[j]);
       dma16(d.A, d.aoff[j] + adv, la + j * 1024);
     }
 #pragma unroll
     for (int j = 0; j < T::NJB; ++j) {
-      const uint32_t adv = (k0 + d.kcb[j] < d.K) ? static_cast<uint32_t>(k0) * 2 : 0u;
+      const uint32_t adv = (k0 + d.kcb[j] < d.K) ? static_cast<uint32_t>(k0) * 2
+                                                 : static_cast<uint32_t>(-2 * d.kcb[j]);
       dma16(d.B, d.boff[j] + adv, lb + j * 1024);
     }
   } else {
@@ -332,52 +349,111 @@ __device__ __forceinline__ void dma_stage_at(const DmaCtx<T>& d, uint32_t buf, i
 
 template <class T>
 struct Frag {
-  uint32_t ao[T::BLK_M][DBK / 16], bo[T::BLK_N][DBK / 16];   // per-lane LDS byte offsets
+  uint32_t ao[T::BLK_M][KS], bo[T::BLK_N][KS];   // per-lane LDS byte offsets
 };
 
-// One stage of MFMAs on ring buffer `buf`: the per-lane LDS byte offsets of the operand
-// reads are precomputed; a template-constant buffer becomes an immediate offset.
+// Operands of one 16-wide K step: BLK_M A fragments and BLK_N B fragments, read from ring
+// buffer `buf` (a template constant in the steady loop becomes an immediate offset).
 template <class T>
-__device__ __forceinline__ void mma_stage_at(const uint16_t* sA, const uint16_t* sB, uint32_t buf,
-                                             const Frag<T>& f, floatx16 (&acc)[T::BLK_M][T::BLK_N]) {
+struct Ops {
+  bf16x8 a[T::BLK_M], b[T::BLK_N];
+};
+
+template <class T>
+__device__ __forceinline__ void load_ops(const uint16_t* sA, const uint16_t* sB, uint32_t buf, int ks,
+                                         const Frag<T>& f, Ops<T>& o) {
   const char* a = reinterpret_cast<const char*>(sA) + buf * (T::SA * 2);
   const char* b = reinterpret_cast<const char*>(sB) + buf * (T::SB * 2);
 #pragma unroll
-  for (int ks = 0; ks < DBK / 16; ++ks) {
-    bf16x8 av[T::BLK_M], bv[T::BLK_N];
+  for (int i = 0; i < T::BLK_M; ++i) o.a[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(a + f.ao[i][ks]));
 #pragma unroll
-    for (int i = 0; i < T::BLK_M; ++i) av[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(a + f.ao[i][ks]));
+  for (int j = 0; j < T::BLK_N; ++j) o.b[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(b + f.bo[j][ks]));
+}
+
+template <class T>
+__device__ __forceinline__ void mfma_ops(const Ops<T>& o, floatx16 (&acc)[T::BLK_M][T::BLK_N]) {
 #pragma unroll
-    for (int j = 0; j < T::BLK_N; ++j) bv[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(b + f.bo[j][ks]));
+  for (int i = 0; i < T::BLK_M; ++i)
 #pragma unroll
-    for (int i = 0; i < T::BLK_M; ++i)
+    for (int j = 0; j < T::BLK_N; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Zero every element at k >= K of stage kt (in ring buffer buf) in the pieces this lane's
+// own loads wrote; the caller then waits and meets the other waves.
+template <class T>
+__device__ __forceinline__ void zero_k_tail(const DmaCtx<T>& d, uint16_t* sA, uint16_t* sB, int buf,
+                                            int kt, int wave, int lane) {
+  const int k0 = kt * DBK;
 #pragma unroll
-      for (int j = 0; j < T::BLK_N; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  for (int j = 0; j < T::NJA; ++j) {
+    const int pos = buf * T::SA + ((T::TM / T::NW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (k0 + d.kca[j] + e >= d.K) sA[pos + e] = 0;
+  }
+#pragma unroll
+  for (int j = 0; j < T::NJB; ++j) {
+    const int pos = buf * T::SB + ((T::TN / T::NW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (k0 + d.kcb[j] + e >= d.K) sB[pos + e] = 0;
   }
 }
 
-// Steady-state steps, unrolled by the ring depth so every buffer offset is static: wait for
-// stage kt (STAGES - 2 later stages stay in flight), refill the buffer freed by stage
-// kt - 1 with stage kt + STAGES - 1, multiply stage kt.
+// K steps 1 .. KS - 1 of a stage, each read before the previous step's MFMAs are issued
+// (o0 holds step 0 on entry; on return the operands of step KS - 1 are in o1 and every
+// earlier step has been multiplied).  KS is even, so step s lives in o0 for even s.
+template <class T>
+__device__ __forceinline__ void inner_steps(const uint16_t* sA, const uint16_t* sB, uint32_t buf,
+                                            const Frag<T>& f, Ops<T>& o0, Ops<T>& o1,
+                                            floatx16 (&acc)[T::BLK_M][T::BLK_N]) {
+#pragma unroll
+  for (int ks = 1; ks < KS; ++ks) {
+    if (ks & 1) {
+      load_ops<T>(sA, sB, buf, ks, f, o1);
+      mfma_ops<T>(o0, acc);
+    } else {
+      load_ops<T>(sA, sB, buf, ks, f, o0);
+      mfma_ops<T>(o1, acc);
+    }
+  }
+}
+
+// One K step kt whose stage sits in ring buffer BUF, while every later stage up to
+// kt + T::STAGES - 1 is already issued: o0 holds the operands of its first 16-wide step.
+// The second step's operands are read before the first step's MFMAs are issued; once
+// every wave has them (and stage kt + 1 has landed), the buffer is refilled with stage
+// kt + T::STAGES and the next step's first operands are read while this step's second
+// MFMAs run.  The MFMA order per output element is unchanged: ascending K.
+template <class T, int BUF>
+__device__ __forceinline__ void steady_step(const DmaCtx<T>& d, const uint16_t* sA, const uint16_t* sB,
+                                            int kt, const Frag<T>& f, Ops<T>& o0, Ops<T>& o1,
+                                            floatx16 (&acc)[T::BLK_M][T::BLK_N]) {
+  inner_steps<T>(sA, sB, BUF, f, o0, o1, acc);
+  wait_and_barrier<(T::STAGES - 2) * T::PER>();
+  dma_stage_at<T>(d, BUF, kt + T::STAGES);
+  load_ops<T>(sA, sB, (BUF + 1) % T::STAGES, 0, f, o0);
+  mfma_ops<T>(o1, acc);
+}
+
 template <class T, int BUF>
 __device__ __forceinline__ void unrolled_steps(const DmaCtx<T>& d, const uint16_t* sA,
                                                const uint16_t* sB, int kt, const Frag<T>& f,
+                                               Ops<T>& o0, Ops<T>& o1,
                                                floatx16 (&acc)[T::BLK_M][T::BLK_N]) {
-  if constexpr (BUF < STAGES) {
-    wait_and_barrier<(STAGES - 2) * T::PER>();
-    dma_stage_at<T>(d, (BUF + STAGES - 1) % STAGES, kt + BUF + STAGES - 1);
-    mma_stage_at<T>(sA, sB, BUF, f, acc);
-    unrolled_steps<T, BUF + 1>(d, sA, sB, kt, f, acc);
+  if constexpr (BUF < T::STAGES) {
+    steady_step<T, BUF>(d, sA, sB, kt + BUF, f, o0, o1, acc);
+    unrolled_steps<T, BUF + 1>(d, sA, sB, kt, f, o0, o1, acc);
   }
 }
 
 template <class T>
-__global__ __launch_bounds__(T::THREADS, 2) void gemm_dma_kernel(
+__global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
     int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint16_t sA[STAGES * T::SA];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB[STAGES * T::SB];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA[T::STAGES * T::SA];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB[T::STAGES * T::SB];
 
   // Tile order: consecutive workgroup ids land on different XCDs (round robin over 8), so
   // give each XCD a contiguous band of tiles, walked column-major inside bands of 8
@@ -429,7 +505,7 @@ __global__ __launch_bounds__(T::THREADS, 2) void gemm_dma_kernel(
   Frag<T> f;
   const int orow = lane & 31, okc = lane >> 5;
 #pragma unroll
-  for (int ks = 0; ks < DBK / 16; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
     for (int i = 0; i < T::BLK_M; ++i) {
       const int r = (wm * T::BLK_M + i) * 32 + orow;
@@ -450,45 +526,44 @@ __global__ __launch_bounds__(T::THREADS, 2) void gemm_dma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // prologue: every ring buffer receives a stage
   const int nk = d.nk;
 #pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
+  for (int st = 0; st < T::STAGES; ++st)
     if (st < nk) dma_stage_at<T>(d, st, st);
-
-  // steady state: stages kt <= nk - STAGES
-  const int full = nk - STAGES + 1 > 0 ? nk - STAGES + 1 : 0;
-  int kt = 0;
-  for (; kt + STAGES <= full; kt += STAGES) unrolled_steps<T, 0>(d, sA, sB, kt, f, acc);
-  for (; kt < full; ++kt) {
-    wait_and_barrier<(STAGES - 2) * T::PER>();
-    dma_stage_at<T>(d, (kt + STAGES - 1) % STAGES, kt + STAGES - 1);
-    mma_stage_at<T>(sA, sB, kt % STAGES, f, acc);
+  Ops<T> o0, o1;
+  wait_stage<T::PER, T::STAGES - 1>(min(T::STAGES - 1, nk - 1));
+  if (d.ktail && nk == 1) {
+    zero_k_tail<T>(d, sA, sB, 0, 0, wave, lane);
+    wait_and_barrier<0>();
   }
-  // drain: the last STAGES - 1 stages (fewer if nk is small)
-  for (; kt < nk; ++kt) {
-    const int buf = kt % STAGES;
-    wait_stage<T::PER, STAGES - 2>(min(STAGES - 2, nk - 1 - kt));
-    if (d.ktail && kt == nk - 1) {
-      // zero every element at k >= K in the pieces this lane's own loads wrote
-      const int k0 = kt * DBK;
-#pragma unroll
-      for (int j = 0; j < T::NJA; ++j) {
-        const int pos = buf * T::SA + ((T::TM / T::NW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (k0 + d.kca[j] + e >= K) sA[pos + e] = 0;
-      }
-#pragma unroll
-      for (int j = 0; j < T::NJB; ++j) {
-        const int pos = buf * T::SB + ((T::TN / T::NW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (k0 + d.kcb[j] + e >= K) sB[pos + e] = 0;
-      }
+  load_ops<T>(sA, sB, 0, 0, f, o0);
+
+  // steady state: steps kt with stage kt + T::STAGES still to issue
+  const int steady = nk - T::STAGES > 0 ? nk - T::STAGES : 0;
+  int kt = 0;
+  for (; kt + T::STAGES <= steady; kt += T::STAGES) unrolled_steps<T, 0>(d, sA, sB, kt, f, o0, o1, acc);
+  for (; kt < steady; ++kt) {
+    const int buf = kt % T::STAGES;
+    inner_steps<T>(sA, sB, buf, f, o0, o1, acc);
+    wait_and_barrier<(T::STAGES - 2) * T::PER>();
+    dma_stage_at<T>(d, buf, kt + T::STAGES);
+    load_ops<T>(sA, sB, (kt + 1) % T::STAGES, 0, f, o0);
+    mfma_ops<T>(o1, acc);
+  }
+  // drain: nothing left to issue; stages kt + 1 .. nk - 1 may still be in flight
+  for (; kt < nk - 1; ++kt) {
+    inner_steps<T>(sA, sB, kt % T::STAGES, f, o0, o1, acc);
+    wait_stage<T::PER, T::STAGES - 2>(min(T::STAGES - 2, nk - 2 - kt));
+    if (d.ktail && kt + 1 == nk - 1) {
+      zero_k_tail<T>(d, sA, sB, (kt + 1) % T::STAGES, kt + 1, wave, lane);
       wait_and_barrier<0>();
     }
-    mma_stage_at<T>(sA, sB, buf, f, acc);
+    load_ops<T>(sA, sB, (kt + 1) % T::STAGES, 0, f, o0);
+    mfma_ops<T>(o1, acc);
   }
+  inner_steps<T>(sA, sB, (nk - 1) % T::STAGES, f, o0, o1, acc);
+  mfma_ops<T>(o1, acc);
 
   // epilogue: register r of block (i, j) is row 8 (r / 4) + 4 (lane / 32) + r % 4 and
   // column lane % 32 of that block
@@ -510,12 +585,15 @@ __global__ __launch_bounds__(T::THREADS, 2) void gemm_dma_kernel(
     }
 }
 
-// Workgroup tile of the main kernel for an M x N output.  Both tiles give every output
+// Workgroup tile of the main kernel for an M x N output.  Every tile gives every output
 // element the same bits (same instruction, same K order), so this choice changes only the
-// time: the 256 x 256 tile streams half the operand bytes per flop but runs one workgroup
-// per CU, so it wins once there are enough tiles to fill the CUs.  The cost below counts
-// rounds of the CU array with round times measured on MI355X at K = 4096 (both scale
-// with K): 256 x 256, one per CU: 120; 128 x 128, two per CU: 82, one per CU: 48.
+// time.  The 256 x 256 tile streams half the operand bytes per flop but runs one workgroup
+// per CU; the 128 x 128 tile runs two per CU, or one with a deeper ring when the grid has
+// no more tiles than CUs.  The cost counts rounds of the CU array, with round times
+// measured on MI355X at K = 4096 (all scale with K): 256 x 256: 121; 128 x 128 two per CU:
+// 69, one per CU: 48 (44 with the deeper ring).
+enum class TileKind { k128, k128deep, k256 };
+
 int cu_count() {
   static std::atomic<int> cached[64];
   int dev = 0;
@@ -528,13 +606,14 @@ int cu_count() {
   return v;
 }
 
-bool big_tile(int64_t M, int64_t N, int cus) {
+TileKind pick_tile(int64_t M, int64_t N, int cus) {
   const int64_t n256 = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t n128 = ((M + 127) / 128) * ((N + 127) / 128);
-  const int64_t cost256 = 120 * ((n256 + cus - 1) / cus);
+  if (n128 <= cus) return TileKind::k128deep;
+  const int64_t cost256 = 121 * ((n256 + cus - 1) / cus);
   const int64_t rem = n128 % (2 * cus);
-  const int64_t cost128 = 82 * (n128 / (2 * cus)) + (rem == 0 ? 0 : rem <= cus ? 48 : 82);
-  return cost256 < cost128;
+  const int64_t cost128 = 69 * (n128 / (2 * cus)) + (rem == 0 ? 0 : rem <= cus ? 48 : 69);
+  return cost256 < cost128 ? TileKind::k256 : TileKind::k128;
 }
 
 template <class T>
@@ -598,8 +677,11 @@ extern "C" int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t
         A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
         0, int(K), 0);
   else if (M * lda * 2 < (int64_t(1) << 32) && N * ldb * 2 < (int64_t(1) << 32)) {
-    if (big_tile(M, N, cu_count())) launch_dma<Tile256>(A, B, C, M, N, K, lda, ldb, ldc, cf, s);
-    else launch_dma<Tile128>(A, B, C, M, N, K, lda, ldb, ldc, cf, s);
+    switch (pick_tile(M, N, cu_count())) {
+      case TileKind::k256: launch_dma<Tile256>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
+      case TileKind::k128deep: launch_dma<Tile128Deep>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
+      default: launch_dma<Tile128>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
+    }
   }
   else  // operands of 4 GiB or more: register-staged kernel (same tile, instruction, K order)
     gemm_kernel<false><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
@@ -609,13 +691,22 @@ extern "C" int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t
 }
 
 extern "C" int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_t* tile_m,
-                            int32_t* tile_n) {
-  if (!tile_m || !tile_n) return BI_ERR_NULL;
+                            int32_t* tile_n, int32_t* stages) {
+  if (!tile_m || !tile_n || !stages) return BI_ERR_NULL;
   if (M < 0 || N < 0 || K < 0) return BI_ERR_SHAPE;
   if (a_dtype != BI_BF16 && a_dtype != BI_F32) return BI_ERR_DTYPE;
-  const bool big = a_dtype == BI_BF16 && M > 0 && N > 0 && big_tile(M, N, cu_count());
-  *tile_m = big ? Tile256::TM : Tile128::TM;
-  *tile_n = big ? Tile256::TN : Tile128::TN;
+  if (a_dtype == BI_F32 || M == 0 || N == 0) {  // register-staged kernel (or nothing to do)
+    *tile_m = BM;
+    *tile_n = BN;
+    *stages = 2;
+    return BI_OK;
+  }
+  switch (pick_tile(M, N, cu_count())) {
+    case TileKind::k256: *tile_m = Tile256::TM; *tile_n = Tile256::TN; *stages = Tile256::STAGES; break;
+    case TileKind::k128deep:
+      *tile_m = Tile128Deep::TM; *tile_n = Tile128Deep::TN; *stages = Tile128Deep::STAGES; break;
+    default: *tile_m = Tile128::TM; *tile_n = Tile128::TN; *stages = Tile128::STAGES; break;
+  }
   return BI_OK;
 }
 

@@ -43,10 +43,10 @@ def test_vs_oracle(lib, m, n, k):
     assert r["ok"], r
 
 
-@pytest.mark.parametrize("m,n,k", [(1536, 6144, 256), (1100, 8000, 200)])
+@pytest.mark.parametrize("m,n,k", [(4096, 4096, 256), (3100, 8000, 200)])
 def test_large_tile_vs_oracle(lib, m, n, k):
     # output grids large enough for the 256 x 256 workgroup tile, ragged in M, N and K
-    assert lib.bi_gemm_tile(m, n, k) == (256, 256)
+    assert lib.bi_gemm_tile(m, n, k)[:2] == (256, 256)
     say("gemm large tile", m, n, k)
     a, b = gemm_inputs(m, n, k, cfg=36)
     c = lib.bi_gemm(bf16(a), bf16(_nk(b)))
@@ -55,20 +55,21 @@ def test_large_tile_vs_oracle(lib, m, n, k):
 
 
 def test_tile_switch_changes_no_bit(lib):
-    # the same rows computed under the 256 x 256 tile (large M) and the 128 x 128 tile
-    # (small M), at several positions, for a square and a ragged N
-    for n, k in [(4096, 4096), (6000, 1000)]:
-        a, b = gemm_inputs(4096, n, k, cfg=37)
+    # the same rows computed under every workgroup configuration (256 x 256; 128 x 128 with
+    # a 2- or 3-stage ring), chosen by the grid size, at several positions, for a square
+    # and a ragged N
+    for n, k, full_m in [(4096, 4096, 4096), (6000, 1000, 8192)]:
+        a, b = gemm_inputs(full_m, n, k, cfg=37)
         A, B = bf16(a), bf16(_nk(b))
-        assert lib.bi_gemm_tile(4096, n, k) == (256, 256)
+        assert lib.bi_gemm_tile(full_m, n, k)[:2] == (256, 256)
         full = lib.bi_gemm(A, B)
-        tiles = set()
+        configs = {lib.bi_gemm_tile(full_m, n, k)}
         for m in (1, 255, 1000, 2048, 2560, 3000):
-            tiles.add(lib.bi_gemm_tile(m, n, k))
+            configs.add(lib.bi_gemm_tile(m, n, k))
             assert same_bits(lib.bi_gemm(A[:m], B), full[:m]), (n, k, m)
-        assert tiles == {(128, 128), (256, 256)}, tiles
-        sel = torch.tensor([4095, 17, 2600, 300], device="cuda")
-        assert lib.bi_gemm_tile(4, n, k) == (128, 128)
+        assert configs == {(128, 128, 3), (128, 128, 2), (256, 256, 2)}, configs
+        sel = torch.tensor([full_m - 1, 17, 2600, 300], device="cuda")
+        assert lib.bi_gemm_tile(4, n, k) == (128, 128, 3)
         assert same_bits(lib.bi_gemm(A[sel].contiguous(), B), full[sel])
         ff = lib.bi_gemm(A, B, out_dtype=torch.float32)
         assert same_bits(lib.bi_gemm(A[sel].contiguous(), B, out_dtype=torch.float32), ff[sel])
@@ -168,7 +169,7 @@ def test_fp32_operand_variant(lib):
 def test_k_tail_with_garbage_past_k(lib):
     # rows padded to a multiple of 8 elements, the padding filled with NaN: every product
     # past K must be an exact zero
-    for m, n, k in [(65, 70, 1003), (3, 130, 77), (200, 33, 9), (1100, 8000, 77)]:
+    for m, n, k in [(65, 70, 1003), (3, 130, 77), (200, 33, 9), (3100, 8000, 77), (1000, 600, 50)]:
         a, b = gemm_inputs(m, n, k, cfg=35)
         kp = (k + 7) // 8 * 8 + 8
         A = torch.full((m, kp), float("nan"), device="cuda").to(torch.bfloat16)
