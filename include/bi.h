@@ -172,7 +172,8 @@ int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  *   v_cache  [num_pages, Hkv, D, page_size] bf16: each page stores V transposed (slot
  *            fastest, natural slot order), the operand order of the P.V product
  *   block_table [batch, max_pages_per_seq] int32: physical page of logical page j
- *            (entries at j >= ceil(seq_lens[b] / page_size) are never read)
+ *            (entries at j >= ceil(seq_lens[b] / page_size) may be read, their values
+ *            are never used)
  *   seq_lens [batch] int32, query_start_loc [batch + 1] int32 (device)
  *   out      [num_tokens, Hq, D], dtype out_dtype (BI_BF16 | BI_F32)
  *   scale    softmax scale (1/sqrt(D) for the standard reading)
@@ -187,9 +188,12 @@ int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * Supported: D = 128, Hq/Hkv in {1, 2, 4, 8, 16}, page_size a multiple of 16 dividing
  * 256.  max_seq_len is an upper bound of seq_lens (sizes the grid); every seq_len must
  * be <= max_pages_per_seq * page_size.
- * workspace >= bi_attention_workspace_bytes(num_tokens, Hq, D, max_seq_len).
- * Errors: BI_ERR_NULL, BI_ERR_SHAPE, BI_ERR_UNSUPPORTED, BI_ERR_WORKSPACE,
- * BI_ERR_ALIGN (16-byte alignment of every tensor).
+ * workspace >= bi_attention_workspace_bytes(num_tokens, Hq, D, max_seq_len): for calls
+ * of at most 1024 tokens, the fp32 chunk partials (m, l and o of every token, q head and
+ * chunk) and a 16-byte record per token; 0 for longer calls (no workspace is used).
+ * Errors: BI_ERR_NULL, BI_ERR_SHAPE (also when num_tokens * ceil(max_seq_len / 256) *
+ * Hkv reaches 2^31 on the split path), BI_ERR_UNSUPPORTED, BI_ERR_WORKSPACE, BI_ERR_ALIGN
+ * (16-byte alignment of every tensor).
  */
 size_t bi_attention_workspace_bytes(int64_t num_tokens, int32_t num_q_heads, int32_t head_dim,
                                     int64_t max_seq_len);

@@ -35,6 +35,8 @@
 //           s' = s with bits 2 and 3 swapped (0-3, 8-11, 4-7, 12-15), which puts the 8
 //           keys one matrix instruction reads from a page next to each other;
 //   v_cache [page][kv head][128 d][slot]  (V transposed, slots in order).
+#include <algorithm>
+
 #include "bi_common.h"
 
 namespace bi {
@@ -87,9 +89,11 @@ struct Seq {
   const uint16_t* kc;   // k_cache base
   const uint16_t* vc;   // v_cache base
   const int32_t* bt;    // block-table row of the sequence
-  int ps;               // page size
+  int ps;               // page size (a power of two)
   int hkv, kvh;
   int seq_len;
+  int maxp;             // columns of the block table (pages per sequence)
+  int ps_shift;         // log2(ps)
 };
 
 // Exchange area of one workgroup for one chunk.
@@ -99,73 +103,88 @@ struct ChunkLDS {
   floatx4 o[4][8][64];
 };
 
-// One 256-key chunk for the workgroup's 16 columns (all 4 waves call it together).
-// pcol: absolute position of this lane's column (-1: unused column).  Returns, in every
-// wave, m_c and l_c of column lane % 16 and, in wave w, o_c for d-blocks 2w and 2w + 1 in
-// the MFMA output layout (oc[j][r] is d = 16 (2w + j) + 4 (lane / 16) + r).
-__device__ __forceinline__ void chunk_partial(const Seq& sq, int c, const u16x8 (&qop)[4], int pcol,
-                                              float sl2, ChunkLDS& sh, float& m_c, float& l_c,
-                                              floatx4 (&oc)[2]) {
+// The reduction of one 256-key chunk for the workgroup's 16 columns, in phases (all 4
+// waves call each phase together): the page ids, the K and V operand loads, the scores
+// with the chunk maximum and P, and the values with the workgroup sums.  chunk_partial
+// runs them back to back; the split kernel interleaves them with the loads of its next
+// chunk.  The operations of a chunk, and so its bits, are the same either way.
+
+// Physical page of chunk page l, held by lane l (0 for lanes past the chunk's pages and
+// for pages past the sequence: page 0 always exists, its data is masked out).
+__device__ __forceinline__ int chunk_pages(const Seq& sq, int c) {
+  const int lane = threadIdx.x & 63;
+  const int ppc = CHUNK >> sq.ps_shift;
+  const int l = lane < ppc ? lane : 0;
+  const int pg = sq.bt[min(max(c * ppc + l, 0), sq.maxp - 1)];
+  return (lane < ppc && c * CHUNK + lane * sq.ps < sq.seq_len) ? pg : 0;
+}
+
+// K operands of this wave's 64 keys (4 tiles of 16 keys x 4 d-steps).  Every address is
+// inside the cache: a key past the sequence reads a slot of its page that holds no key yet,
+// or page 0; its score is masked to -inf later.
+__device__ __forceinline__ void chunk_load_k(const Seq& sq, int pg, u16x8 (&kop)[2][2][4]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int kr0 = 8 * (i >> 2) + (i & 3);           // key of MFMA row i in the first tile of a pair
   const int64_t page_elems = static_cast<int64_t>(sq.ps) * HD;
-  const int c0 = c * CHUNK;
-  const int ppc = CHUNK / sq.ps;                    // pages per chunk
-  // physical page of chunk page l, held by lane l (read once, then shuffled)
-  int pg = 0;
-  if (lane < ppc && (c0 + lane * sq.ps) < sq.seq_len) pg = sq.bt[c * ppc + lane];
-
-  // V^T operands of this wave's two 32-key slices (independent of P: issued first)
-  u16x8 vop[2][8];
-#pragma unroll
-  for (int uu = 0; uu < 2; ++uu) {
-    const int kk0 = 32 * (2 * w + uu) + 8 * g;      // first of this lane's 8 keys
-    const int nvalid = sq.seq_len - (c0 + kk0);     // keys kk0 + e valid for e < nvalid
-    const int phys = __shfl(pg, kk0 / sq.ps, 64);
-    const uint16_t* vbase =
-        sq.vc + (static_cast<int64_t>(phys) * sq.hkv + sq.kvh) * page_elems + (kk0 % sq.ps);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (nvalid > 0) {
-        v = *reinterpret_cast<const u16x8*>(vbase + static_cast<int64_t>(16 * db + i) * sq.ps);
-        if (nvalid < 8) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e >= nvalid) v[e] = 0;
-        }
-      }
-      vop[uu][db] = v;
-    }
-  }
-
-  floatx4 s[2][2];
 #pragma unroll
   for (int uu = 0; uu < 2; ++uu) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const int kk = 32 * (2 * w + uu) + kr0 + 4 * h2;   // chunk-relative key of this lane's row
-      const int phys = __shfl(pg, kk / sq.ps, 64);
-      u16x8 kop[4];
-      if (c0 + kk < sq.seq_len) {
-        const uint16_t* kp = sq.kc + (static_cast<int64_t>(phys) * sq.hkv + sq.kvh) * page_elems +
-                             (static_cast<int64_t>(4 * g) * sq.ps + k_slot(kk % sq.ps)) * 8;
+      const int phys = __shfl(pg, kk >> sq.ps_shift, 64);
+      const uint16_t* kp = sq.kc + (static_cast<int64_t>(phys) * sq.hkv + sq.kvh) * page_elems +
+                           ((4 * g) * sq.ps + k_slot(kk & (sq.ps - 1))) * 8;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          kop[t] = *reinterpret_cast<const u16x8*>(kp + static_cast<int64_t>(t) * sq.ps * 8);
-      } else {
+      for (int t = 0; t < 4; ++t)
+        kop[uu][h2][t] = *reinterpret_cast<const u16x8*>(kp + static_cast<int64_t>(t) * sq.ps * 8);
+    }
+  }
+}
+
+// V^T operands of this wave's two 32-key slices (masked later, in chunk_values).
+__device__ __forceinline__ void chunk_load_v(const Seq& sq, int pg, u16x8 (&vop)[2][8]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int64_t page_elems = static_cast<int64_t>(sq.ps) * HD;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) kop[t] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+  for (int uu = 0; uu < 2; ++uu) {
+    const int kk0 = 32 * (2 * w + uu) + 8 * g;      // first of this lane's 8 keys
+    const int phys = __shfl(pg, kk0 >> sq.ps_shift, 64);
+    const uint16_t* vbase =
+        sq.vc + (static_cast<int64_t>(phys) * sq.hkv + sq.kvh) * page_elems + (kk0 & (sq.ps - 1));
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      vop[uu][db] = *reinterpret_cast<const u16x8*>(vbase + static_cast<int64_t>(16 * db + i) * sq.ps);
+  }
+}
+
+// Keep every load issued so far above this point: the scheduler would otherwise sink
+// loads next to their uses and leave one or two in flight.
+__device__ __forceinline__ void issue_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// S = K Q^T for this wave's keys, scaled to log2 units and masked beyond the column's
+// position; m = the chunk maximum of column lane % 16 (the 4 wave maxima exchanged
+// through LDS); on return s holds P = 2^(t - m) and lsum this wave's sum of P.
+__device__ __forceinline__ void chunk_scores(int c, const u16x8 (&kop)[2][2][4], const u16x8 (&qop)[4],
+                                             int pcol, float sl2, ChunkLDS& sh, floatx4 (&s)[2][2],
+                                             float& m, float& lsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int c0 = c * CHUNK;
+#pragma unroll
+  for (int uu = 0; uu < 2; ++uu) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc = mfma16(kop[t], qop[t], acc);
+      for (int t = 0; t < 4; ++t) acc = mfma16(kop[uu][h2][t], qop[t], acc);
       s[uu][h2] = acc;
     }
   }
-
-  // scale, causal mask, chunk maximum
   float mx = -__builtin_huge_valf();
 #pragma unroll
   for (int uu = 0; uu < 2; ++uu)
@@ -182,9 +201,9 @@ __device__ __forceinline__ void chunk_partial(const Seq& sq, int c, const u16x8 
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   if (g == 0) sh.mx[w][i] = mx;
   __syncthreads();
-  const float m = fmaxf(fmaxf(sh.mx[0][i], sh.mx[1][i]), fmaxf(sh.mx[2][i], sh.mx[3][i]));
+  m = fmaxf(fmaxf(sh.mx[0][i], sh.mx[1][i]), fmaxf(sh.mx[2][i], sh.mx[3][i]));
 
-  float lsum = 0.f;
+  lsum = 0.f;
 #pragma unroll
   for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
@@ -198,22 +217,50 @@ __device__ __forceinline__ void chunk_partial(const Seq& sq, int c, const u16x8 
       }
   lsum = lsum + __shfl_xor(lsum, 16, 64);
   lsum = lsum + __shfl_xor(lsum, 32, 64);
+}
 
+// O_w^T = V^T . P^T over this wave's two 32-key slices (V past the sequence zeroed, P
+// split into bf16 hi + lo), then l_c = (l_0 + l_1) + (l_2 + l_3) and
+// o_c = (O_0 + O_1) + (O_2 + O_3) through LDS.  Returns, in every wave, m_c and l_c of
+// column lane % 16 and, in wave w, o_c for d-blocks 2w and 2w + 1 in the MFMA output
+// layout (oc[j][r] is d = 16 (2w + j) + 4 (lane / 16) + r).
+__device__ __forceinline__ void chunk_values(const Seq& sq, int c, u16x8 (&vop)[2][8],
+                                             const floatx4 (&s)[2][2], float m, float lsum,
+                                             ChunkLDS& sh, float& m_c, float& l_c, floatx4 (&oc)[2]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int c0 = c * CHUNK;
+  if (c0 + 64 * (w + 1) > sq.seq_len) {   // this wave's keys reach past the sequence
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      const int nvalid = sq.seq_len - (c0 + 32 * (2 * w + uu) + 8 * g);   // keys kk0 + e valid for e < nvalid
+      u32x4 keep;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        keep[k] = (2 * k < nvalid ? 0x0000ffffu : 0u) | (2 * k + 1 < nvalid ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        vop[uu][db] = __builtin_bit_cast(u16x8, __builtin_bit_cast(u32x4, vop[uu][db]) & keep);
+    }
+  }
   floatx4 o[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) o[db] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int uu = 0; uu < 2; ++uu) {
-    u16x8 phi, plo;
+    // P = hi + lo, both rounded to nearest even (v_cvt_pk_bf16_f32 converts two at a time)
+    u32x4 hi, lo;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = s[uu][h2][r];
-        const uint16_t h = f32_to_bf16(p);
-        phi[4 * h2 + r] = h;
-        plo[4 * h2 + r] = f32_to_bf16(p - bf16_to_f32(h));
+      for (int r = 0; r < 4; r += 2) {
+        const floatx2 p = {s[uu][h2][r], s[uu][h2][r + 1]};
+        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+        const floatx2 back = {__uint_as_float(h << 16), __uint_as_float(h & 0xffff0000u)};
+        hi[2 * h2 + r / 2] = h;
+        lo[2 * h2 + r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p - back, bf16x2));
       }
+    const u16x8 phi = __builtin_bit_cast(u16x8, hi), plo = __builtin_bit_cast(u16x8, lo);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       o[db] = mfma16(vop[uu][db], phi, o[db]);
@@ -231,6 +278,23 @@ __device__ __forceinline__ void chunk_partial(const Seq& sq, int c, const u16x8 
     oc[j] = (sh.o[0][db][lane] + sh.o[1][db][lane]) + (sh.o[2][db][lane] + sh.o[3][db][lane]);
   }
   m_c = m;
+}
+
+// One 256-key chunk, phases back to back.  pcol: absolute position of this lane's column
+// (-1: unused column).  K is loaded first: loads complete in order, so the scores are
+// computed while V is still arriving.
+__device__ __forceinline__ void chunk_partial(const Seq& sq, int c, const u16x8 (&qop)[4], int pcol,
+                                              float sl2, ChunkLDS& sh, float& m_c, float& l_c,
+                                              floatx4 (&oc)[2]) {
+  const int pg = chunk_pages(sq, c);
+  u16x8 kop[2][2][4], vop[2][8];
+  chunk_load_k(sq, pg, kop);
+  chunk_load_v(sq, pg, vop);
+  issue_fence();
+  floatx4 s[2][2];
+  float m, lsum;
+  chunk_scores(c, kop, qop, pcol, sl2, sh, s, m, lsum);
+  chunk_values(sq, c, vop, s, m, lsum, sh, m_c, l_c, oc);
 }
 
 __device__ __forceinline__ void merge_step(float& m, float& l, float mc, float lc, float& a,
@@ -263,10 +327,11 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch,
-    int max_pages, int hkv, int ps) {
+    int max_pages, int hkv, int ps, int4* __restrict__ tok) {
   const int t = blockIdx.x;
   const int b = find_seq_wave(qsl, batch, t);
   const int pos = seq_lens[b] - (qsl[b + 1] - qsl[b]) + (t - qsl[b]);
+  if (tok && threadIdx.x == 0) tok[t] = make_int4(b, pos, seq_lens[b], 0);
   const int phys = bt[static_cast<int64_t>(b) * max_pages + pos / ps];
   const int slot = pos % ps;
   const int nvec = hkv * HD / 8;
@@ -288,40 +353,151 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 }
 
 // ---------------------------------------------------------------- step 2a: split-KV chunks
-// grid.x = num_tokens * max_chunks, grid.y = kv heads; one workgroup per (token, chunk,
-// kv head), its 16 columns are the token's G q heads (the rest unused).
+// Work items: chunk c of token t for kv head h, ordered by (t, c, h); the item's 16 columns
+// are the token's G q heads (the rest unused).  A persistent grid: workgroup w reduces
+// items w, w + gridDim.x, ...  The token records (sequence, position, length) written by
+// kv_write_kernel and the running count of chunks per token sit in LDS.  Loads are
+// software-pipelined across items: the next item's q and K go out once this item's scores
+// are done, the page ids of the item three ahead and the next item's V once its values
+// are done, so a workgroup keeps loads in flight while it computes.  Which workgroup reduces
+// an item, and when, changes no bit of it.
+struct SplitItem {
+  int t, c, kvh, pos;
+  Seq sq;
+};
+
+// Item `item` (a 32-bit index: the host bounds the count); `t0` is a token at or before the
+// item's token: the items of a workgroup advance, so a short forward scan finds it.
+__device__ __forceinline__ SplitItem split_item(int item, int t0, const int4* s_tok, const int* s_start,
+                                                int num_tokens, const uint16_t* kc, const uint16_t* vc,
+                                                const int32_t* bt, int max_pages, int ps, int hkv) {
+  SplitItem it;
+  const unsigned j = static_cast<unsigned>(item) / static_cast<unsigned>(hkv);
+  it.kvh = item - static_cast<int>(j) * hkv;
+  if (t0 < 0 || t0 >= num_tokens || s_start[t0] > static_cast<int>(j)) t0 = 0;   // hint past the item
+  int t = t0;
+  if (s_start[t0 + 1] <= static_cast<int>(j)) {   // past t0: binary search above it
+    int lo = t0 + 1, hi = num_tokens - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_start[mid] <= static_cast<int>(j)) lo = mid;
+      else hi = mid - 1;
+    }
+    t = lo;
+  }
+  // the item is the same for the whole workgroup: keep its fields in scalar registers
+  const int4 r = s_tok[t];
+  it.t = __builtin_amdgcn_readfirstlane(t);
+  it.c = __builtin_amdgcn_readfirstlane(static_cast<int>(j) - s_start[t]);
+  it.pos = __builtin_amdgcn_readfirstlane(r.y);
+  const int b = __builtin_amdgcn_readfirstlane(r.x);
+  const int len = __builtin_amdgcn_readfirstlane(r.z);
+  it.sq = Seq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, it.kvh, len, max_pages,
+              __builtin_ctz(ps)};
+  return it;
+}
+
+// Q operands of one column, loaded unconditionally (an unused column loads the group's
+// first head; its scores are masked and its output is never stored).
+__device__ __forceinline__ void load_q_col(const uint16_t* q, int64_t token, int head, int hq,
+                                           u16x8 (&qop)[4]) {
+  const int g = (threadIdx.x & 63) >> 4;
+  const uint16_t* p = q + (token * hq + head) * HD + 32 * g;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) qop[t] = *reinterpret_cast<const u16x8*>(p + 8 * t);
+}
+
 __global__ __launch_bounds__(256) void attn_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch,
-    int max_pages, int hq, int hkv, int ps, int max_chunks, float sl2, float* __restrict__ ws_ml,
-    float* __restrict__ ws_o) {
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt, const int4* __restrict__ tok,
+    int num_tokens, int max_pages, int hq, int hkv, int ps, int max_chunks, float sl2,
+    float* __restrict__ ws_ml, float* __restrict__ ws_o) {
   __shared__ ChunkLDS sh;
-  const int t = blockIdx.x / max_chunks;
-  const int c = blockIdx.x % max_chunks;
-  const int kvh = blockIdx.y;
-  const int b = find_seq_wave(qsl, batch, t);
-  const int L = seq_lens[b];
-  const int pos = L - (qsl[b + 1] - qsl[b]) + (t - qsl[b]);
-  if (c * CHUNK > pos) return;
-  const int G = hq / hkv;
+  __shared__ int4 s_tok[SPLIT_MAX_TOKENS];
+  __shared__ int s_start[SPLIT_MAX_TOKENS + 1];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int t = threadIdx.x; t < num_tokens; t += 256) s_tok[t] = tok[t];
+  __syncthreads();
+  if (w == 0) {   // s_start[t] = chunks of tokens 0 .. t-1 (token t has pos / 256 + 1)
+    int carry = 0;
+    for (int base = 0; base < num_tokens; base += 64) {
+      const int t = base + lane;
+      const int pos = t < num_tokens ? s_tok[t].y : -1;
+      int v = pos >= 0 ? pos / CHUNK + 1 : 0;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+      }
+      if (t < num_tokens) s_start[t + 1] = carry + v;
+      carry += __shfl(v, 63, 64);
+    }
+    if (lane == 0) s_start[0] = 0;
+  }
+  __syncthreads();
+  const int n_items = s_start[num_tokens] * hkv;
+  int item = blockIdx.x;
+  if (item >= n_items) return;
+  const int stride = gridDim.x;
+  const int G = hq / hkv;
   const int col = lane & 15;
   const bool used = col < G;
-  u16x8 qop[4];
-  load_q(q, t, kvh * G + col, hq, used, qop);
-  Seq sq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, kvh, L};
-  float m_c, l_c;
-  floatx4 oc[2];
-  chunk_partial(sq, c, qop, used ? pos : -1, sl2, sh, m_c, l_c, oc);
-  if (!used) return;
-  const int64_t slot = (static_cast<int64_t>(t) * hq + kvh * G + col) * max_chunks + c;
-  float* po = ws_o + slot * HD + 4 * (lane >> 4);
+  const int hcol = used ? col : 0;
+  auto at = [&](int it, int t0) {
+    return split_item(it, t0, s_tok, s_start, num_tokens, kc, vc, bt, max_pages, ps, hkv);
+  };
+
+  // the k-th item ahead of `item`, or the last one this workgroup has (reloads past the end
+  // are never used); non-decreasing in k, as the token hints of split_item require
+  auto ahead = [&](int k) {
+    int v = item + k * stride;
+    while (v >= n_items) v -= stride;
+    return v;
+  };
+
+  SplitItem cur = at(item, 0);
+  int pg = chunk_pages(cur.sq, cur.c);
+  u16x8 qop[4], kop[2][2][4], vop[2][8];
+  load_q_col(q, cur.t, cur.kvh * G + hcol, hq, qop);
+  chunk_load_k(cur.sq, pg, kop);
+  SplitItem nxt = at(ahead(1), cur.t);
+  int pgn = chunk_pages(nxt.sq, nxt.c);
+  SplitItem nxt2 = at(ahead(2), nxt.t);
+  int pgn2 = chunk_pages(nxt2.sq, nxt2.c);
+  chunk_load_v(cur.sq, pg, vop);
+  issue_fence();
+  for (;;) {
+    const bool has_next = item + stride < n_items;
+    const SplitItem nxt3 = at(ahead(3), nxt2.t);
+    floatx4 s[2][2];
+    float m, lsum;
+    chunk_scores(cur.c, kop, qop, used ? cur.pos : -1, sl2, sh, s, m, lsum);
+    load_q_col(q, nxt.t, nxt.kvh * G + hcol, hq, qop);
+    chunk_load_k(nxt.sq, pgn, kop);
+    issue_fence();
+    float m_c, l_c;
+    floatx4 oc[2];
+    chunk_values(cur.sq, cur.c, vop, s, m, lsum, sh, m_c, l_c, oc);
+    const int pgn3 = chunk_pages(nxt3.sq, nxt3.c);   // page ids three items ahead
+    chunk_load_v(nxt.sq, pgn, vop);
+    issue_fence();
+    if (used) {
+      const int64_t slot = (static_cast<int64_t>(cur.t) * hq + cur.kvh * G + col) * max_chunks + cur.c;
+      float* po = ws_o + slot * HD + 4 * (lane >> 4);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) *reinterpret_cast<floatx4*>(po + 16 * (2 * w + j)) = oc[j];
-  if (w == 0 && (lane >> 4) == 0) {
-    ws_ml[2 * slot] = m_c;
-    ws_ml[2 * slot + 1] = l_c;
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<floatx4*>(po + 16 * (2 * w + j)) = oc[j];
+      if (w == 0 && (lane >> 4) == 0) {
+        ws_ml[2 * slot] = m_c;
+        ws_ml[2 * slot + 1] = l_c;
+      }
+    }
+    if (!has_next) break;
+    item += stride;
+    cur = nxt;
+    nxt = nxt2;
+    pgn = pgn2;
+    nxt2 = nxt3;
+    pgn2 = pgn3;
   }
 }
 
@@ -408,7 +584,7 @@ __global__ __launch_bounds__(256) void attn_group_kernel(
   const bool used = col < G;
   u16x8 qop[4];
   load_q(q, t, kvh * G + col, hq, used, qop);
-  Seq sq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, kvh, L};
+  Seq sq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, kvh, L, max_pages, __builtin_ctz(ps)};
   float m = 0.f, l = 0.f;
   floatx4 o[2];
   for (int c = c_first; c <= c_last; ++c) {
@@ -473,7 +649,7 @@ __global__ __launch_bounds__(256) void attn_walk_kernel(
     u16x8 qop[4];
     load_q(q, mine ? my_tok : 0, head, hq, mine, qop);
     const int L = seq_lens[b];
-    Seq sq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, kvh, L};
+    Seq sq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, kvh, L, max_pages, __builtin_ctz(ps)};
     // highest position among this sequence's columns (the same in every wave)
     int pmax = pcol;
 #pragma unroll
@@ -514,6 +690,17 @@ __global__ __launch_bounds__(256) void attn_walk_kernel(
   }
 }
 
+// Workgroups of attn_split_kernel resident per CU (read once).
+int split_resident() {
+  static std::atomic<int> cached{0};
+  int v = cached.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, attn_split_kernel, 256, 0) != hipSuccess || v < 1)
+    v = 1;
+  cached.store(v, std::memory_order_relaxed);
+  return v;
+}
+
 int64_t chunks_for(int64_t max_seq_len) { return max_seq_len <= 0 ? 1 : (max_seq_len + CHUNK - 1) / CHUNK; }
 
 // (m, l) pairs first, padded so the partial outputs start on a 16-byte boundary.
@@ -529,7 +716,8 @@ extern "C" size_t bi_attention_workspace_bytes(int64_t num_tokens, int32_t num_q
   if (num_tokens <= 0 || num_tokens > SPLIT_MAX_TOKENS || num_q_heads <= 0 || head_dim <= 0)
     return 0;
   const int64_t rows = num_tokens * num_q_heads * chunks_for(max_seq_len);
-  return static_cast<size_t>(ml_floats(rows) + rows * head_dim) * sizeof(float);
+  return static_cast<size_t>(ml_floats(rows) + rows * head_dim) * sizeof(float) +
+         static_cast<size_t>(num_tokens) * sizeof(int4);
 }
 
 extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new, void* k_cache,
@@ -561,21 +749,28 @@ extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new,
   const bool split = num_tokens <= SPLIT_MAX_TOKENS;
   const size_t need = bi_attention_workspace_bytes(num_tokens, num_q_heads, head_dim, max_seq_len);
   if (split && (!workspace || workspace_bytes < need)) return BI_ERR_WORKSPACE;
+  // the split path indexes its work items (token, chunk, kv head) with 32-bit integers
+  if (split && num_tokens * chunks_for(max_seq_len) * num_kv_heads >= (int64_t(1) << 31))
+    return BI_ERR_SHAPE;
 
   hipStream_t s = as_stream(stream);
   const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  const int64_t maxc = chunks_for(max_seq_len);
+  float* ws_ml = static_cast<float*>(workspace);
+  float* ws_o = ws_ml + ml_floats(num_tokens * num_q_heads * maxc);
+  int4* ws_tok = split ? reinterpret_cast<int4*>(ws_o + num_tokens * num_q_heads * maxc * HD) : nullptr;
   kv_write_kernel<<<dim3(static_cast<unsigned>(num_tokens)), dim3(256), 0, s>>>(
       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_table, seq_lens,
-      query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size);
+      query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size, ws_tok);
   const int of = out_dtype == BI_F32;
   if (split) {
-    const int64_t maxc = chunks_for(max_seq_len);
-    float* ws_ml = static_cast<float*>(workspace);
-    float* ws_o = ws_ml + ml_floats(num_tokens * num_q_heads * maxc);
-    attn_split_kernel<<<dim3(static_cast<unsigned>(num_tokens * maxc), num_kv_heads), dim3(256), 0, s>>>(
+    // as many workgroups as can be resident at once, never more than there are items
+    const int64_t items = num_tokens * maxc * num_kv_heads;   // an upper bound of the work items
+    const int64_t grid = std::min<int64_t>(items, static_cast<int64_t>(split_resident()) * cu_count());
+    attn_split_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, s>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-        static_cast<const uint16_t*>(v_cache), block_table, seq_lens, query_start_loc, batch,
+        static_cast<const uint16_t*>(v_cache), block_table, ws_tok, static_cast<int>(num_tokens),
         max_pages_per_seq, num_q_heads, num_kv_heads, page_size, static_cast<int>(maxc), sl2,
         ws_ml, ws_o);
     const int64_t rows = num_tokens * num_q_heads;
@@ -631,7 +826,7 @@ extern "C" int bi_attention_batchdep_split(
   kv_write_kernel<<<dim3(static_cast<unsigned>(num_tokens)), dim3(256), 0, s>>>(
       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_table, seq_lens,
-      query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size);
+      query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size, nullptr);
   float* ws_ml = static_cast<float*>(workspace);
   float* ws_o = ws_ml + ml_floats(num_tokens * num_q_heads * maxg);
   attn_group_kernel<<<dim3(static_cast<unsigned>(num_tokens * maxg), num_kv_heads), dim3(256), 0, s>>>(

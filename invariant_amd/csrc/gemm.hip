@@ -29,8 +29,6 @@
 // split exactly into bf16 hi + mid + lo (truncations, so hi + mid + lo == a for normal
 // numbers) and the three products are accumulated into the same fp32 accumulator in
 // the order hi, mid, lo for every 16-wide K step.
-#include <atomic>
-
 #include "bi_common.h"
 
 namespace bi {
@@ -593,18 +591,6 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
 // measured on MI355X at K = 4096 (all scale with K): 256 x 256: 121; 128 x 128 two per CU:
 // 69, one per CU: 48 (44 with the deeper ring).
 enum class TileKind { k128, k128deep, k256 };
-
-int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = cached[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
-    v = 256;
-  cached[dev].store(v, std::memory_order_relaxed);
-  return v;
-}
 
 TileKind pick_tile(int64_t M, int64_t N, int cus) {
   const int64_t n256 = ((M + 255) / 256) * ((N + 255) / 256);

@@ -72,7 +72,7 @@ def test_validation_rejects_before_launch(lib):
     assert att(ps=24) == -6
     assert att(msl=65) == -2
     assert att() == -5
-    assert lib.bi_attention_workspace_bytes(4, 32, 128, 64) == (4 * 32 * 1 * 2 + 4 * 32 * 128) * 4
+    assert lib.bi_attention_workspace_bytes(4, 32, 128, 64) == (4 * 32 * 1 * 2 + 4 * 32 * 128) * 4 + 4 * 16
     assert lib.bi_attention_workspace_bytes(2000, 32, 128, 64) == 0
     assert lib.bi_gemm_splitk_workspace_bytes(2048, 2048, 2048) == 2 * 2048 * 2048 * 4
 

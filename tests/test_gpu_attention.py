@@ -82,6 +82,25 @@ def test_batch_position_page_invariance(lib):
         assert same_bits(op, out), ps
 
 
+def test_split_work_list_edges(lib):
+    # decode batches of many short or mixed sequences: the split kernel's work list (token,
+    # chunk, kv head) is walked by a persistent grid with look-ahead, so every workgroup
+    # runs past the end of its list, and the smallest call has fewer items than workgroups
+    rng = np.random.default_rng(44)
+    for B, lo, hi, hq, hkv in [(97, 1, 1500, 32, 8), (3, 1, 20, 8, 1), (40, 250, 260, 16, 1)]:
+        say("split work list", B, lo, hi, hq, hkv)
+        L = [int(x) for x in rng.integers(lo, hi + 1, B)]
+        dec = attention_case(L, [1] * B, n_q_heads=hq, n_kv_heads=hkv, cfg=44)
+        kc, vc, bt = make_cache(dec, 16, [l - 1 for l in L], cfg=84)
+        out, qsl = run(lib, dec, kc, vc, bt)
+        _check_vs_oracle(dec, out, qsl)
+        for b in (0, B // 2, B - 1):   # each sequence alone gives the same bits
+            one = {k: [dec[k][b]] for k in ("seq_lens", "q_lens", "k", "v", "q")}
+            kc1, vc1, bt1 = make_cache(one, 16, [L[b] - 1], cfg=85)
+            o1, _ = run(lib, one, kc1, vc1, bt1)
+            assert same_bits(o1[0], out[b]), (B, b)
+
+
 def test_chunked_prefill_matches_full_prefill(lib):
     L = 1100
     full = attention_case([L], [L], cfg=43)
