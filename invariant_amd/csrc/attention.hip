@@ -119,6 +119,14 @@ __device__ __forceinline__ int chunk_pages(const Seq& sq, int c) {
   return (lane < ppc && c * CHUNK + lane * sq.ps < sq.seq_len) ? pg : 0;
 }
 
+// 16 bytes of the K/V cache.  Every cache byte is read once per call, so the loads are
+// non-temporal: they do not displace the partial results, page table and queries from
+// the caches (without the hint, the partials written back under the K/V stream cost
+// about a tenth of the call).
+__device__ __forceinline__ u16x8 stream_load(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p));
+}
+
 // K operands of this wave's 64 keys (4 tiles of 16 keys x 4 d-steps).  Every address is
 // inside the cache: a key past the sequence reads a slot of its page that holds no key yet,
 // or page 0; its score is masked to -inf later.
@@ -137,7 +145,7 @@ __device__ __forceinline__ void chunk_load_k(const Seq& sq, int pg, u16x8 (&kop)
                            ((4 * g) * sq.ps + k_slot(kk & (sq.ps - 1))) * 8;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        kop[uu][h2][t] = *reinterpret_cast<const u16x8*>(kp + static_cast<int64_t>(t) * sq.ps * 8);
+        kop[uu][h2][t] = stream_load(kp + static_cast<int64_t>(t) * sq.ps * 8);
     }
   }
 }
@@ -155,7 +163,7 @@ __device__ __forceinline__ void chunk_load_v(const Seq& sq, int pg, u16x8 (&vop)
         sq.vc + (static_cast<int64_t>(phys) * sq.hkv + sq.kvh) * page_elems + (kk0 & (sq.ps - 1));
 #pragma unroll
     for (int db = 0; db < 8; ++db)
-      vop[uu][db] = *reinterpret_cast<const u16x8*>(vbase + static_cast<int64_t>(16 * db + i) * sq.ps);
+      vop[uu][db] = stream_load(vbase + static_cast<int64_t>(16 * db + i) * sq.ps);
   }
 }
 
