@@ -180,17 +180,21 @@ int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * Step 1 writes k_new/v_new into their pages.  Step 2: token at position p of q head
  * h (kv head h / (Hq/Hkv)) computes, for each chunk c <= p/256, the partial
  * (m_c, l_c, o_c) over keys [256c, min(256c + 256, p + 1)) with fp32 scores, P kept
- * as an exact bf16 hi + lo pair, fp32 accumulation; step 3 merges c = 0, 1, ... in
- * that order: m' = max(m, m_c), a = 2^(m - m'), b = 2^(m_c - m'), l' = a l + b l_c,
- * o' = a o + b o_c;  out = o / l.  Decode-sized calls compute the chunks in parallel
- * and merge in a second kernel, longer calls walk the chunks in registers; both use
- * the same arithmetic, so the bits never depend on which is used.
+ * as an exact bf16 hi + lo pair, fp32 accumulation.  Step 3 merges in two fixed levels,
+ * both set by absolute positions: the chunks of each group of 4 (keys [1024g,
+ * 1024g + 1024)) in ascending c, then the groups in ascending g; each level copies its
+ * first partial, then m' = max(m, m_c), a = 2^(m - m'), b = 2^(m_c - m'),
+ * l' = a l + b l_c, o' = a o + b o_c;  out = o / l.  Decode-sized calls reduce the
+ * groups in parallel and merge them in a second kernel, longer calls walk the chunks in
+ * registers; both use the same arithmetic, so the bits never depend on which is used.
  * Supported: D = 128, Hq/Hkv in {1, 2, 4, 8, 16}, page_size a multiple of 16 dividing
  * 256.  max_seq_len is an upper bound of seq_lens (sizes the grid); every seq_len must
  * be <= max_pages_per_seq * page_size.
  * workspace >= bi_attention_workspace_bytes(num_tokens, Hq, D, max_seq_len): for calls
- * of at most 1024 tokens, the fp32 chunk partials (m, l and o of every token, q head and
- * chunk) and a 16-byte record per token; 0 for longer calls (no workspace is used).
+ * of at most 1024 tokens, room for fp32 partials (m, l and o) of every token, q head and
+ * 256-key chunk (bi_attention fills a quarter of it, one per 4-chunk group; the
+ * comparison variant below may use all of it) and a 16-byte record per token; 0 for
+ * longer calls (no workspace is used).
  * Errors: BI_ERR_NULL, BI_ERR_SHAPE (also when num_tokens * ceil(max_seq_len / 256) *
  * Hkv reaches 2^31 on the split path), BI_ERR_UNSUPPORTED, BI_ERR_WORKSPACE, BI_ERR_ALIGN
  * (16-byte alignment of every tensor).

@@ -25,8 +25,12 @@
 //   l_c = (l_0 + l_1) + (l_2 + l_3),  o_c = (O_0 + O_1) + (O_2 + O_3).
 //   Rounding P itself to bf16 would cost tens of bf16 ulps in the output; hi + lo keeps
 //   16 bits.
-// Merge (ascending c, first chunk copied):  m' = max(m, m_c); a = 2^(m - m');
-//   b = 2^(m_c - m');  l' = a l + b l_c;  o' = a o + b o_c;  out = o / l.
+// Merge, in two fixed levels set by absolute positions only: the chunks of each group of
+// GROUP = 4 (keys [1024g, 1024g + 1024)) are merged in ascending c, then the groups in
+// ascending g; each level copies its first partial and then applies
+//   m' = max(m, m_c); a = 2^(m - m'); b = 2^(m_c - m');  l' = a l + b l_c;  o' = a o + b o_c,
+// and out = o / l.  Split-KV decode writes one partial per group (a quarter of the
+// per-chunk partials' bytes); the prefill walk applies the same two levels in registers.
 //
 // Cache layout, chosen so every matrix-operand load of a wave covers whole 128-byte
 // lines:
@@ -43,6 +47,7 @@ namespace bi {
 namespace {
 
 constexpr int CHUNK = 256;
+constexpr int GROUP = 4;                // chunks per merge group (1024 keys at absolute positions)
 constexpr int HD = 128;
 constexpr int SPLIT_MAX_TOKENS = 1024;  // calls with more tokens walk chunks in registers
 
@@ -360,29 +365,31 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
   }
 }
 
-// ---------------------------------------------------------------- step 2a: split-KV chunks
-// Work items: chunk c of token t for kv head h, ordered by (t, c, h); the item's 16 columns
-// are the token's G q heads (the rest unused).  A persistent grid: workgroup w reduces
-// items w, w + gridDim.x, ...  The token records (sequence, position, length) written by
-// kv_write_kernel and the running count of chunks per token sit in LDS.  Loads are
-// software-pipelined across items: the next item's q and K go out once this item's scores
-// are done, the page ids of the item three ahead and the next item's V once its values
-// are done, so a workgroup keeps loads in flight while it computes.  Which workgroup reduces
-// an item, and when, changes no bit of it.
-struct SplitItem {
-  int t, c, kvh, pos;
+// ---------------------------------------------------------------- step 2a: split-KV groups
+// Work units: group g (chunks 4g .. 4g + 3, those at or before the token's position) of
+// token t for kv head h, ordered by (t, g, h); the unit's 16 columns are the token's G q
+// heads (the rest unused).  A persistent grid: workgroup w reduces units w, w + gridDim.x,
+// ... chunk by chunk, merging each unit's chunks in registers and writing one partial per
+// unit.  The token records (sequence, position, length) written by kv_write_kernel and the
+// running count of units per token sit in LDS.  Loads are software-pipelined across
+// chunks: the next chunk's q and K go out once this chunk's scores are done, the page ids
+// of the chunk three ahead and the next chunk's V once its values are done, so a
+// workgroup keeps loads in flight while it computes.  Which workgroup reduces a unit, and
+// when, changes no bit of it.
+struct SplitStep {
+  int u, k, nk;      // unit index, chunk offset in the unit, chunks in the unit
+  int t, g, c, kvh, pos;
   Seq sq;
 };
 
-// Item `item` (a 32-bit index: the host bounds the count); `t0` is a token at or before the
-// item's token: the items of a workgroup advance, so a short forward scan finds it.
-__device__ __forceinline__ SplitItem split_item(int item, int t0, const int4* s_tok, const int* s_start,
+// First chunk of unit `u` (a 32-bit index: the host bounds the count); `t0` is a token at
+// or before the unit's token: a workgroup's units advance, so a short search finds it.
+__device__ __forceinline__ SplitStep split_unit(int u, int t0, const int4* s_tok, const int* s_start,
                                                 int num_tokens, const uint16_t* kc, const uint16_t* vc,
                                                 const int32_t* bt, int max_pages, int ps, int hkv) {
-  SplitItem it;
-  const unsigned j = static_cast<unsigned>(item) / static_cast<unsigned>(hkv);
-  it.kvh = item - static_cast<int>(j) * hkv;
-  if (t0 < 0 || t0 >= num_tokens || s_start[t0] > static_cast<int>(j)) t0 = 0;   // hint past the item
+  SplitStep it;
+  const unsigned j = static_cast<unsigned>(u) / static_cast<unsigned>(hkv);
+  if (t0 < 0 || t0 >= num_tokens || s_start[t0] > static_cast<int>(j)) t0 = 0;   // hint past the unit
   int t = t0;
   if (s_start[t0 + 1] <= static_cast<int>(j)) {   // past t0: binary search above it
     int lo = t0 + 1, hi = num_tokens - 1;
@@ -393,11 +400,16 @@ __device__ __forceinline__ SplitItem split_item(int item, int t0, const int4* s_
     }
     t = lo;
   }
-  // the item is the same for the whole workgroup: keep its fields in scalar registers
+  // the unit is the same for the whole workgroup: keep its fields in scalar registers
   const int4 r = s_tok[t];
+  it.u = u;
+  it.k = 0;
+  it.kvh = __builtin_amdgcn_readfirstlane(u - static_cast<int>(j) * hkv);
   it.t = __builtin_amdgcn_readfirstlane(t);
-  it.c = __builtin_amdgcn_readfirstlane(static_cast<int>(j) - s_start[t]);
+  it.g = __builtin_amdgcn_readfirstlane(static_cast<int>(j) - s_start[t]);
   it.pos = __builtin_amdgcn_readfirstlane(r.y);
+  it.c = GROUP * it.g;
+  it.nk = min(GROUP, it.pos / CHUNK - it.c + 1);
   const int b = __builtin_amdgcn_readfirstlane(r.x);
   const int len = __builtin_amdgcn_readfirstlane(r.z);
   it.sq = Seq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, it.kvh, len, max_pages,
@@ -418,7 +430,7 @@ __device__ __forceinline__ void load_q_col(const uint16_t* q, int64_t token, int
 __global__ __launch_bounds__(256) void attn_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt, const int4* __restrict__ tok,
-    int num_tokens, int max_pages, int hq, int hkv, int ps, int max_chunks, float sl2,
+    int num_tokens, int max_pages, int hq, int hkv, int ps, int max_groups, float sl2,
     float* __restrict__ ws_ml, float* __restrict__ ws_o) {
   __shared__ ChunkLDS sh;
   __shared__ int4 s_tok[SPLIT_MAX_TOKENS];
@@ -426,12 +438,12 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int t = threadIdx.x; t < num_tokens; t += 256) s_tok[t] = tok[t];
   __syncthreads();
-  if (w == 0) {   // s_start[t] = chunks of tokens 0 .. t-1 (token t has pos / 256 + 1)
+  if (w == 0) {   // s_start[t] = groups of tokens 0 .. t-1 (token t has pos / 1024 + 1)
     int carry = 0;
     for (int base = 0; base < num_tokens; base += 64) {
       const int t = base + lane;
       const int pos = t < num_tokens ? s_tok[t].y : -1;
-      int v = pos >= 0 ? pos / CHUNK + 1 : 0;
+      int v = pos >= 0 ? pos / (CHUNK * GROUP) + 1 : 0;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int u = __shfl_up(v, o, 64);
@@ -443,40 +455,43 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
     if (lane == 0) s_start[0] = 0;
   }
   __syncthreads();
-  const int n_items = s_start[num_tokens] * hkv;
-  int item = blockIdx.x;
-  if (item >= n_items) return;
+  const int n_units = s_start[num_tokens] * hkv;
+  if (static_cast<int>(blockIdx.x) >= n_units) return;
   const int stride = gridDim.x;
   const int G = hq / hkv;
   const int col = lane & 15;
   const bool used = col < G;
   const int hcol = used ? col : 0;
-  auto at = [&](int it, int t0) {
-    return split_item(it, t0, s_tok, s_start, num_tokens, kc, vc, bt, max_pages, ps, hkv);
+  // the chunk after `p` in this workgroup's sequence (p itself after the last one: those
+  // reloads are never used); the token hint only moves forward
+  auto advance = [&](const SplitStep& p) {
+    if (p.k + 1 < p.nk) {
+      SplitStep n = p;
+      n.k = p.k + 1;
+      n.c = p.c + 1;
+      return n;
+    }
+    if (p.u + stride < n_units)
+      return split_unit(p.u + stride, p.t, s_tok, s_start, num_tokens, kc, vc, bt, max_pages, ps, hkv);
+    return p;
   };
 
-  // the k-th item ahead of `item`, or the last one this workgroup has (reloads past the end
-  // are never used); non-decreasing in k, as the token hints of split_item require
-  auto ahead = [&](int k) {
-    int v = item + k * stride;
-    while (v >= n_items) v -= stride;
-    return v;
-  };
-
-  SplitItem cur = at(item, 0);
+  SplitStep cur = split_unit(blockIdx.x, 0, s_tok, s_start, num_tokens, kc, vc, bt, max_pages, ps, hkv);
   int pg = chunk_pages(cur.sq, cur.c);
   u16x8 qop[4], kop[2][2][4], vop[2][8];
   load_q_col(q, cur.t, cur.kvh * G + hcol, hq, qop);
   chunk_load_k(cur.sq, pg, kop);
-  SplitItem nxt = at(ahead(1), cur.t);
+  SplitStep nxt = advance(cur);
   int pgn = chunk_pages(nxt.sq, nxt.c);
-  SplitItem nxt2 = at(ahead(2), nxt.t);
+  SplitStep nxt2 = advance(nxt);
   int pgn2 = chunk_pages(nxt2.sq, nxt2.c);
   chunk_load_v(cur.sq, pg, vop);
   issue_fence();
+  float mu = 0.f, lu = 0.f;   // the unit's running merge (column lane % 16)
+  floatx4 ou[2];
   for (;;) {
-    const bool has_next = item + stride < n_items;
-    const SplitItem nxt3 = at(ahead(3), nxt2.t);
+    const bool last = cur.k + 1 == cur.nk && cur.u + stride >= n_units;
+    const SplitStep nxt3 = advance(nxt2);
     floatx4 s[2][2];
     float m, lsum;
     chunk_scores(cur.c, kop, qop, used ? cur.pos : -1, sl2, sh, s, m, lsum);
@@ -486,21 +501,33 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
     float m_c, l_c;
     floatx4 oc[2];
     chunk_values(cur.sq, cur.c, vop, s, m, lsum, sh, m_c, l_c, oc);
-    const int pgn3 = chunk_pages(nxt3.sq, nxt3.c);   // page ids three items ahead
+    const int pgn3 = chunk_pages(nxt3.sq, nxt3.c);   // page ids three chunks ahead
     chunk_load_v(nxt.sq, pgn, vop);
     issue_fence();
-    if (used) {
-      const int64_t slot = (static_cast<int64_t>(cur.t) * hq + cur.kvh * G + col) * max_chunks + cur.c;
+    if (cur.k == 0) {
+      mu = m_c;
+      lu = l_c;
+      ou[0] = oc[0];
+      ou[1] = oc[1];
+    } else {
+      float a, bb;
+      merge_step(mu, lu, m_c, l_c, a, bb);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ou[j][r] = mix(ou[j][r], oc[j][r], a, bb);
+    }
+    if (cur.k + 1 == cur.nk && used) {
+      const int64_t slot = (static_cast<int64_t>(cur.t) * hq + cur.kvh * G + col) * max_groups + cur.g;
       float* po = ws_o + slot * HD + 4 * (lane >> 4);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) *reinterpret_cast<floatx4*>(po + 16 * (2 * w + j)) = oc[j];
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<floatx4*>(po + 16 * (2 * w + j)) = ou[j];
       if (w == 0 && (lane >> 4) == 0) {
-        ws_ml[2 * slot] = m_c;
-        ws_ml[2 * slot + 1] = l_c;
+        ws_ml[2 * slot] = mu;
+        ws_ml[2 * slot + 1] = lu;
       }
     }
-    if (!has_next) break;
-    item += stride;
+    if (last) break;
     cur = nxt;
     nxt = nxt2;
     pgn = pgn2;
@@ -662,25 +689,40 @@ __global__ __launch_bounds__(256) void attn_walk_kernel(
     int pmax = pcol;
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) pmax = max(pmax, __shfl_xor(pmax, off, 64));
-    float m = 0.f, l = 0.f;
-    floatx4 o[2];
+    // two merge levels, as the split path: chunks within each group of GROUP, then groups
+    float m = 0.f, l = 0.f, mg = 0.f, lg = 0.f;
+    floatx4 o[2], og[2];
     for (int c = 0; c * CHUNK <= pmax; ++c) {
       float m_c, l_c;
       floatx4 oc[2];
       chunk_partial(sq, c, qop, pcol, sl2, sh, m_c, l_c, oc);
       if (c * CHUNK > pcol) continue;
-      if (c == 0) {
-        m = m_c;
-        l = l_c;
-        o[0] = oc[0];
-        o[1] = oc[1];
+      if (c % GROUP == 0) {
+        mg = m_c;
+        lg = l_c;
+        og[0] = oc[0];
+        og[1] = oc[1];
       } else {
         float a, bb;
-        merge_step(m, l, m_c, l_c, a, bb);
+        merge_step(mg, lg, m_c, l_c, a, bb);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[j][r] = mix(o[j][r], oc[j][r], a, bb);
+          for (int r = 0; r < 4; ++r) og[j][r] = mix(og[j][r], oc[j][r], a, bb);
+      }
+      if (c % GROUP != GROUP - 1 && c != pcol / CHUNK) continue;   // group not complete yet
+      if (c < GROUP) {
+        m = mg;
+        l = lg;
+        o[0] = og[0];
+        o[1] = og[1];
+      } else {
+        float a, bb;
+        merge_step(m, l, mg, lg, a, bb);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[j][r] = mix(o[j][r], og[j][r], a, bb);
       }
     }
     if (!mine) continue;
@@ -773,18 +815,20 @@ extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new,
       query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size, ws_tok);
   const int of = out_dtype == BI_F32;
   if (split) {
-    // as many workgroups as can be resident at once, never more than there are items
-    const int64_t items = num_tokens * maxc * num_kv_heads;   // an upper bound of the work items
-    const int64_t grid = std::min<int64_t>(items, static_cast<int64_t>(split_resident()) * cu_count());
+    // as many workgroups as can be resident at once, never more than there are units
+    const int64_t maxg = (maxc + GROUP - 1) / GROUP;
+    float* gs_o = ws_ml + ml_floats(num_tokens * num_q_heads * maxg);   // per-group partials
+    const int64_t units = num_tokens * maxg * num_kv_heads;   // an upper bound of the work units
+    const int64_t grid = std::min<int64_t>(units, static_cast<int64_t>(split_resident()) * cu_count());
     attn_split_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, s>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
         static_cast<const uint16_t*>(v_cache), block_table, ws_tok, static_cast<int>(num_tokens),
-        max_pages_per_seq, num_q_heads, num_kv_heads, page_size, static_cast<int>(maxc), sl2,
-        ws_ml, ws_o);
+        max_pages_per_seq, num_q_heads, num_kv_heads, page_size, static_cast<int>(maxg), sl2,
+        ws_ml, gs_o);
     const int64_t rows = num_tokens * num_q_heads;
     attn_combine_kernel<<<dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s>>>(
-        ws_ml, ws_o, seq_lens, query_start_loc, batch, num_q_heads, static_cast<int>(maxc), rows,
-        out, of, 1);
+        ws_ml, gs_o, seq_lens, query_start_loc, batch, num_q_heads, static_cast<int>(maxg), rows,
+        out, of, GROUP);
   } else {
     const int NT = 16 / G;
     const int64_t blocks = (num_tokens + NT - 1) / NT;
