@@ -399,6 +399,19 @@ __device__ __forceinline__ void zero_k_tail(const DmaCtx<T>& d, uint16_t* sA, ui
   }
 }
 
+// Scheduling hint for one K step: alternate the step's MFMAs with the next step's LDS
+// operand reads (one read after each MFMA), so the LDS works while the matrix core does.
+template <class T>
+__device__ __forceinline__ void interleave() {
+  constexpr int NR = T::BLK_M + T::BLK_N, NM = T::BLK_M * T::BLK_N;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+}
+
 // K steps 1 .. KS - 1 of a stage, each read before the previous step's MFMAs are issued
 // (o0 holds step 0 on entry; on return the operands of step KS - 1 are in o1 and every
 // earlier step has been multiplied).  KS is even, so step s lives in o0 for even s.
@@ -415,6 +428,7 @@ __device__ __forceinline__ void inner_steps(const uint16_t* sA, const uint16_t* 
       load_ops<T>(sA, sB, buf, ks, f, o0);
       mfma_ops<T>(o1, acc);
     }
+    interleave<T>();
   }
 }
 
@@ -433,6 +447,7 @@ __device__ __forceinline__ void steady_step(const DmaCtx<T>& d, const uint16_t* 
   dma_stage_at<T>(d, BUF, kt + T::STAGES);
   load_ops<T>(sA, sB, (BUF + 1) % T::STAGES, 0, f, o0);
   mfma_ops<T>(o1, acc);
+  interleave<T>();
 }
 
 template <class T, int BUF>
@@ -548,6 +563,7 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
     dma_stage_at<T>(d, buf, kt + T::STAGES);
     load_ops<T>(sA, sB, (kt + 1) % T::STAGES, 0, f, o0);
     mfma_ops<T>(o1, acc);
+    interleave<T>();
   }
   // drain: nothing left to issue; stages kt + 1 .. nk - 1 may still be in flight
   for (; kt < nk - 1; ++kt) {
@@ -559,6 +575,7 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
     }
     load_ops<T>(sA, sB, (kt + 1) % T::STAGES, 0, f, o0);
     mfma_ops<T>(o1, acc);
+    interleave<T>();
   }
   inner_steps<T>(sA, sB, (nk - 1) % T::STAGES, f, o0, o1, acc);
   mfma_ops<T>(o1, acc);
