@@ -283,6 +283,24 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
       : "memory");
 }
 
+// Loads J .. N - 1 of one operand: load j lands 1024 j bytes past lds_base (added to m0
+// inside the asm, so one scalar register holds the base of the whole run).
+template <int J, int N>
+__device__ __forceinline__ void dma16_run(const void* base, const uint32_t* off, uint32_t lds_base) {
+  if constexpr (J < N) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_add_u32 m0, %1, %4\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_base), "v"(off[J]), "s"(base), "n"(J * 1024)
+        : "memory", "scc");
+    dma16_run<J + 1, N>(base, off, lds_base);
+  }
+}
+
 // Wait until at most N of this wave's vector-memory operations are outstanding and all
 // its LDS operations are done, then meet the other waves.
 template <int N>
@@ -336,12 +354,8 @@ __device__ __forceinline__ void dma_stage_at(const DmaCtx<T>& d, uint32_t buf, i
       dma16(d.B, d.boff[j] + adv, lb + j * 1024);
     }
   } else {
-    const uint16_t* ab = d.A + k0;
-    const uint16_t* bb = d.B + k0;
-#pragma unroll
-    for (int j = 0; j < T::NJA; ++j) dma16(ab, d.aoff[j], la + j * 1024);
-#pragma unroll
-    for (int j = 0; j < T::NJB; ++j) dma16(bb, d.boff[j], lb + j * 1024);
+    dma16_run<0, T::NJA>(d.A + k0, d.aoff, la);
+    dma16_run<0, T::NJB>(d.B + k0, d.boff, lb);
   }
 }
 
@@ -362,10 +376,13 @@ __device__ __forceinline__ void load_ops(const uint16_t* sA, const uint16_t* sB,
                                          const Frag<T>& f, Ops<T>& o) {
   const char* a = reinterpret_cast<const char*>(sA) + buf * (T::SA * 2);
   const char* b = reinterpret_cast<const char*>(sB) + buf * (T::SB * 2);
-#pragma unroll
-  for (int i = 0; i < T::BLK_M; ++i) o.a[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(a + f.ao[i][ks]));
+  // in the order the MFMAs consume them: A0, every B, then A1 .. (the first MFMAs can
+  // start after 1 + BLK_N reads)
+  o.a[0] = as_bf16x8(*reinterpret_cast<const u16x8*>(a + f.ao[0][ks]));
 #pragma unroll
   for (int j = 0; j < T::BLK_N; ++j) o.b[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(b + f.bo[j][ks]));
+#pragma unroll
+  for (int i = 1; i < T::BLK_M; ++i) o.a[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(a + f.ao[i][ks]));
 }
 
 template <class T>
