@@ -22,10 +22,14 @@ struct Vec;
 template <>
 struct Vec<false> {  // 8 bf16
   static constexpr int W = 8;
+  // NT: the row is read once (it fits in the registers), so the load does not allocate in
+  // the caches
+  template <bool NT = false>
   __device__ static void load(const void* row, int v, int D, bool vec_ok, float (&e)[8]) {
     const uint16_t* p = static_cast<const uint16_t*>(row) + static_cast<int64_t>(v) * 8;
     if (vec_ok && v * 8 + 8 <= D) {
-      u16x8 q = *reinterpret_cast<const u16x8*>(p);
+      u16x8 q = NT ? __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p))
+                   : *reinterpret_cast<const u16x8*>(p);
 #pragma unroll
       for (int i = 0; i < 8; ++i) e[i] = bf16_to_f32(q[i]);
     } else {
@@ -37,6 +41,7 @@ struct Vec<false> {  // 8 bf16
 template <>
 struct Vec<true> {  // 4 fp32
   static constexpr int W = 4;
+  template <bool NT = false>
   __device__ static void load(const void* row, int v, int D, bool vec_ok, float (&e)[4]) {
     const float* p = static_cast<const float*>(row) + static_cast<int64_t>(v) * 4;
     if (vec_ok && v * 4 + 4 <= D) {
@@ -70,7 +75,8 @@ __device__ __forceinline__ void store_out(void* yrow, int v, int D, bool vec_ok,
       u16x8 q;
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[i] = f32_to_bf16(o[i]);
-      *reinterpret_cast<u16x8*>(p) = q;
+      if (FULL) __builtin_nontemporal_store(q, reinterpret_cast<u16x8*>(p));   // written once
+      else *reinterpret_cast<u16x8*>(p) = q;
     } else {
 #pragma unroll
       for (int i = 0; i < W; ++i)
@@ -80,8 +86,9 @@ __device__ __forceinline__ void store_out(void* yrow, int v, int D, bool vec_ok,
 }
 
 // NV vectors per lane stay in registers between the two passes; longer rows re-read.
-// FULL: D is a multiple of the vector width and every row is 16-byte aligned, so no
-// element needs a bounds check.
+// FULL (bf16 in and out): D is a multiple of the vector width, at most NV vectors per
+// lane (D <= 8192) and every row is 16-byte aligned, so no element needs a bounds check
+// and x and y are each touched once: their loads and stores bypass the caches.
 template <bool XF32, bool YF32, bool FULL>
 __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restrict__ x,
                                                            const uint16_t* __restrict__ gamma,
@@ -105,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restric
     for (int j = 0; j < NV; ++j) {
       const int v = tid + j * T;
       if (v < nvec) {
-        V::load(xrow, v, D, FULL || vec_x, cache[j]);
+        V::template load<FULL>(xrow, v, D, FULL || vec_x, cache[j]);
 #pragma unroll
         for (int i = 0; i < W; ++i)
           if (FULL || v * W + i < D) acc = acc + cache[j][i] * cache[j][i];
@@ -181,7 +188,9 @@ extern "C" int bi_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, 
   const int vec_g = aligned16(gamma);
   dim3 grid(static_cast<unsigned>(M)), block(kThreads);
   hipStream_t s = as_stream(stream);
-  const bool full_bf16 = !xf && !yf && vec_x && vec_y && vec_g && (D % 8) == 0;
+  // bf16 rows that fit in the registers of one workgroup (D <= 8192), aligned: one read and
+  // one write per element, streamed past the caches
+  const bool full_bf16 = !xf && !yf && vec_x && vec_y && vec_g && (D % 8) == 0 && D <= 4 * kThreads * 8;
   if (full_bf16)
     rmsnorm_kernel<false, false, true><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, vec_y, vec_g);
   else if (!xf && !yf)
