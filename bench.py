@@ -164,6 +164,26 @@ def measured_traffic(root):
     return int(rec["traffic_bytes"])
 
 
+def gemm_profile(torch, bi, shape):
+    """One Mistral-shaped bi_gemm (A [M, K], W [N, K] bf16 ~N(0,1)), timed with HIP events."""
+    M, N, K = shape
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    A = torch.randn((M, K), generator=g, device="cuda:0").to(torch.bfloat16)
+    W = torch.randn((N, K), generator=g, device="cuda:0").to(torch.bfloat16)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    for _ in range(5):
+        bi.bi_gemm(A, W, out=C)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        bi.bi_gemm(A, W, out=C)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 20 * 1e-3
+    print(json.dumps({"gemm": [M, N, K], "tile": list(bi.bi_gemm_tile(M, N, K)),
+                      "ms": round(t * 1e3, 4), "TFLOPs": round(2 * M * N * K / t / 1e12, 1)}), flush=True)
+
+
 def gemm_sweep(torch, bi):
     """Mistral-shaped GEMMs (N, K) x M, TFLOP/s of bi_gemm and of the split-K variant."""
     dev = "cuda:0"
@@ -201,6 +221,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gemm-sweep", action="store_true")
+    ap.add_argument("--gemm-profile", metavar="M,N,K",
+                    help="run bi_gemm on one shape (5 warm-up + 20 timed calls) and print its "
+                         "TFLOP/s, for rocprofv3 counter runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (to scale rocprof byte counters)")
     args = ap.parse_args()
@@ -217,6 +240,9 @@ def main():
 
     if args.gemm_sweep:
         gemm_sweep(torch, bi)
+        return
+    if args.gemm_profile:
+        gemm_profile(torch, bi, [int(v) for v in args.gemm_profile.split(",")])
         return
 
     if args.copy_calibration:
