@@ -233,28 +233,32 @@ static_assert(DBK == 32 || DBK == 64, "the main loop takes an even number of 16-
 // the same instruction sequence (one fp32 chain from +0 over ascending 16-wide K steps,
 // lane l holding k = 8 (l / 32) .. + 7 of each step), so they give identical bits; the tile
 // only decides which workgroup computes which outputs.
-template <int WAVES_M_, int WAVES_N_, int BLK_M_, int BLK_N_, int STAGES_, int WAVES_PER_SIMD_ = 2>
+template <int WAVES_M_, int WAVES_N_, int BLK_M_, int BLK_N_, int STAGES_, int WAVES_PER_SIMD_ = 2,
+          int DMA_WAVES_ = WAVES_M_ * WAVES_N_>
 struct Tile {
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BLK_M = BLK_M_, BLK_N = BLK_N_;
   static constexpr int STAGES = STAGES_;   // LDS ring depth
   static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;   // register budget: 512 / this
   static constexpr int NW = WAVES_M * WAVES_N;
+  // waves 0 .. DW - 1 issue the operand loads of a stage; the others only read LDS and
+  // multiply, so a wave held up issuing loads leaves its SIMD to one that is not
+  static constexpr int DW = DMA_WAVES_;
   static constexpr int THREADS = NW * 64;
   static constexpr int TM = WAVES_M * BLK_M * 32;
   static constexpr int TN = WAVES_N * BLK_N * 32;
-  static constexpr int NJA = TM / NW / RPI;  // A loads per wave per stage
-  static constexpr int NJB = TN / NW / RPI;  // B loads per wave per stage
+  static constexpr int NJA = TM / DW / RPI;  // A loads per issuing wave per stage
+  static constexpr int NJB = TN / DW / RPI;  // B loads per issuing wave per stage
   static constexpr int PER = NJA + NJB;
   static constexpr int SA = TM * DBK, SB = TN * DBK;  // bf16 elements per stage
-  static_assert(TM % (NW * RPI) == 0 && TN % (NW * RPI) == 0, "tile rows per wave");
+  static_assert(TM % (DW * RPI) == 0 && TN % (DW * RPI) == 0 && DW <= NW, "tile rows per wave");
   static_assert(STAGES >= 2, "unsupported staging");
 };
 // 128 x 128, 4 waves of 64 x 64: a 2-stage ring (64 KB, two workgroups per CU), or a
 // 3-stage ring (96 KB, one per CU) for grids with no more tiles than CUs; 256 x 256, 8 waves
-// of 128 x 64, 2-stage ring (128 KB, one per CU).
+// of 128 x 64, 2-stage ring (128 KB, one per CU), loads issued by one wave per SIMD.
 using Tile128 = Tile<2, 2, 2, 2, 2>;
 using Tile128Deep = Tile<2, 2, 2, 2, 3>;
-using Tile256 = Tile<2, 4, 4, 2, 2>;
+using Tile256 = Tile<2, 4, 4, 2, 2, 2, 4>;
 
 // Chunk c of LDS row r sits at position c ^ swz(r): the 16-byte reads of 8 (or 16)
 // consecutive rows at one chunk index then fall into distinct banks.
@@ -329,6 +333,7 @@ struct DmaCtx {
   uint32_t lds_a, lds_b;                 // LDS byte address of this wave's rows in stage 0
   int K, nk;
   bool ktail;
+  bool issuer;                           // this wave issues loads (wave < T::DW)
 };
 
 // Stage kt into ring buffer `buf` (a template constant in the steady loop, a run-time
@@ -395,21 +400,21 @@ __device__ __forceinline__ void mfma_ops(const Ops<T>& o, floatx16 (&acc)[T::BLK
 }
 
 // Zero every element at k >= K of stage kt (in ring buffer buf) in the pieces this lane's
-// own loads wrote; the caller then waits and meets the other waves.
+// own loads wrote (issuing waves only); the caller then waits and meets the other waves.
 template <class T>
 __device__ __forceinline__ void zero_k_tail(const DmaCtx<T>& d, uint16_t* sA, uint16_t* sB, int buf,
                                             int kt, int wave, int lane) {
   const int k0 = kt * DBK;
 #pragma unroll
   for (int j = 0; j < T::NJA; ++j) {
-    const int pos = buf * T::SA + ((T::TM / T::NW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
+    const int pos = buf * T::SA + ((T::TM / T::DW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (k0 + d.kca[j] + e >= d.K) sA[pos + e] = 0;
   }
 #pragma unroll
   for (int j = 0; j < T::NJB; ++j) {
-    const int pos = buf * T::SB + ((T::TN / T::NW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
+    const int pos = buf * T::SB + ((T::TN / T::DW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (k0 + d.kcb[j] + e >= d.K) sB[pos + e] = 0;
@@ -461,7 +466,7 @@ __device__ __forceinline__ void steady_step(const DmaCtx<T>& d, const uint16_t* 
                                             floatx16 (&acc)[T::BLK_M][T::BLK_N]) {
   inner_steps<T>(sA, sB, BUF, f, o0, o1, acc);
   wait_and_barrier<(T::STAGES - 2) * T::PER>();
-  dma_stage_at<T>(d, BUF, kt + T::STAGES);
+  if (d.issuer) dma_stage_at<T>(d, BUF, kt + T::STAGES);
   load_ops<T>(sA, sB, (BUF + 1) % T::STAGES, 0, f, o0);
   mfma_ops<T>(o1, acc);
   interleave<T>();
@@ -503,20 +508,22 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
 
-  // DMA assignment: load j of wave w fills the wave's tile rows RPI j .. RPI j + RPI - 1
-  // (A rows w TM/NW .., B rows w TN/NW ..); lane l writes chunk position l % CPR of its
-  // row with k-chunk (l % CPR) ^ swz(row).
+  // DMA assignment: load j of issuing wave w fills tile rows RPI j .. RPI j + RPI - 1 of
+  // its share (A rows w TM/DW .., B rows w TN/DW ..); lane l writes chunk position l % CPR
+  // of its row with k-chunk (l % CPR) ^ swz(row).
   DmaCtx<T> d;
   d.A = A;
   d.B = B;
   d.K = K;
   d.nk = (K + DBK - 1) / DBK;
   d.ktail = (K % DBK) != 0;
-  d.lds_a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sA)) + (T::TM / T::NW) * wave * DBK * 2;
-  d.lds_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sB)) + (T::TN / T::NW) * wave * DBK * 2;
+  d.issuer = wave < T::DW;
+  const int dw = wave % T::DW;   // (only issuing waves use what follows)
+  d.lds_a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sA)) + (T::TM / T::DW) * dw * DBK * 2;
+  d.lds_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sB)) + (T::TN / T::DW) * dw * DBK * 2;
 #pragma unroll
   for (int j = 0; j < T::NJA; ++j) {
-    const int R = (T::TM / T::NW) * wave + RPI * j + lane / CPR;
+    const int R = (T::TM / T::DW) * dw + RPI * j + lane / CPR;
     const int c = (lane % CPR) ^ swz(R);
     const int ra = min(tm * T::TM + R, M - 1);
     d.aoff[j] = static_cast<uint32_t>((static_cast<int64_t>(ra) * lda + c * 8) * 2);
@@ -524,7 +531,7 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
   }
 #pragma unroll
   for (int j = 0; j < T::NJB; ++j) {
-    const int R = (T::TN / T::NW) * wave + RPI * j + lane / CPR;
+    const int R = (T::TN / T::DW) * dw + RPI * j + lane / CPR;
     const int c = (lane % CPR) ^ swz(R);
     const int rb = min(tn * T::TN + R, N - 1);
     d.boff[j] = static_cast<uint32_t>((static_cast<int64_t>(rb) * ldb + c * 8) * 2);
@@ -560,11 +567,11 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
   const int nk = d.nk;
 #pragma unroll
   for (int st = 0; st < T::STAGES; ++st)
-    if (st < nk) dma_stage_at<T>(d, st, st);
+    if (st < nk && d.issuer) dma_stage_at<T>(d, st, st);
   Ops<T> o0, o1;
   wait_stage<T::PER, T::STAGES - 1>(min(T::STAGES - 1, nk - 1));
   if (d.ktail && nk == 1) {
-    zero_k_tail<T>(d, sA, sB, 0, 0, wave, lane);
+    if (d.issuer) zero_k_tail<T>(d, sA, sB, 0, 0, wave, lane);
     wait_and_barrier<0>();
   }
   load_ops<T>(sA, sB, 0, 0, f, o0);
@@ -577,7 +584,7 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
     const int buf = kt % T::STAGES;
     inner_steps<T>(sA, sB, buf, f, o0, o1, acc);
     wait_and_barrier<(T::STAGES - 2) * T::PER>();
-    dma_stage_at<T>(d, buf, kt + T::STAGES);
+    if (d.issuer) dma_stage_at<T>(d, buf, kt + T::STAGES);
     load_ops<T>(sA, sB, (kt + 1) % T::STAGES, 0, f, o0);
     mfma_ops<T>(o1, acc);
     interleave<T>();
@@ -587,7 +594,7 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
     inner_steps<T>(sA, sB, kt % T::STAGES, f, o0, o1, acc);
     wait_stage<T::PER, T::STAGES - 2>(min(T::STAGES - 2, nk - 2 - kt));
     if (d.ktail && kt + 1 == nk - 1) {
-      zero_k_tail<T>(d, sA, sB, (kt + 1) % T::STAGES, kt + 1, wave, lane);
+      if (d.issuer) zero_k_tail<T>(d, sA, sB, (kt + 1) % T::STAGES, kt + 1, wave, lane);
       wait_and_barrier<0>();
     }
     load_ops<T>(sA, sB, (kt + 1) % T::STAGES, 0, f, o0);
@@ -622,17 +629,17 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
 // time.  The 256 x 256 tile streams half the operand bytes per flop but runs one workgroup
 // per CU; the 128 x 128 tile runs two per CU, or one with a deeper ring when the grid has
 // no more tiles than CUs.  The cost counts rounds of the CU array, with round times
-// measured on MI355X at K = 4096 (all scale with K): 256 x 256: 121; 128 x 128 two per CU:
-// 69, one per CU: 48 (44 with the deeper ring).
+// measured on MI355X at K = 4096 (all scale with K): 256 x 256: 109; 128 x 128 two per CU:
+// 66, one per CU: 46.
 enum class TileKind { k128, k128deep, k256 };
 
 TileKind pick_tile(int64_t M, int64_t N, int cus) {
   const int64_t n256 = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t n128 = ((M + 127) / 128) * ((N + 127) / 128);
   if (n128 <= cus) return TileKind::k128deep;
-  const int64_t cost256 = 121 * ((n256 + cus - 1) / cus);
+  const int64_t cost256 = 109 * ((n256 + cus - 1) / cus);
   const int64_t rem = n128 % (2 * cus);
-  const int64_t cost128 = 69 * (n128 / (2 * cus)) + (rem == 0 ? 0 : rem <= cus ? 48 : 69);
+  const int64_t cost128 = 66 * (n128 / (2 * cus)) + (rem == 0 ? 0 : rem <= cus ? 46 : 66);
   return cost256 < cost128 ? TileKind::k256 : TileKind::k128;
 }
 
