@@ -208,12 +208,16 @@ def bi_attention_batchdep_split(q, k_new, v_new, k_cache, v_cache, block_table, 
 
 def bi_logsoftmax_argmax(logits, logprobs=None, argmax=None, want_logprobs: bool = True):
     M, V = logits.shape
+    ld = _ld(logits)
     if argmax is None:
         argmax = torch.empty((M,), dtype=torch.int32, device=logits.device)
     if logprobs is None and want_logprobs:
-        logprobs = torch.empty_like(logits)
+        # the call writes logprobs with the row stride of logits
+        logprobs = torch.empty_strided((M, V), (ld, 1), dtype=logits.dtype, device=logits.device)
+    elif logprobs is not None and (tuple(logprobs.shape) != (M, V) or _ld(logprobs) != ld):
+        raise ValueError("logprobs must have the shape and row stride of logits")
     _check("bi_logsoftmax_argmax", load().bi_logsoftmax_argmax(
-        _ptr(logits), M, V, _ld(logits), _ptr(logprobs), _ptr(argmax), _stream(logits)))
+        _ptr(logits), M, V, ld, _ptr(logprobs), _ptr(argmax), _stream(logits)))
     return logprobs, argmax
 
 

@@ -221,6 +221,109 @@ __global__ __launch_bounds__(kThreads) void logsoftmax_argmax_kernel(
   }
 }
 
+// Wide form for rows of 1024 .. 32768 elements (V % 4 == 0, 16-byte aligned rows): the same
+// tree with its elementwise work spread over four times the threads.  Thread (g, t),
+// g = tid / 256, holds vectors j = 8 g .. 8 g + 7 of tree lane t (vector t + 256 j), takes
+// their maximum and their EXP values, and parks the EXP values in LDS; tree lane t (g = 0)
+// then adds its own 4 x 32 values in the same ascending order as above.  The maximum is a
+// selection under a total order, so splitting it changes nothing either: the bits equal
+// the one-row-per-256-threads form.
+constexpr int kWideGroups = 4;
+constexpr int kWideThreads = kWideGroups * kThreads;
+constexpr int kWideJ = NVC / kWideGroups;   // vectors per thread
+
+__global__ __launch_bounds__(kWideThreads) void logsoftmax_argmax_wide_kernel(
+    const float* __restrict__ logits, int V, int64_t ld, float* __restrict__ logprobs,
+    int32_t* __restrict__ argmax) {
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int t = tid % kThreads, g = tid / kThreads;
+  const int nvec = V / 4;                     // kThreads <= nvec <= NVC * kThreads
+  const float* x = logits + row * ld;
+  __shared__ floatx4 se[NVC * kThreads];     // EXP values, vector j of lane t at j * 256 + t
+  __shared__ float sv[kWideThreads / kWave];
+  __shared__ int si[kWideThreads / kWave];
+  __shared__ float ss[kThreads / kWave];
+
+  float c[kWideJ][4];
+#pragma unroll
+  for (int jj = 0; jj < kWideJ; ++jj) {
+    const int v = t + (g * kWideJ + jj) * kThreads;
+    if (v < nvec) {
+      const floatx4 q = *reinterpret_cast<const floatx4*>(x + static_cast<int64_t>(v) * 4);
+      c[jj][0] = q[0]; c[jj][1] = q[1]; c[jj][2] = q[2]; c[jj][3] = q[3];
+    }
+  }
+  float bv = -__builtin_huge_valf();
+  int bidx = 0x7fffffff;
+#pragma unroll
+  for (int jj = 0; jj < kWideJ; ++jj) {
+    const int v = t + (g * kWideJ + jj) * kThreads;
+    if (v < nvec) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pick(bv, bidx, c[jj][i], v * 4 + i);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float ov = __shfl_xor(bv, off, kWave);
+    const int oi = __shfl_xor(bidx, off, kWave);
+    pick(bv, bidx, ov, oi);
+  }
+  if ((tid & (kWave - 1)) == 0) {
+    sv[tid / kWave] = bv;
+    si[tid / kWave] = bidx;
+  }
+  __syncthreads();
+  float mv = sv[0];
+  int mi = si[0];
+#pragma unroll
+  for (int w = 1; w < kWideThreads / kWave; ++w) pick(mv, mi, sv[w], si[w]);
+  const float m = mv;
+
+#pragma unroll
+  for (int jj = 0; jj < kWideJ; ++jj) {
+    const int j = g * kWideJ + jj;
+    if (t + j * kThreads < nvec) {
+      floatx4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = exp_cw(c[jj][i] - m);
+      se[j * kThreads + t] = e;
+    }
+  }
+  __syncthreads();
+  if (g == 0) {
+    float acc = 0.f;
+    for (int j = 0; j < NVC; ++j) {
+      if (t + j * kThreads >= nvec) break;
+      const floatx4 e = se[j * kThreads + t];
+      acc = acc + e[0];
+      acc = acc + e[1];
+      acc = acc + e[2];
+      acc = acc + e[3];
+    }
+    const float wsum = wave_tree_sum(acc);
+    if ((tid & (kWave - 1)) == 0) ss[tid / kWave] = wsum;
+  }
+  __syncthreads();
+  const float s = (ss[0] + ss[1]) + (ss[2] + ss[3]);
+  const float L = log_at(s);
+
+  if (tid == 0) argmax[row] = mi;
+  if (logprobs == nullptr) return;
+  float* out = logprobs + row * ld;
+#pragma unroll
+  for (int jj = 0; jj < kWideJ; ++jj) {
+    const int v = t + (g * kWideJ + jj) * kThreads;
+    if (v < nvec) {
+      floatx4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = (c[jj][i] - m) - L;
+      *reinterpret_cast<floatx4*>(out + static_cast<int64_t>(v) * 4) = o;
+    }
+  }
+}
+
 }  // namespace
 }  // namespace bi
 
@@ -236,7 +339,11 @@ extern "C" int bi_logsoftmax_argmax(const float* logits, int64_t M, int64_t V, i
   const int vec_in = aligned16(logits) && (ld % 4) == 0;
   const int vec_out = logprobs && aligned16(logprobs) && (ld % 4) == 0;
   const bool full = vec_in && (V % 4) == 0 && (!logprobs || vec_out);
-  if (full)
+  if (full && V >= 4 * kThreads && V <= 4 * NVC * kThreads)
+    logsoftmax_argmax_wide_kernel<<<dim3(static_cast<unsigned>(M)), dim3(kWideThreads), 0,
+                                    as_stream(stream)>>>(logits, static_cast<int>(V), ld,
+                                                         logprobs, argmax);
+  else if (full)
     logsoftmax_argmax_kernel<true><<<dim3(static_cast<unsigned>(M)), dim3(kThreads), 0,
                                      as_stream(stream)>>>(logits, static_cast<int>(V), ld,
                                                           logprobs, argmax, vec_in, vec_out);

@@ -24,7 +24,8 @@ def _cmp(lib, x):
     assert np.array_equal(got[~nan].view(np.uint32), rlp[~nan].view(np.uint32))
 
 
-@pytest.mark.parametrize("m,v", [(1, 32000), (49, 32000), (3, 1000), (2, 37), (5, 4099), (1, 1), (2, 262144)])
+@pytest.mark.parametrize("m,v", [(1, 32000), (49, 32000), (3, 1000), (2, 37), (5, 4099), (1, 1), (2, 262144),
+                                 (4, 32768), (3, 1024), (2, 1020), (2, 8196), (2, 32772)])
 def test_bit_exact(lib, m, v):
     say("logsoftmax", m, v)
     rng = np.random.default_rng(m * 7 + v)
@@ -57,3 +58,15 @@ def test_batch_invariance_and_repeats(lib):
         assert same_bits(l2, lp) and torch.equal(a2, am)
     _, only = lib.bi_logsoftmax_argmax(X, want_logprobs=False)
     assert torch.equal(only, am)
+
+
+def test_row_stride(lib):
+    # rows ld = V + 4 apart (a view of a wider buffer): logprobs come back with the same stride
+    for v in (32000, 4099):
+        x = (np.random.default_rng(v).standard_normal((5, v + 4)) * 1.7).astype(np.float32)
+        X = f32(x)[:, :v]
+        lp, am = lib.bi_logsoftmax_argmax(X)
+        assert lp.stride(0) == v + 4
+        rlp, ram = logsoftmax_argmax(np.ascontiguousarray(x[:, :v]))
+        assert np.array_equal(host(am), ram)
+        assert np.array_equal(host(lp).view(np.uint32), rlp.view(np.uint32))
