@@ -253,11 +253,12 @@ struct Tile {
   static_assert(TM % (DW * RPI) == 0 && TN % (DW * RPI) == 0 && DW <= NW, "tile rows per wave");
   static_assert(STAGES >= 2, "unsupported staging");
 };
-// 128 x 128, 4 waves of 64 x 64: a 2-stage ring (64 KB, two workgroups per CU), or a
-// 3-stage ring (96 KB, one per CU) for grids with no more tiles than CUs; 256 x 256, 8 waves
-// of 128 x 64, 2-stage ring (128 KB, one per CU), loads issued by one wave per SIMD.
+// 128 x 128, 4 waves of 64 x 64 with a 2-stage ring (64 KB, two workgroups per CU); for
+// grids with no more tiles than CUs, 128 x 128 as 8 waves of 64 x 32 with a 3-stage ring
+// (96 KB, one workgroup but two waves per SIMD); 256 x 256, 8 waves of 128 x 64, 2-stage
+// ring (128 KB, one per CU).  With 8 waves, one wave per SIMD issues the stage loads.
 using Tile128 = Tile<2, 2, 2, 2, 2>;
-using Tile128Deep = Tile<2, 2, 2, 2, 3>;
+using Tile128Deep = Tile<2, 4, 2, 1, 3, 2, 4>;
 using Tile256 = Tile<2, 4, 4, 2, 2, 2, 4>;
 
 // Chunk c of LDS row r sits at position c ^ swz(r): the 16-byte reads of 8 (or 16)
@@ -426,12 +427,14 @@ __device__ __forceinline__ void zero_k_tail(const DmaCtx<T>& d, uint16_t* sA, ui
 template <class T>
 __device__ __forceinline__ void interleave() {
   constexpr int NR = T::BLK_M + T::BLK_N, NM = T::BLK_M * T::BLK_N;
+  constexpr int NP = NR < NM ? NR : NM;
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
+  for (int i = 0; i < NP; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+  if constexpr (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
+  if constexpr (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
 }
 
 // K steps 1 .. KS - 1 of a stage, each read before the previous step's MFMAs are issued
@@ -487,8 +490,10 @@ template <class T>
 __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
     int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint16_t sA[T::STAGES * T::SA];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB[T::STAGES * T::SB];
+  // one LDS block: the A stages, then the B stages; reused by the epilogue
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[T::STAGES * (T::SA + T::SB)];
+  uint16_t* const sA = smem;
+  uint16_t* const sB = smem + T::STAGES * T::SA;
 
   // Tile order: consecutive workgroup ids land on different XCDs (round robin over 8), so
   // give each XCD a contiguous band of tiles, walked column-major inside bands of 8
@@ -606,6 +611,47 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
 
   // epilogue: register r of block (i, j) is row 8 (r / 4) + 4 (lane / 32) + r % 4 and
   // column lane % 32 of that block
+  if (!c_f32) {
+    // bf16 output goes through LDS: each wave rounds its WM x WN sub-tile into its own
+    // region (16-byte chunk c of row r at position c ^ (r % CW)), then reads it back as
+    // 16-byte row pieces, so a store instruction writes whole sub-tile row segments
+    constexpr int WM = T::BLK_M * 32, WN = T::BLK_N * 32;
+    constexpr int CW = WN / 8, RPW = 64 / CW;   // chunks per row, rows per read
+    static_assert(T::NW * WM * WN <= T::STAGES * (T::SA + T::SB) && WM % RPW == 0, "epilogue staging");
+    __syncthreads();   // every wave is done with the stage buffers
+    uint16_t* const st = smem + wave * (WM * WN);
+#pragma unroll
+    for (int i = 0; i < T::BLK_M; ++i)
+#pragma unroll
+      for (int j = 0; j < T::BLK_N; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rw = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int cw = j * 32 + (lane & 31);
+          st[rw * WN + (((cw >> 3) ^ (rw % CW)) << 3) + (cw & 7)] = f32_to_bf16(acc[i][j][r]);
+        }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the region is this wave's own
+    const bool vec = ((reinterpret_cast<uintptr_t>(C) | static_cast<uintptr_t>(ldc * 2)) & 15) == 0;
+    const int cc = lane % CW;
+    const int col = tn * T::TN + wn * WN + cc * 8;
+    uint16_t* const Cb = static_cast<uint16_t*>(C);
+#pragma unroll
+    for (int it = 0; it < WM / RPW; ++it) {
+      const int rw = it * RPW + lane / CW;
+      const u16x8 v = *reinterpret_cast<const u16x8*>(st + rw * WN + ((cc ^ (rw % CW)) << 3));
+      const int row = tm * T::TM + wm * WM + rw;
+      if (row >= M || col >= N) continue;
+      uint16_t* const dst = Cb + static_cast<int64_t>(row) * ldc + col;
+      if (vec && col + 8 <= N) {
+        *reinterpret_cast<u16x8*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (col + e < N) dst[e] = v[e];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < T::BLK_M; ++i)
 #pragma unroll
@@ -616,10 +662,7 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
       for (int r = 0; r < 16; ++r) {
         const int row = tm * T::TM + (wm * T::BLK_M + i) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row >= M) continue;
-        if (c_f32)
-          static_cast<float*>(C)[static_cast<int64_t>(row) * ldc + col] = acc[i][j][r];
-        else
-          static_cast<uint16_t*>(C)[static_cast<int64_t>(row) * ldc + col] = f32_to_bf16(acc[i][j][r]);
+        static_cast<float*>(C)[static_cast<int64_t>(row) * ldc + col] = acc[i][j][r];
       }
     }
 }

@@ -188,3 +188,23 @@ def test_empty_and_ragged(lib):
     a, b = gemm_inputs(1, 1, 8, cfg=33)
     c = lib.bi_gemm(bf16(a), bf16(_nk(b)), out_dtype=torch.float32)
     assert f32_within_rel(host(c), gemm_f64(a, b))["ok"]
+
+
+def test_output_views(lib):
+    # C written into row-strided views: 16-byte-aligned rows with a ragged last chunk, and rows
+    # that start off 16-byte alignment; every element equals the contiguous result and nothing
+    # outside the view changes (grids for the 128 x 128 and the 256 x 256 tiles)
+    sentinel = -7.0
+    for m, n, k in [(300, 1003, 64), (1000, 600, 56), (3100, 8000, 80), (4096, 4092, 40)]:
+        say("gemm output views", m, n, k)
+        a, b = gemm_inputs(m, n, k, cfg=38)
+        A, W = bf16(a), bf16(_nk(b))
+        ref = lib.bi_gemm(A, W)
+        for lo, width in [(0, (n + 7) // 8 * 8 + 8), (1, n + 5)]:
+            big = torch.full((m, width), sentinel, dtype=torch.bfloat16, device="cuda")
+            out = big[:, lo:lo + n]
+            lib.bi_gemm(A, W, out=out)
+            assert same_bits(out.contiguous(), ref), (m, n, k, lo)
+            rest = torch.ones_like(big, dtype=torch.bool)
+            rest[:, lo:lo + n] = False
+            assert bool((big[rest] == sentinel).all()), (m, n, k, lo)
