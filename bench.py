@@ -214,6 +214,62 @@ def gemm_sweep(torch, bi):
     return out
 
 
+def model_bench(torch, bi):
+    """The composition rows: 32-layer Mistral-7B-shaped greedy decoding (random bf16 weights,
+    std 0.02) of a 1400-token prompt alone and inside a ragged batch of 49 prompts, as in the
+    batch-invariance test.  Prefill time = a 1-token generation; decode step = the difference
+    between a 17- and a 1-token generation over 16 steps.  Reported, not graded."""
+    import synth
+    from invariant_amd.model import Dims, PagedKVCache, greedy_generate, random_model
+    dims = Dims()
+    model = random_model(dims, seed=5)
+    prompt = synth.uniform_ints(1400, 0, 31999, 5, 0)
+    lens = synth.ragged_lengths(48, 200, 4000, 5, 1)
+    others = [synth.uniform_ints(int(L), 0, 31999, 5, 10 + i) for i, L in enumerate(lens)]
+    prompts = others[:24] + [prompt] + others[24:]
+    total = sum(len(p) + 64 for p in prompts)
+    cache = PagedKVCache(dims, n_pages=total // 16 + 2 * len(prompts) + 16, seed=5)
+
+    def timed(ps, n):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        greedy_generate(model, ps, n, cache, dims)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t
+
+    timed([prompt], 2)
+    weight_bytes = sum(t.numel() * t.element_size() for t in _tensors(model))
+    out = {"workload": "Mistral-7B-shaped 32-layer greedy decode, random bf16 weights",
+           "weight_bytes": weight_bytes}
+    for name, ps in (("alone_1x1400", [prompt]), ("batched_49_ragged", prompts)):
+        t1 = timed(ps, 1)
+        t17 = timed(ps, 17)
+        step = (t17 - t1) / 16
+        ntok = sum(len(p) for p in ps)
+        out[name] = dict(prefill_tokens=ntok, prefill_s=round(t1, 4),
+                         prefill_tokens_per_s=round(ntok / t1, 1),
+                         decode_step_ms=round(step * 1e3, 3),
+                         decode_tokens_per_s=round(len(ps) / step, 1),
+                         decode_weight_GBps=round(weight_bytes / step / 1e9, 1))
+        log(name, out[name])
+    print(json.dumps(out), flush=True)
+
+
+def _tensors(obj):
+    import torch
+    if isinstance(obj, torch.Tensor):
+        yield obj
+    elif isinstance(obj, dict):
+        for v in obj.values():
+            yield from _tensors(v)
+    elif isinstance(obj, (list, tuple)):
+        for v in obj:
+            yield from _tensors(v)
+    elif hasattr(obj, "__dict__"):
+        for v in vars(obj).values():
+            yield from _tensors(v)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +280,8 @@ def main():
     ap.add_argument("--gemm-profile", metavar="M,N,K",
                     help="run bi_gemm on one shape (5 warm-up + 20 timed calls) and print its "
                          "TFLOP/s, for rocprofv3 counter runs")
+    ap.add_argument("--model", action="store_true",
+                    help="time 32-layer greedy decoding alone and in a 49-prompt batch (reported)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (to scale rocprof byte counters)")
     args = ap.parse_args()
@@ -240,6 +298,9 @@ def main():
 
     if args.gemm_sweep:
         gemm_sweep(torch, bi)
+        return
+    if args.model:
+        model_bench(torch, bi)
         return
     if args.gemm_profile:
         gemm_profile(torch, bi, [int(v) for v in args.gemm_profile.split(",")])

@@ -686,6 +686,104 @@ TileKind pick_tile(int64_t M, int64_t N, int cus) {
   return cost256 < cost128 ? TileKind::k256 : TileKind::k128;
 }
 
+// Few-row GEMM (M <= 64, K a multiple of 16 and at least 32 steps of 16).  At decode sizes the weight stream bounds the
+// call, and a 128 x 128 grid leaves most CUs idle (N = 4096 gives 32 workgroups).  Here one
+// wave owns one 32-column block and all of M (RB 32-row blocks) and loads its instruction
+// operands straight from global memory into registers, PF K steps ahead: lane l takes the 16
+// bytes at row l % 32, k offset 16 t + 8 (l / 32) of K step t, which is exactly its operand of
+// the instruction, so there is no LDS, no barrier and no other wave to wait for.  What is left
+// is the chain itself: K / 16 dependent instructions per accumulator.  Every output element
+// sees the instruction sequence of every other configuration (same instruction, +0 start,
+// ascending 16-wide K steps, same lane-to-k assignment), so its bits do not change.
+template <int RB, int PF>
+__global__ __launch_bounds__(64) void gemm_rows_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
+    int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32) {
+  const int lane = threadIdx.x;
+  const int col0 = blockIdx.x * 32;
+  const uint16_t* pa[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)   // rows past M repeat the last row; they are never stored
+    pa[rb] = A + static_cast<int64_t>(min(rb * 32 + (lane & 31), M - 1)) * lda + 8 * (lane >> 5);
+  const uint16_t* pb = B + static_cast<int64_t>(min(col0 + (lane & 31), N - 1)) * ldb + 8 * (lane >> 5);
+  bf16x8 ra[PF][RB], rv[PF];
+  auto load = [&](int t, int slot_a, bf16x8 (&dst_a)[RB], bf16x8& dst_b) {
+    (void)slot_a;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) dst_a[rb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pa[rb] + 16 * t));
+    dst_b = as_bf16x8(*reinterpret_cast<const u16x8*>(pb + 16 * t));
+  };
+  floatx16 acc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[rb][r] = 0.f;
+
+  auto mma = [&](int p) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[p][rb], rv[p], acc[rb], 0, 0, 0);
+  };
+  const int nsteps = K / 16;   // >= 2 PF (the host checks)
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load(p, p, ra[p], rv[p]);
+  // full rounds: step t multiplies slot t % PF and refills it with step t + PF (straight-line
+  // code, so the compiler's load counters stay exact and PF steps stay in flight)
+  int t0 = 0;
+  for (; t0 + 2 * PF <= nsteps; t0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      mma(p);
+      load(t0 + PF + p, p, ra[p], rv[p]);
+    }
+  }
+  // last (up to 2 PF - 1) steps
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    if (t0 + p < nsteps) {
+      mma(p);
+      if (t0 + PF + p < nsteps) load(t0 + PF + p, p, ra[p], rv[p]);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (t0 + PF + p < nsteps) mma(p);
+  // register r of row block rb is row 32 rb + 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
+  const int col = col0 + (lane & 31);
+  if (col >= N) return;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row >= M) continue;
+      if (c_f32)
+        static_cast<float*>(C)[static_cast<int64_t>(row) * ldc + col] = acc[rb][r];
+      else
+        static_cast<uint16_t*>(C)[static_cast<int64_t>(row) * ldc + col] = f32_to_bf16(acc[rb][r]);
+    }
+}
+
+constexpr int kRowsMinK = 2 * 16 * 16;   // 2 PF steps of 16
+
+// The few-row kernel for up to 32 rows, and for 33..64 rows while the column blocks number at
+// most two per CU (with more, its doubled per-wave streams lose to the 128 x 128 tiles).
+bool use_rows(int64_t M, int64_t N, int64_t K, int cus) {
+  if (M > 64 || K % 16 != 0 || K < kRowsMinK) return false;
+  return M <= 32 || (N + 31) / 32 <= 2 * static_cast<int64_t>(cus);
+}
+
+void launch_rows(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                 int64_t lda, int64_t ldb, int64_t ldc, int cf, hipStream_t s) {
+  const unsigned wgs = static_cast<unsigned>((N + 31) / 32);
+  const uint16_t* a = static_cast<const uint16_t*>(A);
+  const uint16_t* b = static_cast<const uint16_t*>(B);
+  if (M <= 32)
+    gemm_rows_kernel<1, 16><<<dim3(wgs), dim3(64), 0, s>>>(a, b, C, int(M), int(N), int(K), lda, ldb, ldc, cf);
+  else
+    gemm_rows_kernel<2, 12><<<dim3(wgs), dim3(64), 0, s>>>(a, b, C, int(M), int(N), int(K), lda, ldb, ldc, cf);
+}
+
 template <class T>
 void launch_dma(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
                 int64_t ldb, int64_t ldc, int cf, hipStream_t s) {
@@ -747,6 +845,10 @@ extern "C" int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t
         A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
         0, int(K), 0);
   else if (M * lda * 2 < (int64_t(1) << 32) && N * ldb * 2 < (int64_t(1) << 32)) {
+    if (use_rows(M, N, K, cu_count())) {
+      launch_rows(A, B, C, M, N, K, lda, ldb, ldc, cf, s);
+      return launch_status();
+    }
     switch (pick_tile(M, N, cu_count())) {
       case TileKind::k256: launch_dma<Tile256>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
       case TileKind::k128deep: launch_dma<Tile128Deep>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
@@ -769,6 +871,12 @@ extern "C" int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_
     *tile_m = BM;
     *tile_n = BN;
     *stages = 2;
+    return BI_OK;
+  }
+  if (use_rows(M, N, K, cu_count())) {   // few-row kernel: one wave per 32-column block
+    *tile_m = M <= 32 ? 32 : 64;
+    *tile_n = 32;
+    *stages = M <= 32 ? 16 : 12;
     return BI_OK;
   }
   switch (pick_tile(M, N, cu_count())) {
