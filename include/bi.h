@@ -129,11 +129,14 @@ int bi_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t D, 
 int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
             int64_t ldb, int64_t ldc, int b_layout, int a_dtype, int c_dtype, void* stream);
 
-/* The workgroup tile bi_gemm uses for an M x N output with A of dtype a_dtype on the
- * current device: *tile_m x *tile_n outputs per workgroup and *stages K slices in its LDS
- * ring.  256 x 256 (2 stages) when that grid finishes in fewer rounds of the CU array;
- * else 128 x 128, with a 3-stage ring when the grid has no more tiles than CUs and a
- * 2-stage ring (two workgroups per CU) otherwise; fp32 A: 128 x 128, register staged.
+/* The workgroup tile bi_gemm uses for an M x N x K product with A of dtype a_dtype on the
+ * current device: *tile_m x *tile_n outputs per workgroup and *stages K slices in flight.
+ * Up to 32 rows (up to 64 while ceil(N / 32) is at most twice the CU count), with K a
+ * multiple of 16 and at least 512: 32 (or 64) x 32, one wave whose instruction operands
+ * are loaded straight into registers 16 (or 12) K steps ahead.  Otherwise 256 x 256
+ * (2-stage LDS ring) when that grid finishes in fewer rounds of the CU array; else
+ * 128 x 128, with a 3-stage ring when the grid has no more tiles than CUs and a 2-stage
+ * ring (two workgroups per CU) otherwise; fp32 A: 128 x 128, register staged.
  * Informational: the bits of C do not depend on it.  Errors: BI_ERR_NULL, BI_ERR_SHAPE
  * (negative sizes), BI_ERR_DTYPE. */
 int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_t* tile_m, int32_t* tile_n,

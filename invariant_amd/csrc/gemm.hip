@@ -11,19 +11,17 @@
 //   8 (l / 32) .. + 7 of each step.  Products past K are exact zeros; rows past M
 //   (columns past N) are never stored.
 // Output element (i, j) is therefore the result of the same instruction sequence for
-// every M, every position of row i inside its tile and every workgroup tile.  The
-// workgroup tile only decides which workgroup computes which outputs: 128 x 128 (4 waves
-// of 64 x 64, two workgroups per CU) or 256 x 256 (8 waves of 128 x 64, one per CU), picked
-// from the size of the output grid; the two give identical bits, which the tests check
-// across the switch.
-//
-// Main kernel (bf16 A, B as [N, K]): 32-wide K slices of both tiles stream into LDS by
-// direct-to-LDS 16-byte loads through a 4-stage ring (three slices in flight while one is
-// multiplied); the 16-byte k-chunks of row r sit at chunk position c ^ swz(r) so that the
-// 16-byte operand reads of consecutive rows hit distinct banks.  How K is staged does not
-// change the instruction sequence per element.  The fp32-A path, operands of 4 GiB or more
-// and the split-K comparison variant stage through registers instead (128 x 128 tile);
-// they share the instruction and the K order.
+// every M, every position of row i inside its tile and every workgroup configuration; the
+// configuration only decides which wave computes which outputs, and the tests check the
+// bits across every switch.  Configurations, picked from the output grid:
+//   256 x 256 (8 waves of 128 x 64) or 128 x 128 (4 waves of 64 x 64, two workgroups per CU;
+//   8 waves of 64 x 32 when the grid has no more tiles than CUs): 64-wide K slices of both
+//   tiles stream into an LDS ring by direct-to-LDS 16-byte loads; the 16-byte k-chunks of
+//   row r sit at chunk position c ^ swz(r) so that the operand reads of consecutive rows hit
+//   distinct banks; bf16 results leave through LDS as 16-byte row pieces.
+//   Up to 64 rows: one wave per 32-column block loads its operands straight into registers.
+// The fp32-A path, operands of 4 GiB or more and the split-K comparison variant stage
+// through registers instead (128 x 128 tile); they share the instruction and the K order.
 //
 // A may be fp32 ("FP32 upcast" of the cross-vendor mismatch abstract): each value is
 // split exactly into bf16 hi + mid + lo (truncations, so hi + mid + lo == a for normal
