@@ -239,8 +239,9 @@ def model_bench(torch, bi):
 
     timed([prompt], 2)
     weight_bytes = sum(t.numel() * t.element_size() for t in _tensors(model))
+    out_layer = layer_bench(torch, model, dims)
     out = {"workload": "Mistral-7B-shaped 32-layer greedy decode, random bf16 weights",
-           "weight_bytes": weight_bytes}
+           "weight_bytes": weight_bytes, "decoder_layer_decode": out_layer}
     for name, ps in (("alone_1x1400", [prompt]), ("batched_49_ragged", prompts)):
         t1 = timed(ps, 1)
         t17 = timed(ps, 17)
@@ -253,6 +254,41 @@ def model_bench(torch, bi):
                          decode_weight_GBps=round(weight_bytes / step / 1e9, 1))
         log(name, out[name])
     print(json.dumps(out), flush=True)
+
+
+def layer_bench(torch, model, dims):
+    """One decoder layer at decode: B requests with contexts L ~ U[0, 4096] (cache pages
+    reserved, contents as they are), one new token each; time per layer call."""
+    import synth
+    from invariant_amd.model import PagedKVCache, decoder_layer, make_batch
+    out = {}
+    layer = model["layers"][0]
+    ctx = synth.ragged_lengths(256, 0, 4096, 3, 2)
+    cache = PagedKVCache(dims, n_pages=int(ctx.sum()) // 16 + 2 * 256 + 16, seed=3, n_layers=1)
+    lw_bytes = sum(t.numel() * t.element_size() for t in _tensors(layer))
+    for B in (1, 8, 64, 256):
+        sids = list(range(B))
+        batch = make_batch(cache, sids, [int(c) for c in ctx[:B]],
+                           [np.asarray([7], np.int32)] * B, dims=dims)
+        h = torch.randn((B, dims.hidden), device="cuda").to(torch.bfloat16)
+        f = lambda: decoder_layer(layer, h, batch, cache.k[0], cache.v[0], dims)
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 20 * 1e-3
+        kv = 2 * 2 * dims.n_kv_heads * dims.head_dim * int(ctx[:B].sum() + B)
+        out[f"B{B}"] = dict(us=round(t * 1e6, 1), weight_GBps=round(lw_bytes / t / 1e9, 1),
+                            weights_plus_kv_GBps=round((lw_bytes + kv) / t / 1e9, 1))
+        log("layer", B, out[f"B{B}"])
+        for sid in sids:
+            cache.release(sid)
+    return out
 
 
 def _tensors(obj):
