@@ -705,8 +705,7 @@ __global__ __launch_bounds__(64) void gemm_rows_kernel(
     pa[rb] = A + static_cast<int64_t>(min(rb * 32 + (lane & 31), M - 1)) * lda + 8 * (lane >> 5);
   const uint16_t* pb = B + static_cast<int64_t>(min(col0 + (lane & 31), N - 1)) * ldb + 8 * (lane >> 5);
   bf16x8 ra[PF][RB], rv[PF];
-  auto load = [&](int t, int slot_a, bf16x8 (&dst_a)[RB], bf16x8& dst_b) {
-    (void)slot_a;
+  auto load = [&](int t, bf16x8 (&dst_a)[RB], bf16x8& dst_b) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) dst_a[rb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pa[rb] + 16 * t));
     dst_b = as_bf16x8(*reinterpret_cast<const u16x8*>(pb + 16 * t));
@@ -724,7 +723,7 @@ __global__ __launch_bounds__(64) void gemm_rows_kernel(
   };
   const int nsteps = K / 16;   // >= 2 PF (the host checks)
 #pragma unroll
-  for (int p = 0; p < PF; ++p) load(p, p, ra[p], rv[p]);
+  for (int p = 0; p < PF; ++p) load(p, ra[p], rv[p]);
   // full rounds: step t multiplies slot t % PF and refills it with step t + PF (straight-line
   // code, so the compiler's load counters stay exact and PF steps stay in flight)
   int t0 = 0;
@@ -732,7 +731,7 @@ __global__ __launch_bounds__(64) void gemm_rows_kernel(
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       mma(p);
-      load(t0 + PF + p, p, ra[p], rv[p]);
+      load(t0 + PF + p, ra[p], rv[p]);
     }
   }
   // last (up to 2 PF - 1) steps
@@ -740,7 +739,7 @@ __global__ __launch_bounds__(64) void gemm_rows_kernel(
   for (int p = 0; p < PF; ++p) {
     if (t0 + p < nsteps) {
       mma(p);
-      if (t0 + PF + p < nsteps) load(t0 + PF + p, p, ra[p], rv[p]);
+      if (t0 + PF + p < nsteps) load(t0 + PF + p, ra[p], rv[p]);
     }
   }
 #pragma unroll
