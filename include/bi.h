@@ -136,7 +136,9 @@ int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
  * are loaded straight into registers 16 (or 12) K steps ahead.  Otherwise 256 x 256
  * (2-stage LDS ring) when that grid finishes in fewer rounds of the CU array; else
  * 128 x 128, with a 3-stage ring when the grid has no more tiles than CUs and a 2-stage
- * ring (two workgroups per CU) otherwise; fp32 A: 128 x 128, register staged.
+ * ring (two workgroups per CU) otherwise; when fewer than three quarters of the CUs would
+ * get a 128 x 128 tile, 64 x 128 or (fewer still) 64 x 64 with a 3-stage ring; fp32 A:
+ * 128 x 128, register staged.
  * Informational: the bits of C do not depend on it.  Errors: BI_ERR_NULL, BI_ERR_SHAPE
  * (negative sizes), BI_ERR_DTYPE. */
 int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_t* tile_m, int32_t* tile_n,

@@ -15,7 +15,8 @@
 // configuration only decides which wave computes which outputs, and the tests check the
 // bits across every switch.  Configurations, picked from the output grid:
 //   256 x 256 (8 waves of 128 x 64) or 128 x 128 (4 waves of 64 x 64, two workgroups per CU;
-//   8 waves of 64 x 32 when the grid has no more tiles than CUs): 64-wide K slices of both
+//   8 waves of 64 x 32 when the grid has no more tiles than CUs), or for grids well under one
+//   such tile per CU 64 x 128 / 64 x 64 (waves of 32 x 32): 64-wide K slices of both
 //   tiles stream into an LDS ring by direct-to-LDS 16-byte loads; the 16-byte k-chunks of
 //   row r sit at chunk position c ^ swz(r) so that the operand reads of consecutive rows hit
 //   distinct banks; bf16 results leave through LDS as 16-byte row pieces.
@@ -257,6 +258,10 @@ struct Tile {
 // ring (128 KB, one per CU).  With 8 waves, one wave per SIMD issues the stage loads.
 using Tile128 = Tile<2, 2, 2, 2, 2>;
 using Tile128Deep = Tile<2, 4, 2, 1, 3, 2, 4>;
+// Grids with well under one 128 x 128 tile per CU (a few hundred rows): 64 x 128 as 8 waves
+// of 32 x 32, or 64 x 64 as 4 waves of 32 x 32, both with a 3-stage ring.
+using Tile64x128 = Tile<2, 4, 1, 1, 3, 2, 4>;
+using Tile64 = Tile<2, 2, 1, 1, 3>;
 using Tile256 = Tile<2, 4, 4, 2, 2, 2, 4>;
 
 // Chunk c of LDS row r sits at position c ^ swz(r): the 16-byte reads of 8 (or 16)
@@ -672,12 +677,18 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
 // no more tiles than CUs.  The cost counts rounds of the CU array, with round times
 // measured on MI355X at K = 4096 (all scale with K): 256 x 256: 109; 128 x 128 two per CU:
 // 66, one per CU: 46.
-enum class TileKind { k128, k128deep, k256 };
+enum class TileKind { k64, k64x128, k128, k128deep, k256 };
 
 TileKind pick_tile(int64_t M, int64_t N, int cus) {
   const int64_t n256 = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t n128 = ((M + 127) / 128) * ((N + 127) / 128);
-  if (n128 <= cus) return TileKind::k128deep;
+  if (n128 <= cus) {
+    // one round or less: the largest tile whose grid still covers three quarters of the CUs
+    const int64_t n64x128 = ((M + 63) / 64) * ((N + 127) / 128);
+    if (4 * n128 >= 3 * cus) return TileKind::k128deep;
+    if (4 * n64x128 >= 3 * cus) return TileKind::k64x128;
+    return TileKind::k64;
+  }
   const int64_t cost256 = 109 * ((n256 + cus - 1) / cus);
   const int64_t rem = n128 % (2 * cus);
   const int64_t cost128 = 66 * (n128 / (2 * cus)) + (rem == 0 ? 0 : rem <= cus ? 46 : 66);
@@ -849,6 +860,8 @@ extern "C" int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t
     switch (pick_tile(M, N, cu_count())) {
       case TileKind::k256: launch_dma<Tile256>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
       case TileKind::k128deep: launch_dma<Tile128Deep>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
+      case TileKind::k64x128: launch_dma<Tile64x128>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
+      case TileKind::k64: launch_dma<Tile64>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
       default: launch_dma<Tile128>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
     }
   }
@@ -880,6 +893,9 @@ extern "C" int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_
     case TileKind::k256: *tile_m = Tile256::TM; *tile_n = Tile256::TN; *stages = Tile256::STAGES; break;
     case TileKind::k128deep:
       *tile_m = Tile128Deep::TM; *tile_n = Tile128Deep::TN; *stages = Tile128Deep::STAGES; break;
+    case TileKind::k64x128:
+      *tile_m = Tile64x128::TM; *tile_n = Tile64x128::TN; *stages = Tile64x128::STAGES; break;
+    case TileKind::k64: *tile_m = Tile64::TM; *tile_n = Tile64::TN; *stages = Tile64::STAGES; break;
     default: *tile_m = Tile128::TM; *tile_n = Tile128::TN; *stages = Tile128::STAGES; break;
   }
   return BI_OK;

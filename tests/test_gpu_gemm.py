@@ -64,12 +64,12 @@ def test_tile_switch_changes_no_bit(lib):
         assert lib.bi_gemm_tile(full_m, n, k)[:2] == (256, 256)
         full = lib.bi_gemm(A, B)
         configs = {lib.bi_gemm_tile(full_m, n, k)}
-        for m in (1, 33, 64, 65, 255, 1000, 2048, 2560, 3000):
+        for m in (1, 33, 64, 65, 255, 500, 640, 1000, 2048, 2560, 3000):
             configs.add(lib.bi_gemm_tile(m, n, k))
             assert same_bits(lib.bi_gemm(A[:m], B), full[:m]), (n, k, m)
-        assert {(128, 128, 3), (128, 128, 2), (256, 256, 2)} <= configs, configs
+        assert {(64, 64, 3), (64, 128, 3), (128, 128, 3), (128, 128, 2), (256, 256, 2)} <= configs, configs
         # K a multiple of 16 and at least 512: up to 64 rows take the few-row kernel
-        assert any(c[0] in (32, 64) for c in configs) == (k % 16 == 0 and k >= 512), configs
+        assert any(c[1] == 32 for c in configs) == (k % 16 == 0 and k >= 512), configs
         sel = torch.tensor([full_m - 1, 17, 2600, 300], device="cuda")
         assert same_bits(lib.bi_gemm(A[sel].contiguous(), B), full[sel])
         ff = lib.bi_gemm(A, B, out_dtype=torch.float32)
@@ -215,7 +215,7 @@ def test_output_views(lib):
 def test_few_rows_vs_oracle(lib, m, n, k):
     # the few-row kernel (M <= 64, K % 16 == 0, K >= 512): ragged column blocks, rows past M,
     # the last partial round of prefetched K steps
-    assert lib.bi_gemm_tile(m, n, k)[0] in (32, 64)
+    assert lib.bi_gemm_tile(m, n, k)[1] == 32
     say("gemm few rows", m, n, k)
     a, b = gemm_inputs(m, n, k, cfg=39)
     c = lib.bi_gemm(bf16(a), bf16(_nk(b)))
@@ -238,7 +238,7 @@ def test_few_rows_match_large_m(lib, n, k):
     for m in (1, 17, 32, 33, 49, 64):
         # up to 32 rows always; 33..64 rows only while N / 32 <= 2 x CUs
         cus = torch.cuda.get_device_properties(0).multi_processor_count
-        assert (lib.bi_gemm_tile(m, n, k)[0] in (32, 64)) == (m <= 32 or (n + 31) // 32 <= 2 * cus), (m, n)
+        assert (lib.bi_gemm_tile(m, n, k)[1] == 32) == (m <= 32 or (n + 31) // 32 <= 2 * cus), (m, n)
         assert same_bits(lib.bi_gemm(A[:m], W), full[:m]), (n, k, m)
         assert same_bits(lib.bi_gemm(A[:m], W, out_dtype=torch.float32), ff[:m]), (n, k, m)
     rows = torch.tensor([300, 5, 511], device="cuda")
