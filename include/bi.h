@@ -132,8 +132,9 @@ int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
 /* The workgroup tile bi_gemm uses for an M x N x K product with A of dtype a_dtype on the
  * current device: *tile_m x *tile_n outputs per workgroup and *stages K slices in flight.
  * Up to 32 rows (up to 64 while ceil(N / 32) is at most twice the CU count), with K a
- * multiple of 16 and at least 512: 32 (or 64) x 32, one wave whose instruction operands
- * are loaded straight into registers 16 (or 12) K steps ahead.  Otherwise 256 x 256
+ * multiple of 16 and at least 512: 32 x 32 per wave (64 x 32 when 33..64 rows would need
+ * more than one wave per CU as 32 x 32 blocks), the wave's instruction operands loaded
+ * straight into registers 16 (or 12) K steps ahead.  Otherwise 256 x 256
  * (2-stage LDS ring) when that grid finishes in fewer rounds of the CU array; else
  * 128 x 128, with a 3-stage ring when the grid has no more tiles than CUs and a 2-stage
  * ring (two workgroups per CU) otherwise; when fewer than three quarters of the CUs would

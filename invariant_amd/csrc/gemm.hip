@@ -20,7 +20,8 @@
 //   tiles stream into an LDS ring by direct-to-LDS 16-byte loads; the 16-byte k-chunks of
 //   row r sit at chunk position c ^ swz(r) so that the operand reads of consecutive rows hit
 //   distinct banks; bf16 results leave through LDS as 16-byte row pieces.
-//   Up to 64 rows: one wave per 32-column block loads its operands straight into registers.
+//   Up to 64 rows: one wave per 32 (or 64) x 32 output block loads its operands straight into
+//   registers.
 // The fp32-A path, operands of 4 GiB or more and the split-K comparison variant stage
 // through registers instead (128 x 128 tile); they share the instruction and the K order.
 //
@@ -710,10 +711,11 @@ __global__ __launch_bounds__(64) void gemm_rows_kernel(
     int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32) {
   const int lane = threadIdx.x;
   const int col0 = blockIdx.x * 32;
+  const int row0 = blockIdx.y * (RB * 32);   // 32-row blocks beyond the first: more waves
   const uint16_t* pa[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)   // rows past M repeat the last row; they are never stored
-    pa[rb] = A + static_cast<int64_t>(min(rb * 32 + (lane & 31), M - 1)) * lda + 8 * (lane >> 5);
+    pa[rb] = A + static_cast<int64_t>(min(row0 + rb * 32 + (lane & 31), M - 1)) * lda + 8 * (lane >> 5);
   const uint16_t* pb = B + static_cast<int64_t>(min(col0 + (lane & 31), N - 1)) * ldb + 8 * (lane >> 5);
   bf16x8 ra[PF][RB], rv[PF];
   auto load = [&](int t, bf16x8 (&dst_a)[RB], bf16x8& dst_b) {
@@ -763,7 +765,7 @@ __global__ __launch_bounds__(64) void gemm_rows_kernel(
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int row = row0 + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (row >= M) continue;
       if (c_f32)
         static_cast<float*>(C)[static_cast<int64_t>(row) * ldc + col] = acc[rb][r];
@@ -781,13 +783,18 @@ bool use_rows(int64_t M, int64_t N, int64_t K, int cus) {
   return M <= 32 || (N + 31) / 32 <= 2 * static_cast<int64_t>(cus);
 }
 
+// 33..64 rows: a second wave per column block for the second 32 rows while that keeps at
+// most one wave per CU, else one wave with both row blocks.
+bool rows_split(int64_t M, int64_t N, int cus) { return M > 32 && 2 * ((N + 31) / 32) <= cus; }
+
 void launch_rows(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                  int64_t lda, int64_t ldb, int64_t ldc, int cf, hipStream_t s) {
   const unsigned wgs = static_cast<unsigned>((N + 31) / 32);
   const uint16_t* a = static_cast<const uint16_t*>(A);
   const uint16_t* b = static_cast<const uint16_t*>(B);
-  if (M <= 32)
-    gemm_rows_kernel<1, 16><<<dim3(wgs), dim3(64), 0, s>>>(a, b, C, int(M), int(N), int(K), lda, ldb, ldc, cf);
+  if (M <= 32 || rows_split(M, N, cu_count()))
+    gemm_rows_kernel<1, 16><<<dim3(wgs, M <= 32 ? 1 : 2), dim3(64), 0, s>>>(a, b, C, int(M), int(N), int(K),
+                                                                           lda, ldb, ldc, cf);
   else
     gemm_rows_kernel<2, 12><<<dim3(wgs), dim3(64), 0, s>>>(a, b, C, int(M), int(N), int(K), lda, ldb, ldc, cf);
 }
@@ -883,10 +890,11 @@ extern "C" int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_
     *stages = 2;
     return BI_OK;
   }
-  if (use_rows(M, N, K, cu_count())) {   // few-row kernel: one wave per 32-column block
-    *tile_m = M <= 32 ? 32 : 64;
+  if (use_rows(M, N, K, cu_count())) {   // few-row kernel: one wave per 32 (or 64) x 32 block
+    const bool one = M <= 32 || rows_split(M, N, cu_count());
+    *tile_m = one ? 32 : 64;
     *tile_n = 32;
-    *stages = M <= 32 ? 16 : 12;
+    *stages = one ? 16 : 12;
     return BI_OK;
   }
   switch (pick_tile(M, N, cu_count())) {
