@@ -142,3 +142,55 @@ def test_cfg5_greedy_alone_vs_batched(lib, fp32_variant):
                                   keep_logits=[4], max_chunk_tokens=3000)
     assert np.array_equal(tok_c[4], tok_a[0][:8])
     assert same_bits(lg_c[4], lg_a[0][:8])
+
+
+def test_prefill_chunking_and_prefix_cache_bitwise(lib):
+    # A prompt's hidden states and logits are the same bits whether it is prefilled in one
+    # pass, in chunks of 1, 8, 64 or 256 tokens, or as a suffix on top of KV pages another
+    # request already filled (a cached prefix).  Two full-width layers; every chunk size
+    # lands on a different GEMM configuration and attention mixes cached and new keys.
+    from dataclasses import replace
+    from invariant_amd.model import forward, head, make_batch
+    dims = replace(Dims(), n_layers=2)
+    model = random_model(dims, seed=9)
+    prompt = synth.uniform_ints(320, 0, 31999, 9, 0).astype(np.int32)
+    cache = PagedKVCache(dims, n_pages=320, seed=9)
+    say("prefix/chunk invariance: full pass")
+    full = make_batch(cache, [0], [0], [prompt], dims=dims)
+    h_full = forward(model, full, cache, dims)
+    rows = torch.arange(320, dtype=torch.int32, device="cuda")
+    lg_full, _ = head(model, h_full, rows, dims)
+
+    def chunked(sid, chunk):
+        got_h, got_lg, done = [], [], 0
+        while done < len(prompt):
+            part = prompt[done:done + chunk]
+            b = make_batch(cache, [sid], [done], [part], dims=dims)
+            h = forward(model, b, cache, dims)
+            lg, _ = head(model, h, torch.arange(len(part), dtype=torch.int32, device="cuda"), dims)
+            got_h.append(h)
+            got_lg.append(lg)
+            done += len(part)
+        return torch.cat(got_h), torch.cat(got_lg)
+
+    for sid, chunk in ((1, 1), (2, 8), (3, 64), (4, 256)):
+        say("chunk", chunk)
+        h, lg = chunked(sid, chunk)
+        assert same_bits(h, h_full), chunk
+        assert same_bits(lg, lg_full), chunk
+        cache.release(sid)
+
+    # cached prefix: request 5 prefills the first 256 tokens (16 full pages); request 6 takes
+    # those pages into its block table and prefills only the last 64 tokens
+    say("cached prefix")
+    pre = make_batch(cache, [5], [0], [prompt[:256]], dims=dims)
+    forward(model, pre, cache, dims)
+    cache.pages[6] = list(cache.pages[5])
+    suf = make_batch(cache, [6], [256], [prompt[256:]], dims=dims)
+    h6 = forward(model, suf, cache, dims)
+    lg6, _ = head(model, h6, torch.arange(64, dtype=torch.int32, device="cuda"), dims)
+    assert same_bits(h6, h_full[256:])
+    assert same_bits(lg6, lg_full[256:])
+    cache.pages[6] = cache.pages[6][16:]      # the shared prefix pages stay with request 5
+    for sid in (0, 5, 6):
+        cache.release(sid)
