@@ -238,7 +238,10 @@ def model_bench(torch, bi):
         return time.perf_counter() - t
 
     timed([prompt], 2)
-    weight_bytes = sum(t.numel() * t.element_size() for t in _tensors(model))
+    # bytes a decode step reads: every weight except the gate-then-up copy of the MLP rows
+    # (decoding reads their interleaved copy)
+    weight_bytes = sum(t.numel() * t.element_size() for t in _tensors(model)) - sum(
+        w["wgate_up"].numel() * 2 for w in model["layers"])
     out_layer = layer_bench(torch, model, dims)
     out = {"workload": "Mistral-7B-shaped 32-layer greedy decode, random bf16 weights",
            "weight_bytes": weight_bytes, "decoder_layer_decode": out_layer}
@@ -265,7 +268,7 @@ def layer_bench(torch, model, dims):
     layer = model["layers"][0]
     ctx = synth.ragged_lengths(256, 0, 4096, 3, 2)
     cache = PagedKVCache(dims, n_pages=int(ctx.sum()) // 16 + 2 * 256 + 16, seed=3, n_layers=1)
-    lw_bytes = sum(t.numel() * t.element_size() for t in _tensors(layer))
+    lw_bytes = sum(t.numel() * t.element_size() for t in _tensors(layer)) - layer["wgate_up"].numel() * 2
     for B in (1, 8, 64, 256):
         sids = list(range(B))
         batch = make_batch(cache, sids, [int(c) for c in ctx[:B]],

@@ -275,6 +275,21 @@ int bi_rope_qkv(const void* qkv, int64_t ldqkv, int qkv_dtype, const int32_t* po
  *   gu [T, 2F] bf16 (row stride ldgu, a multiple of 8), out [T, F] bf16. */
 int bi_swiglu(const void* gu, int64_t ldgu, void* out, int64_t T, int64_t F, void* stream);
 
+/* bi_gemm_swiglu: the gate/up projection and bi_swiglu in one call (the fusion of
+ *   pointwise work into the producing kernel that "Defeating nondeterminism in LLM
+ *   inference" allows because pointwise operations are batch-invariant): out[M, F] =
+ *   swiglu(A . W^T) where W [2F, K] bf16 holds the gate and up rows interleaved in blocks
+ *   of 16 (rows 32 b .. 32 b + 15 = gate rows 16 b .., rows 32 b + 16 .. = up rows 16 b ..).
+ *   Each gate and up value is the bi_gemm element (same instruction sequence) rounded to
+ *   bf16, and the pair goes through bi_swiglu's arithmetic, so out equals
+ *   bi_swiglu(bi_gemm(A, W_gate_up)) bit for bit without writing the [M, 2F] intermediate.
+ *   A [M, K] bf16 (row stride lda), W row stride ldw, out row stride ldo (bf16).
+ *   Errors: BI_ERR_NULL, BI_ERR_SHAPE (F not a multiple of 16, strides too small),
+ *   BI_ERR_ALIGN (16-byte pointers, lda and ldw multiples of 8), BI_ERR_UNSUPPORTED
+ *   (A or W spanning 4 GiB or more: use bi_gemm and bi_swiglu). */
+int bi_gemm_swiglu(const void* A, const void* W, void* out, int64_t M, int64_t F, int64_t K,
+                   int64_t lda, int64_t ldw, int64_t ldo, void* stream);
+
 /* bi_residual_add: out = a + b elementwise over n elements, each operand of its own
  *   dtype (BI_BF16 | BI_F32); out may alias a or b. */
 int bi_residual_add(const void* a, int a_dtype, const void* b, int b_dtype, void* out,

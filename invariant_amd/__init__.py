@@ -40,6 +40,7 @@ _SIGS = {
     "bi_embedding": (_c.c_int, [_P, _P, _c.c_int, _P, _I64, _I64, _I64, _c.c_int, _P]),
     "bi_rope_qkv": (_c.c_int, [_P, _I64, _c.c_int, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F64, _P]),
     "bi_swiglu": (_c.c_int, [_P, _I64, _P, _I64, _I64, _P]),
+    "bi_gemm_swiglu": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
     "bi_residual_add": (_c.c_int, [_P, _c.c_int, _P, _c.c_int, _P, _c.c_int, _I64, _P]),
 }
 EXPORTS = tuple(_SIGS)
@@ -251,6 +252,23 @@ def bi_swiglu(gu, out=None):
     if out is None:
         out = torch.empty((T, F), dtype=torch.bfloat16, device=gu.device)
     _check("bi_swiglu", load().bi_swiglu(_ptr(gu), _ld(gu), _ptr(out), T, F, _stream(gu)))
+    return out
+
+
+def interleave_gate_up(w):
+    """[2F, K] gate-then-up weight -> the 16-row interleave bi_gemm_swiglu takes."""
+    F2, K = w.shape
+    return w.view(2, F2 // 32, 16, K).permute(1, 0, 2, 3).reshape(F2, K).contiguous()
+
+
+def bi_gemm_swiglu(a, w_interleaved, out=None):
+    """swiglu(a @ W^T) with W given as interleave_gate_up(W) (out [M, F] bf16)."""
+    M, K = a.shape
+    F = w_interleaved.shape[0] // 2
+    if out is None:
+        out = torch.empty((M, F), dtype=torch.bfloat16, device=a.device)
+    _check("bi_gemm_swiglu", load().bi_gemm_swiglu(_ptr(a), _ptr(w_interleaved), _ptr(out), M, F, K,
+                                                    _ld(a), _ld(w_interleaved), _ld(out), _stream(a)))
     return out
 
 

@@ -35,6 +35,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// SwiGLU of one bf16 (gate, up) pair: silu(g) u in fp32 (silu(g) = g / (1 + 2^(-g log2 e)),
+// hardware exp2, correctly rounded division), one RNE rounding.  The stand-alone kernel and
+// the GEMM epilogue both call this, so fused and unfused outputs share every bit.
+__device__ __forceinline__ uint16_t swiglu_bf16(uint16_t gb, uint16_t ub) {
+  const float g = bf16_to_f32(gb);
+  const float u = bf16_to_f32(ub);
+  const float e = __builtin_amdgcn_exp2f(-g * 1.44269502f);
+  const float silu = g / (1.0f + e);
+  return f32_to_bf16(silu * u);
+}
+
 __device__ __forceinline__ float wave_xor(float v, int off) { return __shfl_xor(v, off, kWave); }
 
 // Butterfly over the 64 lanes with offsets 1, 2, 4, 8, 16, 32.  fp32 addition is

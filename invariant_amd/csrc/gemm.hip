@@ -35,6 +35,9 @@ namespace bi {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 64;
+// Output modes of the kernels' c_f32 argument: bf16 C, fp32 C, or SwiGLU of column pairs
+// (bf16, half the columns; only the LDS-staged and few-row kernels implement it).
+constexpr int kOutBF16 = 0, kOutF32 = 1, kOutSwiGLU = 2;
 constexpr int kThreads = 256;
 constexpr int LDS_LD = BK + 8;  // bf16 per LDS row: 144 bytes keeps 16-byte reads conflict-free
 
@@ -615,7 +618,7 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
 
   // epilogue: register r of block (i, j) is row 8 (r / 4) + 4 (lane / 32) + r % 4 and
   // column lane % 32 of that block
-  if (!c_f32) {
+  if (c_f32 != kOutF32) {
     // bf16 output goes through LDS: each wave rounds its WM x WN sub-tile into its own
     // region (16-byte chunk c of row r at position c ^ (r % CW)), then reads it back as
     // 16-byte row pieces, so a store instruction writes whole sub-tile row segments
@@ -636,6 +639,34 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
         }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the region is this wave's own
     const bool vec = ((reinterpret_cast<uintptr_t>(C) | static_cast<uintptr_t>(ldc * 2)) & 15) == 0;
+    if (c_f32 == kOutSwiGLU) {
+      // each 32-column block holds 16 gate then 16 up columns; output chunk q of block b
+      // (8 columns) pairs staged chunks 4 b + q and 4 b + 2 + q
+      constexpr int OC = WN / 16, ORW = 64 / OC;   // output chunks per row, rows per pass
+      const int oc = lane % OC;
+      const int cg = 4 * (oc >> 1) + (oc & 1), cu = cg + 2;
+      const int ocol = (tn * T::TN + wn * WN) / 2 + oc * 8;
+      uint16_t* const Ob = static_cast<uint16_t*>(C);
+#pragma unroll
+      for (int it = 0; it < WM / ORW; ++it) {
+        const int rw = it * ORW + lane / OC;
+        const u16x8 g = *reinterpret_cast<const u16x8*>(st + rw * WN + ((cg ^ (rw % CW)) << 3));
+        const u16x8 u = *reinterpret_cast<const u16x8*>(st + rw * WN + ((cu ^ (rw % CW)) << 3));
+        const int row = tm * T::TM + wm * WM + rw;
+        if (row >= M || 2 * ocol >= N) continue;
+        u16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = swiglu_bf16(g[e], u[e]);
+        uint16_t* const dst = Ob + static_cast<int64_t>(row) * ldc + ocol;
+        if (vec) {
+          *reinterpret_cast<u16x8*>(dst) = o;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dst[e] = o[e];
+        }
+      }
+      return;
+    }
     const int cc = lane % CW;
     const int col = tn * T::TN + wn * WN + cc * 8;
     uint16_t* const Cb = static_cast<uint16_t*>(C);
@@ -759,6 +790,22 @@ __global__ __launch_bounds__(64) void gemm_rows_kernel(
   for (int p = 0; p < PF; ++p)
     if (t0 + PF + p < nsteps) mma(p);
   // register r of row block rb is row 32 rb + 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
+  if (c_f32 == kOutSwiGLU) {
+    // 16 gate then 16 up columns per block: lane l < 16 (of each half) pairs with lane l + 16
+    const bool gate = (lane & 31) < 16;
+    const int ocol = col0 / 2 + (lane & 15);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint16_t v = f32_to_bf16(acc[rb][r]);
+        const uint16_t u = static_cast<uint16_t>(__shfl(static_cast<int>(v), (lane + 16) & 63, 64));
+        const int row = row0 + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (gate && row < M)   // (N is a multiple of 32: every block lies inside N)
+          static_cast<uint16_t*>(C)[static_cast<int64_t>(row) * ldc + ocol] = swiglu_bf16(v, u);
+      }
+    return;
+  }
   const int col = col0 + (lane & 31);
   if (col >= N) return;
 #pragma unroll
@@ -830,10 +877,27 @@ int splitk_count(int64_t M, int64_t N, int64_t K) {
   return static_cast<int>(s);
 }
 
+// bf16 A and B, both under 4 GiB: the few-row kernel or the LDS-staged tiles by grid size.
+void launch_bf16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                 int64_t lda, int64_t ldb, int64_t ldc, int mode, hipStream_t s) {
+  if (use_rows(M, N, K, cu_count())) {
+    launch_rows(A, B, C, M, N, K, lda, ldb, ldc, mode, s);
+    return;
+  }
+  switch (pick_tile(M, N, cu_count())) {
+    case TileKind::k256: launch_dma<Tile256>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
+    case TileKind::k128deep: launch_dma<Tile128Deep>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
+    case TileKind::k64x128: launch_dma<Tile64x128>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
+    case TileKind::k64: launch_dma<Tile64>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
+    default: launch_dma<Tile128>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
+  }
+}
+
 }  // namespace
 }  // namespace bi
 
 using namespace bi;
+
 
 extern "C" int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                        int64_t lda, int64_t ldb, int64_t ldc, int b_layout, int a_dtype,
@@ -859,19 +923,8 @@ extern "C" int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t
     gemm_kernel<true><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
         A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
         0, int(K), 0);
-  else if (M * lda * 2 < (int64_t(1) << 32) && N * ldb * 2 < (int64_t(1) << 32)) {
-    if (use_rows(M, N, K, cu_count())) {
-      launch_rows(A, B, C, M, N, K, lda, ldb, ldc, cf, s);
-      return launch_status();
-    }
-    switch (pick_tile(M, N, cu_count())) {
-      case TileKind::k256: launch_dma<Tile256>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
-      case TileKind::k128deep: launch_dma<Tile128Deep>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
-      case TileKind::k64x128: launch_dma<Tile64x128>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
-      case TileKind::k64: launch_dma<Tile64>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
-      default: launch_dma<Tile128>(A, B, C, M, N, K, lda, ldb, ldc, cf, s); break;
-    }
-  }
+  else if (M * lda * 2 < (int64_t(1) << 32) && N * ldb * 2 < (int64_t(1) << 32))
+    launch_bf16(A, B, C, M, N, K, lda, ldb, ldc, cf, s);
   else  // operands of 4 GiB or more: register-staged kernel (same tile, instruction, K order)
     gemm_kernel<false><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
         A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
@@ -937,5 +990,20 @@ extern "C" int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, 
   const int64_t total = M * N;
   splitk_reduce_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(
       static_cast<const float*>(workspace), C, int(M), int(N), ldc, c_dtype == BI_F32, splits);
+  return launch_status();
+}
+
+extern "C" int bi_gemm_swiglu(const void* A, const void* W, void* out, int64_t M, int64_t F, int64_t K,
+                              int64_t lda, int64_t ldw, int64_t ldo, void* stream) {
+  if (M < 0 || F < 0 || K < 0) return BI_ERR_SHAPE;
+  if (M == 0 || F == 0) return BI_OK;
+  if (K < 1 || F % 16 != 0 || lda < K || ldw < K || ldo < F || M > (1 << 30) || F > (1 << 29) ||
+      K > (1 << 30))
+    return BI_ERR_SHAPE;
+  if (!A || !W || !out) return BI_ERR_NULL;
+  if (!aligned16(A) || !aligned16(W) || (lda % 8) || (ldw % 8)) return BI_ERR_ALIGN;
+  const int64_t N = 2 * F;
+  if (!(M * lda * 2 < (int64_t(1) << 32) && N * ldw * 2 < (int64_t(1) << 32))) return BI_ERR_UNSUPPORTED;
+  launch_bf16(A, W, out, M, N, K, lda, ldw, ldo, kOutSwiGLU, as_stream(stream));
   return launch_status();
 }

@@ -67,11 +67,7 @@ __global__ void swiglu_kernel(const uint16_t* __restrict__ gu, int64_t ld, uint1
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= T * F) return;
   const int64_t t = i / F, j = i % F;
-  const float g = bf16_to_f32(gu[t * ld + j]);
-  const float u = bf16_to_f32(gu[t * ld + F + j]);
-  const float e = __builtin_amdgcn_exp2f(-g * 1.44269502f);
-  const float silu = g / (1.0f + e);
-  out[i] = f32_to_bf16(silu * u);
+  out[i] = swiglu_bf16(gu[t * ld + j], gu[t * ld + F + j]);
 }
 
 __global__ void residual_add_kernel(const void* __restrict__ a, int af, const void* __restrict__ b,

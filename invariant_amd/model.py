@@ -29,7 +29,8 @@ import numpy as np
 import torch
 
 from . import (bi_attention, bi_attention_workspace_bytes, bi_embedding, bi_gemm,
-               bi_logsoftmax_argmax, bi_residual_add, bi_rmsnorm, bi_rope_qkv, bi_swiglu)
+               bi_logsoftmax_argmax, bi_residual_add, bi_rmsnorm, bi_rope_qkv, bi_swiglu,
+               bi_gemm_swiglu, interleave_gate_up)
 
 BF16, F32 = torch.bfloat16, torch.float32
 
@@ -60,7 +61,7 @@ def _normal(shape, mean, sd, gen, device):
 def random_layer(dims: Dims, gen, device="cuda", sd=0.02):
     d, hd = dims.hidden, dims.head_dim
     qkv = (dims.n_q_heads + 2 * dims.n_kv_heads) * hd
-    return dict(
+    w = dict(
         attn_norm=_normal((d,), 1.0, 0.02, gen, device),
         wqkv=_normal((qkv, d), 0.0, sd, gen, device),
         wo=_normal((d, dims.n_q_heads * hd), 0.0, sd, gen, device),
@@ -68,6 +69,10 @@ def random_layer(dims: Dims, gen, device="cuda", sd=0.02):
         wgate_up=_normal((2 * dims.ffn, d), 0.0, sd, gen, device),
         wdown=_normal((d, dims.ffn), 0.0, sd, gen, device),
     )
+    # the same gate/up rows interleaved in blocks of 16 for the fused GEMM + SwiGLU call
+    # (wgate_up keeps the gate-then-up order the reference computations read)
+    w["wgate_up_i"] = interleave_gate_up(w["wgate_up"])
+    return w
 
 
 def random_model(dims: Dims, seed: int, device="cuda", sd=0.02):
@@ -167,8 +172,10 @@ def decoder_layer(w, h, batch: Batch, k_cache, v_cache, dims: Dims, fp32_variant
     o = bi_gemm(a.view(T, dims.n_q_heads * dims.head_dim), w["wo"], out_dtype=act)
     h2 = bi_residual_add(h, o, out_dtype=act)
     x2 = bi_rmsnorm(h2, w["ffn_norm"], dims.eps, out_dtype=BF16)
-    gu = bi_gemm(x2, w["wgate_up"])
-    m = bi_swiglu(gu)
+    if "wgate_up_i" in w:   # fused: == bi_swiglu(bi_gemm(x2, wgate_up)) bit for bit
+        m = bi_gemm_swiglu(x2, w["wgate_up_i"])
+    else:
+        m = bi_swiglu(bi_gemm(x2, w["wgate_up"]))
     dn = bi_gemm(m, w["wdown"])
     return bi_residual_add(h2, dn, out_dtype=act)
 

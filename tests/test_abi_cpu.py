@@ -60,6 +60,12 @@ def test_validation_rejects_before_launch(lib):
     assert lib.bi_gemm(ctypes.c_void_p(18), P, P, 4, 4, 8, 8, 8, 4, 1, 1, 1, None) == -4
     assert lib.bi_gemm(P, P, P, 4, 4, 8, 9, 8, 4, 1, 1, 1, None) == -4
     assert lib.bi_gemm(None, P, P, 4, 4, 8, 8, 8, 4, 1, 1, 1, None) == -1
+    # fused gate/up + SwiGLU: F must be a multiple of 16; null and misaligned operands
+    assert lib.bi_gemm_swiglu(P, P, P, 4, 24, 64, 64, 64, 24, None) == -2
+    assert lib.bi_gemm_swiglu(P, P, P, 4, 32, 64, 60, 64, 32, None) == -2
+    assert lib.bi_gemm_swiglu(None, P, P, 4, 32, 64, 64, 64, 32, None) == -1
+    assert lib.bi_gemm_swiglu(P, ctypes.c_void_p(18), P, 4, 32, 64, 64, 64, 32, None) == -4
+    assert lib.bi_gemm_swiglu(None, None, None, 0, 32, 64, 64, 64, 32, None) == 0
     assert lib.bi_logsoftmax_argmax(P, 2, 10, 8, None, P, None) == -2
     assert lib.bi_logsoftmax_argmax(None, 2, 10, 12, None, P, None) == -1
     # attention: unsupported head_dim, group, page size; missing workspace

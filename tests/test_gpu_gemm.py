@@ -243,3 +243,23 @@ def test_few_rows_match_large_m(lib, n, k):
         assert same_bits(lib.bi_gemm(A[:m], W, out_dtype=torch.float32), ff[:m]), (n, k, m)
     rows = torch.tensor([300, 5, 511], device="cuda")
     assert same_bits(lib.bi_gemm(A[rows].contiguous(), W), full[rows])
+
+
+@pytest.mark.parametrize("f,k", [(14336, 4096), (3008, 1000), (48, 512)])
+def test_gemm_swiglu_equals_unfused(lib, f, k):
+    # bi_gemm_swiglu with the 16-row interleaved weight == bi_swiglu(bi_gemm(., gate-then-up
+    # weight)) bit for bit, for row counts that select every GEMM configuration
+    from invariant_amd import interleave_gate_up
+    say("gemm + swiglu fused", f, k)
+    a, b = gemm_inputs(3000, 2 * f, k, cfg=45, sd=0.5)
+    A, W = bf16(a), bf16(_nk(b))
+    Wi = interleave_gate_up(W)
+    for m in (1, 17, 33, 64, 65, 255, 500, 1000, 3000):
+        fused = lib.bi_gemm_swiglu(A[:m], Wi)
+        ref = lib.bi_swiglu(lib.bi_gemm(A[:m], W))
+        assert same_bits(fused, ref), (f, k, m, lib.bi_gemm_tile(m, 2 * f, k))
+    # row-strided, unaligned output view; nothing outside it changes
+    big = torch.full((300, f + 5), -3.0, dtype=torch.bfloat16, device="cuda")
+    lib.bi_gemm_swiglu(A[:300], Wi, out=big[:, 1:f + 1])
+    assert same_bits(big[:, 1:f + 1].contiguous(), lib.bi_swiglu(lib.bi_gemm(A[:300], W)))
+    assert bool((big[:, 0] == -3.0).all()) and bool((big[:, f + 1:] == -3.0).all())
