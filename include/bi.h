@@ -295,6 +295,17 @@ int bi_gemm_swiglu(const void* A, const void* W, void* out, int64_t M, int64_t F
 int bi_residual_add(const void* a, int a_dtype, const void* b, int b_dtype, void* out,
                     int out_dtype, int64_t n, void* stream);
 
+/* bi_add_rmsnorm: the residual add and the RMSNorm after it in one pass over M contiguous
+ *   rows of D (pointwise work fused into the producing kernel, which keeps batch invariance):
+ *   sum = a + b (fp32 add, rounded to dtype, exactly bi_residual_add) and
+ *   y = rmsnorm(sum, gamma, eps) from the rounded sum with bi_rmsnorm's tree for that dtype,
+ *   so both outputs equal the two calls bit for bit.  a, b, sum of dtype (BI_BF16 | BI_F32);
+ *   sum may alias a or b; y of y_dtype; gamma bf16 [D].
+ *   Errors: BI_ERR_DTYPE, BI_ERR_SHAPE, BI_ERR_NULL, BI_ERR_UNSUPPORTED (D not a multiple of
+ *   8 or above 8192: use the two calls), BI_ERR_ALIGN (a, b, sum, y not 16-byte aligned). */
+int bi_add_rmsnorm(const void* a, const void* b, void* sum, int dtype, const void* gamma, void* y,
+                   int y_dtype, int64_t M, int64_t D, float eps, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,6 +41,7 @@ _SIGS = {
     "bi_rope_qkv": (_c.c_int, [_P, _I64, _c.c_int, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F64, _P]),
     "bi_swiglu": (_c.c_int, [_P, _I64, _P, _I64, _I64, _P]),
     "bi_gemm_swiglu": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
+    "bi_add_rmsnorm": (_c.c_int, [_P, _P, _P, _c.c_int, _P, _P, _c.c_int, _I64, _I64, _c.c_float, _P]),
     "bi_residual_add": (_c.c_int, [_P, _c.c_int, _P, _c.c_int, _P, _c.c_int, _I64, _P]),
 }
 EXPORTS = tuple(_SIGS)
@@ -278,3 +279,20 @@ def bi_residual_add(a, b, out=None, out_dtype=None):
     _check("bi_residual_add", load().bi_residual_add(_ptr(a), _code(a.dtype), _ptr(b), _code(b.dtype),
                                                       _ptr(out), _code(out.dtype), a.numel(), _stream(a)))
     return out
+
+
+def bi_add_rmsnorm(a, b, gamma, eps: float, sum_out=None, out=None, out_dtype=torch.bfloat16):
+    """(a + b, rmsnorm(a + b)) in one pass; a and b [M, D] contiguous of one dtype."""
+    M, D = a.shape
+    if sum_out is None:
+        sum_out = torch.empty_like(a)
+    if out is None:
+        out = torch.empty((M, D), dtype=out_dtype, device=a.device)
+    for t in (a, b, sum_out, out):
+        if t.shape != (M, D) or not t.is_contiguous():
+            raise ValueError("bi_add_rmsnorm: operands must be contiguous [M, D]")
+    if b.dtype != a.dtype or sum_out.dtype != a.dtype:
+        raise ValueError("bi_add_rmsnorm: a, b and the sum share one dtype")
+    _check("bi_add_rmsnorm", load().bi_add_rmsnorm(_ptr(a), _ptr(b), _ptr(sum_out), _code(a.dtype), _ptr(gamma),
+                                                    _ptr(out), _code(out.dtype), M, D, float(eps), _stream(a)))
+    return sum_out, out

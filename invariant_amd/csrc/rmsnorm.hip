@@ -166,6 +166,108 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restric
   }
 }
 
+// Residual add fused with the RMSNorm that follows it: s = a + b (fp32 add, rounded to the
+// dtype of s, as bi_residual_add), written out, and y = rmsnorm(s) from those rounded values
+// with the tree above (w = the vector width of s's dtype).  Both outputs equal the two calls'
+// bits.  Rows are contiguous, 16-byte aligned, D a multiple of 8 and at most 8192: each lane
+// holds its vectors in registers.  Every lane loads all of its a and b elements before it
+// stores any element of s, and touches only its own elements, so s may be a or b itself.
+template <bool F32, bool YF32>
+__global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(const void* a, const void* b, void* sum,
+                                                               const uint16_t* __restrict__ gamma,
+                                                               void* __restrict__ y, int D, float eps) {
+  constexpr int W = F32 ? 4 : 8;              // elements per 16-byte vector of a, b and s
+  constexpr int NV = F32 ? 8 : 4;             // vectors per lane: D <= 8192
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nvec = D / W;
+  const int T = nvec < kThreads ? nvec : kThreads;
+  float x[NV][W];
+  float acc = 0.f;
+  if (tid < T) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int v = tid + j * T;
+      if (v >= nvec) continue;
+      const int64_t e0 = row * D + static_cast<int64_t>(v) * W;
+      if constexpr (F32) {
+        const floatx4 qa = *reinterpret_cast<const floatx4*>(static_cast<const float*>(a) + e0);
+        const floatx4 qb = *reinterpret_cast<const floatx4*>(static_cast<const float*>(b) + e0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[j][i] = qa[i] + qb[i];
+      } else {
+        const u16x8 qa = *reinterpret_cast<const u16x8*>(static_cast<const uint16_t*>(a) + e0);
+        const u16x8 qb = *reinterpret_cast<const u16x8*>(static_cast<const uint16_t*>(b) + e0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[j][i] = bf16_to_f32(f32_to_bf16(bf16_to_f32(qa[i]) + bf16_to_f32(qb[i])));
+      }
+#pragma unroll
+      for (int i = 0; i < W; ++i) acc = acc + x[j][i] * x[j][i];
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {             // s: x holds it exactly in either dtype
+      const int v = tid + j * T;
+      if (v >= nvec) continue;
+      const int64_t e0 = row * D + static_cast<int64_t>(v) * W;
+      if constexpr (F32) {
+        floatx4 q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = x[j][i];
+        *reinterpret_cast<floatx4*>(static_cast<float*>(sum) + e0) = q;
+      } else {
+        u16x8 q;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = f32_to_bf16(x[j][i]);
+        *reinterpret_cast<u16x8*>(static_cast<uint16_t*>(sum) + e0) = q;
+      }
+    }
+  }
+  __shared__ float wave_part[kThreads / kWave];
+  const float wsum = wave_tree_sum(acc);
+  if ((tid & (kWave - 1)) == 0) wave_part[tid / kWave] = wsum;
+  __syncthreads();
+  const float ssum = (wave_part[0] + wave_part[1]) + (wave_part[2] + wave_part[3]);
+  const float mean = ssum / static_cast<float>(D);
+  const float var = mean + eps;
+  const float r = 1.0f / __builtin_sqrtf(var);
+  if (tid >= T) return;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = tid + j * T;
+    if (v >= nvec) continue;
+    const int64_t e0 = row * D + static_cast<int64_t>(v) * W;
+    float g[W];
+#pragma unroll
+    for (int i = 0; i < W; i += 4) {            // gamma is 16-byte aligned: W elements from v*W
+      const u16x4 q = *reinterpret_cast<const u16x4*>(gamma + static_cast<int64_t>(v) * W + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[i + e] = bf16_to_f32(q[e]);
+    }
+    float o[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) o[i] = (x[j][i] * r) * g[i];
+    if constexpr (YF32) {
+#pragma unroll
+      for (int i = 0; i < W; i += 4) {
+        floatx4 q;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = o[i + e];
+        *reinterpret_cast<floatx4*>(static_cast<float*>(y) + e0 + i) = q;
+      }
+    } else if constexpr (W == 8) {
+      u16x8 q;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = f32_to_bf16(o[i]);
+      *reinterpret_cast<u16x8*>(static_cast<uint16_t*>(y) + e0) = q;
+    } else {
+      u16x4 q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = f32_to_bf16(o[i]);
+      *reinterpret_cast<u16x4*>(static_cast<uint16_t*>(y) + e0) = q;
+    }
+  }
+}
+
 }  // namespace
 }  // namespace bi
 
@@ -201,5 +303,31 @@ extern "C" int bi_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, 
     rmsnorm_kernel<true, false, false><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, 0, vec_g);
   else
     rmsnorm_kernel<true, true, false><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(gamma), y, int(D), ldx, ldy, eps, vec_x, vec_y, vec_g);
+  return launch_status();
+}
+
+extern "C" int bi_add_rmsnorm(const void* a, const void* b, void* sum, int dtype, const void* gamma,
+                              void* y, int y_dtype, int64_t M, int64_t D, float eps, void* stream) {
+  if ((dtype != BI_BF16 && dtype != BI_F32) || (y_dtype != BI_BF16 && y_dtype != BI_F32))
+    return BI_ERR_DTYPE;
+  if (M < 0 || D < 0) return BI_ERR_SHAPE;
+  if (M == 0) return BI_OK;
+  if (D < 1 || M > 0x7fffffffLL) return BI_ERR_SHAPE;
+  if (!a || !b || !sum || !gamma || !y) return BI_ERR_NULL;
+  if (D % 8 != 0 || D > 4 * kThreads * 8) return BI_ERR_UNSUPPORTED;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(sum) || !aligned16(y) || !aligned16(gamma))
+    return BI_ERR_ALIGN;
+  const dim3 grid(static_cast<unsigned>(M)), block(kThreads);
+  hipStream_t s = as_stream(stream);
+  const uint16_t* g = static_cast<const uint16_t*>(gamma);
+  const int di = static_cast<int>(D);
+  if (dtype == BI_BF16 && y_dtype == BI_BF16)
+    add_rmsnorm_kernel<false, false><<<grid, block, 0, s>>>(a, b, sum, g, y, di, eps);
+  else if (dtype == BI_BF16)
+    add_rmsnorm_kernel<false, true><<<grid, block, 0, s>>>(a, b, sum, g, y, di, eps);
+  else if (y_dtype == BI_BF16)
+    add_rmsnorm_kernel<true, false><<<grid, block, 0, s>>>(a, b, sum, g, y, di, eps);
+  else
+    add_rmsnorm_kernel<true, true><<<grid, block, 0, s>>>(a, b, sum, g, y, di, eps);
   return launch_status();
 }

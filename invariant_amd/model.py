@@ -30,7 +30,7 @@ import torch
 
 from . import (bi_attention, bi_attention_workspace_bytes, bi_embedding, bi_gemm,
                bi_logsoftmax_argmax, bi_residual_add, bi_rmsnorm, bi_rope_qkv, bi_swiglu,
-               bi_gemm_swiglu, interleave_gate_up)
+               bi_gemm_swiglu, interleave_gate_up, bi_add_rmsnorm)
 
 BF16, F32 = torch.bfloat16, torch.float32
 
@@ -159,10 +159,21 @@ def make_batch(cache: PagedKVCache, sids, done, new_tokens, device="cuda", dims:
 
 
 # ------------------------------------------------------------------------- forward
-def decoder_layer(w, h, batch: Batch, k_cache, v_cache, dims: Dims, fp32_variant=False):
+def _fusable(h, o, dims: Dims):
+    """bi_add_rmsnorm takes contiguous rows of one dtype, D a multiple of 8 up to 8192."""
+    return dims.hidden % 8 == 0 and dims.hidden <= 8192 and o.dtype == h.dtype
+
+
+def decoder_layer(w, h, batch: Batch, k_cache, v_cache, dims: Dims, fp32_variant=False,
+                  x=None, next_norm=None):
+    """One layer on the residual stream h.  x, if given, is rmsnorm(h) with this layer's
+    attention norm (the previous layer computed it with its residual add).  With next_norm the
+    layer returns (h_out, rmsnorm(h_out) with next_norm), else h_out.  Every path gives the
+    same bits as the separate calls."""
     T = h.shape[0]
     act = F32 if fp32_variant else BF16
-    x = bi_rmsnorm(h, w["attn_norm"], dims.eps, out_dtype=act)
+    if x is None:
+        x = bi_rmsnorm(h, w["attn_norm"], dims.eps, out_dtype=act)
     qkv = bi_gemm(x, w["wqkv"], out_dtype=act)
     q, k, v = bi_rope_qkv(qkv, batch.positions, dims.n_q_heads, dims.n_kv_heads, dims.head_dim,
                           dims.rope_base)
@@ -170,21 +181,35 @@ def decoder_layer(w, h, batch: Batch, k_cache, v_cache, dims: Dims, fp32_variant
                      batch.max_seq_len, 1.0 / float(np.sqrt(dims.head_dim)), out_dtype=act,
                      workspace=batch.workspace)
     o = bi_gemm(a.view(T, dims.n_q_heads * dims.head_dim), w["wo"], out_dtype=act)
-    h2 = bi_residual_add(h, o, out_dtype=act)
-    x2 = bi_rmsnorm(h2, w["ffn_norm"], dims.eps, out_dtype=BF16)
+    if _fusable(h, o, dims):
+        h2, x2 = bi_add_rmsnorm(h, o, w["ffn_norm"], dims.eps, out_dtype=BF16)
+    else:
+        h2 = bi_residual_add(h, o, out_dtype=act)
+        x2 = bi_rmsnorm(h2, w["ffn_norm"], dims.eps, out_dtype=BF16)
     if "wgate_up_i" in w:   # fused: == bi_swiglu(bi_gemm(x2, wgate_up)) bit for bit
         m = bi_gemm_swiglu(x2, w["wgate_up_i"])
     else:
         m = bi_swiglu(bi_gemm(x2, w["wgate_up"]))
     dn = bi_gemm(m, w["wdown"])
-    return bi_residual_add(h2, dn, out_dtype=act)
+    if next_norm is None:
+        return bi_residual_add(h2, dn, out_dtype=act)
+    if _fusable(h2, dn, dims):
+        return bi_add_rmsnorm(h2, dn, next_norm, dims.eps, out_dtype=act)
+    h3 = bi_residual_add(h2, dn, out_dtype=act)
+    return h3, bi_rmsnorm(h3, next_norm, dims.eps, out_dtype=act)
 
 
 def forward(model, batch: Batch, cache: PagedKVCache, dims: Dims, fp32_variant=False):
     act = F32 if fp32_variant else BF16
     h = bi_embedding(batch.tokens, model["embed"], out_dtype=act)
-    for li, w in enumerate(model["layers"]):
-        h = decoder_layer(w, h, batch, cache.k[li], cache.v[li], dims, fp32_variant)
+    layers = model["layers"]
+    x = None
+    for li, w in enumerate(layers):
+        if li + 1 < len(layers):   # the next layer's attention norm rides on this residual add
+            h, x = decoder_layer(w, h, batch, cache.k[li], cache.v[li], dims, fp32_variant,
+                                 x=x, next_norm=layers[li + 1]["attn_norm"])
+        else:
+            h = decoder_layer(w, h, batch, cache.k[li], cache.v[li], dims, fp32_variant, x=x)
     return h
 
 

@@ -66,6 +66,12 @@ def test_validation_rejects_before_launch(lib):
     assert lib.bi_gemm_swiglu(None, P, P, 4, 32, 64, 64, 64, 32, None) == -1
     assert lib.bi_gemm_swiglu(P, ctypes.c_void_p(18), P, 4, 32, 64, 64, 64, 32, None) == -4
     assert lib.bi_gemm_swiglu(None, None, None, 0, 32, 64, 64, 64, 32, None) == 0
+    # fused residual add + RMSNorm: dtype, D a multiple of 8 up to 8192, null operands
+    assert lib.bi_add_rmsnorm(P, P, P, 3, P, P, 1, 4, 64, 1e-5, None) == -3
+    assert lib.bi_add_rmsnorm(P, P, P, 1, P, P, 1, 4, 60, 1e-5, None) == -6
+    assert lib.bi_add_rmsnorm(P, P, P, 1, P, P, 1, 4, 8200, 1e-5, None) == -6
+    assert lib.bi_add_rmsnorm(P, None, P, 1, P, P, 1, 4, 64, 1e-5, None) == -1
+    assert lib.bi_add_rmsnorm(P, P, P, 1, P, P, 1, -1, 64, 1e-5, None) == -2
     assert lib.bi_logsoftmax_argmax(P, 2, 10, 8, None, P, None) == -2
     assert lib.bi_logsoftmax_argmax(None, 2, 10, 12, None, P, None) == -1
     # attention: unsupported head_dim, group, page size; missing workspace

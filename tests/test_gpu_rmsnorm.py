@@ -97,3 +97,23 @@ def test_repeat_determinism(lib):
     ref = lib.bi_rmsnorm(X, G, 1e-5)
     for _ in range(200):
         assert same_bits(lib.bi_rmsnorm(X, G, 1e-5), ref)
+
+
+@pytest.mark.parametrize("dtype,ydtype", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float32),
+                                          (torch.float32, torch.bfloat16), (torch.bfloat16, torch.float32)])
+def test_add_rmsnorm_equals_two_calls(lib, dtype, ydtype):
+    # bi_add_rmsnorm == bi_residual_add then bi_rmsnorm, both outputs bit for bit, including
+    # the sum written over one of its inputs
+    rng = np.random.default_rng(11)
+    for m, d in [(1, 4096), (7, 512), (300, 4096), (3, 8192), (5, 1032)]:
+        say("add + rmsnorm", m, d, dtype, ydtype)
+        a = torch.from_numpy(rng.standard_normal((m, d)).astype(np.float32)).cuda().to(dtype)
+        b = torch.from_numpy((rng.standard_normal((m, d)) * 0.3).astype(np.float32)).cuda().to(dtype)
+        g = bf16(normal_bf16((d,), 1.0, 0.02, 12, d))
+        s_ref = lib.bi_residual_add(a, b)
+        y_ref = lib.bi_rmsnorm(s_ref, g, 1e-5, out_dtype=ydtype)
+        s_got, y_got = lib.bi_add_rmsnorm(a, b, g, 1e-5, out_dtype=ydtype)
+        assert same_bits(s_got, s_ref) and same_bits(y_got, y_ref), (m, d)
+        a2 = a.clone()
+        s2, y2 = lib.bi_add_rmsnorm(a2, b, g, 1e-5, sum_out=a2, out_dtype=ydtype)
+        assert same_bits(s2, s_ref) and same_bits(y2, y_ref), (m, d)
