@@ -115,7 +115,8 @@ int bi_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t D, 
  *         stride ldb;  BI_B_KN: B is [K, N] (torch.mm orientation), row stride ldb
  *   C     dtype c_dtype (BI_BF16: one RNE rounding of the fp32 sum; BI_F32), stride ldc
  * Every output element is produced by the same sequence of matrix instructions
- * (v_mfma_f32_32x32x16_bf16, one fp32 accumulator from +0, K in ascending 16-wide steps)
+ * (v_mfma_f32_16x16x32_bf16, one fp32 accumulator from +0, K in ascending 32-wide steps,
+ * the k offsets of a step assigned to the instruction's lanes the same way every time)
  * whatever M is, wherever its row sits and whichever workgroup tile computes it; the
  * workgroup tile (bi_gemm_tile) follows the size of the output grid and changes no bit.
  * Alignment: A and B 16-byte aligned; lda, ldb multiples of 8 elements (4 for fp32 A).
@@ -131,10 +132,12 @@ int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
 
 /* The workgroup tile bi_gemm uses for an M x N x K product with A of dtype a_dtype on the
  * current device: *tile_m x *tile_n outputs per workgroup and *stages K slices in flight.
- * Up to 32 rows (up to 64 while ceil(N / 32) is at most twice the CU count), with K a
- * multiple of 16 and at least 512: 32 x 32 per wave (64 x 32 when 33..64 rows would need
- * more than one wave per CU as 32 x 32 blocks), the wave's instruction operands loaded
- * straight into registers 16 (or 12) K steps ahead.  Otherwise 256 x 256
+ * Up to 32 rows (up to 64 while ceil(N / 32) is at most the CU count), with K a multiple of
+ * 8 and at least 2 x (16 or 12) whole 32-wide steps: one wave per output block with its
+ * instruction operands loaded straight into registers 16 (or 12) K steps ahead; the block
+ * is 16 x 16 up to 16 rows (16 x 32 when N / 16 is at least four times the CU count),
+ * 32 x 32 above, with two waves per column block (one per 32-row half) above 32 rows.
+ * Otherwise 256 x 256
  * (2-stage LDS ring) when that grid finishes in fewer rounds of the CU array; else
  * 128 x 128, with a 3-stage ring when the grid has no more tiles than CUs and a 2-stage
  * ring (two workgroups per CU) otherwise; when fewer than three quarters of the CUs would

@@ -6,10 +6,10 @@
 // stream-K (it even loses batch-position invariance); use one kernel configuration, so
 // that no shape switches to another reduction order.  Here the configuration that fixes
 // the order is:
-//   one instruction, v_mfma_f32_32x32x16_bf16; fp32 accumulators starting at +0; K walked
-//   in ascending 16-wide steps from 0 to K, lane l of the instruction holding k offsets
-//   8 (l / 32) .. + 7 of each step.  Products past K are exact zeros; rows past M
-//   (columns past N) are never stored.
+//   one instruction, v_mfma_f32_16x16x32_bf16; fp32 accumulators starting at +0; K walked
+//   in ascending 32-wide steps from 0 to K, lane l of the instruction holding row (or
+//   column) l % 16 and k offsets 8 (l / 16) .. + 7 of each step.  Products past K are exact
+//   zeros; rows past M (columns past N) are never stored.
 // Output element (i, j) is therefore the result of the same instruction sequence for
 // every M, every position of row i inside its tile and every workgroup configuration; the
 // configuration only decides which wave computes which outputs, and the tests check the
@@ -20,15 +20,15 @@
 //   tiles stream into an LDS ring by direct-to-LDS 16-byte loads; the 16-byte k-chunks of
 //   row r sit at chunk position c ^ swz(r) so that the operand reads of consecutive rows hit
 //   distinct banks; bf16 results leave through LDS as 16-byte row pieces.
-//   Up to 64 rows: one wave per 32 (or 64) x 32 output block loads its operands straight into
-//   registers.
+//   Up to 64 rows: one wave per 16 (or 32) output columns and all rows loads its operands
+//   straight into registers.
 // The fp32-A path, operands of 4 GiB or more and the split-K comparison variant stage
 // through registers instead (128 x 128 tile); they share the instruction and the K order.
 //
 // A may be fp32 ("FP32 upcast" of the cross-vendor mismatch abstract): each value is
 // split exactly into bf16 hi + mid + lo (truncations, so hi + mid + lo == a for normal
 // numbers) and the three products are accumulated into the same fp32 accumulator in
-// the order hi, mid, lo for every 16-wide K step.
+// the order hi, mid, lo for every 32-wide K step.
 #include "bi_common.h"
 
 namespace bi {
@@ -156,13 +156,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
   };
 
-  floatx16 acc[2][2];
+  floatx4 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
   const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
   Stage<AF32> st;
@@ -172,47 +172,48 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   }
   __syncthreads();
 
-  // operand read coordinates: lane holds row (lane % 32) and k (lane / 32) * 8 .. +7
-  const int orow = lane & 31;
-  const int okk = (lane >> 5) * 8;
+  // operand read coordinates: lane holds row (lane % 16) of each 16-row block and k
+  // (lane / 16) * 8 .. +7 of each 32-wide step
+  const int orow = lane & 15;
+  const int okk = (lane >> 4) * 8;
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) load_stage(st, kb + (kt + 1) * BK);
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 bv[2];
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8 bv[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 4; ++j)
         bv[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(
-            &sB[cur][(wn * 64 + j * 32 + orow) * LDS_LD + kk + okk]));
+            &sB[cur][(wn * 64 + j * 16 + orow) * LDS_LD + kk + okk]));
 #pragma unroll
       for (int t = 0; t < NA; ++t) {
-        bf16x8 av[2];
+        bf16x8 av[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
           av[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(
-              &sA[cur][t][(wm * 64 + i * 32 + orow) * LDS_LD + kk + okk]));
+              &sA[cur][t][(wm * 64 + i * 16 + orow) * LDS_LD + kk + okk]));
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
       }
     }
     if (kt + 1 < nk) store_stage(st, cur ^ 1);
     __syncthreads();
   }
 
-  // epilogue: register r of block (i, j) is row 8(r/4) + 4(lane/32) + r%4, column lane%32
+  // epilogue: register r of block (i, j) is row 4 (lane / 16) + r, column lane % 16 of it
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = tn * BN + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 4; ++j) {
+      const int col = tn * BN + wn * 64 + j * 16 + (lane & 15);
       if (col >= N) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = tm * BM + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int row = tm * BM + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
         if (row >= M) continue;
         if (c_f32)
           static_cast<float*>(C)[static_cast<int64_t>(row) * ldc + col] = acc[i][j][r];
@@ -222,19 +223,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
 }
 
-#ifndef BI_GEMM_DBK
-#define BI_GEMM_DBK 64
-#endif
-constexpr int DBK = BI_GEMM_DBK;         // K depth of one LDS stage in the main kernel
-constexpr int KS = DBK / 16;             // 16-wide K steps per stage
+constexpr int DBK = 64;                  // K depth of one LDS stage in the main kernel
+constexpr int KS = DBK / 32;             // 32-wide K steps per stage (even: see inner_steps)
 constexpr int CPR = DBK / 8;             // 16-byte chunks per LDS row
 constexpr int RPI = 64 / CPR;            // tile rows filled by one 1 KB wave-wide load
-static_assert(DBK == 32 || DBK == 64, "the main loop takes an even number of 16-wide K steps");
+constexpr uint32_t kBlkBytes = 16 * DBK * 2;   // LDS bytes of one 16-row block of a stage
 
 // Workgroup tile: WAVES_M x WAVES_N waves, each wave BLK_M x BLK_N blocks of the one
-// 32 x 32 x 16 matrix instruction.  Every configuration computes each output element with
-// the same instruction sequence (one fp32 chain from +0 over ascending 16-wide K steps,
-// lane l holding k = 8 (l / 32) .. + 7 of each step), so they give identical bits; the tile
+// 16 x 16 x 32 matrix instruction.  Every configuration computes each output element with
+// the same instruction sequence (one fp32 chain from +0 over ascending 32-wide K steps,
+// lane l holding k = 8 (l / 16) .. + 7 of each step), so they give identical bits; the tile
 // only decides which workgroup computes which outputs.
 template <int WAVES_M_, int WAVES_N_, int BLK_M_, int BLK_N_, int STAGES_, int WAVES_PER_SIMD_ = 2,
           int DMA_WAVES_ = WAVES_M_ * WAVES_N_>
@@ -247,12 +245,15 @@ struct Tile {
   // multiply, so a wave held up issuing loads leaves its SIMD to one that is not
   static constexpr int DW = DMA_WAVES_;
   static constexpr int THREADS = NW * 64;
-  static constexpr int TM = WAVES_M * BLK_M * 32;
-  static constexpr int TN = WAVES_N * BLK_N * 32;
+  static constexpr int TM = WAVES_M * BLK_M * 16;
+  static constexpr int TN = WAVES_N * BLK_N * 16;
   static constexpr int NJA = TM / DW / RPI;  // A loads per issuing wave per stage
   static constexpr int NJB = TN / DW / RPI;  // B loads per issuing wave per stage
   static constexpr int PER = NJA + NJB;
   static constexpr int SA = TM * DBK, SB = TN * DBK;  // bf16 elements per stage
+  // operands of the next K step read in place (see advance) rather than into a second set
+  static constexpr bool INPLACE = BLK_M * BLK_N >= 32;
+  static constexpr bool OTF = INPLACE;   // load offsets computed per load (see DmaCtx)
   static_assert(TM % (DW * RPI) == 0 && TN % (DW * RPI) == 0 && DW <= NW, "tile rows per wave");
   static_assert(STAGES >= 2, "unsupported staging");
 };
@@ -260,24 +261,19 @@ struct Tile {
 // grids with no more tiles than CUs, 128 x 128 as 8 waves of 64 x 32 with a 3-stage ring
 // (96 KB, one workgroup but two waves per SIMD); 256 x 256, 8 waves of 128 x 64, 2-stage
 // ring (128 KB, one per CU).  With 8 waves, one wave per SIMD issues the stage loads.
-using Tile128 = Tile<2, 2, 2, 2, 2>;
-using Tile128Deep = Tile<2, 4, 2, 1, 3, 2, 4>;
+using Tile128 = Tile<2, 2, 4, 4, 2>;
+using Tile128Deep = Tile<2, 4, 4, 2, 3, 2, 4>;
 // Grids with well under one 128 x 128 tile per CU (a few hundred rows): 64 x 128 as 8 waves
 // of 32 x 32, or 64 x 64 as 4 waves of 32 x 32, both with a 3-stage ring.
-using Tile64x128 = Tile<2, 4, 1, 1, 3, 2, 4>;
-using Tile64 = Tile<2, 2, 1, 1, 3>;
-using Tile256 = Tile<2, 4, 4, 2, 2, 2, 4>;
+using Tile64x128 = Tile<2, 4, 2, 2, 3, 2, 4>;
+using Tile64 = Tile<2, 2, 2, 2, 3>;
+using Tile256 = Tile<2, 4, 8, 4, 2, 2, 4>;
 
-// Chunk c of LDS row r sits at position c ^ swz(r): the 16-byte reads of 8 (or 16)
-// consecutive rows at one chunk index then fall into distinct banks.
-#ifndef BI_GEMM_SWZ
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (CPR == 4) return ((r >> 1) ^ (r >> 3)) & 3;
-  else return ((r >> 1) ^ (r >> 4)) & 7;
-}
-#else
-__device__ __forceinline__ int swz(int r) { return BI_GEMM_SWZ; }
-#endif
+// Chunk c of LDS row r (128 bytes) sits at position c ^ swz(r), swz(r) = (r / 2) % 8: the
+// 16-byte reads of 16 consecutive rows at one chunk index (a quarter of the wave's lanes)
+// then cover all 64 banks once.  The pattern repeats every 16 rows, so a lane's offsets in
+// the 16-row blocks of a wave differ by multiples of kBlkBytes.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 // 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane, addressed as
 // a wave-uniform 64-bit base plus a per-lane 32-bit byte offset.  Written in asm so that
@@ -297,8 +293,8 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
 
 // Loads J .. N - 1 of one operand: load j lands 1024 j bytes past lds_base (added to m0
 // inside the asm, so one scalar register holds the base of the whole run).
-template <int J, int N>
-__device__ __forceinline__ void dma16_run(const void* base, const uint32_t* off, uint32_t lds_base) {
+template <int J, int N, class Off>
+__device__ __forceinline__ void dma16_run(const void* base, const Off& off, uint32_t lds_base) {
   if constexpr (J < N) {
     uint32_t saved;
     asm volatile(
@@ -307,7 +303,7 @@ __device__ __forceinline__ void dma16_run(const void* base, const uint32_t* off,
         "global_load_lds_dwordx4 %2, %3\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "s"(lds_base), "v"(off[J]), "s"(base), "n"(J * 1024)
+        : "s"(lds_base), "v"(off(J)), "s"(base), "n"(J * 1024)
         : "memory", "scc");
     dma16_run<J + 1, N>(base, off, lds_base);
   }
@@ -336,13 +332,55 @@ template <class T>
 struct DmaCtx {
   const uint16_t* A;
   const uint16_t* B;
-  uint32_t aoff[T::NJA], boff[T::NJB];   // per-lane byte offsets of this lane's chunks
-  int kca[T::NJA], kcb[T::NJB];          // k offset of each chunk inside a stage
+  // per-lane byte offsets of this lane's chunks, kept (small tiles) or, for the tile whose
+  // registers the accumulators fill, computed per load from the row of load 0 (load j is
+  // RPI j rows further, clamped to the last row) and the row pitch in bytes
+  uint32_t aoff[T::OTF ? 1 : T::NJA], boff[T::OTF ? 1 : T::NJB];
+  int ra_share, rb_share;   // first tile row of this wave's A and B share (wave-uniform)
+  int a_last, b_last;
+  uint32_t lda2, ldb2;
+  int kc[2];   // k offset inside a stage of this lane's chunk in loads j even / odd (A and B)
   uint32_t lds_a, lds_b;                 // LDS byte address of this wave's rows in stage 0
   int K, nk;
   bool ktail;
   bool issuer;                           // this wave issues loads (wave < T::DW)
 };
+
+// Per-load offsets, computed per load from the lane id.  They are loop-invariant, and the
+// compiler would compute them all once before the loop and keep (or spill) them, so the
+// lane id comes from an asm in every stage, which it cannot hoist.
+template <class T>
+struct LoadOffsets {
+  int ra0, rb0, kc0, kc1;   // row of load 0 (A, B); k offset of the chunk of loads j even / odd
+  __device__ __forceinline__ explicit LoadOffsets(const DmaCtx<T>& d) {
+    if constexpr (T::OTF) {
+      int l;   // the lane id, recomputed in every stage
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+      ra0 = d.ra_share + l / CPR;
+      rb0 = d.rb_share + l / CPR;
+      kc0 = ((l % CPR) ^ swz(l / CPR)) * 8;
+      kc1 = ((l % CPR) ^ swz(RPI + l / CPR)) * 8;
+    } else {
+      ra0 = rb0 = 0;
+      kc0 = d.kc[0];
+      kc1 = d.kc[1];
+    }
+  }
+};
+template <class T>
+__device__ __forceinline__ uint32_t a_off(const DmaCtx<T>& d, const LoadOffsets<T>& o, int j) {
+  if constexpr (T::OTF)
+    return static_cast<uint32_t>(min(o.ra0 + RPI * j, d.a_last)) * d.lda2 + 2 * ((j & 1) ? o.kc1 : o.kc0);
+  else
+    return d.aoff[j];
+}
+template <class T>
+__device__ __forceinline__ uint32_t b_off(const DmaCtx<T>& d, const LoadOffsets<T>& o, int j) {
+  if constexpr (T::OTF)
+    return static_cast<uint32_t>(min(o.rb0 + RPI * j, d.b_last)) * d.ldb2 + 2 * ((j & 1) ? o.kc1 : o.kc0);
+  else
+    return d.boff[j];
+}
 
 // Stage kt into ring buffer `buf` (a template constant in the steady loop, a run-time
 // value in the prologue and the tail, where it only moves the LDS base).
@@ -351,34 +389,46 @@ __device__ __forceinline__ void dma_stage_at(const DmaCtx<T>& d, uint32_t buf, i
   constexpr uint32_t sa_bytes = T::SA * 2, sb_bytes = T::SB * 2;
   const int k0 = kt * DBK;
   const uint32_t la = d.lds_a + buf * sa_bytes, lb = d.lds_b + buf * sb_bytes;
+  const LoadOffsets<T> lo(d);
   if (d.ktail && kt == d.nk - 1) {
     // last, partial step: a chunk wholly past K re-reads the first 8 elements of its row
     // (always inside the row; zeroed after landing)
 #pragma unroll
     for (int j = 0; j < T::NJA; ++j) {
-      const uint32_t adv = (k0 + d.kca[j] < d.K) ? static_cast<uint32_t>(k0) * 2
-                                                 : static_cast<uint32_t>(-2 * d.kca[j]);
-      dma16(d.A, d.aoff[j] + adv, la + j * 1024);
+      const int kc = (j & 1) ? lo.kc1 : lo.kc0;
+      const uint32_t adv = (k0 + kc < d.K) ? static_cast<uint32_t>(k0) * 2 : static_cast<uint32_t>(-2 * kc);
+      dma16(d.A, a_off<T>(d, lo, j) + adv, la + j * 1024);
     }
 #pragma unroll
     for (int j = 0; j < T::NJB; ++j) {
-      const uint32_t adv = (k0 + d.kcb[j] < d.K) ? static_cast<uint32_t>(k0) * 2
-                                                 : static_cast<uint32_t>(-2 * d.kcb[j]);
-      dma16(d.B, d.boff[j] + adv, lb + j * 1024);
+      const int kc = (j & 1) ? lo.kc1 : lo.kc0;
+      const uint32_t adv = (k0 + kc < d.K) ? static_cast<uint32_t>(k0) * 2 : static_cast<uint32_t>(-2 * kc);
+      dma16(d.B, b_off<T>(d, lo, j) + adv, lb + j * 1024);
     }
   } else {
-    dma16_run<0, T::NJA>(d.A + k0, d.aoff, la);
-    dma16_run<0, T::NJB>(d.B + k0, d.boff, lb);
+    dma16_run<0, T::NJA>(d.A + k0, [&](int j) { return a_off<T>(d, lo, j); }, la);
+    dma16_run<0, T::NJB>(d.B + k0, [&](int j) { return b_off<T>(d, lo, j); }, lb);
   }
 }
 
-template <class T>
+// Per-lane LDS byte offsets (from the start of the ring) of the wave's first A and first B
+// block in K step 0 of a stage; block i lies i kBlkBytes further.  Step 1 reads chunks 4..7
+// where step 0 reads 0..3, which under the swizzle is chunk position ^ 4, byte offset ^ 64
+// (computed at each use, through an empty asm, so that it takes no register of its own).
 struct Frag {
-  uint32_t ao[T::BLK_M][KS], bo[T::BLK_N][KS];   // per-lane LDS byte offsets
+  uint32_t a0, b0;
+  __device__ __forceinline__ static uint32_t step(uint32_t base, int ks) {
+    if (ks == 0) return base;
+    asm volatile("" : "+v"(base));
+    return base ^ 64u;
+  }
+  __device__ __forceinline__ uint32_t a(int ks) const { return step(a0, ks); }
+  __device__ __forceinline__ uint32_t b(int ks) const { return step(b0, ks); }
 };
 
-// Operands of one 16-wide K step: BLK_M A fragments and BLK_N B fragments, read from ring
-// buffer `buf` (a template constant in the steady loop becomes an immediate offset).
+// Operands of one 32-wide K step: BLK_M A fragments and BLK_N B fragments, read from ring
+// buffer `buf` (a template constant in the steady loop; with the block offsets it becomes
+// the reads' immediate offset).
 template <class T>
 struct Ops {
   bf16x8 a[T::BLK_M], b[T::BLK_N];
@@ -386,25 +436,25 @@ struct Ops {
 
 template <class T>
 __device__ __forceinline__ void load_ops(const uint16_t* sA, const uint16_t* sB, uint32_t buf, int ks,
-                                         const Frag<T>& f, Ops<T>& o) {
-  const char* a = reinterpret_cast<const char*>(sA) + buf * (T::SA * 2);
-  const char* b = reinterpret_cast<const char*>(sB) + buf * (T::SB * 2);
+                                         const Frag& f, Ops<T>& o) {
+  const char* a = reinterpret_cast<const char*>(sA) + f.a(ks) + buf * (T::SA * 2);
+  const char* b = reinterpret_cast<const char*>(sA) + f.b(ks) + buf * (T::SB * 2);
   // in the order the MFMAs consume them: A0, every B, then A1 .. (the first MFMAs can
   // start after 1 + BLK_N reads)
-  o.a[0] = as_bf16x8(*reinterpret_cast<const u16x8*>(a + f.ao[0][ks]));
+  o.a[0] = as_bf16x8(*reinterpret_cast<const u16x8*>(a));
 #pragma unroll
-  for (int j = 0; j < T::BLK_N; ++j) o.b[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(b + f.bo[j][ks]));
+  for (int j = 0; j < T::BLK_N; ++j) o.b[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(b + j * kBlkBytes));
 #pragma unroll
-  for (int i = 1; i < T::BLK_M; ++i) o.a[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(a + f.ao[i][ks]));
+  for (int i = 1; i < T::BLK_M; ++i) o.a[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(a + i * kBlkBytes));
 }
 
 template <class T>
-__device__ __forceinline__ void mfma_ops(const Ops<T>& o, floatx16 (&acc)[T::BLK_M][T::BLK_N]) {
+__device__ __forceinline__ void mfma_ops(const Ops<T>& o, floatx4 (&acc)[T::BLK_M][T::BLK_N]) {
 #pragma unroll
   for (int i = 0; i < T::BLK_M; ++i)
 #pragma unroll
     for (int j = 0; j < T::BLK_N; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
 }
 
 // Zero every element at k >= K of stage kt (in ring buffer buf) in the pieces this lane's
@@ -413,19 +463,20 @@ template <class T>
 __device__ __forceinline__ void zero_k_tail(const DmaCtx<T>& d, uint16_t* sA, uint16_t* sB, int buf,
                                             int kt, int wave, int lane) {
   const int k0 = kt * DBK;
+  const LoadOffsets<T> lo(d);
 #pragma unroll
   for (int j = 0; j < T::NJA; ++j) {
     const int pos = buf * T::SA + ((T::TM / T::DW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (k0 + d.kca[j] + e >= d.K) sA[pos + e] = 0;
+      if (k0 + ((j & 1) ? lo.kc1 : lo.kc0) + e >= d.K) sA[pos + e] = 0;
   }
 #pragma unroll
   for (int j = 0; j < T::NJB; ++j) {
     const int pos = buf * T::SB + ((T::TN / T::DW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (k0 + d.kcb[j] + e >= d.K) sB[pos + e] = 0;
+      if (k0 + ((j & 1) ? lo.kc1 : lo.kc0) + e >= d.K) sB[pos + e] = 0;
   }
 }
 
@@ -444,49 +495,90 @@ __device__ __forceinline__ void interleave() {
   if constexpr (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
 }
 
-// K steps 1 .. KS - 1 of a stage, each read before the previous step's MFMAs are issued
-// (o0 holds step 0 on entry; on return the operands of step KS - 1 are in o1 and every
-// earlier step has been multiplied).  KS is even, so step s lives in o0 for even s.
-template <class T>
-__device__ __forceinline__ void inner_steps(const uint16_t* sA, const uint16_t* sB, uint32_t buf,
-                                            const Frag<T>& f, Ops<T>& o0, Ops<T>& o1,
-                                            floatx16 (&acc)[T::BLK_M][T::BLK_N]) {
+// MFMAs of one 32-wide K step while the operands of the next step (ring buffer buf, step ks
+// of that stage) are read from LDS.
+//  - Two operand sets (o0 holds the even steps of a stage, o1 the odd ones): the next step's
+//    reads go to the other set, alternated with this step's MFMAs.
+//  - A in place (wave tiles whose two full sets would not fit beside the accumulators): B
+//    fragments alternate between o0 (even steps) and o1 (odd steps) as above and are read
+//    during the first BLK_N MFMAs; the A fragments live in o0, and next A fragment i
+//    replaces current A fragment i right after the BLK_N MFMAs that use it.
+template <class T, int PAR>
+__device__ __forceinline__ void advance(const uint16_t* sA, const uint16_t* sB, uint32_t buf, int ks,
+                                        const Frag& f, Ops<T>& o0, Ops<T>& o1,
+                                        floatx4 (&acc)[T::BLK_M][T::BLK_N]) {
+  if constexpr (T::INPLACE) {
+    // B: o0 holds the even steps' fragments, o1 the odd ones'; A: always o0, in place
+    const Ops<T>& cb = PAR == 0 ? o0 : o1;
+    Ops<T>& nbo = PAR == 0 ? o1 : o0;
+    const char* a = reinterpret_cast<const char*>(sA) + f.a(ks) + buf * (T::SA * 2);
+    const char* b = reinterpret_cast<const char*>(sA) + f.b(ks) + buf * (T::SB * 2);
 #pragma unroll
-  for (int ks = 1; ks < KS; ++ks) {
-    if (ks & 1) {
-      load_ops<T>(sA, sB, buf, ks, f, o1);
-      mfma_ops<T>(o0, acc);
-    } else {
-      load_ops<T>(sA, sB, buf, ks, f, o0);
-      mfma_ops<T>(o1, acc);
+    for (int j = 0; j < T::BLK_N; ++j) nbo.b[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(b + j * kBlkBytes));
+#pragma unroll
+    for (int i = 0; i < T::BLK_M; ++i) {
+#pragma unroll
+      for (int j = 0; j < T::BLK_N; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o0.a[i], cb.b[j], acc[i][j], 0, 0, 0);
+      o0.a[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(a + i * kBlkBytes));
     }
+#pragma unroll
+    for (int j = 0; j < T::BLK_N; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // B fragment j
+    }
+#pragma unroll
+    for (int i = 1; i < T::BLK_M; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // A fragment i - 1
+      __builtin_amdgcn_sched_group_barrier(0x008, T::BLK_N, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // A fragment BLK_M - 1
+  } else if constexpr (PAR == 0) {
+    load_ops<T>(sA, sB, buf, ks, f, o1);
+    mfma_ops<T>(o0, acc);
+    interleave<T>();
+  } else {
+    load_ops<T>(sA, sB, buf, ks, f, o0);
+    mfma_ops<T>(o1, acc);
     interleave<T>();
   }
 }
 
+// The last K step (an odd step): its operands are in o1 (A in o0 when read in place).
+template <class T>
+__device__ __forceinline__ void last_step(const Ops<T>& o0, const Ops<T>& o1,
+                                          floatx4 (&acc)[T::BLK_M][T::BLK_N]) {
+#pragma unroll
+  for (int i = 0; i < T::BLK_M; ++i)
+#pragma unroll
+    for (int j = 0; j < T::BLK_N; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T::INPLACE ? o0.a[i] : o1.a[i], o1.b[j],
+                                                           acc[i][j], 0, 0, 0);
+}
+
+static_assert(KS == 2, "a stage is two K steps: advance<0> inside it, advance<1> across stages");
+
 // One K step kt whose stage sits in ring buffer BUF, while every later stage up to
-// kt + T::STAGES - 1 is already issued: o0 holds the operands of its first 16-wide step.
-// The second step's operands are read before the first step's MFMAs are issued; once
-// every wave has them (and stage kt + 1 has landed), the buffer is refilled with stage
-// kt + T::STAGES and the next step's first operands are read while this step's second
-// MFMAs run.  The MFMA order per output element is unchanged: ascending K.
+// kt + T::STAGES - 1 is already issued: o0 holds the operands of its first 32-wide step.
+// The second step's operands are read while the first step's MFMAs run; once every wave
+// has them (and stage kt + 1 has landed), the buffer is refilled with stage kt + T::STAGES
+// and the next stage's first operands are read while this stage's second MFMAs run.  The
+// MFMA order per output element is unchanged: ascending K.
 template <class T, int BUF>
 __device__ __forceinline__ void steady_step(const DmaCtx<T>& d, const uint16_t* sA, const uint16_t* sB,
-                                            int kt, const Frag<T>& f, Ops<T>& o0, Ops<T>& o1,
-                                            floatx16 (&acc)[T::BLK_M][T::BLK_N]) {
-  inner_steps<T>(sA, sB, BUF, f, o0, o1, acc);
+                                            int kt, const Frag& f, Ops<T>& o0, Ops<T>& o1,
+                                            floatx4 (&acc)[T::BLK_M][T::BLK_N]) {
+  advance<T, 0>(sA, sB, BUF, 1, f, o0, o1, acc);
   wait_and_barrier<(T::STAGES - 2) * T::PER>();
   if (d.issuer) dma_stage_at<T>(d, BUF, kt + T::STAGES);
-  load_ops<T>(sA, sB, (BUF + 1) % T::STAGES, 0, f, o0);
-  mfma_ops<T>(o1, acc);
-  interleave<T>();
+  advance<T, 1>(sA, sB, (BUF + 1) % T::STAGES, 0, f, o0, o1, acc);
 }
 
 template <class T, int BUF>
 __device__ __forceinline__ void unrolled_steps(const DmaCtx<T>& d, const uint16_t* sA,
-                                               const uint16_t* sB, int kt, const Frag<T>& f,
+                                               const uint16_t* sB, int kt, const Frag& f,
                                                Ops<T>& o0, Ops<T>& o1,
-                                               floatx16 (&acc)[T::BLK_M][T::BLK_N]) {
+                                               floatx4 (&acc)[T::BLK_M][T::BLK_N]) {
   if constexpr (BUF < T::STAGES) {
     steady_step<T, BUF>(d, sA, sB, kt + BUF, f, o0, o1, acc);
     unrolled_steps<T, BUF + 1>(d, sA, sB, kt, f, o0, o1, acc);
@@ -533,47 +625,49 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
   const int dw = wave % T::DW;   // (only issuing waves use what follows)
   d.lds_a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sA)) + (T::TM / T::DW) * dw * DBK * 2;
   d.lds_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sB)) + (T::TN / T::DW) * dw * DBK * 2;
+  // every wave's share starts at a multiple of 16 rows, so swz(R) = swz(RPI j + l / CPR),
+  // which depends on j only through its parity
+  static_assert((T::TM / T::DW) % 16 == 0 && (T::TN / T::DW) % 16 == 0 && RPI == 8, "row shares");
+  d.kc[0] = ((lane % CPR) ^ swz(lane / CPR)) * 8;
+  d.kc[1] = ((lane % CPR) ^ swz(RPI + lane / CPR)) * 8;
+  d.ra_share = tm * T::TM + (T::TM / T::DW) * dw;
+  d.rb_share = tn * T::TN + (T::TN / T::DW) * dw;
+  d.a_last = M - 1;
+  d.b_last = N - 1;
+  d.lda2 = static_cast<uint32_t>(lda * 2);
+  d.ldb2 = static_cast<uint32_t>(ldb * 2);
+  if constexpr (!T::OTF) {
 #pragma unroll
-  for (int j = 0; j < T::NJA; ++j) {
-    const int R = (T::TM / T::DW) * dw + RPI * j + lane / CPR;
-    const int c = (lane % CPR) ^ swz(R);
-    const int ra = min(tm * T::TM + R, M - 1);
-    d.aoff[j] = static_cast<uint32_t>((static_cast<int64_t>(ra) * lda + c * 8) * 2);
-    d.kca[j] = c * 8;
-  }
-#pragma unroll
-  for (int j = 0; j < T::NJB; ++j) {
-    const int R = (T::TN / T::DW) * dw + RPI * j + lane / CPR;
-    const int c = (lane % CPR) ^ swz(R);
-    const int rb = min(tn * T::TN + R, N - 1);
-    d.boff[j] = static_cast<uint32_t>((static_cast<int64_t>(rb) * ldb + c * 8) * 2);
-    d.kcb[j] = c * 8;
-  }
-  // operand reads: lane holds row (lane % 32) of each 32-row block and k-chunk
-  // 2 ks + lane / 32 of each 16-wide K step
-  Frag<T> f;
-  const int orow = lane & 31, okc = lane >> 5;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-    for (int i = 0; i < T::BLK_M; ++i) {
-      const int r = (wm * T::BLK_M + i) * 32 + orow;
-      f.ao[i][ks] = static_cast<uint32_t>((r * DBK + (((2 * ks + okc) ^ swz(r)) * 8)) * 2);
+    for (int j = 0; j < T::NJA; ++j) {
+      const int ra = min(d.ra_share + lane / CPR + RPI * j, M - 1);
+      d.aoff[j] = static_cast<uint32_t>((static_cast<int64_t>(ra) * lda + d.kc[j & 1]) * 2);
     }
 #pragma unroll
-    for (int j = 0; j < T::BLK_N; ++j) {
-      const int r = (wn * T::BLK_N + j) * 32 + orow;
-      f.bo[j][ks] = static_cast<uint32_t>((r * DBK + (((2 * ks + okc) ^ swz(r)) * 8)) * 2);
+    for (int j = 0; j < T::NJB; ++j) {
+      const int rb = min(d.rb_share + lane / CPR + RPI * j, N - 1);
+      d.boff[j] = static_cast<uint32_t>((static_cast<int64_t>(rb) * ldb + d.kc[j & 1]) * 2);
     }
+  }
+  // operand reads: lane holds row (lane % 16) of each 16-row block and k-chunk
+  // 4 ks + lane / 16 of each 32-wide K step (swz(row) = swz(lane % 16) in every block)
+  Frag f;
+  const int orow = lane & 15, okc = lane >> 4;
+  {
+    const int c = (okc ^ swz(orow)) * 8;
+    f.a0 = static_cast<uint32_t>(((wm * T::BLK_M * 16 + orow) * DBK + c) * 2);
+    f.b0 = static_cast<uint32_t>((T::STAGES * T::SA + (wn * T::BLK_N * 16 + orow) * DBK + c) * 2);
+    // opaque to the compiler: the constant parts of a read's address (ring buffer, block)
+    // then stay small enough for the read's immediate offset
+    asm volatile("" : "+v"(f.a0), "+v"(f.b0));
   }
 
-  floatx16 acc[T::BLK_M][T::BLK_N];
+  floatx4 acc[T::BLK_M][T::BLK_N];
 #pragma unroll
   for (int i = 0; i < T::BLK_M; ++i)
 #pragma unroll
     for (int j = 0; j < T::BLK_N; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
   // prologue: every ring buffer receives a stage
   const int nk = d.nk;
@@ -594,35 +688,31 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
   for (; kt + T::STAGES <= steady; kt += T::STAGES) unrolled_steps<T, 0>(d, sA, sB, kt, f, o0, o1, acc);
   for (; kt < steady; ++kt) {
     const int buf = kt % T::STAGES;
-    inner_steps<T>(sA, sB, buf, f, o0, o1, acc);
+    advance<T, 0>(sA, sB, buf, 1, f, o0, o1, acc);
     wait_and_barrier<(T::STAGES - 2) * T::PER>();
     if (d.issuer) dma_stage_at<T>(d, buf, kt + T::STAGES);
-    load_ops<T>(sA, sB, (kt + 1) % T::STAGES, 0, f, o0);
-    mfma_ops<T>(o1, acc);
-    interleave<T>();
+    advance<T, 1>(sA, sB, (kt + 1) % T::STAGES, 0, f, o0, o1, acc);
   }
   // drain: nothing left to issue; stages kt + 1 .. nk - 1 may still be in flight
   for (; kt < nk - 1; ++kt) {
-    inner_steps<T>(sA, sB, kt % T::STAGES, f, o0, o1, acc);
+    advance<T, 0>(sA, sB, kt % T::STAGES, 1, f, o0, o1, acc);
     wait_stage<T::PER, T::STAGES - 2>(min(T::STAGES - 2, nk - 2 - kt));
     if (d.ktail && kt + 1 == nk - 1) {
       if (d.issuer) zero_k_tail<T>(d, sA, sB, (kt + 1) % T::STAGES, kt + 1, wave, lane);
       wait_and_barrier<0>();
     }
-    load_ops<T>(sA, sB, (kt + 1) % T::STAGES, 0, f, o0);
-    mfma_ops<T>(o1, acc);
-    interleave<T>();
+    advance<T, 1>(sA, sB, (kt + 1) % T::STAGES, 0, f, o0, o1, acc);
   }
-  inner_steps<T>(sA, sB, (nk - 1) % T::STAGES, f, o0, o1, acc);
-  mfma_ops<T>(o1, acc);
+  advance<T, 0>(sA, sB, (nk - 1) % T::STAGES, 1, f, o0, o1, acc);
+  last_step<T>(o0, o1, acc);
 
-  // epilogue: register r of block (i, j) is row 8 (r / 4) + 4 (lane / 32) + r % 4 and
-  // column lane % 32 of that block
+  // epilogue: register r of block (i, j) is row 4 (lane / 16) + r and column lane % 16 of
+  // that block
   if (c_f32 != kOutF32) {
     // bf16 output goes through LDS: each wave rounds its WM x WN sub-tile into its own
     // region (16-byte chunk c of row r at position c ^ (r % CW)), then reads it back as
     // 16-byte row pieces, so a store instruction writes whole sub-tile row segments
-    constexpr int WM = T::BLK_M * 32, WN = T::BLK_N * 32;
+    constexpr int WM = T::BLK_M * 16, WN = T::BLK_N * 16;
     constexpr int CW = WN / 8, RPW = 64 / CW;   // chunks per row, rows per read
     static_assert(T::NW * WM * WN <= T::STAGES * (T::SA + T::SB) && WM % RPW == 0, "epilogue staging");
     __syncthreads();   // every wave is done with the stage buffers
@@ -632,9 +722,9 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
 #pragma unroll
       for (int j = 0; j < T::BLK_N; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rw = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int cw = j * 32 + (lane & 31);
+        for (int r = 0; r < 4; ++r) {
+          const int rw = i * 16 + 4 * (lane >> 4) + r;
+          const int cw = j * 16 + (lane & 15);
           st[rw * WN + (((cw >> 3) ^ (rw % CW)) << 3) + (cw & 7)] = f32_to_bf16(acc[i][j][r]);
         }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the region is this wave's own
@@ -691,11 +781,11 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
   for (int i = 0; i < T::BLK_M; ++i)
 #pragma unroll
     for (int j = 0; j < T::BLK_N; ++j) {
-      const int col = tn * T::TN + (wn * T::BLK_N + j) * 32 + (lane & 31);
+      const int col = tn * T::TN + (wn * T::BLK_N + j) * 16 + (lane & 15);
       if (col >= N) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = tm * T::TM + (wm * T::BLK_M + i) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int row = tm * T::TM + (wm * T::BLK_M + i) * 16 + 4 * (lane >> 4) + r;
         if (row >= M) continue;
         static_cast<float*>(C)[static_cast<int64_t>(row) * ldc + col] = acc[i][j][r];
       }
@@ -727,45 +817,75 @@ TileKind pick_tile(int64_t M, int64_t N, int cus) {
   return cost256 < cost128 ? TileKind::k256 : TileKind::k128;
 }
 
-// Few-row GEMM (M <= 64, K a multiple of 16 and at least 32 steps of 16).  At decode sizes the weight stream bounds the
-// call, and a 128 x 128 grid leaves most CUs idle (N = 4096 gives 32 workgroups).  Here one
-// wave owns one 32-column block and all of M (RB 32-row blocks) and loads its instruction
-// operands straight from global memory into registers, PF K steps ahead: lane l takes the 16
-// bytes at row l % 32, k offset 16 t + 8 (l / 32) of K step t, which is exactly its operand of
-// the instruction, so there is no LDS, no barrier and no other wave to wait for.  What is left
-// is the chain itself: K / 16 dependent instructions per accumulator.  Every output element
+// Few-row GEMM (M <= 64).  At decode sizes the weight stream bounds the call, and a
+// 128 x 128 grid leaves most CUs idle (N = 4096 gives 32 workgroups).  Here one wave owns CB
+// 16-column blocks and RB 16-row blocks (all M rows, or with `split` = 2 one of two 32-row
+// halves; the two waves of a column block then sit on one XCD, whose L2 serves the second
+// its weights) and loads its instruction operands
+// straight from global memory into registers, PF K steps ahead: lane l takes the 16 bytes
+// at row l % 16, k offset 32 t + 8 (l / 16) of K step t, which is exactly its operand of the
+// instruction, so there is no LDS, no barrier and no other wave to wait for.  What is left is
+// the chain itself: K / 32 dependent instructions per accumulator.  Every output element
 // sees the instruction sequence of every other configuration (same instruction, +0 start,
-// ascending 16-wide K steps, same lane-to-k assignment), so its bits do not change.
-template <int RB, int PF>
+// ascending 32-wide K steps, same lane-to-k assignment), so its bits do not change.
+// K is a multiple of 8 with at least 2 PF whole steps; a last, partial step is loaded up
+// front, with the chunks at or past K replaced by zeros.
+template <int RB, int CB, int PF>
 __global__ __launch_bounds__(64) void gemm_rows_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
-    int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32) {
+    int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int split) {
   const int lane = threadIdx.x;
-  const int col0 = blockIdx.x * 32;
-  const int row0 = blockIdx.y * (RB * 32);   // 32-row blocks beyond the first: more waves
+  // workgroup id -> (column block, row half): ids 8 s + x and 8 (s + 1) + x (one XCD) share
+  // a column block; with split = 1 the id is the column block
+  int cblk = blockIdx.x, row0 = 0;
+  if (split == 2) {
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    cblk = (slot >> 1) * 8 + x;
+    row0 = (slot & 1) * RB * 16;
+    if (cblk * CB * 16 >= N || row0 >= M) return;   // grid padding (wave-uniform)
+  }
+  const int col0 = cblk * (CB * 16);
+  const int kl = 8 * (lane >> 4);
   const uint16_t* pa[RB];
+  const uint16_t* pb[CB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)   // rows past M repeat the last row; they are never stored
-    pa[rb] = A + static_cast<int64_t>(min(row0 + rb * 32 + (lane & 31), M - 1)) * lda + 8 * (lane >> 5);
-  const uint16_t* pb = B + static_cast<int64_t>(min(col0 + (lane & 31), N - 1)) * ldb + 8 * (lane >> 5);
-  bf16x8 ra[PF][RB], rv[PF];
-  auto load = [&](int t, bf16x8 (&dst_a)[RB], bf16x8& dst_b) {
+    pa[rb] = A + static_cast<int64_t>(min(row0 + rb * 16 + (lane & 15), M - 1)) * lda + kl;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) dst_a[rb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pa[rb] + 16 * t));
-    dst_b = as_bf16x8(*reinterpret_cast<const u16x8*>(pb + 16 * t));
+  for (int cb = 0; cb < CB; ++cb)
+    pb[cb] = B + static_cast<int64_t>(min(col0 + cb * 16 + (lane & 15), N - 1)) * ldb + kl;
+  bf16x8 ra[PF][RB], rv[PF][CB];
+  auto load = [&](int t, bf16x8 (&dst_a)[RB], bf16x8 (&dst_b)[CB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) dst_a[rb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pa[rb] + 32 * t));
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) dst_b[cb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pb[cb] + 32 * t));
   };
-  floatx16 acc[RB];
+  floatx4 acc[RB][CB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[rb][r] = 0.f;
-
-  auto mma = [&](int p) {
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[rb][cb][r] = 0.f;
+  auto mma = [&](const bf16x8 (&a)[RB], const bf16x8 (&b)[CB]) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
-      acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[p][rb], rv[p], acc[rb], 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
   };
-  const int nsteps = K / 16;   // >= 2 PF (the host checks)
+  const int nsteps = K / 32;   // whole steps, >= 2 PF (the host checks)
+  // the partial last step (if any): a chunk at or past K re-reads k offset 0 of its row and
+  // is zeroed once it has landed
+  const int ktail = 32 * nsteps;
+  const bool tin = ktail + kl < K;
+  const int tofs = tin ? ktail : -kl;
+  bf16x8 ta[RB], tb[CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) ta[rb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pa[rb] + tofs));
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) tb[cb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pb[cb] + tofs));
 #pragma unroll
   for (int p = 0; p < PF; ++p) load(p, ra[p], rv[p]);
   // full rounds: step t multiplies slot t % PF and refills it with step t + PF (straight-line
@@ -774,76 +894,104 @@ __global__ __launch_bounds__(64) void gemm_rows_kernel(
   for (; t0 + 2 * PF <= nsteps; t0 += PF) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      mma(p);
+      mma(ra[p], rv[p]);
       load(t0 + PF + p, ra[p], rv[p]);
     }
   }
-  // last (up to 2 PF - 1) steps
+  // last (up to 2 PF - 1) whole steps
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
     if (t0 + p < nsteps) {
-      mma(p);
+      mma(ra[p], rv[p]);
       if (t0 + PF + p < nsteps) load(t0 + PF + p, ra[p], rv[p]);
     }
   }
 #pragma unroll
   for (int p = 0; p < PF; ++p)
-    if (t0 + PF + p < nsteps) mma(p);
-  // register r of row block rb is row 32 rb + 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
+    if (t0 + PF + p < nsteps) mma(ra[p], rv[p]);
+  if (ktail < K) {
+    const bf16x8 z = {};
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) ta[rb] = tin ? ta[rb] : z;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) tb[cb] = tin ? tb[cb] : z;
+    mma(ta, tb);
+  }
+  // register r of block (rb, cb) is row 16 rb + 4 (lane / 16) + r, column 16 cb + lane % 16
   if (c_f32 == kOutSwiGLU) {
-    // 16 gate then 16 up columns per block: lane l < 16 (of each half) pairs with lane l + 16
-    const bool gate = (lane & 31) < 16;
+    // CB == 2: block 0 holds 16 gate columns, block 1 the matching 16 up columns
     const int ocol = col0 / 2 + (lane & 15);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint16_t v = f32_to_bf16(acc[rb][r]);
-        const uint16_t u = static_cast<uint16_t>(__shfl(static_cast<int>(v), (lane + 16) & 63, 64));
-        const int row = row0 + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (gate && row < M)   // (N is a multiple of 32: every block lies inside N)
-          static_cast<uint16_t*>(C)[static_cast<int64_t>(row) * ldc + ocol] = swiglu_bf16(v, u);
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + rb * 16 + 4 * (lane >> 4) + r;
+        if (row < M)   // (N is a multiple of 32: every block lies inside N)
+          static_cast<uint16_t*>(C)[static_cast<int64_t>(row) * ldc + ocol] =
+              swiglu_bf16(f32_to_bf16(acc[rb][0][r]), f32_to_bf16(acc[rb][CB - 1][r]));
       }
     return;
   }
-  const int col = col0 + (lane & 31);
-  if (col >= N) return;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int cb = 0; cb < CB; ++cb) {
+    const int col = col0 + cb * 16 + (lane & 15);
+    if (col >= N) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = row0 + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (row >= M) continue;
-      if (c_f32)
-        static_cast<float*>(C)[static_cast<int64_t>(row) * ldc + col] = acc[rb][r];
-      else
-        static_cast<uint16_t*>(C)[static_cast<int64_t>(row) * ldc + col] = f32_to_bf16(acc[rb][r]);
-    }
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + rb * 16 + 4 * (lane >> 4) + r;
+        if (row >= M) continue;
+        if (c_f32)
+          static_cast<float*>(C)[static_cast<int64_t>(row) * ldc + col] = acc[rb][cb][r];
+        else
+          static_cast<uint16_t*>(C)[static_cast<int64_t>(row) * ldc + col] = f32_to_bf16(acc[rb][cb][r]);
+      }
+  }
 }
 
-constexpr int kRowsMinK = 2 * 16 * 16;   // 2 PF steps of 16
-
-// The few-row kernel for up to 32 rows, and for 33..64 rows while the column blocks number at
-// most two per CU (with more, its doubled per-wave streams lose to the 128 x 128 tiles).
-bool use_rows(int64_t M, int64_t N, int64_t K, int cus) {
-  if (M > 64 || K % 16 != 0 || K < kRowsMinK) return false;
-  return M <= 32 || (N + 31) / 32 <= 2 * static_cast<int64_t>(cus);
+// Few-row configurations.  A wave's A operand reads (RB row blocks per step) come from L2 and
+// hit the same few lines in every wave, so a wave takes at least as many column blocks as
+// row blocks: up to 16 rows one 16 x 16 block (16 x 32 for wide N and for SwiGLU, whose gate
+// and up blocks pair up), above that 32 x 32 blocks, and above 32 rows two waves per column
+// block, one per 32-row half.
+struct RowsCfg {
+  int rb, cb, pf, split;
+};
+RowsCfg rows_cfg(int64_t M, int64_t N, int mode) {
+  if (M <= 16) {
+    const bool wide = mode == kOutSwiGLU || (N + 15) / 16 >= 4 * static_cast<int64_t>(cu_count());
+    return {1, wide ? 2 : 1, 16, 1};
+  }
+  return {2, 2, 12, M <= 32 ? 1 : 2};
 }
 
-// 33..64 rows: a second wave per column block for the second 32 rows while that keeps at
-// most one wave per CU, else one wave with both row blocks.
-bool rows_split(int64_t M, int64_t N, int cus) { return M > 32 && 2 * ((N + 31) / 32) <= cus; }
+// The few-row kernel for up to 32 rows, and for 33..64 rows while its two waves per 32-column
+// block number at most two per CU (wider grids go faster through the LDS-staged tiles, whose
+// loads cover whole 128-byte lines), when K is a multiple of 8 with at least 2 PF whole
+// 32-wide steps.
+bool use_rows(int64_t M, int64_t N, int64_t K, int mode) {
+  if (M > 64 || K % 8 != 0) return false;
+  if (M > 32 && (N + 31) / 32 > static_cast<int64_t>(cu_count())) return false;
+  return K / 32 >= 2 * rows_cfg(M, N, mode).pf;
+}
+
+template <int RB, int CB, int PF>
+void launch_rows_t(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                   int64_t lda, int64_t ldb, int64_t ldc, int cf, int split, hipStream_t s) {
+  const int64_t ncb = (N + CB * 16 - 1) / (CB * 16);
+  const unsigned wgs = static_cast<unsigned>(split == 1 ? ncb : 16 * ((ncb + 7) / 8));
+  gemm_rows_kernel<RB, CB, PF><<<dim3(wgs), dim3(64), 0, s>>>(
+      static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, int(M), int(N), int(K),
+      lda, ldb, ldc, cf, split);
+}
 
 void launch_rows(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                  int64_t lda, int64_t ldb, int64_t ldc, int cf, hipStream_t s) {
-  const unsigned wgs = static_cast<unsigned>((N + 31) / 32);
-  const uint16_t* a = static_cast<const uint16_t*>(A);
-  const uint16_t* b = static_cast<const uint16_t*>(B);
-  if (M <= 32 || rows_split(M, N, cu_count()))
-    gemm_rows_kernel<1, 16><<<dim3(wgs, M <= 32 ? 1 : 2), dim3(64), 0, s>>>(a, b, C, int(M), int(N), int(K),
-                                                                           lda, ldb, ldc, cf);
-  else
-    gemm_rows_kernel<2, 12><<<dim3(wgs), dim3(64), 0, s>>>(a, b, C, int(M), int(N), int(K), lda, ldb, ldc, cf);
+  const RowsCfg c = rows_cfg(M, N, cf);
+  if (c.rb == 2) launch_rows_t<2, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, c.split, s);
+  else if (c.cb == 2) launch_rows_t<1, 2, 16>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
+  else launch_rows_t<1, 1, 16>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
 }
 
 template <class T>
@@ -880,7 +1028,7 @@ int splitk_count(int64_t M, int64_t N, int64_t K) {
 // bf16 A and B, both under 4 GiB: the few-row kernel or the LDS-staged tiles by grid size.
 void launch_bf16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                  int64_t lda, int64_t ldb, int64_t ldc, int mode, hipStream_t s) {
-  if (use_rows(M, N, K, cu_count())) {
+  if (use_rows(M, N, K, mode)) {
     launch_rows(A, B, C, M, N, K, lda, ldb, ldc, mode, s);
     return;
   }
@@ -943,11 +1091,11 @@ extern "C" int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_
     *stages = 2;
     return BI_OK;
   }
-  if (use_rows(M, N, K, cu_count())) {   // few-row kernel: one wave per 32 (or 64) x 32 block
-    const bool one = M <= 32 || rows_split(M, N, cu_count());
-    *tile_m = one ? 32 : 64;
-    *tile_n = 32;
-    *stages = one ? 16 : 12;
+  if (use_rows(M, N, K, kOutBF16)) {   // few-row kernel: one wave per 16 x 16 .. 32 x 32 block
+    const RowsCfg c = rows_cfg(M, N, kOutBF16);
+    *tile_m = 16 * c.rb;
+    *tile_n = 16 * c.cb;
+    *stages = c.pf;
     return BI_OK;
   }
   switch (pick_tile(M, N, cu_count())) {

@@ -54,6 +54,16 @@ def test_large_tile_vs_oracle(lib, m, n, k):
     assert r["ok"], r
 
 
+def few_rows(m, n, k):
+    """Whether the few-row kernel takes an M x N x K product: up to 32 rows, or up to 64 while
+    N / 32 <= CUs, with K a multiple of 8 and at least 2 PF whole 32-wide steps (PF = 16 up
+    to 16 rows, 12 above)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if m > 64 or (m > 32 and (n + 31) // 32 > cus):
+        return False
+    return k % 8 == 0 and k // 32 >= 2 * (16 if m <= 16 else 12)
+
+
 def test_tile_switch_changes_no_bit(lib):
     # the same rows computed under every workgroup configuration (256 x 256; 128 x 128 with
     # a 2- or 3-stage ring), chosen by the grid size, at several positions, for a square
@@ -68,8 +78,9 @@ def test_tile_switch_changes_no_bit(lib):
             configs.add(lib.bi_gemm_tile(m, n, k))
             assert same_bits(lib.bi_gemm(A[:m], B), full[:m]), (n, k, m)
         assert {(64, 64, 3), (64, 128, 3), (128, 128, 3), (128, 128, 2), (256, 256, 2)} <= configs, configs
-        # K a multiple of 16 and at least 512: up to 64 rows take the few-row kernel
-        assert any(c[1] == 32 for c in configs) == (k % 16 == 0 and k >= 512), configs
+        # the few-row kernel (16 or 32 columns per wave) where its K condition holds
+        for m in (1, 33, 64):
+            assert (lib.bi_gemm_tile(m, n, k)[1] <= 32) == few_rows(m, n, k), (m, n, k)
         sel = torch.tensor([full_m - 1, 17, 2600, 300], device="cuda")
         assert same_bits(lib.bi_gemm(A[sel].contiguous(), B), full[sel])
         ff = lib.bi_gemm(A, B, out_dtype=torch.float32)
@@ -211,11 +222,13 @@ def test_output_views(lib):
             assert bool((big[rest] == sentinel).all()), (m, n, k, lo)
 
 
-@pytest.mark.parametrize("m,n,k", [(5, 300, 512), (40, 1000, 528), (64, 96, 1024), (1, 33, 640)])
+@pytest.mark.parametrize("m,n,k", [(5, 300, 1024), (40, 1000, 784), (64, 96, 1024), (1, 33, 1040),
+                                   (17, 200, 1064), (33, 1000, 1024), (50, 72, 800)])
 def test_few_rows_vs_oracle(lib, m, n, k):
-    # the few-row kernel (M <= 64, K % 16 == 0, K >= 512): ragged column blocks, rows past M,
-    # the last partial round of prefetched K steps
-    assert lib.bi_gemm_tile(m, n, k)[1] == 32
+    # the few-row kernel (M <= 64: 16 x 16 or 32 x 32 blocks, two waves per column block above
+    # 32 rows): ragged column blocks, rows past M, padded grids, the last partial round of
+    # prefetched K steps, a partial last K step (K % 32 = 8, 16)
+    assert lib.bi_gemm_tile(m, n, k)[1] <= 32
     say("gemm few rows", m, n, k)
     a, b = gemm_inputs(m, n, k, cfg=39)
     c = lib.bi_gemm(bf16(a), bf16(_nk(b)))
@@ -228,17 +241,15 @@ def test_few_rows_vs_oracle(lib, m, n, k):
 
 @pytest.mark.parametrize("n,k", [(4096, 4096), (28672, 1024), (6144, 14336), (32000, 512)])
 def test_few_rows_match_large_m(lib, n, k):
-    # the few-row kernel (one or two row blocks) gives the rows of the large-M kernels bit
-    # for bit
+    # the few-row kernel (every block shape and row split) gives the rows of the large-M
+    # kernels bit for bit
     say("gemm few rows vs large M", n, k)
     a, b = gemm_inputs(512, n, k, cfg=40)
     A, W = bf16(a), bf16(_nk(b))
     full = lib.bi_gemm(A, W)
     ff = lib.bi_gemm(A, W, out_dtype=torch.float32)
-    for m in (1, 17, 32, 33, 49, 64):
-        # up to 32 rows always; 33..64 rows only while N / 32 <= 2 x CUs
-        cus = torch.cuda.get_device_properties(0).multi_processor_count
-        assert (lib.bi_gemm_tile(m, n, k)[1] == 32) == (m <= 32 or (n + 31) // 32 <= 2 * cus), (m, n)
+    for m in (1, 16, 17, 32, 33, 49, 64):
+        assert (lib.bi_gemm_tile(m, n, k)[1] <= 32) == few_rows(m, n, k), (m, n, k)
         assert same_bits(lib.bi_gemm(A[:m], W), full[:m]), (n, k, m)
         assert same_bits(lib.bi_gemm(A[:m], W, out_dtype=torch.float32), ff[:m]), (n, k, m)
     rows = torch.tensor([300, 5, 511], device="cuda")
