@@ -135,8 +135,9 @@ int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
  * Up to 32 rows (up to 64 while ceil(N / 32) is at most the CU count), with K a multiple of
  * 8 and at least 2 x (16 or 12) whole 32-wide steps: one wave per output block with its
  * instruction operands loaded straight into registers 16 (or 12) K steps ahead; the block
- * is 16 x 16 up to 16 rows (16 x 32 when N / 16 is at least four times the CU count),
- * 32 x 32 above, with two waves per column block (one per 32-row half) above 32 rows.
+ * is 16 x 16 up to 16 rows (16 x 32 from 9 rows when N / 16 is at least four times the CU
+ * count), 32 x 32 up to 32 rows, 64 x 32 above (or, while N / 32 is under three quarters of
+ * the CU count, two waves of 32 x 32 per column block, one per 32-row half).
  * Otherwise 256 x 256
  * (2-stage LDS ring) when that grid finishes in fewer rounds of the CU array; else
  * 128 x 128, with a 3-stage ring when the grid has no more tiles than CUs and a 2-stage

@@ -950,20 +950,25 @@ __global__ __launch_bounds__(64) void gemm_rows_kernel(
   }
 }
 
-// Few-row configurations.  A wave's A operand reads (RB row blocks per step) come from L2 and
-// hit the same few lines in every wave, so a wave takes at least as many column blocks as
-// row blocks: up to 16 rows one 16 x 16 block (16 x 32 for wide N and for SwiGLU, whose gate
-// and up blocks pair up), above that 32 x 32 blocks, and above 32 rows two waves per column
-// block, one per 32-row half.
+// Few-row configurations (measured on MI355X at the decode shapes).  A wave's A operand reads
+// (RB row blocks per step) come from L2 and hit the same few lines in every wave, so once
+// there are several rows a wave takes at least half as many column blocks as row blocks: up
+// to 16 rows one 16 x 16 block (16 x 32 from 9 rows on for wide N, and for SwiGLU, whose
+// gate and up blocks pair up), up to 32 rows 32 x 32 blocks, above that 64 x 32 blocks, or
+// two waves of 32 x 32 per column block (one per 32-row half) while the column blocks
+// number under three quarters of the CUs.
 struct RowsCfg {
   int rb, cb, pf, split;
 };
 RowsCfg rows_cfg(int64_t M, int64_t N, int mode) {
+  const int64_t cus = cu_count();
   if (M <= 16) {
-    const bool wide = mode == kOutSwiGLU || (N + 15) / 16 >= 4 * static_cast<int64_t>(cu_count());
+    const bool wide = mode == kOutSwiGLU || (M > 8 && (N + 15) / 16 >= 4 * cus);
     return {1, wide ? 2 : 1, 16, 1};
   }
-  return {2, 2, 12, M <= 32 ? 1 : 2};
+  if (M <= 32) return {2, 2, 12, 1};
+  if (4 * ((N + 31) / 32) >= 3 * cus) return {4, 2, 12, 1};
+  return {2, 2, 12, 2};
 }
 
 // The few-row kernel for up to 32 rows, and for 33..64 rows while its two waves per 32-column
@@ -989,7 +994,8 @@ void launch_rows_t(const void* A, const void* B, void* C, int64_t M, int64_t N, 
 void launch_rows(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                  int64_t lda, int64_t ldb, int64_t ldc, int cf, hipStream_t s) {
   const RowsCfg c = rows_cfg(M, N, cf);
-  if (c.rb == 2) launch_rows_t<2, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, c.split, s);
+  if (c.rb == 4) launch_rows_t<4, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
+  else if (c.rb == 2) launch_rows_t<2, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, c.split, s);
   else if (c.cb == 2) launch_rows_t<1, 2, 16>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
   else launch_rows_t<1, 1, 16>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
 }
