@@ -830,14 +830,19 @@ TileKind pick_tile(int64_t M, int64_t N, int cus) {
 // ascending 32-wide K steps, same lane-to-k assignment), so its bits do not change.
 // K is a multiple of 8 with at least 2 PF whole steps; a last, partial step is loaded up
 // front, with the chunks at or past K replaced by zeros.
-template <int RB, int CB, int PF>
-__global__ __launch_bounds__(64) void gemm_rows_kernel(
+// PAIR: two waves per workgroup, one 16-column block each (CB = 1, split = 1): for SwiGLU
+// the second wave's block (the up columns) reaches the first through LDS, so a wave streams
+// one block, as in the plain one-block kernel.
+template <int RB, int CB, int PF, bool PAIR = false>
+__global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
     int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int split) {
-  const int lane = threadIdx.x;
+  static_assert(!PAIR || CB == 1, "paired waves hold one block each");
+  const int lane = threadIdx.x & 63;
+  const int wave = PAIR ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   // workgroup id -> (column block, row half): ids 8 s + x and 8 (s + 1) + x (one XCD) share
-  // a column block; with split = 1 the id is the column block
-  int cblk = blockIdx.x, row0 = 0;
+  // a column block; with split = 1 the id is the column block (the pair's, for PAIR)
+  int cblk = PAIR ? 2 * blockIdx.x + wave : blockIdx.x, row0 = 0;
   if (split == 2) {
     const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
     cblk = (slot >> 1) * 8 + x;
@@ -918,6 +923,29 @@ __global__ __launch_bounds__(64) void gemm_rows_kernel(
     mma(ta, tb);
   }
   // register r of block (rb, cb) is row 16 rb + 4 (lane / 16) + r, column 16 cb + lane % 16
+  if (PAIR && c_f32 == kOutSwiGLU) {
+    // wave 0 holds 16 gate columns, wave 1 the matching 16 up columns
+    __shared__ uint16_t up[RB][4][64];
+    if (wave == 1) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) up[rb][r][lane] = f32_to_bf16(acc[rb][0][r]);
+    }
+    __syncthreads();
+    if (wave == 1) return;
+    const int ocol = blockIdx.x * 16 + (lane & 15);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + rb * 16 + 4 * (lane >> 4) + r;
+        if (row < M)   // (N is a multiple of 32: every block lies inside N)
+          static_cast<uint16_t*>(C)[static_cast<int64_t>(row) * ldc + ocol] =
+              swiglu_bf16(f32_to_bf16(acc[rb][0][r]), up[rb][r][lane]);
+      }
+    return;
+  }
   if (c_f32 == kOutSwiGLU) {
     // CB == 2: block 0 holds 16 gate columns, block 1 the matching 16 up columns
     const int ocol = col0 / 2 + (lane & 15);
@@ -959,9 +987,11 @@ __global__ __launch_bounds__(64) void gemm_rows_kernel(
 // number under three quarters of the CUs.
 struct RowsCfg {
   int rb, cb, pf, split;
+  bool pair = false;   // SwiGLU with one 16-column block per wave, two waves per workgroup
 };
 RowsCfg rows_cfg(int64_t M, int64_t N, int mode) {
   const int64_t cus = cu_count();
+  if (M <= 8 && mode == kOutSwiGLU) return {1, 1, 16, 1, true};
   if (M <= 16) {
     const bool wide = mode == kOutSwiGLU || (M > 8 && (N + 15) / 16 >= 4 * cus);
     return {1, wide ? 2 : 1, 16, 1};
@@ -981,12 +1011,12 @@ bool use_rows(int64_t M, int64_t N, int64_t K, int mode) {
   return K / 32 >= 2 * rows_cfg(M, N, mode).pf;
 }
 
-template <int RB, int CB, int PF>
+template <int RB, int CB, int PF, bool PAIR = false>
 void launch_rows_t(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                    int64_t lda, int64_t ldb, int64_t ldc, int cf, int split, hipStream_t s) {
   const int64_t ncb = (N + CB * 16 - 1) / (CB * 16);
-  const unsigned wgs = static_cast<unsigned>(split == 1 ? ncb : 16 * ((ncb + 7) / 8));
-  gemm_rows_kernel<RB, CB, PF><<<dim3(wgs), dim3(64), 0, s>>>(
+  const unsigned wgs = static_cast<unsigned>(PAIR ? (ncb + 1) / 2 : split == 1 ? ncb : 16 * ((ncb + 7) / 8));
+  gemm_rows_kernel<RB, CB, PF, PAIR><<<dim3(wgs), dim3(PAIR ? 128 : 64), 0, s>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, int(M), int(N), int(K),
       lda, ldb, ldc, cf, split);
 }
@@ -994,7 +1024,8 @@ void launch_rows_t(const void* A, const void* B, void* C, int64_t M, int64_t N, 
 void launch_rows(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                  int64_t lda, int64_t ldb, int64_t ldc, int cf, hipStream_t s) {
   const RowsCfg c = rows_cfg(M, N, cf);
-  if (c.rb == 4) launch_rows_t<4, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
+  if (c.pair) launch_rows_t<1, 1, 16, true>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
+  else if (c.rb == 4) launch_rows_t<4, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
   else if (c.rb == 2) launch_rows_t<2, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, c.split, s);
   else if (c.cb == 2) launch_rows_t<1, 2, 16>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
   else launch_rows_t<1, 1, 16>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);

@@ -267,7 +267,7 @@ def test_gemm_swiglu_equals_unfused(lib, f, k):
     a, b = gemm_inputs(3000, 2 * f, k, cfg=45, sd=0.5)
     A, W = bf16(a), bf16(_nk(b))
     Wi = interleave_gate_up(W)
-    for m in (1, 17, 33, 64, 65, 255, 500, 1000, 3000):
+    for m in (1, 8, 9, 17, 33, 64, 65, 255, 500, 1000, 3000):
         fused = lib.bi_gemm_swiglu(A[:m], Wi)
         ref = lib.bi_swiglu(lib.bi_gemm(A[:m], W))
         assert same_bits(fused, ref), (f, k, m, lib.bi_gemm_tile(m, 2 * f, k))
