@@ -30,7 +30,9 @@
 // ascending g; each level copies its first partial and then applies
 //   m' = max(m, m_c); a = 2^(m - m'); b = 2^(m_c - m');  l' = a l + b l_c;  o' = a o + b o_c,
 // and out = o / l.  Split-KV decode writes one partial per group (a quarter of the
-// per-chunk partials' bytes); the prefill walk applies the same two levels in registers.
+// per-chunk partials' bytes), or, when that leaves fewer work units than two per CU, one
+// per chunk, whose first level the combine kernel then applies; the prefill walk applies
+// the same two levels in registers.
 //
 // Cache layout, chosen so every matrix-operand load of a wave covers whole 128-byte
 // lines:
@@ -386,7 +388,7 @@ struct SplitStep {
 // or before the unit's token: a workgroup's units advance, so a short search finds it.
 __device__ __forceinline__ SplitStep split_unit(int u, int t0, const int4* s_tok, const int* s_start,
                                                 int num_tokens, const uint16_t* kc, const uint16_t* vc,
-                                                const int32_t* bt, int max_pages, int ps, int hkv) {
+                                                const int32_t* bt, int max_pages, int ps, int hkv, int uc) {
   SplitStep it;
   const unsigned j = static_cast<unsigned>(u) / static_cast<unsigned>(hkv);
   if (t0 < 0 || t0 >= num_tokens || s_start[t0] > static_cast<int>(j)) t0 = 0;   // hint past the unit
@@ -408,8 +410,8 @@ __device__ __forceinline__ SplitStep split_unit(int u, int t0, const int4* s_tok
   it.t = __builtin_amdgcn_readfirstlane(t);
   it.g = __builtin_amdgcn_readfirstlane(static_cast<int>(j) - s_start[t]);
   it.pos = __builtin_amdgcn_readfirstlane(r.y);
-  it.c = GROUP * it.g;
-  it.nk = min(GROUP, it.pos / CHUNK - it.c + 1);
+  it.c = uc * it.g;
+  it.nk = min(uc, it.pos / CHUNK - it.c + 1);
   const int b = __builtin_amdgcn_readfirstlane(r.x);
   const int len = __builtin_amdgcn_readfirstlane(r.z);
   it.sq = Seq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, it.kvh, len, max_pages,
@@ -431,7 +433,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt, const int4* __restrict__ tok,
     int num_tokens, int max_pages, int hq, int hkv, int ps, int max_groups, float sl2,
-    float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+    float* __restrict__ ws_ml, float* __restrict__ ws_o, int uc) {
   __shared__ ChunkLDS sh;
   __shared__ int4 s_tok[SPLIT_MAX_TOKENS];
   __shared__ int s_start[SPLIT_MAX_TOKENS + 1];
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
     for (int base = 0; base < num_tokens; base += 64) {
       const int t = base + lane;
       const int pos = t < num_tokens ? s_tok[t].y : -1;
-      int v = pos >= 0 ? pos / (CHUNK * GROUP) + 1 : 0;
+      int v = pos >= 0 ? pos / (CHUNK * uc) + 1 : 0;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int u = __shfl_up(v, o, 64);
@@ -472,11 +474,11 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
       return n;
     }
     if (p.u + stride < n_units)
-      return split_unit(p.u + stride, p.t, s_tok, s_start, num_tokens, kc, vc, bt, max_pages, ps, hkv);
+      return split_unit(p.u + stride, p.t, s_tok, s_start, num_tokens, kc, vc, bt, max_pages, ps, hkv, uc);
     return p;
   };
 
-  SplitStep cur = split_unit(blockIdx.x, 0, s_tok, s_start, num_tokens, kc, vc, bt, max_pages, ps, hkv);
+  SplitStep cur = split_unit(blockIdx.x, 0, s_tok, s_start, num_tokens, kc, vc, bt, max_pages, ps, hkv, uc);
   int pg = chunk_pages(cur.sq, cur.c);
   u16x8 qop[4], kop[2][2][4], vop[2][8];
   load_q_col(q, cur.t, cur.kvh * G + hcol, hq, qop);
@@ -537,11 +539,15 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
 }
 
 // ---------------------------------------------------------------- step 3a: merge chunks
-// one wave per (token, q head); lane holds d = 2 lane, 2 lane + 1.
+// one wave per (token, q head); lane holds d = 2 lane, 2 lane + 1.  Each partial covers
+// `group` chunks; with fold = 1 the partials are merged in order, with fold = GROUP (single
+// chunks as partials) in the two levels of the split path: the chunks of each group of
+// GROUP, then the groups -- the same operations in the same order as the in-register merge
+// of a group, so both give the same bits.
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch, int hq,
-    int max_chunks, int64_t n_rows, void* __restrict__ out, int out_f32, int group) {
+    int max_chunks, int64_t n_rows, void* __restrict__ out, int out_f32, int group, int fold) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= n_rows) return;
   const int t = static_cast<int>(row / hq);
@@ -552,6 +558,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   const float* ml = ws_ml + row * max_chunks * 2;
   const float* po = ws_o + row * max_chunks * HD + 2 * lane;
   float m = 0.f, l = 0.f, o0 = 0.f, o1 = 0.f;
+  float mg = 0.f, lg = 0.f, g0 = 0.f, g1 = 0.f;   // the current group of `fold` partials
   // chunks in groups of 64: lane c holds (m_c, l_c) of chunk base + c; 8 o loads in flight
   for (int base = 0; base < nc; base += 64) {
     const int cl = base + lane;
@@ -569,13 +576,22 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
         const int c = base + j0 + j;
         const float mc = __shfl(mc_l, j0 + j, 64);
         const float lc = __shfl(lc_l, j0 + j, 64);
-        if (c == 0) {
-          m = mc; l = lc; o0 = ov[j].x; o1 = ov[j].y;
+        if (c % fold == 0) {
+          mg = mc; lg = lc; g0 = ov[j].x; g1 = ov[j].y;
         } else {
           float a, bb;
-          merge_step(m, l, mc, lc, a, bb);
-          o0 = mix(o0, ov[j].x, a, bb);
-          o1 = mix(o1, ov[j].y, a, bb);
+          merge_step(mg, lg, mc, lc, a, bb);
+          g0 = mix(g0, ov[j].x, a, bb);
+          g1 = mix(g1, ov[j].y, a, bb);
+        }
+        if (c % fold != fold - 1 && c != nc - 1) continue;   // group not complete yet
+        if (c < fold) {
+          m = mg; l = lg; o0 = g0; o1 = g1;
+        } else {
+          float a, bb;
+          merge_step(m, l, mg, lg, a, bb);
+          o0 = mix(o0, g0, a, bb);
+          o1 = mix(o1, g1, a, bb);
         }
       }
     }
@@ -815,20 +831,26 @@ extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new,
       query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size, ws_tok);
   const int of = out_dtype == BI_F32;
   if (split) {
-    // as many workgroups as can be resident at once, never more than there are units
+    // Work units of GROUP chunks, whose partial is the group's in-register merge; when that
+    // leaves fewer units than two per CU (small batches), units of one chunk, whose partials
+    // the combine kernel merges in the same two levels (same bits, four times the units).
     const int64_t maxg = (maxc + GROUP - 1) / GROUP;
-    float* gs_o = ws_ml + ml_floats(num_tokens * num_q_heads * maxg);   // per-group partials
-    const int64_t units = num_tokens * maxg * num_kv_heads;   // an upper bound of the work units
+    const bool fine = num_tokens * maxg * num_kv_heads < 2 * static_cast<int64_t>(cu_count());
+    const int uc = fine ? 1 : GROUP;
+    const int64_t slots = fine ? maxc : maxg;   // partials per (token, q head)
+    float* ps_o = ws_ml + ml_floats(num_tokens * num_q_heads * slots);
+    // as many workgroups as can be resident at once, never more than there are units
+    const int64_t units = num_tokens * slots * num_kv_heads;   // an upper bound of the work units
     const int64_t grid = std::min<int64_t>(units, static_cast<int64_t>(split_resident()) * cu_count());
     attn_split_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, s>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
         static_cast<const uint16_t*>(v_cache), block_table, ws_tok, static_cast<int>(num_tokens),
-        max_pages_per_seq, num_q_heads, num_kv_heads, page_size, static_cast<int>(maxg), sl2,
-        ws_ml, gs_o);
+        max_pages_per_seq, num_q_heads, num_kv_heads, page_size, static_cast<int>(slots), sl2,
+        ws_ml, ps_o, uc);
     const int64_t rows = num_tokens * num_q_heads;
     attn_combine_kernel<<<dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s>>>(
-        ws_ml, gs_o, seq_lens, query_start_loc, batch, num_q_heads, static_cast<int>(maxg), rows,
-        out, of, GROUP);
+        ws_ml, ps_o, seq_lens, query_start_loc, batch, num_q_heads, static_cast<int>(slots), rows,
+        out, of, uc, fine ? GROUP : 1);
   } else {
     const int NT = 16 / G;
     const int64_t blocks = (num_tokens + NT - 1) / NT;
@@ -889,6 +911,6 @@ extern "C" int bi_attention_batchdep_split(
   const int64_t rows = num_tokens * num_q_heads;
   attn_combine_kernel<<<dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s>>>(
       ws_ml, ws_o, seq_lens, query_start_loc, batch, num_q_heads, static_cast<int>(maxg), rows, out,
-      out_dtype == BI_F32, static_cast<int>(group));
+      out_dtype == BI_F32, static_cast<int>(group), 1);
   return launch_status();
 }
