@@ -85,7 +85,9 @@ def test_batch_position_page_invariance(lib):
 def test_split_work_list_edges(lib):
     # decode batches of many short or mixed sequences: the split kernel's work list (token,
     # chunk, kv head) is walked by a persistent grid with look-ahead, so every workgroup
-    # runs past the end of its list, and the smallest call has fewer items than workgroups
+    # runs past the end of its list, and the smallest call has fewer items than workgroups.
+    # The large batches take 4-chunk work units and a single sequence one-chunk units (the
+    # combine kernel then merges the chunks of each group): both give the same bits.
     rng = np.random.default_rng(44)
     for B, lo, hi, hq, hkv in [(97, 1, 1500, 32, 8), (3, 1, 20, 8, 1), (40, 250, 260, 16, 1)]:
         say("split work list", B, lo, hi, hq, hkv)
