@@ -66,12 +66,14 @@ typedef struct bi_config {
   int32_t wave_size;        /* 64                                                      */
   int32_t gemm_tile_m;      /* output tile rows per workgroup (small tile)             */
   int32_t gemm_tile_n;      /* output tile columns per workgroup (small tile)          */
-  int32_t gemm_tile_k;      /* K depth of one staged step of the main kernel           */
+  int32_t gemm_tile_k;      /* K depth of one LDS stage of the main kernel             */
   int32_t gemm_mfma_m, gemm_mfma_n, gemm_mfma_k; /* the one matrix instruction shape     */
   int32_t attn_chunk;       /* 256: split-KV chunk, at absolute positions 256c          */
   int32_t attn_max_group;   /* largest supported q heads per kv head                   */
   int32_t gemm_big_tile_m;  /* rows of the large workgroup tile (same bits, see bi_gemm) */
   int32_t gemm_big_tile_n;  /* columns of the large workgroup tile                     */
+  int32_t attn_merge_group; /* 4: chunk partials merge within groups of 4 chunks, then the
+                               groups, in ascending order (version >= 3)                 */
 } bi_config;
 
 /* Fills *out.  Returns BI_ERR_NULL if out is NULL. */

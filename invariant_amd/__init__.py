@@ -51,7 +51,7 @@ class BIConfig(ctypes.Structure):
     _fields_ = [(n, _I32) for n in (
         "version", "tree_max_lanes", "wave_size", "gemm_tile_m", "gemm_tile_n", "gemm_tile_k",
         "gemm_mfma_m", "gemm_mfma_n", "gemm_mfma_k", "attn_chunk", "attn_max_group",
-        "gemm_big_tile_m", "gemm_big_tile_n")]
+        "gemm_big_tile_m", "gemm_big_tile_n", "attn_merge_group")]
 
 
 class BIError(RuntimeError):

@@ -3,19 +3,20 @@
 
 extern "C" int bi_get_config(bi_config* out) {
   if (!out) return BI_ERR_NULL;
-  out->version = 2;
+  out->version = 3;
   out->tree_max_lanes = 256;
   out->wave_size = 64;
   out->gemm_tile_m = 128;
   out->gemm_tile_n = 128;
-  out->gemm_tile_k = 32;
-  out->gemm_mfma_m = 32;
-  out->gemm_mfma_n = 32;
-  out->gemm_mfma_k = 16;
+  out->gemm_tile_k = 64;
+  out->gemm_mfma_m = 16;
+  out->gemm_mfma_n = 16;
+  out->gemm_mfma_k = 32;
   out->attn_chunk = 256;
   out->attn_max_group = 16;
   out->gemm_big_tile_m = 256;
   out->gemm_big_tile_n = 256;
+  out->attn_merge_group = 4;
   return BI_OK;
 }
 

@@ -42,7 +42,8 @@ def test_every_declared_symbol_is_exported(lib):
 def test_config_and_status_strings(lib):
     cfg = bi.get_config()
     assert cfg["tree_max_lanes"] == 256 and cfg["wave_size"] == 64 and cfg["attn_chunk"] == 256
-    assert cfg["gemm_mfma_k"] == 16
+    assert (cfg["gemm_mfma_m"], cfg["gemm_mfma_n"], cfg["gemm_mfma_k"]) == (16, 16, 32)
+    assert cfg["version"] == 3 and cfg["attn_merge_group"] == 4 and cfg["gemm_tile_k"] == 64
     assert bi.status_string(0) == "BI_OK" and bi.status_string(-2) == "BI_ERR_SHAPE"
     assert bi.status_string(-99) == "BI_ERR_UNKNOWN"
     assert lib.bi_get_config(None) == -1
