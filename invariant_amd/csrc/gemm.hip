@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 }
 
 constexpr int DBK = 64;                  // K depth of one LDS stage in the main kernel
-constexpr int KS = DBK / 32;             // 32-wide K steps per stage (even: see inner_steps)
+constexpr int KS = DBK / 32;             // 32-wide K steps per stage (two: see advance)
 constexpr int CPR = DBK / 8;             // 16-byte chunks per LDS row
 constexpr int RPI = 64 / CPR;            // tile rows filled by one 1 KB wave-wide load
 constexpr uint32_t kBlkBytes = 16 * DBK * 2;   // LDS bytes of one 16-row block of a stage
