@@ -257,11 +257,11 @@ struct Tile {
   static_assert(TM % (DW * RPI) == 0 && TN % (DW * RPI) == 0 && DW <= NW, "tile rows per wave");
   static_assert(STAGES >= 2, "unsupported staging");
 };
-// 128 x 128, 4 waves of 64 x 64 with a 2-stage ring (64 KB, two workgroups per CU); for
-// grids with no more tiles than CUs, 128 x 128 as 8 waves of 64 x 32 with a 3-stage ring
-// (96 KB, one workgroup but two waves per SIMD); 256 x 256, 8 waves of 128 x 64, 2-stage
-// ring (128 KB, one per CU).  With 8 waves, one wave per SIMD issues the stage loads.
-using Tile128 = Tile<2, 2, 4, 4, 2>;
+// 128 x 128 as 8 waves of 64 x 32: with a 2-stage ring (64 KB, two workgroups and four waves
+// per SIMD per CU), or for grids with no more tiles than CUs with a 3-stage ring (96 KB,
+// one workgroup); 256 x 256, 8 waves of 128 x 64, 2-stage ring (128 KB, one per CU).  With
+// 8 waves, one wave per SIMD issues the stage loads.
+using Tile128 = Tile<2, 4, 4, 2, 2, 4, 4>;
 using Tile128Deep = Tile<2, 4, 4, 2, 3, 2, 4>;
 // Grids with well under one 128 x 128 tile per CU (a few hundred rows): 64 x 128 as 8 waves
 // of 32 x 32, or 64 x 64 as 4 waves of 32 x 32, both with a 3-stage ring.
@@ -798,7 +798,8 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
 // per CU; the 128 x 128 tile runs two per CU, or one with a deeper ring when the grid has
 // no more tiles than CUs.  The cost counts rounds of the CU array, with round times
 // measured on MI355X at K = 4096 (all scale with K): 256 x 256: 109; 128 x 128 two per CU:
-// 66, one per CU: 46.
+// 59-66 (64 taken: at 59 wide-N grids of 2048 rows would pick the slower 128 x 128 tiles),
+// one per CU: 46.
 enum class TileKind { k64, k64x128, k128, k128deep, k256 };
 
 TileKind pick_tile(int64_t M, int64_t N, int cus) {
@@ -813,7 +814,7 @@ TileKind pick_tile(int64_t M, int64_t N, int cus) {
   }
   const int64_t cost256 = 109 * ((n256 + cus - 1) / cus);
   const int64_t rem = n128 % (2 * cus);
-  const int64_t cost128 = 66 * (n128 / (2 * cus)) + (rem == 0 ? 0 : rem <= cus ? 46 : 66);
+  const int64_t cost128 = 64 * (n128 / (2 * cus)) + (rem == 0 ? 0 : rem <= cus ? 46 : 64);
   return cost256 < cost128 ? TileKind::k256 : TileKind::k128;
 }
 
