@@ -435,8 +435,8 @@ struct Ops {
 };
 
 template <class T>
-__device__ __forceinline__ void load_ops(const uint16_t* sA, const uint16_t* sB, uint32_t buf, int ks,
-                                         const Frag& f, Ops<T>& o) {
+__device__ __forceinline__ void load_ops(const uint16_t* sA, uint32_t buf, int ks, const Frag& f,
+                                         Ops<T>& o) {
   const char* a = reinterpret_cast<const char*>(sA) + f.a(ks) + buf * (T::SA * 2);
   const char* b = reinterpret_cast<const char*>(sA) + f.b(ks) + buf * (T::SB * 2);
   // in the order the MFMAs consume them: A0, every B, then A1 .. (the first MFMAs can
@@ -504,7 +504,7 @@ __device__ __forceinline__ void interleave() {
 //    during the first BLK_N MFMAs; the A fragments live in o0, and next A fragment i
 //    replaces current A fragment i right after the BLK_N MFMAs that use it.
 template <class T, int PAR>
-__device__ __forceinline__ void advance(const uint16_t* sA, const uint16_t* sB, uint32_t buf, int ks,
+__device__ __forceinline__ void advance(const uint16_t* sA, uint32_t buf, int ks,
                                         const Frag& f, Ops<T>& o0, Ops<T>& o1,
                                         floatx4 (&acc)[T::BLK_M][T::BLK_N]) {
   if constexpr (T::INPLACE) {
@@ -534,11 +534,11 @@ __device__ __forceinline__ void advance(const uint16_t* sA, const uint16_t* sB, 
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // A fragment BLK_M - 1
   } else if constexpr (PAR == 0) {
-    load_ops<T>(sA, sB, buf, ks, f, o1);
+    load_ops<T>(sA, buf, ks, f, o1);
     mfma_ops<T>(o0, acc);
     interleave<T>();
   } else {
-    load_ops<T>(sA, sB, buf, ks, f, o0);
+    load_ops<T>(sA, buf, ks, f, o0);
     mfma_ops<T>(o1, acc);
     interleave<T>();
   }
@@ -565,23 +565,21 @@ static_assert(KS == 2, "a stage is two K steps: advance<0> inside it, advance<1>
 // and the next stage's first operands are read while this stage's second MFMAs run.  The
 // MFMA order per output element is unchanged: ascending K.
 template <class T, int BUF>
-__device__ __forceinline__ void steady_step(const DmaCtx<T>& d, const uint16_t* sA, const uint16_t* sB,
-                                            int kt, const Frag& f, Ops<T>& o0, Ops<T>& o1,
-                                            floatx4 (&acc)[T::BLK_M][T::BLK_N]) {
-  advance<T, 0>(sA, sB, BUF, 1, f, o0, o1, acc);
+__device__ __forceinline__ void steady_step(const DmaCtx<T>& d, const uint16_t* sA, int kt, const Frag& f,
+                                            Ops<T>& o0, Ops<T>& o1, floatx4 (&acc)[T::BLK_M][T::BLK_N]) {
+  advance<T, 0>(sA, BUF, 1, f, o0, o1, acc);
   wait_and_barrier<(T::STAGES - 2) * T::PER>();
   if (d.issuer) dma_stage_at<T>(d, BUF, kt + T::STAGES);
-  advance<T, 1>(sA, sB, (BUF + 1) % T::STAGES, 0, f, o0, o1, acc);
+  advance<T, 1>(sA, (BUF + 1) % T::STAGES, 0, f, o0, o1, acc);
 }
 
 template <class T, int BUF>
-__device__ __forceinline__ void unrolled_steps(const DmaCtx<T>& d, const uint16_t* sA,
-                                               const uint16_t* sB, int kt, const Frag& f,
-                                               Ops<T>& o0, Ops<T>& o1,
+__device__ __forceinline__ void unrolled_steps(const DmaCtx<T>& d, const uint16_t* sA, int kt,
+                                               const Frag& f, Ops<T>& o0, Ops<T>& o1,
                                                floatx4 (&acc)[T::BLK_M][T::BLK_N]) {
   if constexpr (BUF < T::STAGES) {
-    steady_step<T, BUF>(d, sA, sB, kt + BUF, f, o0, o1, acc);
-    unrolled_steps<T, BUF + 1>(d, sA, sB, kt, f, o0, o1, acc);
+    steady_step<T, BUF>(d, sA, kt + BUF, f, o0, o1, acc);
+    unrolled_steps<T, BUF + 1>(d, sA, kt, f, o0, o1, acc);
   }
 }
 
@@ -680,30 +678,30 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
     if (d.issuer) zero_k_tail<T>(d, sA, sB, 0, 0, wave, lane);
     wait_and_barrier<0>();
   }
-  load_ops<T>(sA, sB, 0, 0, f, o0);
+  load_ops<T>(sA, 0, 0, f, o0);
 
   // steady state: steps kt with stage kt + T::STAGES still to issue
   const int steady = nk - T::STAGES > 0 ? nk - T::STAGES : 0;
   int kt = 0;
-  for (; kt + T::STAGES <= steady; kt += T::STAGES) unrolled_steps<T, 0>(d, sA, sB, kt, f, o0, o1, acc);
+  for (; kt + T::STAGES <= steady; kt += T::STAGES) unrolled_steps<T, 0>(d, sA, kt, f, o0, o1, acc);
   for (; kt < steady; ++kt) {
     const int buf = kt % T::STAGES;
-    advance<T, 0>(sA, sB, buf, 1, f, o0, o1, acc);
+    advance<T, 0>(sA, buf, 1, f, o0, o1, acc);
     wait_and_barrier<(T::STAGES - 2) * T::PER>();
     if (d.issuer) dma_stage_at<T>(d, buf, kt + T::STAGES);
-    advance<T, 1>(sA, sB, (kt + 1) % T::STAGES, 0, f, o0, o1, acc);
+    advance<T, 1>(sA, (kt + 1) % T::STAGES, 0, f, o0, o1, acc);
   }
   // drain: nothing left to issue; stages kt + 1 .. nk - 1 may still be in flight
   for (; kt < nk - 1; ++kt) {
-    advance<T, 0>(sA, sB, kt % T::STAGES, 1, f, o0, o1, acc);
+    advance<T, 0>(sA, kt % T::STAGES, 1, f, o0, o1, acc);
     wait_stage<T::PER, T::STAGES - 2>(min(T::STAGES - 2, nk - 2 - kt));
     if (d.ktail && kt + 1 == nk - 1) {
       if (d.issuer) zero_k_tail<T>(d, sA, sB, (kt + 1) % T::STAGES, kt + 1, wave, lane);
       wait_and_barrier<0>();
     }
-    advance<T, 1>(sA, sB, (kt + 1) % T::STAGES, 0, f, o0, o1, acc);
+    advance<T, 1>(sA, (kt + 1) % T::STAGES, 0, f, o0, o1, acc);
   }
-  advance<T, 0>(sA, sB, (nk - 1) % T::STAGES, 1, f, o0, o1, acc);
+  advance<T, 0>(sA, (nk - 1) % T::STAGES, 1, f, o0, o1, acc);
   last_step<T>(o0, o1, acc);
 
   // epilogue: register r of block (i, j) is row 4 (lane / 16) + r and column lane % 16 of
