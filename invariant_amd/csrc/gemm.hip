@@ -820,11 +820,11 @@ TileKind pick_tile(int64_t M, int64_t N, int cus) {
 // 128 x 128 grid leaves most CUs idle (N = 4096 gives 32 workgroups).  Here one wave owns CB
 // 16-column blocks and RB 16-row blocks (all M rows, or with `split` = 2 one of two 32-row
 // halves; the two waves of a column block then sit on one XCD, whose L2 serves the second
-// its weights) and loads its instruction operands
-// straight from global memory into registers, PF K steps ahead: lane l takes the 16 bytes
-// at row l % 16, k offset 32 t + 8 (l / 16) of K step t, which is exactly its operand of the
-// instruction, so there is no LDS, no barrier and no other wave to wait for.  What is left is
-// the chain itself: K / 32 dependent instructions per accumulator.  Every output element
+// its weights) and loads its instruction operands straight from global memory into
+// registers, PF K steps ahead: lane l takes the 16 bytes at row l % 16, k offset
+// 32 t + 8 (l / 16) of K step t, which is exactly its operand of the instruction, so there
+// is no LDS, no barrier and no other wave to wait for.  What is left is the chain itself:
+// K / 32 dependent instructions per accumulator.  Every output element
 // sees the instruction sequence of every other configuration (same instruction, +0 start,
 // ascending 32-wide K steps, same lane-to-k assignment), so its bits do not change.
 // K is a multiple of 8 with at least 2 PF whole steps; a last, partial step is loaded up
