@@ -30,36 +30,40 @@ __global__ void embedding_kernel(const int32_t* __restrict__ ids, const void* __
   store_from_f32(out, i, v, out_f32);
 }
 
-// One thread per (token, head, i < D/2) pair of q or k; v is copied.
+// One thread per (token, i < D/2): the rotation angle depends on the token's position and
+// on i only, so the thread computes its cosine and sine once (fp64 angle, each rounded to
+// fp32) and rotates pair (i, i + D/2) of every q and k head, then copies v.  Each element
+// gets the same operations whatever the number of tokens or heads.
 __global__ void rope_qkv_kernel(const void* __restrict__ qkv, int64_t ld, int qkv_f32,
                                 const int32_t* __restrict__ positions, uint16_t* __restrict__ q,
                                 uint16_t* __restrict__ k, uint16_t* __restrict__ v, int64_t T,
                                 int hq, int hkv, int hd, double base) {
   const int half = hd / 2;
-  const int heads = hq + 2 * hkv;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= T * heads * half) return;
-  const int64_t t = i / (heads * half);
-  const int h = static_cast<int>((i / half) % heads);
+  if (i >= T * half) return;
+  const int64_t t = i / half;
   const int j = static_cast<int>(i % half);
-  const int64_t src = t * ld + static_cast<int64_t>(h) * hd;
-  const float x1 = load_as_f32(qkv, src + j, qkv_f32);
-  const float x2 = load_as_f32(qkv, src + j + half, qkv_f32);
-  if (h >= hq + hkv) {
-    uint16_t* dst = v + (t * hkv + (h - hq - hkv)) * hd;
-    dst[j] = f32_to_bf16(x1);
-    dst[j + half] = f32_to_bf16(x2);
-    return;
-  }
   const double inv = pow(base, -2.0 * j / hd);
   const double ang = static_cast<double>(positions[t]) * inv;
   const float c = static_cast<float>(cos(ang));
   const float s = static_cast<float>(sin(ang));
-  const float y1 = x1 * c - x2 * s;
-  const float y2 = x2 * c + x1 * s;
-  uint16_t* dst = h < hq ? q + (t * hq + h) * hd : k + (t * hkv + (h - hq)) * hd;
-  dst[j] = f32_to_bf16(y1);
-  dst[j + half] = f32_to_bf16(y2);
+  const int64_t row = t * ld;
+  for (int h = 0; h < hq + hkv; ++h) {
+    const int64_t src = row + static_cast<int64_t>(h) * hd;
+    const float x1 = load_as_f32(qkv, src + j, qkv_f32);
+    const float x2 = load_as_f32(qkv, src + j + half, qkv_f32);
+    const float y1 = x1 * c - x2 * s;
+    const float y2 = x2 * c + x1 * s;
+    uint16_t* dst = h < hq ? q + (t * hq + h) * hd : k + (t * hkv + (h - hq)) * hd;
+    dst[j] = f32_to_bf16(y1);
+    dst[j + half] = f32_to_bf16(y2);
+  }
+  for (int h = 0; h < hkv; ++h) {
+    const int64_t src = row + static_cast<int64_t>(hq + hkv + h) * hd;
+    uint16_t* dst = v + (t * hkv + h) * hd;
+    dst[j] = f32_to_bf16(load_as_f32(qkv, src + j, qkv_f32));
+    dst[j + half] = f32_to_bf16(load_as_f32(qkv, src + j + half, qkv_f32));
+  }
 }
 
 __global__ void swiglu_kernel(const uint16_t* __restrict__ gu, int64_t ld, uint16_t* __restrict__ out,
@@ -76,6 +80,19 @@ __global__ void residual_add_kernel(const void* __restrict__ a, int af, const vo
   if (i >= n) return;
   const float v = load_as_f32(a, i, af) + load_as_f32(b, i, bf);
   store_from_f32(out, i, v, of);
+}
+
+// bf16 + bf16 -> bf16 with every pointer 16-byte aligned: 8 elements per thread (the same
+// add and rounding per element as above).
+__global__ void residual_add_bf16x8_kernel(const u16x8* __restrict__ a, const u16x8* __restrict__ b,
+                                           u16x8* out, int64_t n8) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const u16x8 x = a[i], y = b[i];
+  u16x8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16(bf16_to_f32(x[e]) + bf16_to_f32(y[e]));
+  out[i] = o;
 }
 
 unsigned blocks_for(int64_t n, int per) { return static_cast<unsigned>((n + per - 1) / per); }
@@ -107,7 +124,7 @@ extern "C" int bi_rope_qkv(const void* qkv, int64_t ldqkv, int qkv_dtype, const 
   if (ldqkv < static_cast<int64_t>(num_q_heads + 2 * num_kv_heads) * head_dim) return BI_ERR_SHAPE;
   if (T == 0) return BI_OK;
   if (!qkv || !positions || !q || !k || !v) return BI_ERR_NULL;
-  const int64_t n = T * (num_q_heads + 2 * num_kv_heads) * (head_dim / 2);
+  const int64_t n = T * (head_dim / 2);
   rope_qkv_kernel<<<blocks_for(n, 256), 256, 0, as_stream(stream)>>>(
       qkv, ldqkv, qkv_dtype == BI_F32, positions, static_cast<uint16_t*>(q),
       static_cast<uint16_t*>(k), static_cast<uint16_t*>(v), T, num_q_heads, num_kv_heads, head_dim,
@@ -132,6 +149,12 @@ extern "C" int bi_residual_add(const void* a, int a_dtype, const void* b, int b_
   if (n < 0) return BI_ERR_SHAPE;
   if (n == 0) return BI_OK;
   if (!a || !b || !out) return BI_ERR_NULL;
+  if (a_dtype == BI_BF16 && b_dtype == BI_BF16 && out_dtype == BI_BF16 && n % 8 == 0 && aligned16(a) &&
+      aligned16(b) && aligned16(out)) {
+    residual_add_bf16x8_kernel<<<blocks_for(n / 8, 256), 256, 0, as_stream(stream)>>>(
+        static_cast<const u16x8*>(a), static_cast<const u16x8*>(b), static_cast<u16x8*>(out), n / 8);
+    return launch_status();
+  }
   residual_add_kernel<<<blocks_for(n, 256), 256, 0, as_stream(stream)>>>(
       a, a_dtype == BI_F32, b, b_dtype == BI_F32, out, out_dtype == BI_F32, n);
   return launch_status();
