@@ -30,39 +30,49 @@ __global__ void embedding_kernel(const int32_t* __restrict__ ids, const void* __
   store_from_f32(out, i, v, out_f32);
 }
 
-// One thread per (token, i < D/2): the rotation angle depends on the token's position and
-// on i only, so the thread computes its cosine and sine once (fp64 angle, each rounded to
-// fp32) and rotates pair (i, i + D/2) of every q and k head, then copies v.  Each element
-// gets the same operations whatever the number of tokens or heads.
+// One thread per (token, group of hpt heads, i < D/2): the rotation angle depends on the
+// token's position and on i only, so the thread computes its cosine and sine once (fp64
+// angle, each rounded to fp32) for the pairs (i, i + D/2) of all its q and k heads and copies
+// its v heads.  Each element gets the same operations whatever the number of tokens, heads
+// or heads per thread (one for a few tokens, where parallelism matters more than the
+// repeated cosines; eight for many).
 __global__ void rope_qkv_kernel(const void* __restrict__ qkv, int64_t ld, int qkv_f32,
                                 const int32_t* __restrict__ positions, uint16_t* __restrict__ q,
                                 uint16_t* __restrict__ k, uint16_t* __restrict__ v, int64_t T,
-                                int hq, int hkv, int hd, double base) {
+                                int hq, int hkv, int hd, double base, int hpt) {
   const int half = hd / 2;
+  const int heads = hq + 2 * hkv;
+  const int groups = (heads + hpt - 1) / hpt;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= T * half) return;
-  const int64_t t = i / half;
+  if (i >= T * groups * half) return;
   const int j = static_cast<int>(i % half);
-  const double inv = pow(base, -2.0 * j / hd);
-  const double ang = static_cast<double>(positions[t]) * inv;
-  const float c = static_cast<float>(cos(ang));
-  const float s = static_cast<float>(sin(ang));
+  const int64_t tg = i / half;
+  const int64_t t = tg / groups;
+  const int h0 = static_cast<int>(tg % groups) * hpt;
+  const int h1 = min(h0 + hpt, heads);
   const int64_t row = t * ld;
-  for (int h = 0; h < hq + hkv; ++h) {
+  float c = 1.f, s = 0.f;
+  if (h0 < hq + hkv) {
+    const double inv = pow(base, -2.0 * j / hd);
+    const double ang = static_cast<double>(positions[t]) * inv;
+    c = static_cast<float>(cos(ang));
+    s = static_cast<float>(sin(ang));
+  }
+  for (int h = h0; h < h1; ++h) {
     const int64_t src = row + static_cast<int64_t>(h) * hd;
     const float x1 = load_as_f32(qkv, src + j, qkv_f32);
     const float x2 = load_as_f32(qkv, src + j + half, qkv_f32);
+    if (h >= hq + hkv) {   // v: copied
+      uint16_t* dst = v + (t * hkv + (h - hq - hkv)) * hd;
+      dst[j] = f32_to_bf16(x1);
+      dst[j + half] = f32_to_bf16(x2);
+      continue;
+    }
     const float y1 = x1 * c - x2 * s;
     const float y2 = x2 * c + x1 * s;
     uint16_t* dst = h < hq ? q + (t * hq + h) * hd : k + (t * hkv + (h - hq)) * hd;
     dst[j] = f32_to_bf16(y1);
     dst[j + half] = f32_to_bf16(y2);
-  }
-  for (int h = 0; h < hkv; ++h) {
-    const int64_t src = row + static_cast<int64_t>(hq + hkv + h) * hd;
-    uint16_t* dst = v + (t * hkv + h) * hd;
-    dst[j] = f32_to_bf16(load_as_f32(qkv, src + j, qkv_f32));
-    dst[j + half] = f32_to_bf16(load_as_f32(qkv, src + j + half, qkv_f32));
   }
 }
 
@@ -124,11 +134,13 @@ extern "C" int bi_rope_qkv(const void* qkv, int64_t ldqkv, int qkv_dtype, const 
   if (ldqkv < static_cast<int64_t>(num_q_heads + 2 * num_kv_heads) * head_dim) return BI_ERR_SHAPE;
   if (T == 0) return BI_OK;
   if (!qkv || !positions || !q || !k || !v) return BI_ERR_NULL;
-  const int64_t n = T * (head_dim / 2);
+  const int hpt = T >= 256 ? 8 : 1;
+  const int64_t groups = (num_q_heads + 2 * num_kv_heads + hpt - 1) / hpt;
+  const int64_t n = T * groups * (head_dim / 2);
   rope_qkv_kernel<<<blocks_for(n, 256), 256, 0, as_stream(stream)>>>(
       qkv, ldqkv, qkv_dtype == BI_F32, positions, static_cast<uint16_t*>(q),
       static_cast<uint16_t*>(k), static_cast<uint16_t*>(v), T, num_q_heads, num_kv_heads, head_dim,
-      base);
+      base, hpt);
   return launch_status();
 }
 
