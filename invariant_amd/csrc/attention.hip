@@ -665,10 +665,14 @@ __global__ __launch_bounds__(256) void attn_group_kernel(
 }
 
 // ---------------------------------------------------------------- step 2b: prefill walk
-// One workgroup per 16 / G consecutive tokens (a block aligned to the global token index)
-// and kv head, i.e. 16 columns; it walks chunks 0.. in order and merges in registers (wave
-// w keeps d-blocks 2w, 2w + 1).  A block that straddles two sequences is processed once
-// per sequence with the other sequence's columns switched off.
+// One workgroup per WALK_NG blocks of 16 / G consecutive tokens (aligned to the global token
+// index) and kv head: WALK_NG groups of 16 columns.  It walks chunks 0.. in order; each
+// chunk's K and V operands are loaded once and serve every group (chunk_scores and
+// chunk_values per group, the V masking depending on the sequence only), and each group
+// merges its chunks in registers (wave w keeps d-blocks 2w, 2w + 1).  A block that straddles
+// two sequences is processed once per sequence with the other sequence's columns off.
+constexpr int WALK_NG = 2;
+
 __global__ __launch_bounds__(256) void attn_walk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
@@ -681,78 +685,106 @@ __global__ __launch_bounds__(256) void attn_walk_kernel(
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15;
   const int kvh = blockIdx.y;
-  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * NT;
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * NT * WALK_NG;
   if (tok0 >= num_tokens) return;
-  const int64_t my_tok = tok0 + col / G;
-  const bool tok_ok = my_tok < num_tokens;
   const int head = kvh * G + col % G;
-  const int my_b = tok_ok ? find_seq(qsl, batch, static_cast<int>(my_tok)) : -1;
-  const int my_pos = tok_ok ? seq_lens[my_b] - (qsl[my_b + 1] - qsl[my_b]) +
-                                  (static_cast<int>(my_tok) - qsl[my_b])
-                            : -1;
+  int64_t my_tok[WALK_NG];
+  int my_b[WALK_NG], my_pos[WALK_NG];
+#pragma unroll
+  for (int gi = 0; gi < WALK_NG; ++gi) {
+    my_tok[gi] = tok0 + gi * NT + col / G;
+    const bool tok_ok = my_tok[gi] < num_tokens;
+    my_b[gi] = tok_ok ? find_seq(qsl, batch, static_cast<int>(my_tok[gi])) : -1;
+    my_pos[gi] = tok_ok ? seq_lens[my_b[gi]] - (qsl[my_b[gi] + 1] - qsl[my_b[gi]]) +
+                              (static_cast<int>(my_tok[gi]) - qsl[my_b[gi]])
+                        : -1;
+  }
   int b = find_seq(qsl, batch, static_cast<int>(tok0));
-  const int64_t tok_last = (tok0 + NT < num_tokens ? tok0 + NT : num_tokens) - 1;
+  const int64_t tok_last = (tok0 + NT * WALK_NG < num_tokens ? tok0 + NT * WALK_NG : num_tokens) - 1;
   const int b_last = find_seq(qsl, batch, static_cast<int>(tok_last));
   for (; b <= b_last; ++b) {
     if (qsl[b + 1] == qsl[b]) continue;
-    const bool mine = my_b == b;
-    const int pcol = mine ? my_pos : -1;
-    u16x8 qop[4];
-    load_q(q, mine ? my_tok : 0, head, hq, mine, qop);
+    u16x8 qop[WALK_NG][4];
+    int pcol[WALK_NG];
+    int pmax = -1;
+#pragma unroll
+    for (int gi = 0; gi < WALK_NG; ++gi) {
+      const bool mine = my_b[gi] == b;
+      pcol[gi] = mine ? my_pos[gi] : -1;
+      load_q(q, mine ? my_tok[gi] : 0, head, hq, mine, qop[gi]);
+      pmax = max(pmax, pcol[gi]);
+    }
     const int L = seq_lens[b];
     Seq sq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, kvh, L, max_pages, __builtin_ctz(ps)};
     // highest position among this sequence's columns (the same in every wave)
-    int pmax = pcol;
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) pmax = max(pmax, __shfl_xor(pmax, off, 64));
     // two merge levels, as the split path: chunks within each group of GROUP, then groups
-    float m = 0.f, l = 0.f, mg = 0.f, lg = 0.f;
-    floatx4 o[2], og[2];
+    float m[WALK_NG], l[WALK_NG], mg[WALK_NG], lg[WALK_NG];
+    floatx4 o[WALK_NG][2], og[WALK_NG][2];
+#pragma unroll
+    for (int gi = 0; gi < WALK_NG; ++gi) m[gi] = l[gi] = mg[gi] = lg[gi] = 0.f;
     for (int c = 0; c * CHUNK <= pmax; ++c) {
-      float m_c, l_c;
-      floatx4 oc[2];
-      chunk_partial(sq, c, qop, pcol, sl2, sh, m_c, l_c, oc);
-      if (c * CHUNK > pcol) continue;
-      if (c % GROUP == 0) {
-        mg = m_c;
-        lg = l_c;
-        og[0] = oc[0];
-        og[1] = oc[1];
-      } else {
-        float a, bb;
-        merge_step(mg, lg, m_c, l_c, a, bb);
+      const int pg = chunk_pages(sq, c);
+      u16x8 kop[2][2][4], vop[2][8];
+      chunk_load_k(sq, pg, kop);
+      chunk_load_v(sq, pg, vop);
+      issue_fence();
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int gi = 0; gi < WALK_NG; ++gi) {
+        float m_c, l_c;
+        floatx4 oc[2];
+        {
+          floatx4 sc[2][2];
+          float mx, lsum;
+          chunk_scores(c, kop, qop[gi], pcol[gi], sl2, sh, sc, mx, lsum);
+          chunk_values(sq, c, vop, sc, mx, lsum, sh, m_c, l_c, oc);
+        }
+        if (c * CHUNK > pcol[gi]) continue;
+        if (c % GROUP == 0) {
+          mg[gi] = m_c;
+          lg[gi] = l_c;
+          og[gi][0] = oc[0];
+          og[gi][1] = oc[1];
+        } else {
+          float a, bb;
+          merge_step(mg[gi], lg[gi], m_c, l_c, a, bb);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) og[j][r] = mix(og[j][r], oc[j][r], a, bb);
-      }
-      if (c % GROUP != GROUP - 1 && c != pcol / CHUNK) continue;   // group not complete yet
-      if (c < GROUP) {
-        m = mg;
-        l = lg;
-        o[0] = og[0];
-        o[1] = og[1];
-      } else {
-        float a, bb;
-        merge_step(m, l, mg, lg, a, bb);
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+            for (int r = 0; r < 4; ++r) og[gi][j][r] = mix(og[gi][j][r], oc[j][r], a, bb);
+        }
+        if (c % GROUP != GROUP - 1 && c != pcol[gi] / CHUNK) continue;   // group not complete yet
+        if (c < GROUP) {
+          m[gi] = mg[gi];
+          l[gi] = lg[gi];
+          o[gi][0] = og[gi][0];
+          o[gi][1] = og[gi][1];
+        } else {
+          float a, bb;
+          merge_step(m[gi], l[gi], mg[gi], lg[gi], a, bb);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[j][r] = mix(o[j][r], og[j][r], a, bb);
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[gi][j][r] = mix(o[gi][j][r], og[gi][j][r], a, bb);
+        }
       }
     }
-    if (!mine) continue;
-    const int64_t orow = my_tok * hq + head;
-    const int d0 = 4 * (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int gi = 0; gi < WALK_NG; ++gi) {
+      if (my_b[gi] != b) continue;
+      const int64_t orow = my_tok[gi] * hq + head;
+      const int d0 = 4 * (lane >> 4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = o[j][r] / l;
-        const int64_t idx = orow * HD + 16 * (2 * w + j) + d0 + r;
-        if (out_f32) static_cast<float*>(out)[idx] = v;
-        else static_cast<uint16_t*>(out)[idx] = f32_to_bf16(v);
-      }
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = o[gi][j][r] / l[gi];
+          const int64_t idx = orow * HD + 16 * (2 * w + j) + d0 + r;
+          if (out_f32) static_cast<float*>(out)[idx] = v;
+          else static_cast<uint16_t*>(out)[idx] = f32_to_bf16(v);
+        }
+    }
   }
 }
 
@@ -852,7 +884,7 @@ extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new,
         ws_ml, ps_o, seq_lens, query_start_loc, batch, num_q_heads, static_cast<int>(slots), rows,
         out, of, uc, fine ? GROUP : 1);
   } else {
-    const int NT = 16 / G;
+    const int NT = 16 / G * WALK_NG;
     const int64_t blocks = (num_tokens + NT - 1) / NT;
     attn_walk_kernel<<<dim3(static_cast<unsigned>(blocks), num_kv_heads), dim3(256), 0, s>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
