@@ -248,7 +248,9 @@ int bi_attention_batchdep_split(const void* q, const void* k_new, const void* v_
  *   logits   [M, V] fp32, row stride ld
  *   logprobs [M, V] fp32, row stride ld, or NULL to skip
  *   argmax   [M] int32
- * Errors: BI_ERR_NULL, BI_ERR_SHAPE (V < 1 with M > 0, ld < V).
+ * With logprobs NULL only the argmax is computed (the same index).
+ * Errors: BI_ERR_NULL, BI_ERR_SHAPE (V < 1 with M > 0, ld < V, logprobs overlapping
+ * logits).
  */
 int bi_logsoftmax_argmax(const float* logits, int64_t M, int64_t V, int64_t ld, float* logprobs,
                          int32_t* argmax, void* stream);

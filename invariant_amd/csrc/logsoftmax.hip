@@ -324,6 +324,75 @@ __global__ __launch_bounds__(kWideThreads) void logsoftmax_argmax_wide_kernel(
   }
 }
 
+// Argmax alone (logprobs NULL) for the rows the wide form takes: no EXP or LOG is needed,
+// and the maximum is found in two cheap passes instead of the sequential pick: the largest
+// value and whether a NaN is present, then the lowest index holding that value (-0 == +0)
+// or the lowest NaN.  Thread t holds vectors t + 256 j.  The index equals the pick's.
+__global__ __launch_bounds__(kThreads) void argmax_rows_kernel(const float* __restrict__ logits,
+                                                               int V, int64_t ld,
+                                                               int32_t* __restrict__ argmax) {
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int u = tid % kWave, g = tid / kWave;
+  const int nvec = V / 4;                 // kThreads <= nvec <= NVC * kThreads
+  const float* x = logits + row * ld;
+  __shared__ float smax[kThreads / kWave];
+  __shared__ int sflag[kThreads / kWave];
+  __shared__ int sidx[kThreads / kWave];
+
+  float c[NVC][4];
+#pragma unroll
+  for (int j = 0; j < NVC; ++j) {
+    const int v = tid + j * kThreads;
+    if (v < nvec) {
+      const floatx4 e = *reinterpret_cast<const floatx4*>(x + static_cast<int64_t>(v) * 4);
+      c[j][0] = e[0]; c[j][1] = e[1]; c[j][2] = e[2]; c[j][3] = e[3];
+    }
+  }
+  float mx = -__builtin_huge_valf();
+  int nan = 0;
+#pragma unroll
+  for (int j = 0; j < NVC; ++j)
+    if (tid + j * kThreads < nvec) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mx = fmaxf(mx, c[j][i]);
+        nan |= c[j][i] != c[j][i];
+      }
+    }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+    nan |= __shfl_xor(nan, off, kWave);
+  }
+  if (u == 0) {
+    smax[g] = mx;
+    sflag[g] = nan;
+  }
+  __syncthreads();
+  mx = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+  const bool any_nan = (sflag[0] | sflag[1] | sflag[2] | sflag[3]) != 0;
+
+  int best = 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < NVC; ++j) {
+    const int v = tid + j * kThreads;
+    if (v < nvec) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = c[j][i];
+        const bool hit = any_nan ? (e != e) : (e == mx);
+        best = hit ? min(best, v * 4 + i) : best;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) best = min(best, __shfl_xor(best, off, kWave));
+  if (u == 0) sidx[g] = best;
+  __syncthreads();
+  if (tid == 0) argmax[row] = min(min(sidx[0], sidx[1]), min(sidx[2], sidx[3]));
+}
+
 }  // namespace
 }  // namespace bi
 
@@ -339,7 +408,15 @@ extern "C" int bi_logsoftmax_argmax(const float* logits, int64_t M, int64_t V, i
   const int vec_in = aligned16(logits) && (ld % 4) == 0;
   const int vec_out = logprobs && aligned16(logprobs) && (ld % 4) == 0;
   const bool full = vec_in && (V % 4) == 0 && (!logprobs || vec_out);
-  if (full && V >= 4 * kThreads && V <= 4 * NVC * kThreads)
+  if (logprobs) {
+    // outputs must not alias inputs (rows past the register cache are read twice)
+    const int64_t extent = (M - 1) * ld + V;
+    if (logprobs < logits + extent && logits < logprobs + extent) return BI_ERR_SHAPE;
+  }
+  if (full && !logprobs && V >= 4 * kThreads && V <= 4 * NVC * kThreads)
+    argmax_rows_kernel<<<dim3(static_cast<unsigned>(M)), dim3(kThreads), 0, as_stream(stream)>>>(
+        logits, static_cast<int>(V), ld, argmax);
+  else if (full && V >= 4 * kThreads && V <= 4 * NVC * kThreads)
     logsoftmax_argmax_wide_kernel<<<dim3(static_cast<unsigned>(M)), dim3(kWideThreads), 0,
                                     as_stream(stream)>>>(logits, static_cast<int>(V), ld,
                                                          logprobs, argmax);

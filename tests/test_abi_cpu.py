@@ -75,6 +75,7 @@ def test_validation_rejects_before_launch(lib):
     assert lib.bi_add_rmsnorm(P, P, P, 1, P, P, 1, -1, 64, 1e-5, None) == -2
     assert lib.bi_logsoftmax_argmax(P, 2, 10, 8, None, P, None) == -2
     assert lib.bi_logsoftmax_argmax(None, 2, 10, 12, None, P, None) == -1
+    assert lib.bi_logsoftmax_argmax(P, 2, 1024, 1024, P, P, None) == -2   # logprobs over logits
     # attention: unsupported head_dim, group, page size; missing workspace
     args = [P] * 8
     def att(T=4, hq=32, hkv=8, d=128, ps=16, maxp=4, msl=64, ws=None, wsz=0, B=2):

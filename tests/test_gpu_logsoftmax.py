@@ -43,7 +43,20 @@ def test_special_rows(lib):
     x[4, :] = -np.inf; x[4, 100] = 1.0
     x[5, 17] = 150.0
     x[6] = np.random.default_rng(0).standard_normal(v).astype(np.float32) * 40
+    # rows whose candidates lie in different parts of the row (the split form reduces the
+    # maximum across workgroups): far ties, a late NaN after an early maximum, all NaN,
+    # +inf, the maximum in the last element
+    y = (np.random.default_rng(1).standard_normal((6, v)) * 2).astype(np.float32)
+    y[0, 300] = y[0, 31999] = y[0, 17000] = 9.0      # tie -> 300
+    y[1, 2] = 50.0; y[1, 29999] = np.nan             # NaN wins -> 29999
+    y[2, :] = np.nan
+    y[3, 8000] = np.inf; y[3, 8001] = np.inf         # -> 8000, logprobs NaN / -inf
+    y[4, v - 1] = 30.0
+    y[5, :] = -np.inf; y[5, 70] = -0.0; y[5, 4000] = 0.0   # -> 70
+    x = np.concatenate([x, y])
     _cmp(lib, x)
+    _, only = lib.bi_logsoftmax_argmax(f32(x), want_logprobs=False)
+    assert np.array_equal(host(only), logsoftmax_argmax(x)[1])
 
 
 def test_batch_invariance_and_repeats(lib):
