@@ -818,9 +818,9 @@ TileKind pick_tile(int64_t M, int64_t N, int cus) {
 
 // Few-row GEMM (M <= 64).  At decode sizes the weight stream bounds the call, and a
 // 128 x 128 grid leaves most CUs idle (N = 4096 gives 32 workgroups).  Here one wave owns CB
-// 16-column blocks and RB 16-row blocks (all M rows, or with `split` = 2 one of two 32-row
-// halves; the two waves of a column block then sit on one XCD, whose L2 serves the second
-// its weights) and loads its instruction operands straight from global memory into
+// 16-column blocks and RB 16-row blocks (all M rows, or with `split` = 2 or 4 one of that many
+// row slices of 16 RB rows; the waves of a column block then sit on one XCD, whose L2 serves
+// the later ones their weights) and loads its instruction operands straight from global memory into
 // registers, PF K steps ahead: lane l takes the 16 bytes at row l % 16, k offset
 // 32 t + 8 (l / 16) of K step t, which is exactly its operand of the instruction, so there
 // is no LDS, no barrier and no other wave to wait for.  What is left is the chain itself:
@@ -839,13 +839,14 @@ __global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
   static_assert(!PAIR || CB == 1, "paired waves hold one block each");
   const int lane = threadIdx.x & 63;
   const int wave = PAIR ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
-  // workgroup id -> (column block, row half): ids 8 s + x and 8 (s + 1) + x (one XCD) share
-  // a column block; with split = 1 the id is the column block (the pair's, for PAIR)
+  // workgroup id -> (column block, row slice): ids 8 s + x, s = split c .. split c + split - 1
+  // (one XCD) share column block 8 c + x; with split = 1 the id is the column block (the
+  // pair's, for PAIR)
   int cblk = PAIR ? 2 * blockIdx.x + wave : blockIdx.x, row0 = 0;
-  if (split == 2) {
+  if (split > 1) {
     const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    cblk = (slot >> 1) * 8 + x;
-    row0 = (slot & 1) * RB * 16;
+    cblk = (slot / split) * 8 + x;
+    row0 = (slot % split) * RB * 16;
     if (cblk * CB * 16 >= N || row0 >= M) return;   // grid padding (wave-uniform)
   }
   const int col0 = cblk * (CB * 16);
@@ -983,7 +984,9 @@ __global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
 // to 16 rows one 16 x 16 block (16 x 32 from 9 rows on for wide N, and for SwiGLU, whose
 // gate and up blocks pair up), up to 32 rows 32 x 32 blocks, above that 64 x 32 blocks, or
 // two waves of 32 x 32 per column block (one per 32-row half) while the column blocks
-// number under three quarters of the CUs.
+// number under three quarters of the CUs.  Where waves of 16-row slices still fit one round
+// (2 or 4 per 32-column block, at most one per CU), each takes a 16 x 32 block: two or four
+// times the waves streaming weights, with A reads half the weight reads.
 struct RowsCfg {
   int rb, cb, pf, split;
   bool pair = false;   // SwiGLU with one 16-column block per wave, two waves per workgroup
@@ -995,8 +998,10 @@ RowsCfg rows_cfg(int64_t M, int64_t N, int mode) {
     const bool wide = mode == kOutSwiGLU || (M > 8 && (N + 15) / 16 >= 4 * cus);
     return {1, wide ? 2 : 1, 16, 1};
   }
-  if (M <= 32) return {2, 2, 12, 1};
-  if (4 * ((N + 31) / 32) >= 3 * cus) return {4, 2, 12, 1};
+  const int64_t ncb = (N + 31) / 32;
+  if (M <= 32) return 2 * ncb <= cus ? RowsCfg{1, 2, 12, 2} : RowsCfg{2, 2, 12, 1};
+  if (4 * ncb >= 3 * cus) return {4, 2, 12, 1};
+  if (4 * ncb <= cus) return {1, 2, 12, 4};
   return {2, 2, 12, 2};
 }
 
@@ -1014,7 +1019,7 @@ template <int RB, int CB, int PF, bool PAIR = false>
 void launch_rows_t(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                    int64_t lda, int64_t ldb, int64_t ldc, int cf, int split, hipStream_t s) {
   const int64_t ncb = (N + CB * 16 - 1) / (CB * 16);
-  const unsigned wgs = static_cast<unsigned>(PAIR ? (ncb + 1) / 2 : split == 1 ? ncb : 16 * ((ncb + 7) / 8));
+  const unsigned wgs = static_cast<unsigned>(PAIR ? (ncb + 1) / 2 : split == 1 ? ncb : 8 * split * ((ncb + 7) / 8));
   gemm_rows_kernel<RB, CB, PF, PAIR><<<dim3(wgs), dim3(PAIR ? 128 : 64), 0, s>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, int(M), int(N), int(K),
       lda, ldb, ldc, cf, split);
@@ -1026,6 +1031,7 @@ void launch_rows(const void* A, const void* B, void* C, int64_t M, int64_t N, in
   if (c.pair) launch_rows_t<1, 1, 16, true>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
   else if (c.rb == 4) launch_rows_t<4, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
   else if (c.rb == 2) launch_rows_t<2, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, c.split, s);
+  else if (c.split > 1) launch_rows_t<1, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, c.split, s);
   else if (c.cb == 2) launch_rows_t<1, 2, 16>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
   else launch_rows_t<1, 1, 16>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
 }

@@ -224,10 +224,10 @@ def test_output_views(lib):
 
 @pytest.mark.parametrize("m,n,k", [(5, 300, 1024), (40, 1000, 784), (64, 96, 1024), (1, 33, 1040),
                                    (17, 200, 1064), (33, 1000, 1024), (50, 72, 800), (9, 5000, 1024),
-                                   (49, 6200, 808)])
+                                   (49, 6200, 808), (24, 4096, 1048), (33, 2048, 1032)])
 def test_few_rows_vs_oracle(lib, m, n, k):
-    # the few-row kernel (M <= 64: 16 x 16, 16 x 32, 32 x 32 or 64 x 32 blocks, two waves per
-    # column block above 32 rows for narrow N): ragged column blocks, rows past M, padded
+    # the few-row kernel (M <= 64: 16 x 16, 16 x 32, 32 x 32 or 64 x 32 blocks, two or four
+    # waves of 16- or 32-row slices per column block for narrow N, up to one per CU): ragged column blocks, rows past M, padded
     # grids, the last partial round of prefetched K steps, a partial last K step (K % 32 = 8,
     # 16)
     assert lib.bi_gemm_tile(m, n, k)[1] <= 32
