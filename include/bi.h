@@ -139,7 +139,9 @@ int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
  * instruction operands loaded straight into registers 16 (or 12) K steps ahead; the block
  * is 16 x 16 up to 16 rows (16 x 32 from 9 rows when N / 16 is at least four times the CU
  * count), 32 x 32 up to 32 rows, 64 x 32 above (or, while N / 32 is under three quarters of
- * the CU count, two waves of 32 x 32 per column block, one per 32-row half).
+ * the CU count, two waves of 32 x 32 per column block, one per 32-row half); 16 x 32 in two
+ * (up to 32 rows) or four (above) waves per column block, one per 16-row slice, while those
+ * waves number at most the CU count.
  * Otherwise 256 x 256
  * (2-stage LDS ring) when that grid finishes in fewer rounds of the CU array; else
  * 128 x 128, with a 3-stage ring when the grid has no more tiles than CUs and a 2-stage
