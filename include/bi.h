@@ -22,8 +22,12 @@
  *
  * Conventions shared by every call
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library never
- *     allocates, frees or keeps device memory and holds no mutable global state, so
- *     calls may be issued from several threads.
+ *     allocates or frees device memory.  Its only process-wide state is read-only
+ *     after first use: the compute-unit count of each device and the number of
+ *     attention workgroups resident per CU, each queried from the HIP runtime on first
+ *     use and cached in an atomic (a race stores the same value twice).  They choose
+ *     launch shapes only, never a reduction order.  Calls may be issued from several
+ *     threads.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue work on it
  *     and return without waiting.
  *   - Arguments are validated before anything is launched.  On a validation error
@@ -122,12 +126,15 @@ int bi_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t D, 
  * whatever M is, wherever its row sits and whichever workgroup tile computes it; the
  * workgroup tile (bi_gemm_tile) follows the size of the output grid and changes no bit.
  * Alignment: A and B 16-byte aligned; lda, ldb multiples of 8 elements (4 for fp32 A).
- * Rows are read in 16-byte pieces: row i of A (of B) must be readable up to element
- * round_up(K, 8) (round_up(K, 4) for fp32 A), which lda (ldb) >= that guarantees for
- * every row but the last.
+ * Rows are read in 16-byte pieces: row i of A (of a [N, K] B) must be readable up to
+ * element round_up(K, 8) (round_up(K, 4) for fp32 A), which lda (ldb) >= that guarantees
+ * for every row but the last.
+ * BI_B_KN runs a register-staged 128 x 128 tile that transposes each 4 x 8 block of B on
+ * its way into on-chip memory; every output element then sees the same operands, lanes and
+ * instruction sequence as with the [N, K] copy of B, so C is bit for bit the BI_B_NK result
+ * (at a lower rate than the [N, K] kernels).  A [K, N] B is read only inside its N columns.
  * Errors: BI_ERR_NULL, BI_ERR_SHAPE (negative sizes, K < 1 with M*N > 0, strides too
- * small), BI_ERR_DTYPE, BI_ERR_ALIGN; BI_B_KN is not implemented yet and returns
- * BI_ERR_UNSUPPORTED.
+ * small), BI_ERR_DTYPE, BI_ERR_ALIGN.
  */
 int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
             int64_t ldb, int64_t ldc, int b_layout, int a_dtype, int c_dtype, void* stream);

@@ -22,8 +22,10 @@
 //   distinct banks; bf16 results leave through LDS as 16-byte row pieces.
 //   Up to 64 rows: one wave per 16 (or 32) output columns and all rows loads its operands
 //   straight into registers.
-// The fp32-A path, operands of 4 GiB or more and the split-K comparison variant stage
-// through registers instead (128 x 128 tile); they share the instruction and the K order.
+// The fp32-A path, B given as [K, N] (the torch.mm orientation; each 4 x 8 block of it is
+// transposed on its way into LDS), operands of 4 GiB or more and the split-K comparison
+// variant stage through registers instead (128 x 128 tile); they share the instruction, the
+// lane-to-k assignment and the K order, so a [K, N] B gives the bits of its [N, K] copy.
 //
 // A may be fp32 ("FP32 upcast" of the cross-vendor mismatch abstract): each value is
 // split exactly into bf16 hi + mid + lo (truncations, so hi + mid + lo == a for normal
@@ -89,7 +91,25 @@ __device__ __forceinline__ void split3(const float* p, int64_t k, int64_t K, boo
   }
 }
 
-template <bool AF32>
+// B given as [K, N] (torch.mm orientation): 8 consecutive columns of one k row, columns at
+// or past N and rows at or past ke read as zeros (nothing past the matrix is touched).
+__device__ __forceinline__ u16x8 load_kn_bf16x8(const uint16_t* B, int64_t ldb, int k, int n, int ke,
+                                                int N) {
+  u16x8 r = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (k >= ke || n >= N) return r;
+  const uint16_t* p = B + static_cast<int64_t>(k) * ldb + n;
+  if (n + 8 <= N) return *reinterpret_cast<const u16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (n + e < N) r[e] = p[e];
+  return r;
+}
+
+// Register-staged kernel.  BKN: B is [K, N]; each thread loads a 4 (k) x 8 (n) block of it
+// and writes the block transposed into the same [n][k] LDS layout the [N, K] operand fills,
+// so the operand reads, instructions and K order -- and every output bit -- are those of
+// the [N, K] layout.
+template <bool AF32, bool BKN = false>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const void* __restrict__ Ap, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
     int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int tiles_m, int tiles_n,
@@ -138,12 +158,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     b_off[i] = static_cast<int64_t>(b_ok[i] ? rb : 0) * ldb;
   }
 
+  // [K, N] staging: thread tid owns columns 8 (tid % 16) .. + 7 and k rows 4 (tid / 16) .. + 3
+  // of the 128 x 64 B stage
+  const int kn_n = tn * BN + (tid & 15) * 8, kn_k = (tid >> 4) * 4;
   auto load_stage = [&](Stage<AF32>& s, int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (AF32) split3(Af + a_off[i], k0 + st_k, ke, a_ok[i], s.a[0][i], s.a[NA > 1 ? 1 : 0][i], s.a[NA - 1][i]);
       else s.a[0][i] = load_bf16x8(Ab + a_off[i], k0 + st_k, ke, a_ok[i]);
-      s.b[i] = load_bf16x8(B + b_off[i], k0 + st_k, ke, b_ok[i]);
+      if (BKN) s.b[i] = load_kn_bf16x8(B, ldb, k0 + kn_k + i, kn_n, ke, N);
+      else s.b[i] = load_bf16x8(B + b_off[i], k0 + st_k, ke, b_ok[i]);
     }
   };
   auto store_stage = [&](const Stage<AF32>& s, int buf) {
@@ -152,7 +176,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
       const int o = (st_row + 32 * i) * LDS_LD + st_k;
 #pragma unroll
       for (int t = 0; t < NA; ++t) *reinterpret_cast<u16x8*>(&sA[buf][t][o]) = s.a[t][i];
-      *reinterpret_cast<u16x8*>(&sB[buf][o]) = s.b[i];
+      if (!BKN) *reinterpret_cast<u16x8*>(&sB[buf][o]) = s.b[i];
+    }
+    if (BKN) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const u16x4 col = {s.b[0][e], s.b[1][e], s.b[2][e], s.b[3][e]};
+        *reinterpret_cast<u16x4*>(&sB[buf][((tid & 15) * 8 + e) * LDS_LD + kn_k]) = col;
+      }
     }
   };
 
@@ -1103,13 +1134,21 @@ extern "C" int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t
   if (!A || !B || !C) return BI_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || (lda % (a_dtype == BI_F32 ? 4 : 8)) || (ldb % 8))
     return BI_ERR_ALIGN;
-  if (b_layout == BI_B_KN) return BI_ERR_UNSUPPORTED;
   const int tm = static_cast<int>((M + BM - 1) / BM), tn = static_cast<int>((N + BN - 1) / BN);
   const int64_t nwg = static_cast<int64_t>(tm) * tn;
   if (nwg > 0x7fffffffLL) return BI_ERR_SHAPE;
   hipStream_t s = as_stream(stream);
   const int cf = c_dtype == BI_F32;
-  if (a_dtype == BI_F32)
+  if (b_layout == BI_B_KN) {   // [K, N] B: register-staged kernel, transposed into LDS
+    if (a_dtype == BI_F32)
+      gemm_kernel<true, true><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
+          A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
+          0, int(K), 0);
+    else
+      gemm_kernel<false, true><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
+          A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
+          0, int(K), 0);
+  } else if (a_dtype == BI_F32)
     gemm_kernel<true><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
         A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,
         0, int(K), 0);

@@ -165,11 +165,12 @@ def _fusable(h, o, dims: Dims):
 
 
 def decoder_layer(w, h, batch: Batch, k_cache, v_cache, dims: Dims, fp32_variant=False,
-                  x=None, next_norm=None):
+                  x=None, next_norm=None, trace=None):
     """One layer on the residual stream h.  x, if given, is rmsnorm(h) with this layer's
     attention norm (the previous layer computed it with its residual add).  With next_norm the
     layer returns (h_out, rmsnorm(h_out) with next_norm), else h_out.  Every path gives the
-    same bits as the separate calls."""
+    same bits as the separate calls.  trace, if a dict, receives the layer's intermediate
+    tensors by name (h, x, qkv, q, k, v, attn, o, h2, x2, mlp, dn, out, next_x)."""
     T = h.shape[0]
     act = F32 if fp32_variant else BF16
     if x is None:
@@ -192,24 +193,37 @@ def decoder_layer(w, h, batch: Batch, k_cache, v_cache, dims: Dims, fp32_variant
         m = bi_swiglu(bi_gemm(x2, w["wgate_up"]))
     dn = bi_gemm(m, w["wdown"])
     if next_norm is None:
-        return bi_residual_add(h2, dn, out_dtype=act)
-    if _fusable(h2, dn, dims):
-        return bi_add_rmsnorm(h2, dn, next_norm, dims.eps, out_dtype=act)
-    h3 = bi_residual_add(h2, dn, out_dtype=act)
-    return h3, bi_rmsnorm(h3, next_norm, dims.eps, out_dtype=act)
+        res = bi_residual_add(h2, dn, out_dtype=act)
+        h3, x3 = res, None
+    elif _fusable(h2, dn, dims):
+        res = h3, x3 = bi_add_rmsnorm(h2, dn, next_norm, dims.eps, out_dtype=act)
+    else:
+        h3 = bi_residual_add(h2, dn, out_dtype=act)
+        res = h3, x3 = h3, bi_rmsnorm(h3, next_norm, dims.eps, out_dtype=act)
+    if trace is not None:
+        trace.update(h=h, x=x, qkv=qkv, q=q, k=k, v=v, attn=a, o=o, h2=h2, x2=x2, mlp=m, dn=dn,
+                     out=h3, next_x=x3)
+    return res
 
 
-def forward(model, batch: Batch, cache: PagedKVCache, dims: Dims, fp32_variant=False):
+def forward(model, batch: Batch, cache: PagedKVCache, dims: Dims, fp32_variant=False,
+            on_layer=None):
+    """The layers over one ragged call.  on_layer(li, trace) is called after each layer with
+    its intermediate tensors (see decoder_layer); trace["emb"] holds the embedding rows."""
     act = F32 if fp32_variant else BF16
     h = bi_embedding(batch.tokens, model["embed"], out_dtype=act)
     layers = model["layers"]
     x = None
     for li, w in enumerate(layers):
+        tr = None if on_layer is None else ({"emb": h} if li == 0 else {})
         if li + 1 < len(layers):   # the next layer's attention norm rides on this residual add
             h, x = decoder_layer(w, h, batch, cache.k[li], cache.v[li], dims, fp32_variant,
-                                 x=x, next_norm=layers[li + 1]["attn_norm"])
+                                 x=x, next_norm=layers[li + 1]["attn_norm"], trace=tr)
         else:
-            h = decoder_layer(w, h, batch, cache.k[li], cache.v[li], dims, fp32_variant, x=x)
+            h = decoder_layer(w, h, batch, cache.k[li], cache.v[li], dims, fp32_variant, x=x,
+                              trace=tr)
+        if on_layer is not None:
+            on_layer(li, tr)
     return h
 
 

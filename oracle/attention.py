@@ -23,26 +23,44 @@ import numpy as np
 from .fp import bf16_to_f64
 
 
-def attention_rows_f64(q_bits, k_bits, v_bits, positions, n_kv_heads=None) -> np.ndarray:
-    """q_bits [T, Hq, D] for the query tokens at absolute ``positions`` (length T);
-    k_bits, v_bits [L, Hkv, D] logical keys/values of the sequence.
+def attention_values_f64(q, k, v, positions, block: int = 256) -> np.ndarray:
+    """The definition above on float64 values: q [T, Hq, D] (queries at absolute
+    ``positions``), k, v [L, Hkv, D] (keys/values of positions 0..L-1).  Written as matrix
+    products over all heads of a kv group at once (a library product per step; the
+    arithmetic is the plain fp64 softmax-weighted sum), in blocks of queries.
     Returns o [T, Hq, D] float64."""
-    q = bf16_to_f64(q_bits)
-    k = bf16_to_f64(k_bits)
-    v = bf16_to_f64(v_bits)
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    pos = np.asarray(positions, dtype=np.int64)
     t, hq, d = q.shape
     hkv = k.shape[1]
     g = hq // hkv
     out = np.zeros((t, hq, d), dtype=np.float64)
+    if t == 0:
+        return out
     scale = 1.0 / np.sqrt(d)
-    for i, p in enumerate(np.asarray(positions, dtype=np.int64)):
-        kk = k[: p + 1]                                   # [p+1, Hkv, D]
-        vv = v[: p + 1]
-        for h in range(hq):
-            s = kk[:, h // g, :] @ q[i, h] * scale        # [p+1]
-            w = np.exp(s - s.max())
-            out[i, h] = (w @ vv[:, h // g, :]) / w.sum()
+    kt = np.ascontiguousarray(k.transpose(1, 2, 0))          # [Hkv, D, L]
+    vt = np.ascontiguousarray(v.transpose(1, 0, 2))          # [Hkv, L, D]
+    for b0 in range(0, t, block):
+        b1 = min(t, b0 + block)
+        pb = pos[b0:b1]
+        n = int(pb.max()) + 1                                # keys any query here can see
+        qg = q[b0:b1].reshape(b1 - b0, hkv, g, d).transpose(1, 2, 0, 3)   # [Hkv, G, T, D]
+        s = (qg @ kt[:, None, :, :n]) * scale                # [Hkv, G, T, n]
+        s = np.where(np.arange(n)[None, None, None, :] <= pb[None, None, :, None], s, -np.inf)
+        w = np.exp(s - s.max(axis=-1, keepdims=True))
+        o = (w @ vt[:, None, :n, :]) / w.sum(axis=-1, keepdims=True)       # [Hkv, G, T, D]
+        out[b0:b1] = o.transpose(2, 0, 1, 3).reshape(b1 - b0, hq, d)
     return out
+
+
+def attention_rows_f64(q_bits, k_bits, v_bits, positions, n_kv_heads=None) -> np.ndarray:
+    """q_bits [T, Hq, D] for the query tokens at absolute ``positions`` (length T);
+    k_bits, v_bits [L, Hkv, D] logical keys/values of the sequence (bf16 bits).
+    Returns o [T, Hq, D] float64."""
+    return attention_values_f64(bf16_to_f64(q_bits), bf16_to_f64(k_bits), bf16_to_f64(v_bits),
+                                positions)
 
 
 def attention_case_f64(case, which=None) -> list:

@@ -91,12 +91,33 @@ def test_validation_rejects_before_launch(lib):
     assert lib.bi_gemm_splitk_workspace_bytes(2048, 2048, 2048) == 2 * 2048 * 2048 * 4
 
 
+def _fn_constants(src, name):
+    """The f32c(0x...u) constants of device function `name`, in source order."""
+    start = src.index(name + "(")
+    body = src[src.index("{", start):]
+    depth, end = 0, 0
+    for i, ch in enumerate(body):
+        depth += ch == "{"
+        depth -= ch == "}"
+        if depth == 0:
+            end = i
+            break
+    return [int(h, 16) for h in re.findall(r"f32c\((0x[0-9a-f]+)u\)", body[:end])]
+
+
+def _bits(v):
+    return int(np.float32(v).view(np.uint32))
+
+
 def test_hip_constants_equal_oracle_derivation():
     """The EXP/LOG constants written as bit patterns in the HIP source are the values the
-    oracle derives from exact rationals (the two sides share no code)."""
+    oracle derives from exact rationals (the two sides share no code), each in its role:
+    EXP = 1/ln2, ln2 head, ln2 tail, then the Horner coefficients 1/7! .. 1/0!; LOG = sqrt 2,
+    the Horner coefficients 2/15 .. 2/1, then ln2 head and tail.  A swap of two coefficients
+    or of head and tail fails here."""
     src = open(os.path.join(ROOT, "invariant_amd", "csrc", "logsoftmax.hip")).read()
-    hexes = set(int(h, 16) for h in re.findall(r"f32c\((0x[0-9a-f]+)u\)", src))
-    want = [ORACLE_K["LOG2E"], ORACLE_K["LN2_HI"], ORACLE_K["LN2_LO"], ORACLE_K["SQRT2"],
-            *ORACLE_K["EXP_C"], *ORACLE_K["LOG_B"]]
-    for w in want:
-        assert int(np.float32(w).view(np.uint32)) in hexes, w
+    k = ORACLE_K
+    exp_want = [k["LOG2E"], k["LN2_HI"], k["LN2_LO"], *reversed(k["EXP_C"])]
+    log_want = [k["SQRT2"], *reversed(k["LOG_B"]), k["LN2_HI"], k["LN2_LO"]]
+    assert _fn_constants(src, "exp_cw") == [_bits(v) for v in exp_want]
+    assert _fn_constants(src, "log_at") == [_bits(v) for v in log_want]

@@ -60,20 +60,42 @@ def test_bits_equal():
     assert not bits_equal(z, nz)["ok"]
 
 
-def test_composed_drift_rejects_gross_errors():
-    from oracle.check import composed_drift
+def test_swiglu_interval_checker():
+    from oracle.check import swiglu_interval_within
+    from oracle.layer import swiglu_f64
     rng = np.random.default_rng(1)
+    g = rng.standard_normal((4, 512)) * 1.5
+    u = rng.standard_normal((4, 512)) * 1.5
+    # the exact composition: rounded gate/up, SwiGLU, one rounding
+    gb, ub = fp.bf16_to_f64(fp.f64_to_bf16(g)), fp.bf16_to_f64(fp.f64_to_bf16(u))
+    good = fp.f64_to_bf16(swiglu_f64(gb, ub))
+    assert swiglu_interval_within(good, g, u)["ok"]
+    # gate values one ulp off their rounding (allowed to the projection) still pass
+    g1 = fp.bf16_to_f64(fp.f64_to_bf16(gb + fp.ulp_bf16(gb)))
+    assert swiglu_interval_within(fp.f64_to_bf16(swiglu_f64(g1, ub)), g, u)["ok"]
+    # swapped gate and up, zeros, a missing silu, 4 ulps off, a NaN fail
+    assert not swiglu_interval_within(fp.f64_to_bf16(swiglu_f64(ub, gb)), g, u)["ok"]
+    assert not swiglu_interval_within(np.zeros_like(good), g, u)["ok"]
+    assert not swiglu_interval_within(fp.f64_to_bf16(gb * ub), g, u)["ok"]
+    off = fp.bf16_to_f64(good) * (1 + 2 ** -5)
+    assert not swiglu_interval_within(fp.f64_to_bf16(off), g, u)["ok"]
+    bad = good.copy(); bad[1, 3] = 0x7FC0
+    assert not swiglu_interval_within(bad, g, u)["ok"]
+
+
+def test_drift_reports():
+    from oracle.check import drift_report, logit_drift_report
+    rng = np.random.default_rng(2)
     ref = rng.standard_normal((1, 4096)) * 2.5
-    good = fp.f64_to_bf16(ref)
-    assert composed_drift(good, ref)["ok"]
-    # an ulp of noise on a third of the elements still passes
-    noisy = fp.bf16_to_f64(good).copy()
-    sel = rng.random((1, 4096)) < 0.33
-    noisy[sel] += fp.ulp_bf16(noisy[sel]) * rng.choice([-1, 1], int(sel.sum()))
-    assert composed_drift(fp.f64_to_bf16(noisy), ref)["ok"]
-    # a missing residual term, a sign flip or zeros fail
-    assert not composed_drift(fp.f64_to_bf16(ref * 0.7), ref)["ok"]
-    assert not composed_drift(fp.f64_to_bf16(-ref), ref)["ok"]
-    assert not composed_drift(np.zeros_like(good), ref)["ok"]
-    wrong = ref.copy(); wrong[0, :300] += 0.5
-    assert not composed_drift(fp.f64_to_bf16(wrong), ref)["ok"]
+    r = drift_report(fp.f64_to_bf16(ref), ref)
+    assert r["frac_exact"] == 1.0 and r["frac_within_1ulp"] == 1.0 and r["max_over_rms"] < 2 ** -6
+    r = drift_report(fp.f64_to_bf16(-ref), ref)
+    assert r["frac_exact"] < 0.01 and r["mean_over_rms"] > 1.0
+    lg = rng.standard_normal((3, 100))
+    got = lg.copy()
+    got[1, np.argmax(lg[1])] -= 10.0                 # row 1 loses its top token
+    rep = logit_drift_report(got, lg, k=5)
+    assert rep["token_agreement"] == 2 / 3 and rep["topk_agreement"] == 2 / 3
+    assert rep["max_abs"] == 10.0 and rep["rows"] == 3
+    top2 = np.sort(lg, axis=1)[:, -2:]
+    assert rep["min_margin"] == float((top2[:, 1] - top2[:, 0]).min())

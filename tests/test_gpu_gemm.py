@@ -132,6 +132,54 @@ def test_cfg2_repeats_prefixes_permutation(lib):
     assert same_bits(cm[0], ref[100]) and same_bits(cm[41], ref[5])
 
 
+def test_cfg2_torch_mm_orientation(lib):
+    # configs[1] in the orientation of the page's torch.mm(A, B): B is [K, N] as drawn.  1000
+    # repeats are bitwise equal, prefix rows equal the full product's rows, and every bit
+    # equals the [N, K] layout's result on the transposed copy of B (same instruction
+    # sequence per element)
+    from invariant_amd import BI_B_KN
+    a, b = gemm_inputs(2048, 2048, 2048, cfg=2)
+    A, Bkn = bf16(a), bf16(b)
+    ref = lib.bi_gemm(A, Bkn, b_layout=BI_B_KN)
+    assert same_bits(ref, lib.bi_gemm(A, bf16(_nk(b))))
+    r = bf16_within_1ulp(bits(ref[:64]), gemm_f64(a[:64], b))
+    assert r["ok"], r
+    for _ in range(1000):
+        c = lib.bi_gemm(A, Bkn, b_layout=BI_B_KN)
+        assert (c.float() - ref.float()).abs().max().item() == 0
+    for m in (1, 3, 17, 128, 511, 2048):
+        assert same_bits(lib.bi_gemm(A[:m], Bkn, b_layout=BI_B_KN), ref[:m]), m
+    perm = torch.randperm(2048, generator=torch.Generator().manual_seed(1)).cuda()
+    assert same_bits(lib.bi_gemm(A[perm].contiguous(), Bkn, b_layout=BI_B_KN), ref[perm])
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1003, 77), (33, 200, 1000), (300, 8, 4096), (130, 4100, 64),
+                                   (3000, 700, 300)])
+def test_b_kn_ragged_equals_b_nk(lib, m, n, k):
+    # [K, N] B with N off a multiple of 8 (row stride padded to one, the padding NaN: nothing
+    # past column N may be read into a stored output) and ragged K: bits of the [N, K] layout,
+    # within 1 ulp of the oracle, for bf16 and fp32 A
+    from invariant_amd import BI_B_KN
+    say("gemm B [K, N]", m, n, k)
+    a, b = gemm_inputs(m, n, k, cfg=46)
+    ldb = (n + 7) // 8 * 8 + 8
+    Bp = torch.full((k, ldb), float("nan"), device="cuda").to(torch.bfloat16)
+    Bp[:, :n] = bf16(b)
+    Bkn = Bp[:, :n]
+    A = bf16(a)
+    c = lib.bi_gemm(A, Bkn, b_layout=BI_B_KN)
+    assert same_bits(c, lib.bi_gemm(A, bf16(_nk(b))))
+    r = bf16_within_1ulp(bits(c), gemm_f64(a, b))
+    assert r["ok"], r
+    cf = lib.bi_gemm(A, Bkn, b_layout=BI_B_KN, out_dtype=torch.float32)
+    assert same_bits(cf, lib.bi_gemm(A, bf16(_nk(b)), out_dtype=torch.float32))
+    afp = torch.zeros((m, (k + 3) // 4 * 4 + 4), device="cuda")
+    afp[:, :k] = A.float()
+    af = afp[:, :k]
+    c32 = lib.bi_gemm(af, Bkn, b_layout=BI_B_KN, out_dtype=torch.float32)
+    assert same_bits(c32, lib.bi_gemm(af, bf16(_nk(b)), out_dtype=torch.float32))
+
+
 def test_splitk_variant_is_not_invariant(lib):
     # the page's linspace example: row 0 of a [1, D] product vs of a [2048, D] product
     Bn, D = 2048, 4096
@@ -241,7 +289,8 @@ def test_few_rows_vs_oracle(lib, m, n, k):
     assert r["ok"], r
 
 
-@pytest.mark.parametrize("n,k", [(4096, 4096), (28672, 1024), (6144, 14336), (32000, 512)])
+@pytest.mark.parametrize("n,k", [(4096, 4096), (28672, 1024), (6144, 14336), (32000, 512), (2048, 1024),
+                                 (1024, 4096)])
 def test_few_rows_match_large_m(lib, n, k):
     # the few-row kernel (every block shape and row split) gives the rows of the large-M
     # kernels bit for bit
@@ -258,7 +307,7 @@ def test_few_rows_match_large_m(lib, n, k):
     assert same_bits(lib.bi_gemm(A[rows].contiguous(), W), full[rows])
 
 
-@pytest.mark.parametrize("f,k", [(14336, 4096), (3008, 1000), (48, 512)])
+@pytest.mark.parametrize("f,k", [(14336, 4096), (3008, 1000), (48, 512), (1024, 1024)])
 def test_gemm_swiglu_equals_unfused(lib, f, k):
     # bi_gemm_swiglu with the 16-row interleaved weight == bi_swiglu(bi_gemm(., gate-then-up
     # weight)) bit for bit, for row counts that select every GEMM configuration

@@ -15,8 +15,7 @@ import synth
 from invariant_amd.model import (Batch, Dims, PagedKVCache, decoder_layer, greedy_generate,
                                  random_model)
 from oracle import fp
-from oracle.check import composed_drift
-from oracle.layer import decoder_layer_ref, model_ref_logits
+from oracle.layer import model_ref_logits
 from tests._attn import k_slot
 from tests._gpu import bf16, bits, host, i32, same_bits, say
 
@@ -49,10 +48,12 @@ def _layer_batch(cache, sids, ctx):
                  workspace=torch.empty(max(ws, 16), dtype=torch.uint8, device="cuda"))
 
 
-def test_cfg3_layer_batch_invariance_and_oracle(lib):
+def _cfg3_setup():
     dims = Dims(n_layers=1)
     wb = synth.layer_weights(cfg=3)
     w = {k: bf16(v) for k, v in wb.items()}
+    from invariant_amd import interleave_gate_up
+    w["wgate_up_i"] = interleave_gate_up(w["wgate_up"])
     R = 256
     ctx = synth.ragged_lengths(R, 0, 4096, 3, 1)
     h = synth.normal_bf16((R, 4096), 0.0, 1.0, 3, 2)
@@ -63,61 +64,182 @@ def test_cfg3_layer_batch_invariance_and_oracle(lib):
         pk[r] = synth.normal_bf16((int(ctx[r]), 8, 128), 0.0, 1.0, 3, 1000 + r)
         pv[r] = synth.normal_bf16((int(ctx[r]), 8, 128), 0.0, 1.0, 3, 5000 + r)
         _write_context(cache, 0, r, pk[r], pv[r])
-    H = bf16(h)
-    full = decoder_layer(w, H, _layer_batch(cache, list(range(R)), ctx), cache.k[0], cache.v[0], dims)
+    return dims, wb, w, ctx, h, cache, pk, pv
+
+
+@pytest.mark.parametrize("fp32_variant", [False, True])
+def test_cfg3_layer_batch_invariance_and_per_op_oracle(lib, fp32_variant):
+    # configs[2]: each request's output is bitwise equal at token batches 1, 8, 64 and 256 and
+    # under a permuted batch; every operation of the layer matches the oracle on the GPU's own
+    # inputs to it (sampled requests of the 256-batch)
+    from invariant_amd.model import decoder_layer
+    from oracle.layer import Spec
+    from tests._compose import check_layer, host_weights, take
+    dims, wb, w, ctx, h, cache, pk, pv = _cfg3_setup()
+    R = 256
+    H = bf16(h).float() if fp32_variant else bf16(h)
+    tr = {}
+    full = decoder_layer(w, H, _layer_batch(cache, list(range(R)), ctx), cache.k[0], cache.v[0], dims,
+                         fp32_variant, trace=tr)
     for B in (1, 8, 64):
         out = decoder_layer(w, H[:B].contiguous(), _layer_batch(cache, list(range(B)), ctx),
-                            cache.k[0], cache.v[0], dims)
+                            cache.k[0], cache.v[0], dims, fp32_variant)
         assert same_bits(out, full[:B]), B
     perm = list(range(63, -1, -1))
     outp = decoder_layer(w, H[torch.tensor(perm).cuda()].contiguous(), _layer_batch(cache, perm, ctx),
-                         cache.k[0], cache.v[0], dims)
+                         cache.k[0], cache.v[0], dims, fp32_variant)
     assert same_bits(outp, full[torch.tensor(perm).cuda()])
-    # oracle rows: fp64 inside each operation, bf16 storage between them.  Each kernel is
-    # graded tightly on its own (test_gpu_*); the composed layer within the drift band of
-    # two correct bf16 chains (oracle.check.composed_drift)
-    got = bits(full)
-    for r in (0, 3, 100, 255):
-        ref, it = decoder_layer_ref(h[r:r + 1], wb, [int(ctx[r])], [pk[r]], [pv[r]])
-        res = composed_drift(got[r:r + 1], ref)
-        say("layer row", r, "ctx", int(ctx[r]), res)
-        assert res["ok"], res
+    rows = [0, 3, 100, 255]
+    rt = take(tr, rows)
+    kn, vn = rt["k"][0], rt["v"][0]
+
+    def kv(i):
+        r = rows[i]
+        return (np.concatenate([fp.bf16_to_f64(pk[r]), kn[i:i + 1]]),
+                np.concatenate([fp.bf16_to_f64(pv[r]), vn[i:i + 1]]))
+    rep = check_layer(lib, rt, host_weights(w), w, ctx[rows], kv, Spec(variant=fp32_variant),
+                      tag=f"cfg3 layer variant={fp32_variant}")
+    assert all(v["ok"] for v in rep.values()), {k: v for k, v in rep.items() if not v["ok"]}
 
 
-def test_model_small_vs_oracle(lib):
+def _traced_run(model, dims, cache, sid, done, toks, fp32_variant, grab):
+    """One forward call of one sequence; grab(li, trace) is called after every layer (it
+    copies what it needs to the host, so the layer's tensors can go)."""
+    from invariant_amd.model import forward, make_batch
+    batch = make_batch(cache, [sid], [done], [np.asarray(toks, np.int32)], dims=dims)
+    return forward(model, batch, cache, dims, fp32_variant, on_layer=grab)
+
+
+def _model_per_op(lib, model, dims, fp32_variant, prompt, n_decode, rows, layers, tag):
+    """Prefill `prompt` then `n_decode` greedy decode steps of one sequence; check every op
+    of the given layers on the given prefill rows and on every decode row, each against the
+    oracle with the GPU's own inputs.  Returns the GPU logits of the prefill's last row and of
+    each decode step [1 + n_decode, V]."""
+    from invariant_amd.model import head
+    from oracle.layer import Spec
+    from tests._compose import check_layer, host_weights, take, values
+    spec = Spec(n_q_heads=dims.n_q_heads, n_kv_heads=dims.n_kv_heads, head_dim=dims.head_dim,
+                eps=dims.eps, base=dims.rope_base, variant=fp32_variant)
+    cache = PagedKVCache(dims, n_pages=(len(prompt) + n_decode) // 16 + 4, seed=17)
+    L = len(prompt)
+    lset = set(layers)
+    got_rows = {}          # (step, layer) -> host rows of the trace
+    kv = {li: ([], []) for li in layers}
+    emb = {}
+
+    def grab(step, sel):
+        def f(li, tr):
+            if step == 0 and li == 0:
+                emb["v"] = values(tr["emb"])
+            if li in lset:
+                got_rows[(step, li)] = take(tr, sel)
+                kv[li][0].append(values(tr["k"]))
+                kv[li][1].append(values(tr["v"]))
+        return f
+
+    hh = _traced_run(model, dims, cache, 0, 0, prompt, fp32_variant, grab(0, rows))
+    lg, ids = head(model, hh, torch.tensor([L - 1], dtype=torch.int32, device="cuda"), dims, fp32_variant)
+    logits = [host(lg[0])]
+    # the embedding rows: a gather, exact (widened for the variant)
+    assert np.array_equal(emb["v"], fp.bf16_to_f64(bits(model["embed"])[np.asarray(prompt)]))
+    tok = int(ids[0].item())
+    for st in range(n_decode):
+        hh = _traced_run(model, dims, cache, 0, L + st, [tok], fp32_variant, grab(st + 1, [0]))
+        lg, ids = head(model, hh, torch.tensor([0], dtype=torch.int32, device="cuda"), dims, fp32_variant)
+        logits.append(host(lg[0]))
+        tok = int(ids[0].item())
+    for li in layers:
+        w = model["layers"][li]
+        wb = host_weights(w)
+        if li + 1 < len(model["layers"]):
+            wb["next_norm"] = bits(model["layers"][li + 1]["attn_norm"])
+        # keys/values of every position the GPU wrote: the prefill's, then each decode step's
+        K = np.concatenate(kv[li][0])
+        V = np.concatenate(kv[li][1])
+        rep = check_layer(lib, got_rows[(0, li)], wb, w, np.asarray(rows),
+                          lambda i: (K[:rows[i] + 1], V[:rows[i] + 1]), spec, tag=f"{tag} prefill layer {li}")
+        assert all(v["ok"] for v in rep.values()), (li, {k: v for k, v in rep.items() if not v["ok"]})
+        for st in range(n_decode):
+            p = L + st
+            rep = check_layer(lib, got_rows[(st + 1, li)], wb, w, np.asarray([p]),
+                              lambda i: (K[:p + 1], V[:p + 1]), spec, tag=f"{tag} decode {st} layer {li}")
+            assert all(v["ok"] for v in rep.values()), (li, st, {k: v for k, v in rep.items() if not v["ok"]})
+    return np.stack(logits)
+
+
+@pytest.mark.parametrize("fp32_variant", [False, True])
+def test_model_small_per_op_and_drift(lib, fp32_variant):
+    # two full-width layers: a 24-token prefill and 3 decode steps, every op of both layers
+    # against the oracle on the GPU's own inputs; the logits' drift from the all-oracle chain
+    # (teacher-forced on the GPU's tokens) is reported, with only a gross-error bound
+    from oracle.check import logit_drift_report
     dims = Dims(n_layers=2)
     model = random_model(dims, seed=11)
     prompt = synth.uniform_ints(24, 0, 31999, 11, 0)
-    forced = synth.uniform_ints(3, 0, 31999, 11, 1)
-    cache = PagedKVCache(dims, n_pages=64, seed=11)
-    from invariant_amd.model import forward, head, make_batch
-    got = []
-    batch = make_batch(cache, [0], [0], [prompt])
-    hh = forward(model, batch, cache, dims)
-    lg, _ = head(model, hh, torch.tensor([len(prompt) - 1], dtype=torch.int32, device="cuda"), dims)
-    got.append(host(lg[0]))
-    done = len(prompt)
-    for t in forced:
-        batch = make_batch(cache, [0], [done], [np.asarray([t], np.int32)])
-        hh = forward(model, batch, cache, dims)
-        lg, _ = head(model, hh, torch.tensor([0], dtype=torch.int32, device="cuda"), dims)
-        got.append(host(lg[0]))
-        done += 1
+    got = _model_per_op(lib, model, dims, fp32_variant, prompt, 3, list(range(24)), [0, 1],
+                        tag=f"small model variant={fp32_variant}")
+    # the GPU's greedy tokens, fed back to the oracle
+    forced = [int(np.argmax(g)) for g in got[:-1]]
     wts = dict(embed=bits(model["embed"]), final_norm=bits(model["final_norm"]),
                lm_head=bits(model["lm_head"]),
-               layers=[{k: bits(v) for k, v in L.items()} for L in model["layers"]])
-    ref = model_ref_logits(prompt, forced, wts)
-    got = np.stack(got).astype(np.float64)
-    scale = np.sqrt(np.mean(ref ** 2, axis=1, keepdims=True))
-    err = np.abs(got - ref) / scale
-    top2 = np.sort(ref, axis=1)[:, -2:]
-    margin = (top2[:, 1] - top2[:, 0]) / scale[:, 0]
-    say("model logits: max err / rms", float(err.max()), "mean", float(err.mean()),
-        "argmax agree", np.mean(np.argmax(got, 1) == np.argmax(ref, 1)), "top1-top2 margin / rms", margin)
-    # drift of a two-layer bf16 chain is reported; the gate only catches gross errors
-    # (a wrong weight, rotation or mask moves logits by the order of their rms)
-    assert err.max() < 2 ** -4 and err.mean() < 2 ** -6
-    clear = margin > 4 * err.max()
+               layers=[{k: bits(v) for k, v in L.items() if k != "wgate_up_i"} for L in model["layers"]])
+    ref = model_ref_logits(prompt, forced, wts, fp32_variant=fp32_variant)
+    rep = logit_drift_report(got.astype(np.float64), ref)
+    say("small model logit drift", fp32_variant, rep)
+    assert rep["max_over_rms"] < 2 ** -4
+    clear = (np.sort(ref, 1)[:, -1] - np.sort(ref, 1)[:, -2]) > 4 * rep["max_abs"]
+    assert np.array_equal(np.argmax(got, 1)[clear], np.argmax(ref, 1)[clear])
+
+
+@pytest.mark.parametrize("fp32_variant", [False, True])
+def test_cfg5_per_op_prefill_and_decode(lib, fp32_variant):
+    # configs[4]'s model and 1400-token prompt: the prefill and one decode step, every op of
+    # every one of the 32 layers against the oracle on the GPU's own inputs (sampled prefill
+    # rows: the first, chunk and group boundaries, the last)
+    dims = Dims()
+    model = random_model(dims, seed=5)
+    prompt = synth.uniform_ints(1400, 0, 31999, 5, 0)
+    rows = [0, 255, 256, 1023, 1024, 1399]
+    _model_per_op(lib, model, dims, fp32_variant, prompt, 1, rows, list(range(32)),
+                  tag=f"cfg5 variant={fp32_variant}")
+
+
+@pytest.mark.parametrize("fp32_variant", [False, True])
+def test_cfg5_teacher_forced_drift_report(lib, fp32_variant):
+    # configs[4]: 64 greedy tokens of the 32-layer model on the 1400-token prompt; the oracle
+    # model (fp64 inside every op, the model's own storage points) is teacher-forced on the
+    # GPU's tokens and the logit mismatch at every step is REPORTED in the metric families of
+    # the cross-vendor abstract (logit difference, top-k and token agreement) with the
+    # top-1/top-2 margins of the sampling section of "Same model, same input, different
+    # answer".  Only gross errors fail (the composition is graded op by op above).
+    import json
+    import os
+    import time
+    from invariant_amd.model import greedy_generate
+    from oracle.check import logit_drift_report
+    dims = Dims()
+    model = random_model(dims, seed=5)
+    prompt = synth.uniform_ints(1400, 0, 31999, 5, 0)
+    cache = PagedKVCache(dims, n_pages=(1400 + 64) // 16 + 8, seed=5)
+    tok, lg = greedy_generate(model, [prompt], 64, cache, dims, fp32_variant, keep_logits=[0])
+    got = host(lg[0]).astype(np.float64)
+    wts = dict(embed=bits(model["embed"]), final_norm=bits(model["final_norm"]),
+               lm_head=bits(model["lm_head"]),
+               layers=[{k: bits(v) for k, v in L.items() if k != "wgate_up_i"} for L in model["layers"]])
+    del model
+    t0 = time.time()
+    ref = model_ref_logits(prompt, tok[0][:63], wts, fp32_variant=fp32_variant, one_pass=True)
+    say("oracle teacher-forced pass", round(time.time() - t0, 1), "s")
+    rep = {"all_steps": logit_drift_report(got, ref), "step0": logit_drift_report(got[:1], ref[:1]),
+           "step63": logit_drift_report(got[63:], ref[63:]),
+           "oracle_greedy_tokens_agree": float(np.mean(np.argmax(ref, 1) == tok[0]))}
+    say("cfg5 logit drift", "fp32 variant" if fp32_variant else "bf16", json.dumps(rep))
+    if os.path.isdir("gpurun_out"):
+        name = "cfg5_drift_fp32variant.json" if fp32_variant else "cfg5_drift_bf16.json"
+        with open(os.path.join("gpurun_out", name), "w") as f:
+            json.dump(rep, f, indent=1)
+    assert np.all(np.isfinite(got)) and rep["all_steps"]["max_over_rms"] < 0.5
+    clear = (np.sort(ref, 1)[:, -1] - np.sort(ref, 1)[:, -2]) > 4 * rep["all_steps"]["max_abs"]
     assert np.array_equal(np.argmax(got, 1)[clear], np.argmax(ref, 1)[clear])
 
 
