@@ -166,18 +166,24 @@ def test_b_kn_ragged_equals_b_nk(lib, m, n, k):
     Bp = torch.full((k, ldb), float("nan"), device="cuda").to(torch.bfloat16)
     Bp[:, :n] = bf16(b)
     Bkn = Bp[:, :n]
-    A = bf16(a)
+    def padded(x):     # row stride a multiple of 8 elements, as bi_gemm requires
+        r, c_ = x.shape
+        p = torch.zeros((r, (c_ + 7) // 8 * 8 + 8), dtype=torch.bfloat16, device="cuda")
+        p[:, :c_] = bf16(x)
+        return p[:, :c_]
+    A = padded(a)
+    Bnk = padded(_nk(b))
     c = lib.bi_gemm(A, Bkn, b_layout=BI_B_KN)
-    assert same_bits(c, lib.bi_gemm(A, bf16(_nk(b))))
+    assert same_bits(c, lib.bi_gemm(A, Bnk))
     r = bf16_within_1ulp(bits(c), gemm_f64(a, b))
     assert r["ok"], r
     cf = lib.bi_gemm(A, Bkn, b_layout=BI_B_KN, out_dtype=torch.float32)
-    assert same_bits(cf, lib.bi_gemm(A, bf16(_nk(b)), out_dtype=torch.float32))
+    assert same_bits(cf, lib.bi_gemm(A, Bnk, out_dtype=torch.float32))
     afp = torch.zeros((m, (k + 3) // 4 * 4 + 4), device="cuda")
-    afp[:, :k] = A.float()
+    afp[:, :k] = bf16(a).float()
     af = afp[:, :k]
     c32 = lib.bi_gemm(af, Bkn, b_layout=BI_B_KN, out_dtype=torch.float32)
-    assert same_bits(c32, lib.bi_gemm(af, bf16(_nk(b)), out_dtype=torch.float32))
+    assert same_bits(c32, lib.bi_gemm(af, Bnk, out_dtype=torch.float32))
 
 
 def test_splitk_variant_is_not_invariant(lib):
