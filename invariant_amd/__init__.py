@@ -33,6 +33,8 @@ _SIGS = {
     "bi_attention_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I64]),
     "bi_attention": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
                                 _I32, _I64, _F32, _P, _c.c_int, _P, _SZ, _P]),
+    "bi_attention_noalloc": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
+                                        _I32, _I64, _F32, _P, _c.c_int, _P]),
     "bi_attention_batchdep_split": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32,
                                                _I32, _I32, _I32, _I64, _I64, _F32, _P, _c.c_int, _P,
                                                _SZ, _P]),
@@ -115,7 +117,9 @@ def _code(dtype):
 def _ld(t):
     if t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
         raise ValueError("expected a 2-D tensor with unit column stride")
-    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+    if t.shape[0] > 1 or t.stride(0) >= t.shape[1]:
+        return max(t.stride(0), 1)
+    return max(t.shape[1], 1)      # one row whose stride torch does not pin down
 
 
 # ----------------------------------------------------------------------------- calls
@@ -184,6 +188,23 @@ def bi_attention(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(seq_lens), _ptr(query_start_loc), B, T, Hq, Hkv, D, page, max_pages, int(max_seq_len),
         float(scale), _ptr(out), _code(out.dtype), _ptr(workspace), wsz, _stream(q)))
+    return out
+
+
+def bi_attention_noalloc(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start_loc,
+                         max_seq_len: int, scale: float, out=None, out_dtype=torch.bfloat16):
+    """bi_attention with the library's own per-device scratch instead of a workspace (no
+    device allocation inside the call; pass `out` to allocate nothing at all)."""
+    T, Hq, D = q.shape
+    Hkv = k_new.shape[1]
+    page = v_cache.shape[3]
+    B, max_pages = block_table.shape
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=out_dtype, device=q.device)
+    _check("bi_attention_noalloc", load().bi_attention_noalloc(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(query_start_loc), B, T, Hq, Hkv, D, page, max_pages, int(max_seq_len),
+        float(scale), _ptr(out), _code(out.dtype), _stream(q)))
     return out
 
 
