@@ -229,6 +229,28 @@ int bi_attention(const void* q, const void* k_new, const void* v_new, void* k_ca
                  int32_t max_pages_per_seq, int64_t max_seq_len, float scale, void* out,
                  int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/* bi_attention without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, layouts, validation and bits as bi_attention.  Its split-KV partials and token
+ * records live in a 64 MiB scratch array that the library holds on every device it runs on
+ * until the process ends (looked up on the first call on a device); the call allocates and
+ * frees nothing.  A call needs, for at most 1024 tokens,
+ *   4 * (R2 + R * D) + 16 * num_tokens bytes,  R = num_tokens * Hq * S, R2 = 2R rounded up to
+ *   a multiple of 4, S = ceil(max_seq_len / 256) when num_tokens * ceil(max_seq_len / 1024) *
+ *   Hkv is below twice the CU count, else ceil(max_seq_len / 1024)
+ * (about 34 MB for 64 tokens of 32768-token contexts, 32 q heads); longer calls need none.
+ * Every call on a device shares that device's scratch and overwrites it: calls that overlap in
+ * time on one device (concurrent streams, several host threads) race and must be serialised by
+ * the caller.  Nothing in the scratch has to start at zero.
+ * Errors: as bi_attention; BI_ERR_WORKSPACE when the call needs more than the 64 MiB;
+ * BI_ERR_HIP when the scratch's device address cannot be obtained. */
+int bi_attention_noalloc(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                         void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* query_start_loc, int32_t batch, int64_t num_tokens,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t page_size, int32_t max_pages_per_seq, int64_t max_seq_len,
+                         float scale, void* out, int out_dtype, void* stream);
+
 /* Comparison variant, NOT batch-invariant (split-KV / FlashDecoding with a number of
  * splits chosen from the batch, as [DN] describes for decode kernels): same arguments and
  * layouts as bi_attention (at most 1024 tokens per call) plus total_chunks = sum over

@@ -818,13 +818,15 @@ extern "C" size_t bi_attention_workspace_bytes(int64_t num_tokens, int32_t num_q
          static_cast<size_t>(num_tokens) * sizeof(int4);
 }
 
-extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new, void* k_cache,
-                            void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
-                            const int32_t* query_start_loc, int32_t batch, int64_t num_tokens,
-                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                            int32_t page_size, int32_t max_pages_per_seq, int64_t max_seq_len,
-                            float scale, void* out, int out_dtype, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+namespace bi {
+namespace {
+
+// Validation shared by bi_attention and bi_attention_noalloc (everything but the workspace).
+int attention_check(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                    void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                    const int32_t* query_start_loc, int32_t batch, int64_t num_tokens,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                    int32_t max_pages_per_seq, int64_t max_seq_len, void* out, int out_dtype) {
   if (out_dtype != BI_BF16 && out_dtype != BI_F32) return BI_ERR_DTYPE;
   if (batch < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
       page_size < 1 || max_pages_per_seq < 1 || max_seq_len < 0)
@@ -844,30 +846,43 @@ extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new,
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
       !aligned16(v_cache) || !aligned16(out))
     return BI_ERR_ALIGN;
-  const bool split = num_tokens <= SPLIT_MAX_TOKENS;
-  const size_t need = bi_attention_workspace_bytes(num_tokens, num_q_heads, head_dim, max_seq_len);
-  if (split && (!workspace || workspace_bytes < need)) return BI_ERR_WORKSPACE;
   // the split path indexes its work items (token, chunk, kv head) with 32-bit integers
-  if (split && num_tokens * chunks_for(max_seq_len) * num_kv_heads >= (int64_t(1) << 31))
+  if (num_tokens <= SPLIT_MAX_TOKENS &&
+      num_tokens * chunks_for(max_seq_len) * num_kv_heads >= (int64_t(1) << 31))
     return BI_ERR_SHAPE;
+  return BI_OK;
+}
 
-  hipStream_t s = as_stream(stream);
+// Partials per (token, q head) on the split path: one per 4-chunk group, or, when that
+// leaves fewer work units than two per CU (small batches), one per chunk.
+bool split_fine(int64_t num_tokens, int64_t maxc, int32_t num_kv_heads) {
+  const int64_t maxg = (maxc + GROUP - 1) / GROUP;
+  return num_tokens * maxg * num_kv_heads < 2 * static_cast<int64_t>(cu_count());
+}
+
+// The kernels of a validated call.  Split path: ws_ml holds the (m, l) pairs of every partial
+// slot, followed (16-byte aligned) by their o vectors; ws_tok the per-token records.
+void attention_launch(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                      void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* query_start_loc, int32_t batch, int64_t num_tokens,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t page_size,
+                      int32_t max_pages_per_seq, int64_t max_seq_len, float scale, void* out,
+                      int out_dtype, float* ws_ml, int4* ws_tok, hipStream_t s) {
+  const bool split = num_tokens <= SPLIT_MAX_TOKENS;
+  const int G = num_q_heads / num_kv_heads;
   const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   const int64_t maxc = chunks_for(max_seq_len);
-  float* ws_ml = static_cast<float*>(workspace);
-  float* ws_o = ws_ml + ml_floats(num_tokens * num_q_heads * maxc);
-  int4* ws_tok = split ? reinterpret_cast<int4*>(ws_o + num_tokens * num_q_heads * maxc * HD) : nullptr;
   kv_write_kernel<<<dim3(static_cast<unsigned>(num_tokens)), dim3(256), 0, s>>>(
       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_table, seq_lens,
-      query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size, ws_tok);
+      query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size, split ? ws_tok : nullptr);
   const int of = out_dtype == BI_F32;
   if (split) {
     // Work units of GROUP chunks, whose partial is the group's in-register merge; when that
     // leaves fewer units than two per CU (small batches), units of one chunk, whose partials
     // the combine kernel merges in the same two levels (same bits, four times the units).
     const int64_t maxg = (maxc + GROUP - 1) / GROUP;
-    const bool fine = num_tokens * maxg * num_kv_heads < 2 * static_cast<int64_t>(cu_count());
+    const bool fine = split_fine(num_tokens, maxc, num_kv_heads);
     const int uc = fine ? 1 : GROUP;
     const int64_t slots = fine ? maxc : maxg;   // partials per (token, q head)
     float* ps_o = ws_ml + ml_floats(num_tokens * num_q_heads * slots);
@@ -891,6 +906,97 @@ extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new,
         static_cast<const uint16_t*>(v_cache), block_table, seq_lens, query_start_loc, batch,
         max_pages_per_seq, num_q_heads, num_kv_heads, page_size, num_tokens, sl2, out, of);
   }
+}
+
+}  // namespace
+}  // namespace bi
+
+extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                            void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, int32_t batch, int64_t num_tokens,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t page_size, int32_t max_pages_per_seq, int64_t max_seq_len,
+                            float scale, void* out, int out_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  const int st = attention_check(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+                                 query_start_loc, batch, num_tokens, num_q_heads, num_kv_heads,
+                                 head_dim, page_size, max_pages_per_seq, max_seq_len, out, out_dtype);
+  if (st != BI_OK || num_tokens == 0 || batch == 0) return st;
+  const bool split = num_tokens <= SPLIT_MAX_TOKENS;
+  const size_t need = bi_attention_workspace_bytes(num_tokens, num_q_heads, head_dim, max_seq_len);
+  if (split && (!workspace || workspace_bytes < need)) return BI_ERR_WORKSPACE;
+  // workspace: (m, l) and o for every (token, q head, chunk), then the token records
+  const int64_t maxc = chunks_for(max_seq_len);
+  float* ws_ml = static_cast<float*>(workspace);
+  float* ws_o = ws_ml + ml_floats(num_tokens * num_q_heads * maxc);
+  int4* ws_tok = split ? reinterpret_cast<int4*>(ws_o + num_tokens * num_q_heads * maxc * HD) : nullptr;
+  attention_launch(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start_loc, batch,
+                   num_tokens, num_q_heads, num_kv_heads, page_size, max_pages_per_seq, max_seq_len,
+                   scale, out, out_dtype, ws_ml, ws_tok, as_stream(stream));
+  return launch_status();
+}
+
+// ---------------------------------------------------------------- no-allocation entry point
+// Scratch of bi_attention_noalloc: one copy per device, held until the process ends.  Host
+// code never uses this name as an address (on the host it is a stand-in symbol): the
+// device address of each GPU's copy is looked up once per device with hipGetSymbolAddress
+// and kept in scratch_ptr.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace bi {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<uintptr_t> scratch_ptr[kMaxDevices];
+
+// This device's copy of the scratch array (0 on failure).  The first call on a device looks
+// it up with that device current; racing first calls store the same address.
+uintptr_t device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  uintptr_t p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return 0;
+  p = reinterpret_cast<uintptr_t>(ptr);
+  scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+}  // namespace bi
+
+extern "C" int bi_attention_noalloc(const void* q, const void* k_new, const void* v_new,
+                                    void* k_cache, void* v_cache, const int32_t* block_table,
+                                    const int32_t* seq_lens, const int32_t* query_start_loc,
+                                    int32_t batch, int64_t num_tokens, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                    int32_t max_pages_per_seq, int64_t max_seq_len, float scale,
+                                    void* out, int out_dtype, void* stream) {
+  const int st = attention_check(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+                                 query_start_loc, batch, num_tokens, num_q_heads, num_kv_heads,
+                                 head_dim, page_size, max_pages_per_seq, max_seq_len, out, out_dtype);
+  if (st != BI_OK || num_tokens == 0 || batch == 0) return st;
+  float* ws_ml = nullptr;
+  int4* ws_tok = nullptr;
+  if (num_tokens <= SPLIT_MAX_TOKENS) {
+    // the partials this call writes, packed: (m, l) pairs, o vectors, token records
+    const int64_t maxc = chunks_for(max_seq_len);
+    const int64_t slots = split_fine(num_tokens, maxc, num_kv_heads) ? maxc : (maxc + GROUP - 1) / GROUP;
+    const int64_t rows = num_tokens * num_q_heads * slots;
+    const int64_t floats = ml_floats(rows) + rows * HD;
+    const size_t need = static_cast<size_t>(floats) * sizeof(float) +
+                        static_cast<size_t>(num_tokens) * sizeof(int4);
+    if (need > kScratchBytes) return BI_ERR_WORKSPACE;
+    const uintptr_t base = device_scratch();
+    if (!base) return BI_ERR_HIP;
+    ws_ml = reinterpret_cast<float*>(base);
+    ws_tok = reinterpret_cast<int4*>(ws_ml + floats);
+  }
+  attention_launch(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start_loc, batch,
+                   num_tokens, num_q_heads, num_kv_heads, page_size, max_pages_per_seq, max_seq_len,
+                   scale, out, out_dtype, ws_ml, ws_tok, as_stream(stream));
   return launch_status();
 }
 

@@ -88,6 +88,10 @@ def test_validation_rejects_before_launch(lib):
     assert att() == -5
     assert lib.bi_attention_workspace_bytes(4, 32, 128, 64) == (4 * 32 * 1 * 2 + 4 * 32 * 128) * 4 + 4 * 16
     assert lib.bi_attention_workspace_bytes(2000, 32, 128, 64) == 0
+    # the no-allocation form rejects a call whose partials exceed its 64 MiB scratch before
+    # anything runs: 1024 tokens of 32768-token contexts need 1024*32*32*(2+128)*4 bytes
+    assert lib.bi_attention_noalloc(*args, 1, 1024, 32, 8, 128, 16, 2048, 32768, 0.088, P, 1, None) == -5
+    assert lib.bi_attention_noalloc(*args, 1, 4, 32, 8, 64, 16, 4, 64, 0.088, P, 1, None) == -6
     assert lib.bi_gemm_splitk_workspace_bytes(2048, 2048, 2048) == 2 * 2048 * 2048 * 4
 
 
