@@ -614,10 +614,23 @@ __device__ __forceinline__ void unrolled_steps(const DmaCtx<T>& d, const uint16_
   }
 }
 
+// k_split: K columns per blockIdx.y (K itself for bi_gemm, whose grid has one y); slice y
+// reads A and B from k = y k_split on and writes its fp32 result split_stride bytes further
+// into C (the split-K comparison variant only).
 template <class T>
 __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
-    int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int tiles_m, int tiles_n) {
+    int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int tiles_m, int tiles_n,
+    int k_split, int64_t split_stride) {
+  if (blockIdx.y > 0) {
+    const int kb = static_cast<int>(blockIdx.y) * k_split;
+    A += kb;
+    B += kb;
+    K = min(k_split, K - kb);
+    C = static_cast<char*>(C) + static_cast<int64_t>(blockIdx.y) * split_stride;
+  } else {
+    K = min(k_split, K);
+  }
   // one LDS block: the A stages, then the B stages; reused by the epilogue
   __shared__ __attribute__((aligned(1024))) uint16_t smem[T::STAGES * (T::SA + T::SB)];
   uint16_t* const sA = smem;
@@ -866,8 +879,19 @@ TileKind pick_tile(int64_t M, int64_t N, int cus) {
 template <int RB, int CB, int PF, bool PAIR = false>
 __global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
-    int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int split) {
+    int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int split, int k_split,
+    int64_t split_stride) {
   static_assert(!PAIR || CB == 1, "paired waves hold one block each");
+  // K slice of blockIdx.y (as in gemm_dma_kernel; the split-K comparison variant only)
+  if (blockIdx.y > 0) {
+    const int kb = static_cast<int>(blockIdx.y) * k_split;
+    A += kb;
+    B += kb;
+    K = min(k_split, K - kb);
+    C = static_cast<char*>(C) + static_cast<int64_t>(blockIdx.y) * split_stride;
+  } else {
+    K = min(k_split, K);
+  }
   const int lane = threadIdx.x & 63;
   const int wave = PAIR ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   // workgroup id -> (column block, row slice): ids 8 s + x, s = split c .. split c + split - 1
@@ -1046,34 +1070,43 @@ bool use_rows(int64_t M, int64_t N, int64_t K, int mode) {
   return K / 32 >= 2 * rows_cfg(M, N, mode).pf;
 }
 
+// Split-K launches (comparison variant only): `ks` slices of k_split columns along grid y,
+// slice y's fp32 result split_stride bytes into C.  bi_gemm launches ks = 1, k_split = K.
+struct KSplit {
+  int ks = 1;
+  int k_split = 0;   // 0: K
+  int64_t stride = 0;
+};
+
 template <int RB, int CB, int PF, bool PAIR = false>
 void launch_rows_t(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                   int64_t lda, int64_t ldb, int64_t ldc, int cf, int split, hipStream_t s) {
+                   int64_t lda, int64_t ldb, int64_t ldc, int cf, int split, hipStream_t s,
+                   KSplit sk = {}) {
   const int64_t ncb = (N + CB * 16 - 1) / (CB * 16);
   const unsigned wgs = static_cast<unsigned>(PAIR ? (ncb + 1) / 2 : split == 1 ? ncb : 8 * split * ((ncb + 7) / 8));
-  gemm_rows_kernel<RB, CB, PF, PAIR><<<dim3(wgs), dim3(PAIR ? 128 : 64), 0, s>>>(
+  gemm_rows_kernel<RB, CB, PF, PAIR><<<dim3(wgs, sk.ks), dim3(PAIR ? 128 : 64), 0, s>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, int(M), int(N), int(K),
-      lda, ldb, ldc, cf, split);
+      lda, ldb, ldc, cf, split, sk.k_split ? sk.k_split : int(K), sk.stride);
 }
 
 void launch_rows(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                 int64_t lda, int64_t ldb, int64_t ldc, int cf, hipStream_t s) {
+                 int64_t lda, int64_t ldb, int64_t ldc, int cf, hipStream_t s, KSplit sk = {}) {
   const RowsCfg c = rows_cfg(M, N, cf);
-  if (c.pair) launch_rows_t<1, 1, 16, true>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
-  else if (c.rb == 4) launch_rows_t<4, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
-  else if (c.rb == 2) launch_rows_t<2, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, c.split, s);
-  else if (c.split > 1) launch_rows_t<1, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, c.split, s);
-  else if (c.cb == 2) launch_rows_t<1, 2, 16>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
-  else launch_rows_t<1, 1, 16>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s);
+  if (c.pair) launch_rows_t<1, 1, 16, true>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s, sk);
+  else if (c.rb == 4) launch_rows_t<4, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s, sk);
+  else if (c.rb == 2) launch_rows_t<2, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, c.split, s, sk);
+  else if (c.split > 1) launch_rows_t<1, 2, 12>(A, B, C, M, N, K, lda, ldb, ldc, cf, c.split, s, sk);
+  else if (c.cb == 2) launch_rows_t<1, 2, 16>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s, sk);
+  else launch_rows_t<1, 1, 16>(A, B, C, M, N, K, lda, ldb, ldc, cf, 1, s, sk);
 }
 
 template <class T>
 void launch_dma(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
-                int64_t ldb, int64_t ldc, int cf, hipStream_t s) {
+                int64_t ldb, int64_t ldc, int cf, hipStream_t s, KSplit sk = {}) {
   const int tm = static_cast<int>((M + T::TM - 1) / T::TM), tn = static_cast<int>((N + T::TN - 1) / T::TN);
-  gemm_dma_kernel<T><<<dim3(static_cast<unsigned>(static_cast<int64_t>(tm) * tn)), dim3(T::THREADS), 0, s>>>(
+  gemm_dma_kernel<T><<<dim3(static_cast<unsigned>(static_cast<int64_t>(tm) * tn), sk.ks), dim3(T::THREADS), 0, s>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, int(M), int(N), int(K),
-      lda, ldb, ldc, cf, tm, tn);
+      lda, ldb, ldc, cf, tm, tn, sk.k_split ? sk.k_split : int(K), sk.stride);
 }
 
 // Fixed-order sum of the split-K partials (comparison variant only).
@@ -1088,29 +1121,57 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ ws, void* __restr
   else static_cast<uint16_t*>(C)[row * ldc + col] = f32_to_bf16(s);
 }
 
-int splitk_count(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int64_t nk = (K + BK - 1) / BK;
-  int64_t s = (2 * 256) / (tiles > 0 ? tiles : 1);
-  if (s < 1) s = 1;
-  if (s > 16) s = 16;
-  if (s > nk) s = nk;
-  return static_cast<int>(s);
+// Comparison variant: slices of K chosen from the size of the output grid -- as many as
+// bring the launch to about two waves (few-row kernel) or two tiles (LDS-staged tiles) per
+// CU, at most 16, each slice a whole number of 64-wide stages (at least 1024 columns for the
+// few-row kernel, whose prefetch needs 32 steps).  So the number of slices, and with it
+// every row's association of partial sums, changes with M.
+KSplit splitk_plan(int64_t M, int64_t N, int64_t K) {
+  const int64_t cus = cu_count();
+  KSplit p;
+  int64_t units, min_slice;
+  if (use_rows(M, N, K, kOutF32)) {
+    const RowsCfg c = rows_cfg(M, N, kOutF32);
+    units = ((N + 16 * c.cb - 1) / (16 * c.cb)) * c.split;
+    min_slice = 1024;
+  } else {
+    switch (pick_tile(M, N, cus)) {
+      case TileKind::k256: units = ((M + 255) / 256) * ((N + 255) / 256); break;
+      case TileKind::k64x128: units = ((M + 63) / 64) * ((N + 127) / 128); break;
+      case TileKind::k64: units = ((M + 63) / 64) * ((N + 63) / 64); break;
+      default: units = ((M + 127) / 128) * ((N + 127) / 128); break;
+    }
+    min_slice = 256;
+  }
+  int64_t ks = (2 * cus + units - 1) / std::max<int64_t>(units, 1);
+  ks = std::min<int64_t>(ks, 16);
+  ks = std::min<int64_t>(ks, std::max<int64_t>(1, K / min_slice));
+  for (; ks > 1; --ks) {   // slices of whole stages, the last one at least min_slice long
+    const int64_t per = ((K + ks - 1) / ks + 63) / 64 * 64;
+    const int64_t n = (K + per - 1) / per;
+    if (n > 1 && K - (n - 1) * per >= min_slice) {
+      p.ks = static_cast<int>(n);
+      p.k_split = static_cast<int>(per);
+      p.stride = M * N * static_cast<int64_t>(sizeof(float));
+      return p;
+    }
+  }
+  return p;
 }
 
 // bf16 A and B, both under 4 GiB: the few-row kernel or the LDS-staged tiles by grid size.
 void launch_bf16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                 int64_t lda, int64_t ldb, int64_t ldc, int mode, hipStream_t s) {
+                 int64_t lda, int64_t ldb, int64_t ldc, int mode, hipStream_t s, KSplit sk = {}) {
   if (use_rows(M, N, K, mode)) {
-    launch_rows(A, B, C, M, N, K, lda, ldb, ldc, mode, s);
+    launch_rows(A, B, C, M, N, K, lda, ldb, ldc, mode, s, sk);
     return;
   }
   switch (pick_tile(M, N, cu_count())) {
-    case TileKind::k256: launch_dma<Tile256>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
-    case TileKind::k128deep: launch_dma<Tile128Deep>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
-    case TileKind::k64x128: launch_dma<Tile64x128>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
-    case TileKind::k64: launch_dma<Tile64>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
-    default: launch_dma<Tile128>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
+    case TileKind::k256: launch_dma<Tile256>(A, B, C, M, N, K, lda, ldb, ldc, mode, s, sk); break;
+    case TileKind::k128deep: launch_dma<Tile128Deep>(A, B, C, M, N, K, lda, ldb, ldc, mode, s, sk); break;
+    case TileKind::k64x128: launch_dma<Tile64x128>(A, B, C, M, N, K, lda, ldb, ldc, mode, s, sk); break;
+    case TileKind::k64: launch_dma<Tile64>(A, B, C, M, N, K, lda, ldb, ldc, mode, s, sk); break;
+    default: launch_dma<Tile128>(A, B, C, M, N, K, lda, ldb, ldc, mode, s, sk); break;
   }
 }
 
@@ -1192,8 +1253,9 @@ extern "C" int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_
 }
 
 extern "C" size_t bi_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0) return 0;
-  return static_cast<size_t>(splitk_count(M, N, K)) * M * N * sizeof(float);
+  if (M <= 0 || N <= 0 || K <= 0 || M > (1 << 30) || N > (1 << 30) || K > (1 << 30)) return 0;
+  const KSplit p = splitk_plan(M, N, K);
+  return p.ks > 1 ? static_cast<size_t>(p.ks) * M * N * sizeof(float) : 0;
 }
 
 extern "C" int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N,
@@ -1206,19 +1268,21 @@ extern "C" int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, 
     return BI_ERR_SHAPE;
   if (!A || !B || !C) return BI_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || (lda % 8) || (ldb % 8)) return BI_ERR_ALIGN;
-  const int splits = splitk_count(M, N, K);
-  if (!workspace || workspace_bytes < bi_gemm_splitk_workspace_bytes(M, N, K))
-    return BI_ERR_WORKSPACE;
-  const int tm = static_cast<int>((M + BM - 1) / BM), tn = static_cast<int>((N + BN - 1) / BN);
-  const int64_t nk = (K + BK - 1) / BK;
-  const int per = static_cast<int>((nk + splits - 1) / splits) * BK;
+  if (!(M * lda * 2 < (int64_t(1) << 32) && N * ldb * 2 < (int64_t(1) << 32))) return BI_ERR_UNSUPPORTED;
+  const KSplit p = splitk_plan(M, N, K);
   hipStream_t s = as_stream(stream);
-  gemm_kernel<false><<<dim3(static_cast<unsigned>(tm * tn), splits), dim3(kThreads), 0, s>>>(
-      A, static_cast<const uint16_t*>(B), workspace, int(M), int(N), int(K), lda, ldb, N, 1, tm,
-      tn, 0, per, static_cast<int64_t>(M) * N * sizeof(float));
+  const int cf = c_dtype == BI_F32;
+  if (p.ks == 1) {   // one slice: the plain kernels write C
+    launch_bf16(A, B, C, M, N, K, lda, ldb, ldc, cf, s);
+    return launch_status();
+  }
+  if (!workspace || workspace_bytes < bi_gemm_splitk_workspace_bytes(M, N, K)) return BI_ERR_WORKSPACE;
+  // the few-row or LDS-staged kernels, each slice's fp32 result into the workspace, then the
+  // slices added in ascending order
+  launch_bf16(A, B, workspace, M, N, K, lda, ldb, N, kOutF32, s, p);
   const int64_t total = M * N;
   splitk_reduce_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(
-      static_cast<const float*>(workspace), C, int(M), int(N), ldc, c_dtype == BI_F32, splits);
+      static_cast<const float*>(workspace), C, int(M), int(N), ldc, cf, p.ks);
   return launch_status();
 }
 

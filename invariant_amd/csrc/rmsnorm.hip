@@ -10,7 +10,7 @@
 //   wave64 butterfly with offsets 1..32; waves combined as (w0 + w1) + (w2 + w3).
 // Lanes t >= T hold +0.  Because every partial sum is >= +0, adding those +0 lanes or
 // waves leaves each partial unchanged bit for bit, so one 256-lane shape serves every D.
-#include "bi_common.h"
+#include "contract_fp.h"
 
 namespace bi {
 namespace {
@@ -132,9 +132,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restric
   if ((tid & (kWave - 1)) == 0) wave_part[tid / kWave] = wsum;
   __syncthreads();
   const float ssum = (wave_part[0] + wave_part[1]) + (wave_part[2] + wave_part[3]);
-  const float mean = ssum / static_cast<float>(D);
-  const float var = mean + eps;
-  const float r = 1.0f / __builtin_sqrtf(var);
+  const float r = rms_scale(ssum, D, eps);
 
   if (tid >= T) return;
   for (int j = 0, v = tid; v < nvec; ++j, v += T) {
@@ -227,9 +225,7 @@ __global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(const void* a, co
   if ((tid & (kWave - 1)) == 0) wave_part[tid / kWave] = wsum;
   __syncthreads();
   const float ssum = (wave_part[0] + wave_part[1]) + (wave_part[2] + wave_part[3]);
-  const float mean = ssum / static_cast<float>(D);
-  const float var = mean + eps;
-  const float r = 1.0f / __builtin_sqrtf(var);
+  const float r = rms_scale(ssum, D, eps);
   if (tid >= T) return;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {

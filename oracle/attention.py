@@ -23,12 +23,12 @@ import numpy as np
 from .fp import bf16_to_f64
 
 
-def attention_values_f64(q, k, v, positions, block: int = 256) -> np.ndarray:
+def attention_values_f64(q, k, v, positions, block: int = 512) -> np.ndarray:
     """The definition above on float64 values: q [T, Hq, D] (queries at absolute
-    ``positions``), k, v [L, Hkv, D] (keys/values of positions 0..L-1).  Written as matrix
-    products over all heads of a kv group at once (a library product per step; the
-    arithmetic is the plain fp64 softmax-weighted sum), in blocks of queries.
-    Returns o [T, Hq, D] float64."""
+    ``positions``), k, v [L, Hkv, D] (keys/values of positions 0..L-1).  Per kv head, the
+    scores of its query heads and a block of queries are one matrix product and the
+    weighted sum another (library products as steps; the arithmetic is the plain fp64
+    softmax-weighted sum).  Returns o [T, Hq, D] float64."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -40,18 +40,20 @@ def attention_values_f64(q, k, v, positions, block: int = 256) -> np.ndarray:
     if t == 0:
         return out
     scale = 1.0 / np.sqrt(d)
-    kt = np.ascontiguousarray(k.transpose(1, 2, 0))          # [Hkv, D, L]
-    vt = np.ascontiguousarray(v.transpose(1, 0, 2))          # [Hkv, L, D]
     for b0 in range(0, t, block):
         b1 = min(t, b0 + block)
         pb = pos[b0:b1]
         n = int(pb.max()) + 1                                # keys any query here can see
-        qg = q[b0:b1].reshape(b1 - b0, hkv, g, d).transpose(1, 2, 0, 3)   # [Hkv, G, T, D]
-        s = (qg @ kt[:, None, :, :n]) * scale                # [Hkv, G, T, n]
-        s = np.where(np.arange(n)[None, None, None, :] <= pb[None, None, :, None], s, -np.inf)
-        w = np.exp(s - s.max(axis=-1, keepdims=True))
-        o = (w @ vt[:, None, :n, :]) / w.sum(axis=-1, keepdims=True)       # [Hkv, G, T, D]
-        out[b0:b1] = o.transpose(2, 0, 1, 3).reshape(b1 - b0, hq, d)
+        row_pos = np.repeat(pb, g)                           # rows: (query, head of the group)
+        mask = np.arange(n)[None, :] <= row_pos[:, None]
+        for h in range(hkv):
+            kh = k[:n, h, :]                                 # [n, D]
+            vh = v[:n, h, :]
+            qh = q[b0:b1, h * g:(h + 1) * g, :].reshape(-1, d)    # [(b1 - b0) G, D]
+            s = np.where(mask, (qh @ kh.T) * scale, -np.inf)
+            w = np.exp(s - s.max(axis=1, keepdims=True))
+            o = (w @ vh) / w.sum(axis=1, keepdims=True)
+            out[b0:b1, h * g:(h + 1) * g, :] = o.reshape(b1 - b0, g, d)
     return out
 
 

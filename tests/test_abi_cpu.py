@@ -119,7 +119,7 @@ def test_hip_constants_equal_oracle_derivation():
     EXP = 1/ln2, ln2 head, ln2 tail, then the Horner coefficients 1/7! .. 1/0!; LOG = sqrt 2,
     the Horner coefficients 2/15 .. 2/1, then ln2 head and tail.  A swap of two coefficients
     or of head and tail fails here."""
-    src = open(os.path.join(ROOT, "invariant_amd", "csrc", "logsoftmax.hip")).read()
+    src = open(os.path.join(ROOT, "invariant_amd", "csrc", "contract_fp.h")).read()
     k = ORACLE_K
     exp_want = [k["LOG2E"], k["LN2_HI"], k["LN2_LO"], *reversed(k["EXP_C"])]
     log_want = [k["SQRT2"], *reversed(k["LOG_B"]), k["LN2_HI"], k["LN2_LO"]]

@@ -146,6 +146,24 @@ def test_cfg4_decode_equals_prefill_long(lib):
         assert same_bits(out_d[b], out_p[qsl_p[b] + l - 1])
 
 
+def test_decode_equals_prefill_at_32k_boundaries(lib):
+    # decode == prefill bitwise across the last 1024-key group boundaries of the 32k context
+    # (16383/16384/16385 and 32767/32768 keys: a group of four chunks just full, or one key
+    # into the next), and the decode rows within 1 ulp of the oracle from the same calls
+    L = [16383, 16384, 16385, 32767, 32768]
+    say("prefill", sum(L), "tokens")
+    pre = attention_case(L, L, cfg=47)
+    kc, vc, bt = make_cache(pre, 16, [0] * len(L))
+    out_p, qsl_p = run(lib, pre, kc, vc, bt)
+    say("decode")
+    dec = attention_case(L, [1] * len(L), cfg=47)
+    kc2, vc2, bt2 = make_cache(dec, 16, [l - 1 for l in L], cfg=86)
+    out_d, qsl_d = run(lib, dec, kc2, vc2, bt2)
+    for b, l in enumerate(L):
+        assert same_bits(out_d[b], out_p[qsl_p[b] + l - 1]), l
+    _check_vs_oracle(dec, out_d, qsl_d, which={b: [0] for b in range(len(L))})
+
+
 def test_batchdep_split_variant_correct_but_not_invariant(lib):
     B = 32
     L = ragged_lengths(B, 1400, 8000, 46, 0)

@@ -205,6 +205,22 @@ def test_splitk_variant_is_not_invariant(lib):
     assert bf16_within_1ulp(bits(sk), gemm_f64(a2, b2))["ok"]
 
 
+def test_splitk_variant_vs_oracle_and_slices(lib):
+    # the comparison variant on the few-row and the LDS-staged kernels, with slice counts
+    # that change with M: a correct GEMM on well-conditioned data, not an invariant one
+    a, b = gemm_inputs(1000, 1024, 4096, cfg=48, sd=1.0)
+    A, W = bf16(a), bf16(np.ascontiguousarray(b.T))
+    slices = set()
+    for m in (1, 33, 64, 300, 1000):
+        need = lib.load().bi_gemm_splitk_workspace_bytes(m, 1024, 4096)
+        slices.add(max(1, need // (4 * m * 1024)))
+        c = lib.bi_gemm_splitk(A[:m], W)
+        r = bf16_within_1ulp(bits(c), gemm_f64(a[:m], b))
+        assert r["ok"], (m, r)
+    say("split-K slice counts over M", sorted(slices))
+    assert len(slices) > 1
+
+
 def test_fp32_operand_variant(lib):
     rng = np.random.default_rng(2)
     af = rng.standard_normal((100, 4096)).astype(np.float32)

@@ -104,3 +104,21 @@ def test_sum_matches_scalar_replay_and_probabilities_sum_to_one():
         lp, a = logsoftmax_argmax(xs)
         e = EXP(xs[0] - xs[0, a[0]])
         assert S.tree_sum([float(t) for t in e], 4) == float(LOG.__globals__["tree_sum"](e[None, :], 4)[0])
+
+
+def test_c_replay_equals_python_oracle():
+    # oracle/explog.c (used for the exhaustive GPU sweeps) is the Python oracle's EXP and LOG
+    # bit for bit: on a stride through every float of each domain, on random values, and on
+    # the special values
+    from oracle import explog_c
+    from oracle.logsoftmax import EXP, LOG
+    bits = np.arange(0x80000000, 0xC2D00001, 97, dtype=np.uint64).astype(np.uint32)
+    x = np.concatenate([bits.view(np.float32),
+                        np.float32([0.0, -0.0, -np.inf, np.nan, -87.33654, -103.97208])])
+    assert np.array_equal(explog_c.EXP(x).view(np.uint32), EXP(x).view(np.uint32))
+    s = np.arange(0x3F800000, 0x47000001, 13, dtype=np.uint32).view(np.float32)
+    s = np.concatenate([s, np.float32([1.0, 32768.0, np.inf, np.nan, 1.4142135])])
+    assert np.array_equal(explog_c.LOG(s).view(np.uint32), LOG(s).view(np.uint32))
+    first = 0xC2000000
+    assert np.array_equal(explog_c.exp_bits(first, 1000).view(np.uint32),
+                          EXP((np.arange(1000, dtype=np.uint32) + np.uint32(first)).view(np.float32)).view(np.uint32))
