@@ -1033,6 +1033,106 @@ __global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
   }
 }
 
+// Split-K comparison variant for up to 4 rows (NOT batch-invariant; bi_gemm never runs it):
+// a workgroup of 4 waves owns one 16-column block, wave w runs the K steps [w S, w S + S)
+// (S = 8, 16 or 32, the smallest with 4 S covering K) from +0 with every load of its segment
+// issued at once, and the four partials are added in wave order -- so all four SIMDs of a CU
+// stream weights, at the price of a different association than the unsplit chain.  The rows
+// of A are staged in LDS and read from there as the instruction's A operand.  (Handing the
+// one chain from wave to wave instead, which keeps bi_gemm's order, measured no faster than
+// one wave per block: the launch and the weight stream, not the chain, bound these sizes.)
+constexpr int kWcWaves = 4, kWcRows = 4;
+
+template <int SEG>
+__global__ __launch_bounds__(256, 2) void gemm_wsplit_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
+    int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32) {
+  constexpr int KP = kWcWaves * SEG * 32;   // staged row length (zeros past K)
+  constexpr int LDR = KP + 8;               // LDS row pitch: rows 16 bytes apart in the banks
+  __shared__ __attribute__((aligned(16))) uint16_t sa[kWcRows * LDR];
+  __shared__ floatx4 xfer[kWcWaves * 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col0 = blockIdx.x * 16;
+  const int kl = 8 * (lane >> 4);
+  const int k0 = wave * SEG * 32;           // first k of this wave's segment
+  // 1. every B operand of the segment (a chunk at or past K reads offset 0 of its row and
+  //    is replaced by zeros)
+  const uint16_t* pb = B + static_cast<int64_t>(min(col0 + (lane & 15), N - 1)) * ldb + kl;
+  u16x8 braw[SEG];
+#pragma unroll
+  for (int s = 0; s < SEG; ++s) {
+    const int k = k0 + 32 * s;
+    braw[s] = *reinterpret_cast<const u16x8*>(pb + (k + kl < K ? k : -kl));
+  }
+  // 2. A rows into LDS, zeros past K
+  constexpr int cpr = KP / 8;               // 16-byte chunks per staged row
+  for (int i = tid; i < M * cpr; i += 256) {
+    const int r = i / cpr, k = (i % cpr) * 8;
+    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (k < K) v = *reinterpret_cast<const u16x8*>(A + static_cast<int64_t>(r) * lda + k);
+    *reinterpret_cast<u16x8*>(sa + r * LDR + k) = v;
+  }
+  __syncthreads();
+  const uint16_t* pa = sa + min(lane & 15, M - 1) * LDR + k0 + kl;
+  // this wave's steps (those below ceil(K / 32))
+  auto run = [&](floatx4 acc) {
+#pragma unroll
+    for (int s = 0; s < SEG; ++s) {
+      if (k0 + 32 * s >= K) break;          // wave-uniform
+      const u16x8 b = (k0 + 32 * s + kl < K) ? braw[s] : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      const u16x8 a = *reinterpret_cast<const u16x8*>(pa + 32 * s);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
+    }
+    return acc;
+  };
+  floatx4 acc = run(floatx4{0.f, 0.f, 0.f, 0.f});
+  xfer[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  acc = xfer[lane];
+#pragma unroll
+  for (int w = 1; w < kWcWaves; ++w) {
+    const floatx4 p = xfer[w * 64 + lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = acc[r] + p[r];
+  }
+  // register r is row 4 (lane / 16) + r, column lane % 16 of the block
+  const int col = col0 + (lane & 15);
+  if (col >= N) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * (lane >> 4) + r;
+    if (row >= M) continue;
+    if (c_f32)
+      static_cast<float*>(C)[static_cast<int64_t>(row) * ldc + col] = acc[r];
+    else
+      static_cast<uint16_t*>(C)[static_cast<int64_t>(row) * ldc + col] = f32_to_bf16(acc[r]);
+  }
+}
+
+// The 4-wave split takes up to 4 rows with K a multiple of 8 in 512 .. 4096 and at most two
+// 16-column blocks per CU.
+bool use_wsplit(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= kWcRows && K % 8 == 0 && K >= 512 && K <= 4096 &&
+         (N + 15) / 16 <= 2 * static_cast<int64_t>(cu_count());
+}
+
+void launch_wsplit(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                   int64_t lda, int64_t ldb, int64_t ldc, int cf, hipStream_t s) {
+  const int64_t steps = (K + 31) / 32;
+  const dim3 grid(static_cast<unsigned>((N + 15) / 16)), block(256);
+  const uint16_t* a = static_cast<const uint16_t*>(A);
+  const uint16_t* b = static_cast<const uint16_t*>(B);
+  if (steps <= kWcWaves * 8)
+    gemm_wsplit_kernel<8><<<grid, block, 0, s>>>(a, b, C, int(M), int(N), int(K), lda, ldb, ldc, cf);
+  else if (steps <= kWcWaves * 16)
+    gemm_wsplit_kernel<16><<<grid, block, 0, s>>>(a, b, C, int(M), int(N), int(K), lda, ldb, ldc, cf);
+  else
+    gemm_wsplit_kernel<32><<<grid, block, 0, s>>>(a, b, C, int(M), int(N), int(K), lda, ldb, ldc, cf);
+}
+
 // Few-row configurations (measured on MI355X at the decode shapes).  A wave's A operand reads
 // (RB row blocks per step) come from L2 and hit the same few lines in every wave, so once
 // there are several rows a wave takes at least half as many column blocks as row blocks: up
@@ -1254,6 +1354,7 @@ extern "C" int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_
 
 extern "C" size_t bi_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || M > (1 << 30) || N > (1 << 30) || K > (1 << 30)) return 0;
+  if (use_wsplit(M, N, K)) return 0;   // split over the waves of a workgroup
   const KSplit p = splitk_plan(M, N, K);
   return p.ks > 1 ? static_cast<size_t>(p.ks) * M * N * sizeof(float) : 0;
 }
@@ -1269,9 +1370,13 @@ extern "C" int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, 
   if (!A || !B || !C) return BI_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || (lda % 8) || (ldb % 8)) return BI_ERR_ALIGN;
   if (!(M * lda * 2 < (int64_t(1) << 32) && N * ldb * 2 < (int64_t(1) << 32))) return BI_ERR_UNSUPPORTED;
-  const KSplit p = splitk_plan(M, N, K);
   hipStream_t s = as_stream(stream);
   const int cf = c_dtype == BI_F32;
+  if (use_wsplit(M, N, K)) {   // up to 4 rows: K split over the 4 waves of a workgroup
+    launch_wsplit(A, B, C, M, N, K, lda, ldb, ldc, cf, s);
+    return launch_status();
+  }
+  const KSplit p = splitk_plan(M, N, K);
   if (p.ks == 1) {   // one slice: the plain kernels write C
     launch_bf16(A, B, C, M, N, K, lda, ldb, ldc, cf, s);
     return launch_status();

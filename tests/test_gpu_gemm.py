@@ -219,6 +219,15 @@ def test_splitk_variant_vs_oracle_and_slices(lib):
         assert r["ok"], (m, r)
     say("split-K slice counts over M", sorted(slices))
     assert len(slices) > 1
+    # up to 4 rows: K split over the 4 waves of a workgroup (segments of 8, 16, 32 steps,
+    # whole steps past K skipped, a partial last step, ragged N)
+    for n, k in ((1024, 1000), (300, 520), (4100, 3000), (6144, 4096)):
+        a, b = gemm_inputs(4, n, k, cfg=50)
+        W = bf16(np.ascontiguousarray(b.T))
+        for m in (1, 2, 4):
+            c = lib.bi_gemm_splitk(bf16(a[:m]), W)
+            r = bf16_within_1ulp(bits(c), gemm_f64(a[:m], b))
+            assert r["ok"], (n, k, m, r)
 
 
 def test_fp32_operand_variant(lib):
