@@ -185,7 +185,10 @@ int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * the last q_b = query_start_loc[b+1] - query_start_loc[b] are new (0 <= q_b <=
  * seq_lens[b]).  New token i of sequence b (row query_start_loc[b] + i of q/k_new/v_new/
  * out) sits at absolute position p = seq_lens[b] - q_b + i.
- *   q        [num_tokens, Hq, D] bf16, contiguous
+ *   q        [num_tokens, Hq, D], contiguous, dtype q_dtype: BI_BF16, or BI_F32 (the FP32 upcast
+ *            of [XV]: each value split exactly into bf16 hi + mid + lo, the three products
+ *            accumulated in that order in every 32-wide step of the score's d-sum, so the
+ *            scores see q at full fp32 precision; keys stay the cache's bf16)
  *   k_new    [num_tokens, Hkv, D] bf16 (keys already rotated), contiguous
  *   v_new    [num_tokens, Hkv, D] bf16, contiguous
  *   k_cache  [num_pages, Hkv, D/8, page_size, 8] bf16: per page and kv head, D is cut
@@ -225,7 +228,7 @@ int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  */
 size_t bi_attention_workspace_bytes(int64_t num_tokens, int32_t num_q_heads, int32_t head_dim,
                                     int64_t max_seq_len);
-int bi_attention(const void* q, const void* k_new, const void* v_new, void* k_cache,
+int bi_attention(const void* q, int q_dtype, const void* k_new, const void* v_new, void* k_cache,
                  void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                  const int32_t* query_start_loc, int32_t batch, int64_t num_tokens,
                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
@@ -247,7 +250,7 @@ int bi_attention(const void* q, const void* k_new, const void* v_new, void* k_ca
  * the caller.  Nothing in the scratch has to start at zero.
  * Errors: as bi_attention; BI_ERR_WORKSPACE when the call needs more than the 64 MiB;
  * BI_ERR_HIP when the scratch's device address cannot be obtained. */
-int bi_attention_noalloc(const void* q, const void* k_new, const void* v_new, void* k_cache,
+int bi_attention_noalloc(const void* q, int q_dtype, const void* k_new, const void* v_new, void* k_cache,
                          void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                          const int32_t* query_start_loc, int32_t batch, int64_t num_tokens,
                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -261,7 +264,7 @@ int bi_attention_noalloc(const void* q, const void* k_new, const void* v_new, vo
  * chunks, merging in registers; the group size is about total_chunks * Hkv / 1024, so the
  * association of a token's merges -- and its bits -- depends on the rest of the batch.
  * workspace >= bi_attention_workspace_bytes(num_tokens, Hq, D, max_seq_len). */
-int bi_attention_batchdep_split(const void* q, const void* k_new, const void* v_new,
+int bi_attention_batchdep_split(const void* q, int q_dtype, const void* k_new, const void* v_new,
                                 void* k_cache, void* v_cache, const int32_t* block_table,
                                 const int32_t* seq_lens, const int32_t* query_start_loc,
                                 int32_t batch, int64_t num_tokens, int32_t num_q_heads,
@@ -303,12 +306,13 @@ int bi_embedding(const int32_t* ids, const void* table, int table_dtype, void* o
                  int64_t D, int64_t vocab, int out_dtype, void* stream);
 
 /* bi_rope_qkv: splits a fused projection qkv [T, (Hq + 2 Hkv) * D] (row stride ldqkv,
- *   dtype qkv_dtype) into q [T, Hq, D], k [T, Hkv, D], v [T, Hkv, D] (bf16, contiguous)
- *   and rotates q and k by position ("rotate half": pairs (i, i + D/2), angle
- *   pos * base^(-2i/D), angle, cos and sin evaluated in fp64 and rounded to fp32).
+ *   dtype qkv_dtype) into q [T, Hq, D] (dtype q_dtype), k [T, Hkv, D], v [T, Hkv, D] (bf16,
+ *   the type of the KV cache; all contiguous) and rotates q and k by position ("rotate half":
+ *   pairs (i, i + D/2), angle pos * base^(-2i/D), angle, cos and sin evaluated in fp64 and
+ *   rounded to fp32; the rotation in fp32, one rounding to the output type).
  *   positions [T] int32. */
 int bi_rope_qkv(const void* qkv, int64_t ldqkv, int qkv_dtype, const int32_t* positions,
-                void* q, void* k, void* v, int64_t T, int32_t num_q_heads,
+                void* q, int q_dtype, void* k, void* v, int64_t T, int32_t num_q_heads,
                 int32_t num_kv_heads, int32_t head_dim, double base, void* stream);
 
 /* bi_swiglu: out[t, j] = silu(g) * u with g = gu[t, j], u = gu[t, F + j];

@@ -31,16 +31,17 @@ _SIGS = {
     "bi_gemm_splitk_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "bi_gemm_splitk": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _c.c_int, _P, _SZ, _P]),
     "bi_attention_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I64]),
-    "bi_attention": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
-                                _I32, _I64, _F32, _P, _c.c_int, _P, _SZ, _P]),
-    "bi_attention_noalloc": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
-                                        _I32, _I64, _F32, _P, _c.c_int, _P]),
-    "bi_attention_batchdep_split": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32,
-                                               _I32, _I32, _I32, _I64, _I64, _F32, _P, _c.c_int, _P,
-                                               _SZ, _P]),
+    "bi_attention": (_c.c_int, [_P, _c.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32,
+                                _I32, _I32, _I64, _F32, _P, _c.c_int, _P, _SZ, _P]),
+    "bi_attention_noalloc": (_c.c_int, [_P, _c.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32,
+                                        _I32, _I32, _I32, _I64, _F32, _P, _c.c_int, _P]),
+    "bi_attention_batchdep_split": (_c.c_int, [_P, _c.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32,
+                                               _I32, _I32, _I32, _I32, _I64, _I64, _F32, _P, _c.c_int,
+                                               _P, _SZ, _P]),
     "bi_logsoftmax_argmax": (_c.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "bi_embedding": (_c.c_int, [_P, _P, _c.c_int, _P, _I64, _I64, _I64, _c.c_int, _P]),
-    "bi_rope_qkv": (_c.c_int, [_P, _I64, _c.c_int, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F64, _P]),
+    "bi_rope_qkv": (_c.c_int, [_P, _I64, _c.c_int, _P, _P, _c.c_int, _P, _P, _I64, _I32, _I32, _I32, _F64,
+                               _P]),
     "bi_swiglu": (_c.c_int, [_P, _I64, _P, _I64, _I64, _P]),
     "bi_gemm_swiglu": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
     "bi_add_rmsnorm": (_c.c_int, [_P, _P, _P, _c.c_int, _P, _P, _c.c_int, _I64, _I64, _c.c_float, _P]),
@@ -185,7 +186,7 @@ def bi_attention(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("bi_attention", load().bi_attention(
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(q), _code(q.dtype), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(seq_lens), _ptr(query_start_loc), B, T, Hq, Hkv, D, page, max_pages, int(max_seq_len),
         float(scale), _ptr(out), _code(out.dtype), _ptr(workspace), wsz, _stream(q)))
     return out
@@ -202,7 +203,7 @@ def bi_attention_noalloc(q, k_new, v_new, k_cache, v_cache, block_table, seq_len
     if out is None:
         out = torch.empty((T, Hq, D), dtype=out_dtype, device=q.device)
     _check("bi_attention_noalloc", load().bi_attention_noalloc(
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(q), _code(q.dtype), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(seq_lens), _ptr(query_start_loc), B, T, Hq, Hkv, D, page, max_pages, int(max_seq_len),
         float(scale), _ptr(out), _code(out.dtype), _stream(q)))
     return out
@@ -222,7 +223,7 @@ def bi_attention_batchdep_split(q, k_new, v_new, k_cache, v_cache, block_table, 
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check("bi_attention_batchdep_split", load().bi_attention_batchdep_split(
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(q), _code(q.dtype), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(seq_lens), _ptr(query_start_loc), B, T, Hq, Hkv, D, page, max_pages, int(max_seq_len),
         int(total_chunks), float(scale), _ptr(out), _code(out.dtype), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(q)))
@@ -256,14 +257,14 @@ def bi_embedding(ids, table, out=None, out_dtype=torch.bfloat16):
 
 
 def bi_rope_qkv(qkv, positions, num_q_heads, num_kv_heads, head_dim, base=10000.0,
-                q=None, k=None, v=None):
+                q=None, k=None, v=None, q_dtype=torch.bfloat16):
     T = qkv.shape[0]
     dev = qkv.device
-    q = q if q is not None else torch.empty((T, num_q_heads, head_dim), dtype=torch.bfloat16, device=dev)
+    q = q if q is not None else torch.empty((T, num_q_heads, head_dim), dtype=q_dtype, device=dev)
     k = k if k is not None else torch.empty((T, num_kv_heads, head_dim), dtype=torch.bfloat16, device=dev)
     v = v if v is not None else torch.empty((T, num_kv_heads, head_dim), dtype=torch.bfloat16, device=dev)
     _check("bi_rope_qkv", load().bi_rope_qkv(_ptr(qkv), _ld(qkv), _code(qkv.dtype), _ptr(positions),
-                                              _ptr(q), _ptr(k), _ptr(v), T, num_q_heads,
+                                              _ptr(q), _code(q.dtype), _ptr(k), _ptr(v), T, num_q_heads,
                                               num_kv_heads, head_dim, float(base), _stream(qkv)))
     return q, k, v
 

@@ -181,10 +181,12 @@ __device__ __forceinline__ void issue_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// S = K Q^T for this wave's keys, scaled to log2 units and masked beyond the column's
-// position; m = the chunk maximum of column lane % 16 (the 4 wave maxima exchanged
+// S = K Q^T for this wave's keys (q as NQ bf16 terms: 1, or hi, mid, lo of an fp32 q,
+// each 32-wide d step accumulating its terms in that order), scaled to log2 units and masked
+// beyond the column's position; m = the chunk maximum of column lane % 16 (the 4 wave maxima exchanged
 // through LDS); on return s holds P = 2^(t - m) and lsum this wave's sum of P.
-__device__ __forceinline__ void chunk_scores(int c, const u16x8 (&kop)[2][2][4], const u16x8 (&qop)[4],
+template <int NQ>
+__device__ __forceinline__ void chunk_scores(int c, const u16x8 (&kop)[2][2][4], const u16x8 (&qop)[NQ][4],
                                              int pcol, float sl2, ChunkLDS& sh, floatx4 (&s)[2][2],
                                              float& m, float& lsum) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -196,7 +198,9 @@ __device__ __forceinline__ void chunk_scores(int c, const u16x8 (&kop)[2][2][4],
     for (int h2 = 0; h2 < 2; ++h2) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc = mfma16(kop[uu][h2][t], qop[t], acc);
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) acc = mfma16(kop[uu][h2][t], qop[j][t], acc);
       s[uu][h2] = acc;
     }
   }
@@ -298,7 +302,8 @@ __device__ __forceinline__ void chunk_values(const Seq& sq, int c, u16x8 (&vop)[
 // One 256-key chunk, phases back to back.  pcol: absolute position of this lane's column
 // (-1: unused column).  K is loaded first: loads complete in order, so the scores are
 // computed while V is still arriving.
-__device__ __forceinline__ void chunk_partial(const Seq& sq, int c, const u16x8 (&qop)[4], int pcol,
+template <int NQ>
+__device__ __forceinline__ void chunk_partial(const Seq& sq, int c, const u16x8 (&qop)[NQ][4], int pcol,
                                               float sl2, ChunkLDS& sh, float& m_c, float& l_c,
                                               floatx4 (&oc)[2]) {
   const int pg = chunk_pages(sq, c);
@@ -323,17 +328,46 @@ __device__ __forceinline__ void merge_step(float& m, float& l, float mc, float l
 
 __device__ __forceinline__ float mix(float o, float oc, float a, float b) { return a * o + b * oc; }
 
-// Q operand of one column: q[token][head][32 g + 8 t .. + 7] for t = 0..3.
-__device__ __forceinline__ void load_q(const uint16_t* q, int64_t token, int head, int hq, bool ok,
-                                       u16x8 (&qop)[4]) {
+// Q operand of one column: q[token][head][32 g + 8 t .. + 7] for t = 0..3; NQ = 1: q is bf16,
+// NQ = 3: q is fp32, split exactly into bf16 hi, mid, lo.
+template <int NQ>
+__device__ __forceinline__ void load_q_at(const void* q, int64_t token, int head, int hq,
+                                          u16x8 (&qop)[NQ][4]) {
   const int g = (threadIdx.x & 63) >> 4;
-  if (ok) {
-    const uint16_t* p = q + (token * hq + head) * HD + 32 * g;
+  const int64_t off = (token * hq + head) * HD + 32 * g;
+  if constexpr (NQ == 1) {
+    const uint16_t* p = static_cast<const uint16_t*>(q) + off;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) qop[t] = *reinterpret_cast<const u16x8*>(p + 8 * t);
+    for (int t = 0; t < 4; ++t) qop[0][t] = *reinterpret_cast<const u16x8*>(p + 8 * t);
+  } else {
+    static_assert(NQ == 3, "bf16 or fp32 q");
+    const float* p = static_cast<const float*>(q) + off;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const floatx4 x0 = *reinterpret_cast<const floatx4*>(p + 8 * t);
+      const floatx4 x1 = *reinterpret_cast<const floatx4*>(p + 8 * t + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint16_t h, m, l;
+        split_bf16x3(e < 4 ? x0[e] : x1[e - 4], h, m, l);
+        qop[0][t][e] = h;
+        qop[1][t][e] = m;
+        qop[2][t][e] = l;
+      }
+    }
+  }
+}
+
+template <int NQ>
+__device__ __forceinline__ void load_q(const void* q, int64_t token, int head, int hq, bool ok,
+                                       u16x8 (&qop)[NQ][4]) {
+  if (ok) {
+    load_q_at<NQ>(q, token, head, hq, qop);
   } else {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) qop[t] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < NQ; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qop[j][t] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
 }
 
@@ -421,16 +455,15 @@ __device__ __forceinline__ SplitStep split_unit(int u, int t0, const int4* s_tok
 
 // Q operands of one column, loaded unconditionally (an unused column loads the group's
 // first head; its scores are masked and its output is never stored).
-__device__ __forceinline__ void load_q_col(const uint16_t* q, int64_t token, int head, int hq,
-                                           u16x8 (&qop)[4]) {
-  const int g = (threadIdx.x & 63) >> 4;
-  const uint16_t* p = q + (token * hq + head) * HD + 32 * g;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) qop[t] = *reinterpret_cast<const u16x8*>(p + 8 * t);
+template <int NQ>
+__device__ __forceinline__ void load_q_col(const void* q, int64_t token, int head, int hq,
+                                           u16x8 (&qop)[NQ][4]) {
+  load_q_at<NQ>(q, token, head, hq, qop);
 }
 
+template <int NQ>
 __global__ __launch_bounds__(256) void attn_split_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const void* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt, const int4* __restrict__ tok,
     int num_tokens, int max_pages, int hq, int hkv, int ps, int max_groups, float sl2,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, int uc) {
@@ -480,8 +513,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
 
   SplitStep cur = split_unit(blockIdx.x, 0, s_tok, s_start, num_tokens, kc, vc, bt, max_pages, ps, hkv, uc);
   int pg = chunk_pages(cur.sq, cur.c);
-  u16x8 qop[4], kop[2][2][4], vop[2][8];
-  load_q_col(q, cur.t, cur.kvh * G + hcol, hq, qop);
+  u16x8 qop[NQ][4], kop[2][2][4], vop[2][8];
+  load_q_col<NQ>(q, cur.t, cur.kvh * G + hcol, hq, qop);
   chunk_load_k(cur.sq, pg, kop);
   SplitStep nxt = advance(cur);
   int pgn = chunk_pages(nxt.sq, nxt.c);
@@ -496,8 +529,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
     const SplitStep nxt3 = advance(nxt2);
     floatx4 s[2][2];
     float m, lsum;
-    chunk_scores(cur.c, kop, qop, used ? cur.pos : -1, sl2, sh, s, m, lsum);
-    load_q_col(q, nxt.t, nxt.kvh * G + hcol, hq, qop);
+    chunk_scores<NQ>(cur.c, kop, qop, used ? cur.pos : -1, sl2, sh, s, m, lsum);
+    load_q_col<NQ>(q, nxt.t, nxt.kvh * G + hcol, hq, qop);
     chunk_load_k(nxt.sq, pgn, kop);
     issue_fence();
     float m_c, l_c;
@@ -613,8 +646,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 // head) walks its chunks and merges them in registers, then the groups are merged.  The
 // group size is chosen from the whole batch's work, so the association of the merges of
 // a token -- and its bits -- change with the batch.
+template <int NQ>
 __global__ __launch_bounds__(256) void attn_group_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const void* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch,
     int max_pages, int hq, int hkv, int ps, int max_groups, int group, float sl2,
@@ -633,15 +667,15 @@ __global__ __launch_bounds__(256) void attn_group_kernel(
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15;
   const bool used = col < G;
-  u16x8 qop[4];
-  load_q(q, t, kvh * G + col, hq, used, qop);
+  u16x8 qop[NQ][4];
+  load_q<NQ>(q, t, kvh * G + col, hq, used, qop);
   Seq sq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, kvh, L, max_pages, __builtin_ctz(ps)};
   float m = 0.f, l = 0.f;
   floatx4 o[2];
   for (int c = c_first; c <= c_last; ++c) {
     float m_c, l_c;
     floatx4 oc[2];
-    chunk_partial(sq, c, qop, used ? pos : -1, sl2, sh, m_c, l_c, oc);
+    chunk_partial<NQ>(sq, c, qop, used ? pos : -1, sl2, sh, m_c, l_c, oc);
     if (c == c_first) {
       m = m_c; l = l_c; o[0] = oc[0]; o[1] = oc[1];
     } else {
@@ -673,8 +707,9 @@ __global__ __launch_bounds__(256) void attn_group_kernel(
 // two sequences is processed once per sequence with the other sequence's columns off.
 constexpr int WALK_NG = 2;
 
+template <int NQ>
 __global__ __launch_bounds__(256) void attn_walk_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const void* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch,
     int max_pages, int hq, int hkv, int ps, int64_t num_tokens, float sl2, void* __restrict__ out,
@@ -704,14 +739,14 @@ __global__ __launch_bounds__(256) void attn_walk_kernel(
   const int b_last = find_seq(qsl, batch, static_cast<int>(tok_last));
   for (; b <= b_last; ++b) {
     if (qsl[b + 1] == qsl[b]) continue;
-    u16x8 qop[WALK_NG][4];
+    u16x8 qop[WALK_NG][NQ][4];
     int pcol[WALK_NG];
     int pmax = -1;
 #pragma unroll
     for (int gi = 0; gi < WALK_NG; ++gi) {
       const bool mine = my_b[gi] == b;
       pcol[gi] = mine ? my_pos[gi] : -1;
-      load_q(q, mine ? my_tok[gi] : 0, head, hq, mine, qop[gi]);
+      load_q<NQ>(q, mine ? my_tok[gi] : 0, head, hq, mine, qop[gi]);
       pmax = max(pmax, pcol[gi]);
     }
     const int L = seq_lens[b];
@@ -737,7 +772,7 @@ __global__ __launch_bounds__(256) void attn_walk_kernel(
         {
           floatx4 sc[2][2];
           float mx, lsum;
-          chunk_scores(c, kop, qop[gi], pcol[gi], sl2, sh, sc, mx, lsum);
+          chunk_scores<NQ>(c, kop, qop[gi], pcol[gi], sl2, sh, sc, mx, lsum);
           chunk_values(sq, c, vop, sc, mx, lsum, sh, m_c, l_c, oc);
         }
         if (c * CHUNK > pcol[gi]) continue;
@@ -788,12 +823,13 @@ __global__ __launch_bounds__(256) void attn_walk_kernel(
   }
 }
 
-// Workgroups of attn_split_kernel resident per CU (read once).
+// Workgroups of attn_split_kernel<NQ> resident per CU (read once).
+template <int NQ>
 int split_resident() {
   static std::atomic<int> cached{0};
   int v = cached.load(std::memory_order_relaxed);
   if (v > 0) return v;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, attn_split_kernel, 256, 0) != hipSuccess || v < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, attn_split_kernel<NQ>, 256, 0) != hipSuccess || v < 1)
     v = 1;
   cached.store(v, std::memory_order_relaxed);
   return v;
@@ -822,12 +858,13 @@ namespace bi {
 namespace {
 
 // Validation shared by bi_attention and bi_attention_noalloc (everything but the workspace).
-int attention_check(const void* q, const void* k_new, const void* v_new, void* k_cache,
+int attention_check(const void* q, int q_dtype, const void* k_new, const void* v_new, void* k_cache,
                     void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                     const int32_t* query_start_loc, int32_t batch, int64_t num_tokens,
                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                     int32_t max_pages_per_seq, int64_t max_seq_len, void* out, int out_dtype) {
-  if (out_dtype != BI_BF16 && out_dtype != BI_F32) return BI_ERR_DTYPE;
+  if ((out_dtype != BI_BF16 && out_dtype != BI_F32) || (q_dtype != BI_BF16 && q_dtype != BI_F32))
+    return BI_ERR_DTYPE;
   if (batch < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
       page_size < 1 || max_pages_per_seq < 1 || max_seq_len < 0)
     return BI_ERR_SHAPE;
@@ -862,6 +899,7 @@ bool split_fine(int64_t num_tokens, int64_t maxc, int32_t num_kv_heads) {
 
 // The kernels of a validated call.  Split path: ws_ml holds the (m, l) pairs of every partial
 // slot, followed (16-byte aligned) by their o vectors; ws_tok the per-token records.
+template <int NQ>
 void attention_launch(const void* q, const void* k_new, const void* v_new, void* k_cache,
                       void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                       const int32_t* query_start_loc, int32_t batch, int64_t num_tokens,
@@ -888,9 +926,9 @@ void attention_launch(const void* q, const void* k_new, const void* v_new, void*
     float* ps_o = ws_ml + ml_floats(num_tokens * num_q_heads * slots);
     // as many workgroups as can be resident at once, never more than there are units
     const int64_t units = num_tokens * slots * num_kv_heads;   // an upper bound of the work units
-    const int64_t grid = std::min<int64_t>(units, static_cast<int64_t>(split_resident()) * cu_count());
-    attn_split_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, s>>>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+    const int64_t grid = std::min<int64_t>(units, static_cast<int64_t>(split_resident<NQ>()) * cu_count());
+    attn_split_kernel<NQ><<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, s>>>(
+        q, static_cast<const uint16_t*>(k_cache),
         static_cast<const uint16_t*>(v_cache), block_table, ws_tok, static_cast<int>(num_tokens),
         max_pages_per_seq, num_q_heads, num_kv_heads, page_size, static_cast<int>(slots), sl2,
         ws_ml, ps_o, uc);
@@ -901,24 +939,40 @@ void attention_launch(const void* q, const void* k_new, const void* v_new, void*
   } else {
     const int NT = 16 / G * WALK_NG;
     const int64_t blocks = (num_tokens + NT - 1) / NT;
-    attn_walk_kernel<<<dim3(static_cast<unsigned>(blocks), num_kv_heads), dim3(256), 0, s>>>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+    attn_walk_kernel<NQ><<<dim3(static_cast<unsigned>(blocks), num_kv_heads), dim3(256), 0, s>>>(
+        q, static_cast<const uint16_t*>(k_cache),
         static_cast<const uint16_t*>(v_cache), block_table, seq_lens, query_start_loc, batch,
         max_pages_per_seq, num_q_heads, num_kv_heads, page_size, num_tokens, sl2, out, of);
   }
 }
 
+void attention_launch_q(int q_dtype, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                        void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                        const int32_t* query_start_loc, int32_t batch, int64_t num_tokens,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t page_size,
+                        int32_t max_pages_per_seq, int64_t max_seq_len, float scale, void* out,
+                        int out_dtype, float* ws_ml, int4* ws_tok, hipStream_t s) {
+  if (q_dtype == BI_F32)
+    attention_launch<3>(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start_loc, batch,
+                        num_tokens, num_q_heads, num_kv_heads, page_size, max_pages_per_seq, max_seq_len,
+                        scale, out, out_dtype, ws_ml, ws_tok, s);
+  else
+    attention_launch<1>(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start_loc, batch,
+                        num_tokens, num_q_heads, num_kv_heads, page_size, max_pages_per_seq, max_seq_len,
+                        scale, out, out_dtype, ws_ml, ws_tok, s);
+}
+
 }  // namespace
 }  // namespace bi
 
-extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new, void* k_cache,
-                            void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
-                            const int32_t* query_start_loc, int32_t batch, int64_t num_tokens,
-                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                            int32_t page_size, int32_t max_pages_per_seq, int64_t max_seq_len,
-                            float scale, void* out, int out_dtype, void* workspace,
-                            size_t workspace_bytes, void* stream) {
-  const int st = attention_check(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+extern "C" int bi_attention(const void* q, int q_dtype, const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache, const int32_t* block_table,
+                            const int32_t* seq_lens, const int32_t* query_start_loc, int32_t batch,
+                            int64_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t page_size, int32_t max_pages_per_seq,
+                            int64_t max_seq_len, float scale, void* out, int out_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = attention_check(q, q_dtype, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
                                  query_start_loc, batch, num_tokens, num_q_heads, num_kv_heads,
                                  head_dim, page_size, max_pages_per_seq, max_seq_len, out, out_dtype);
   if (st != BI_OK || num_tokens == 0 || batch == 0) return st;
@@ -930,7 +984,7 @@ extern "C" int bi_attention(const void* q, const void* k_new, const void* v_new,
   float* ws_ml = static_cast<float*>(workspace);
   float* ws_o = ws_ml + ml_floats(num_tokens * num_q_heads * maxc);
   int4* ws_tok = split ? reinterpret_cast<int4*>(ws_o + num_tokens * num_q_heads * maxc * HD) : nullptr;
-  attention_launch(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start_loc, batch,
+  attention_launch_q(q_dtype, q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start_loc, batch,
                    num_tokens, num_q_heads, num_kv_heads, page_size, max_pages_per_seq, max_seq_len,
                    scale, out, out_dtype, ws_ml, ws_tok, as_stream(stream));
   return launch_status();
@@ -967,14 +1021,14 @@ uintptr_t device_scratch() {
 }  // namespace
 }  // namespace bi
 
-extern "C" int bi_attention_noalloc(const void* q, const void* k_new, const void* v_new,
+extern "C" int bi_attention_noalloc(const void* q, int q_dtype, const void* k_new, const void* v_new,
                                     void* k_cache, void* v_cache, const int32_t* block_table,
                                     const int32_t* seq_lens, const int32_t* query_start_loc,
                                     int32_t batch, int64_t num_tokens, int32_t num_q_heads,
                                     int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                                     int32_t max_pages_per_seq, int64_t max_seq_len, float scale,
                                     void* out, int out_dtype, void* stream) {
-  const int st = attention_check(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+  const int st = attention_check(q, q_dtype, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
                                  query_start_loc, batch, num_tokens, num_q_heads, num_kv_heads,
                                  head_dim, page_size, max_pages_per_seq, max_seq_len, out, out_dtype);
   if (st != BI_OK || num_tokens == 0 || batch == 0) return st;
@@ -994,19 +1048,20 @@ extern "C" int bi_attention_noalloc(const void* q, const void* k_new, const void
     ws_ml = reinterpret_cast<float*>(base);
     ws_tok = reinterpret_cast<int4*>(ws_ml + floats);
   }
-  attention_launch(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start_loc, batch,
+  attention_launch_q(q_dtype, q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start_loc, batch,
                    num_tokens, num_q_heads, num_kv_heads, page_size, max_pages_per_seq, max_seq_len,
                    scale, out, out_dtype, ws_ml, ws_tok, as_stream(stream));
   return launch_status();
 }
 
 extern "C" int bi_attention_batchdep_split(
-    const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    const void* q, int q_dtype, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
     const int32_t* block_table, const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t batch, int64_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t page_size, int32_t max_pages_per_seq, int64_t max_seq_len, int64_t total_chunks,
     float scale, void* out, int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (out_dtype != BI_BF16 && out_dtype != BI_F32) return BI_ERR_DTYPE;
+  if ((out_dtype != BI_BF16 && out_dtype != BI_F32) || (q_dtype != BI_BF16 && q_dtype != BI_F32))
+    return BI_ERR_DTYPE;
   if (batch < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || page_size < 1 ||
       max_pages_per_seq < 1 || max_seq_len < 0 || total_chunks < 0)
     return BI_ERR_SHAPE;
@@ -1041,11 +1096,17 @@ extern "C" int bi_attention_batchdep_split(
       query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size, nullptr);
   float* ws_ml = static_cast<float*>(workspace);
   float* ws_o = ws_ml + ml_floats(num_tokens * num_q_heads * maxg);
-  attn_group_kernel<<<dim3(static_cast<unsigned>(num_tokens * maxg), num_kv_heads), dim3(256), 0, s>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-      static_cast<const uint16_t*>(v_cache), block_table, seq_lens, query_start_loc, batch,
-      max_pages_per_seq, num_q_heads, num_kv_heads, page_size, static_cast<int>(maxg),
-      static_cast<int>(group), sl2, ws_ml, ws_o);
+  const dim3 ggrid(static_cast<unsigned>(num_tokens * maxg), num_kv_heads);
+  if (q_dtype == BI_F32)
+    attn_group_kernel<3><<<ggrid, dim3(256), 0, s>>>(
+        q, static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table,
+        seq_lens, query_start_loc, batch, max_pages_per_seq, num_q_heads, num_kv_heads, page_size,
+        static_cast<int>(maxg), static_cast<int>(group), sl2, ws_ml, ws_o);
+  else
+    attn_group_kernel<1><<<ggrid, dim3(256), 0, s>>>(
+        q, static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table,
+        seq_lens, query_start_loc, batch, max_pages_per_seq, num_q_heads, num_kv_heads, page_size,
+        static_cast<int>(maxg), static_cast<int>(group), sl2, ws_ml, ws_o);
   const int64_t rows = num_tokens * num_q_heads;
   attn_combine_kernel<<<dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s>>>(
       ws_ml, ws_o, seq_lens, query_start_loc, batch, num_q_heads, static_cast<int>(maxg), rows, out,

@@ -36,6 +36,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// fp32 v split exactly into three bf16 terms, v = hi + mid + lo for every normal v (24
+// significand bits = 3 x 8): each term is the truncation to bf16 of what the previous terms
+// leave.  A product of an fp32 operand with a bf16 one is then three exact bf16 products,
+// accumulated hi, mid, lo (the "FP32 upcast" of the cross-vendor mismatch abstract).
+__device__ __forceinline__ void split_bf16x3(float v, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  hi = static_cast<uint16_t>(__float_as_uint(v) >> 16);
+  const float r1 = v - bf16_to_f32(hi);
+  mid = static_cast<uint16_t>(__float_as_uint(r1) >> 16);
+  const float r2 = r1 - bf16_to_f32(mid);
+  lo = static_cast<uint16_t>(__float_as_uint(r2) >> 16);
+}
+
 // SwiGLU of one bf16 (gate, up) pair: silu(g) u in fp32 (silu(g) = g / (1 + 2^(-g log2 e)),
 // hardware exp2, correctly rounded division), one RNE rounding.  The stand-alone kernel and
 // the GEMM epilogue both call this, so fused and unfused outputs share every bit.

@@ -81,13 +81,11 @@ __device__ __forceinline__ void split3(const float* p, int64_t k, int64_t K, boo
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const uint16_t h = bf16_trunc(v[e]);
-    const float r1 = v[e] - bf16_to_f32(h);
-    const uint16_t m = bf16_trunc(r1);
-    const float r2 = r1 - bf16_to_f32(m);
+    uint16_t h, m, l;
+    split_bf16x3(v[e], h, m, l);
     hi[e] = h;
     mid[e] = m;
-    lo[e] = bf16_trunc(r2);
+    lo[e] = l;
   }
 }
 

@@ -37,7 +37,7 @@ __global__ void embedding_kernel(const int32_t* __restrict__ ids, const void* __
 // or heads per thread (one for a few tokens, where parallelism matters more than the
 // repeated cosines; eight for many).
 __global__ void rope_qkv_kernel(const void* __restrict__ qkv, int64_t ld, int qkv_f32,
-                                const int32_t* __restrict__ positions, uint16_t* __restrict__ q,
+                                const int32_t* __restrict__ positions, void* __restrict__ q, int q_f32,
                                 uint16_t* __restrict__ k, uint16_t* __restrict__ v, int64_t T,
                                 int hq, int hkv, int hd, double base, int hpt) {
   const int half = hd / 2;
@@ -70,7 +70,13 @@ __global__ void rope_qkv_kernel(const void* __restrict__ qkv, int64_t ld, int qk
     }
     const float y1 = x1 * c - x2 * s;
     const float y2 = x2 * c + x1 * s;
-    uint16_t* dst = h < hq ? q + (t * hq + h) * hd : k + (t * hkv + (h - hq)) * hd;
+    if (h < hq) {   // q: bf16, or fp32 (the FP32-activation variant)
+      const int64_t o = (t * hq + h) * hd;
+      store_from_f32(q, o + j, y1, q_f32);
+      store_from_f32(q, o + j + half, y2, q_f32);
+      continue;
+    }
+    uint16_t* dst = k + (t * hkv + (h - hq)) * hd;
     dst[j] = f32_to_bf16(y1);
     dst[j + half] = f32_to_bf16(y2);
   }
@@ -126,9 +132,10 @@ extern "C" int bi_embedding(const int32_t* ids, const void* table, int table_dty
 }
 
 extern "C" int bi_rope_qkv(const void* qkv, int64_t ldqkv, int qkv_dtype, const int32_t* positions,
-                           void* q, void* k, void* v, int64_t T, int32_t num_q_heads,
+                           void* q, int q_dtype, void* k, void* v, int64_t T, int32_t num_q_heads,
                            int32_t num_kv_heads, int32_t head_dim, double base, void* stream) {
-  if (qkv_dtype != BI_BF16 && qkv_dtype != BI_F32) return BI_ERR_DTYPE;
+  if ((qkv_dtype != BI_BF16 && qkv_dtype != BI_F32) || (q_dtype != BI_BF16 && q_dtype != BI_F32))
+    return BI_ERR_DTYPE;
   if (T < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 2 || (head_dim & 1))
     return BI_ERR_SHAPE;
   if (ldqkv < static_cast<int64_t>(num_q_heads + 2 * num_kv_heads) * head_dim) return BI_ERR_SHAPE;
@@ -138,7 +145,7 @@ extern "C" int bi_rope_qkv(const void* qkv, int64_t ldqkv, int qkv_dtype, const 
   const int64_t groups = (num_q_heads + 2 * num_kv_heads + hpt - 1) / hpt;
   const int64_t n = T * groups * (head_dim / 2);
   rope_qkv_kernel<<<blocks_for(n, 256), 256, 0, as_stream(stream)>>>(
-      qkv, ldqkv, qkv_dtype == BI_F32, positions, static_cast<uint16_t*>(q),
+      qkv, ldqkv, qkv_dtype == BI_F32, positions, q, q_dtype == BI_F32,
       static_cast<uint16_t*>(k), static_cast<uint16_t*>(v), T, num_q_heads, num_kv_heads, head_dim,
       base, hpt);
   return launch_status();

@@ -17,9 +17,10 @@ Layer (pre-norm, SwiGLU):
   x  = rmsnorm(h);  q, k, v = rope(split(x Wqkv^T));  a = attention(q, k, v | cache)
   h2 = h + a Wo^T;  x2 = rmsnorm(h2);  out = h2 + (silu(x2 Wg^T) * (x2 Wu^T)) Wd^T
 bf16 model: every activation is stored in bf16.  fp32 variant: the residual stream, the
-attention-side norm, projections and attention output are fp32 (fp32 x bf16-weight
-products through bi_gemm's exact three-way split); the MLP (its norm output, gate/up,
-SwiGLU, down) stays bf16; the KV cache stays bf16; logits are fp32 in both.
+attention-side norm, projections, q and the attention output are fp32 (fp32 x bf16 products
+through the exact three-way split in bi_gemm and bi_attention); the MLP (its norm output,
+gate/up, SwiGLU, down) stays bf16; the KV cache stays bf16 (storage, as the weights are);
+logits are fp32 in both.
 """
 from __future__ import annotations
 
@@ -177,7 +178,7 @@ def decoder_layer(w, h, batch: Batch, k_cache, v_cache, dims: Dims, fp32_variant
         x = bi_rmsnorm(h, w["attn_norm"], dims.eps, out_dtype=act)
     qkv = bi_gemm(x, w["wqkv"], out_dtype=act)
     q, k, v = bi_rope_qkv(qkv, batch.positions, dims.n_q_heads, dims.n_kv_heads, dims.head_dim,
-                          dims.rope_base)
+                          dims.rope_base, q_dtype=act)
     a = bi_attention(q, k, v, k_cache, v_cache, batch.block_table, batch.seq_lens, batch.qsl,
                      batch.max_seq_len, 1.0 / float(np.sqrt(dims.head_dim)), out_dtype=act,
                      workspace=batch.workspace)

@@ -25,7 +25,7 @@ rounded once to the type the model STORES it in.  Storage points:
   variant         stay BF16) the residual stream h, the attention-side norm output x, the
                   fused projection qkv, the attention output a, the projection o, h2 and
                   the layer output are fp32 (weights stay bf16 and enter exactly); q is
-                  fp32 or bf16 (Spec.q_dtype); k and v are bf16, the type of the KV cache
+                  fp32 (Spec.q_dtype; bf16 on request); k and v are bf16, the type of the KV cache
                   (storage, as the weights are); the MLP -- its norm output x2, the gate/up
                   values, the SwiGLU output and the down projection -- is bf16; the final
                   norm is fp32.
@@ -50,7 +50,7 @@ class Spec:
     eps: float = 1e-5
     base: float = 10000.0
     variant: bool = False      # the FP32/MLP-BF16 variant
-    q_dtype: str = "bf16"      # storage of q in the variant ("bf16" or "f32"); bf16 model: bf16
+    q_dtype: str = "f32"       # storage of q in the variant ("f32" or "bf16"); bf16 model: bf16
 
     @property
     def act(self) -> str:
@@ -227,7 +227,7 @@ def model_ref_forward(pieces, weights, spec: Spec, logit_rows=None, on_layer=Non
 
 
 def model_ref_logits(prompt, forced, weights, eps=1e-5, base=10000.0, n_q_heads=32,
-                     n_kv_heads=8, head_dim=128, fp32_variant=False, q_dtype="bf16",
+                     n_kv_heads=8, head_dim=128, fp32_variant=False, q_dtype="f32",
                      one_pass=False):
     """Teacher-forced logits (fp64) after the prompt and after each forced token: [1 +
     len(forced), V].  By default the prompt is one piece and every forced token its own

@@ -77,7 +77,7 @@ def test_validation_rejects_before_launch(lib):
     assert lib.bi_logsoftmax_argmax(None, 2, 10, 12, None, P, None) == -1
     assert lib.bi_logsoftmax_argmax(P, 2, 1024, 1024, P, P, None) == -2   # logprobs over logits
     # attention: unsupported head_dim, group, page size; missing workspace
-    args = [P] * 8
+    args = [P, 1] + [P] * 7          # q (bf16), k_new, v_new, caches, table, lengths, offsets
     def att(T=4, hq=32, hkv=8, d=128, ps=16, maxp=4, msl=64, ws=None, wsz=0, B=2):
         return lib.bi_attention(*args, B, T, hq, hkv, d, ps, maxp, msl, 0.088, P, 1, ws, wsz, None)
     assert att(d=64) == -6
@@ -92,6 +92,9 @@ def test_validation_rejects_before_launch(lib):
     # anything runs: 1024 tokens of 32768-token contexts need 1024*32*32*(2+128)*4 bytes
     assert lib.bi_attention_noalloc(*args, 1, 1024, 32, 8, 128, 16, 2048, 32768, 0.088, P, 1, None) == -5
     assert lib.bi_attention_noalloc(*args, 1, 4, 32, 8, 64, 16, 4, 64, 0.088, P, 1, None) == -6
+    bad_q = [P, 7] + [P] * 7          # an unknown q dtype
+    assert lib.bi_attention(*bad_q, 2, 4, 32, 8, 128, 16, 4, 64, 0.088, P, 1, P, 1 << 20, None) == -3
+    assert lib.bi_rope_qkv(P, 6144, 1, P, P, 5, P, P, 4, 32, 8, 128, 10000.0, None) == -3
     assert lib.bi_gemm_splitk_workspace_bytes(2048, 2048, 2048) == 2 * 2048 * 2048 * 4
 
 

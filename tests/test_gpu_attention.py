@@ -164,6 +164,56 @@ def test_decode_equals_prefill_at_32k_boundaries(lib):
     _check_vs_oracle(dec, out_d, qsl_d, which={b: [0] for b in range(len(L))})
 
 
+def test_fp32_q(lib):
+    # q in fp32 (the FP32-activation variant): each value split exactly into bf16 hi + mid + lo
+    # for the scores.  (1) With bf16-representable q values the split adds exact zeros, so the
+    # bits equal the bf16-q call's; (2) with full fp32 q, decode == prefill bitwise on both
+    # paths and the rows are within 1e-3 (fp32 out) and 1 ulp (bf16 out) of the oracle at
+    # output scale, which holds q at full precision
+    from oracle.attention import attention_values_f64
+    from oracle import fp as F
+    from tests._gpu import bf16, f32, i32
+    L = [700, 1500, 2100]
+    dec = attention_case(L, [1, 1, 1], cfg=51)
+    kc, vc, bt = make_cache(dec, 16, [l - 1 for l in L])
+    q_b = np.concatenate(dec["q"])
+    kn = np.concatenate([dec["k"][b][L[b] - 1:L[b]] for b in range(3)])
+    vn = np.concatenate([dec["v"][b][L[b] - 1:L[b]] for b in range(3)])
+    args = (bf16(kn), bf16(vn), kc, vc, i32(bt), i32(L), i32(np.arange(4)))
+    ref16 = lib.bi_attention(bf16(q_b), *args, max_seq_len=max(L), scale=1 / np.sqrt(128.0))
+    got = lib.bi_attention(bf16(q_b).float(), *args, max_seq_len=max(L), scale=1 / np.sqrt(128.0))
+    assert same_bits(got, ref16)
+    # full fp32 q, the same per position in prefill and decode
+    rng = np.random.default_rng(51)
+    qf = {b: rng.standard_normal((L[b], 32, 128)).astype(np.float32) for b in range(3)}
+    pre = attention_case(L, L, cfg=51)
+    kcp, vcp, btp = make_cache(pre, 16, [0, 0, 0], cfg=87)
+    qp = np.concatenate([qf[b] for b in range(3)])
+    knp = np.concatenate(pre["k"])
+    vnp = np.concatenate(pre["v"])
+    qsl = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    outp = lib.bi_attention(f32(qp), bf16(knp), bf16(vnp), kcp, vcp, i32(btp), i32(L), i32(qsl),
+                            max_seq_len=max(L), scale=1 / np.sqrt(128.0), out_dtype=torch.float32)
+    qd = np.stack([qf[b][-1] for b in range(3)])
+    for out_dtype in (torch.float32, torch.bfloat16):
+        outd = lib.bi_attention(f32(qd), *args, max_seq_len=max(L), scale=1 / np.sqrt(128.0),
+                                out_dtype=out_dtype)
+        for b in range(3):
+            ref = attention_values_f64(qd[b:b + 1].astype(np.float64), F.bf16_to_f64(dec["k"][b]),
+                                       F.bf16_to_f64(dec["v"][b]), [L[b] - 1])[0]
+            if out_dtype == torch.float32:
+                assert same_bits(outd[b], outp[qsl[b] + L[b] - 1]), b
+                r = f32_within_rel(host(outd[b]), ref)
+            else:
+                r = bf16_within_1ulp(bits(outd[b]), ref)
+            assert r["ok"], (b, out_dtype, r)
+    # a prefill row checked directly too (the walk path)
+    mid = 1000
+    ref = attention_values_f64(qf[1][mid:mid + 1].astype(np.float64), F.bf16_to_f64(pre["k"][1][:mid + 1]),
+                               F.bf16_to_f64(pre["v"][1][:mid + 1]), [mid])[0]
+    assert f32_within_rel(host(outp[qsl[1] + mid]), ref)["ok"]
+
+
 def test_batchdep_split_variant_correct_but_not_invariant(lib):
     B = 32
     L = ragged_lengths(B, 1400, 8000, 46, 0)

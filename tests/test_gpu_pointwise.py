@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from oracle import fp
-from oracle.check import bf16_within_1ulp, swiglu_interval_within
+from oracle.check import bf16_within_1ulp, f32_within_rel, swiglu_interval_within
 from oracle.gemm import gemm_f64
 from oracle.layer import Spec, op_rope_qkv, store, swiglu_f64
 from oracle.rmsnorm import rmsnorm_tree
@@ -45,6 +45,12 @@ def test_rope_qkv_vs_oracle(lib, T, hq, hkv, hd, qkv_f32):
     q, k, v = lib.bi_rope_qkv(qkv, i32(pos), hq, hkv, hd, 10000.0)
     spec = Spec(n_q_heads=hq, n_kv_heads=hkv, head_dim=hd)
     q64, k64, v64 = op_rope_qkv(x64, pos, spec)
+    # q kept in fp32 (the FP32-activation variant): within 1e-3 at output scale, and its
+    # bf16 rounding is the bf16 call's q
+    q32, k2, _ = lib.bi_rope_qkv(qkv, i32(pos), hq, hkv, hd, 10000.0, q_dtype=torch.float32)
+    r32 = f32_within_rel(host(q32), q64)
+    assert r32["ok"] and r32["max_rel"] < 1e-5, r32
+    assert same_bits(q32.to(torch.bfloat16), q) and same_bits(k2, k)
     rq = bf16_within_1ulp(bits(q), q64)
     rk = bf16_within_1ulp(bits(k), k64)
     say("rope q", rq, "k", rk)

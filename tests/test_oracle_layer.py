@@ -208,8 +208,8 @@ def _is_f32(x):
 
 def test_storage_points_of_both_models():
     # which intermediates are stored in which type: bf16 model -- all bf16; variant --
-    # x, qkv, attention output, o, h2 and the layer output fp32 (and not all bf16), q/k/v
-    # and the MLP (x2, gate/up, SwiGLU, down) bf16
+    # x, qkv, q, attention output, o, h2 and the layer output fp32 (and not all bf16), k/v
+    # (the cache) and the MLP (x2, gate/up, SwiGLU, down) bf16
     w, b = _small(8)
     h = fp.bf16_to_f64(b(6, 64, sd=1.0))
     z = np.zeros((0, 2, 16))
@@ -221,7 +221,8 @@ def test_storage_points_of_both_models():
     for name in ("x", "qkv", "attn", "o", "h2"):
         assert _is_f32(it[name]) and not _is_bf16(it[name]), name
     assert _is_f32(out) and not _is_bf16(out)
-    for name in ("q", "k", "v", "x2", "gu", "mlp", "dn"):
+    assert _is_f32(it["q"]) and not _is_bf16(it["q"])
+    for name in ("k", "v", "x2", "gu", "mlp", "dn"):
         assert _is_bf16(it[name]), name
-    _, it = sequence_layer_ref(h, w, 0, z, z, Spec(**DIMS, variant=True, q_dtype="f32"))
-    assert _is_f32(it["q"]) and not _is_bf16(it["q"]) and _is_bf16(it["k"])
+    _, it = sequence_layer_ref(h, w, 0, z, z, Spec(**DIMS, variant=True, q_dtype="bf16"))
+    assert _is_bf16(it["q"]) and _is_bf16(it["k"])
