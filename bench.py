@@ -297,32 +297,32 @@ def invariance_cost(torch, bi, ms=(1, 64, 1024, 2048), reps=10):
 
 
 def gemm_sweep(torch, bi):
-    """Mistral-shaped GEMMs (N, K) x M, TFLOP/s of bi_gemm and of the split-K variant."""
+    """Mistral-shaped GEMMs (N, K) x M: TFLOP/s of bi_gemm, of the split-K variant and, as
+    context, of torch.mm (the vendor library, hipBLASLt) on the same operands and box."""
     dev = "cuda:0"
     out = []
-    for (N, K) in [(6144, 4096), (4096, 4096), (28672, 4096), (4096, 14336), (32000, 4096)]:
+    for (N, K) in SET2:
         W = torch.randn((N, K), device=dev).to(torch.bfloat16)
+        Wt = W.t()
         for M in (1, 64, 1024, 2048, 4096, 8192, 16384):
             A = torch.randn((M, K), device=dev).to(torch.bfloat16)
             C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            need = bi.load().bi_gemm_splitk_workspace_bytes(M, N, K)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
             res = {}
             for name, fn in (("bi_gemm", lambda: bi.bi_gemm(A, W, out=C)),
-                             ("splitk", lambda: bi.bi_gemm_splitk(A, W, out=C))):
+                             ("splitk", lambda: bi.bi_gemm_splitk(A, W, out=C, workspace=ws)),
+                             ("torch_mm", lambda: torch.mm(A, Wt, out=C))):
                 for _ in range(3):
                     fn()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                reps = 20
-                e0.record()
-                for _ in range(reps):
-                    fn()
-                e1.record(); torch.cuda.synchronize()
-                t = e0.elapsed_time(e1) / reps * 1e-3
+                t = _time_calls(torch, fn, 20)
                 res[name] = dict(ms=t * 1e3, tflops=2.0 * M * N * K / t / 1e12)
             out.append(dict(N=N, K=K, M=M, **{k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in res.items()},
-                            frac_of_peak=round(res["bi_gemm"]["tflops"] * 1e12 / BF16_PEAK, 4)))
+                            frac_of_peak=round(res["bi_gemm"]["tflops"] * 1e12 / BF16_PEAK, 4),
+                            torch_mm_frac=round(res["torch_mm"]["tflops"] * 1e12 / BF16_PEAK, 4)))
             print(json.dumps(out[-1]), flush=True)
-            del A, C
-        del W
+            del A, C, ws
+        del W, Wt
     return out
 
 
