@@ -269,7 +269,9 @@ def gemm_set2(torch, bi, ms=(1024, 2048, 4096, 8192, 16384), reps=10):
 def invariance_cost(torch, bi, ms=(1, 64, 1024, 2048), reps=10):
     """bi_gemm against the non-invariant split-K variant (slices of K chosen from the grid size,
     on the same few-row and LDS-staged kernels, then a fixed-order sum of the slices) on the
-    Mistral shapes at decode- and prefill-sized M: the cost of keeping one reduction order."""
+    Mistral shapes at decode- and prefill-sized M: the cost of keeping one reduction order.
+    The vendor library (torch.mm, hipBLASLt, not batch-invariant) on the same operands is
+    timed beside it as context."""
     dev = "cuda:0"
     g = torch.Generator(device=dev).manual_seed(22)
     out = []
@@ -281,15 +283,19 @@ def invariance_cost(torch, bi, ms=(1, 64, 1024, 2048), reps=10):
             need = bi.load().bi_gemm_splitk_workspace_bytes(M, N, K)
             ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
             t = {}
+            Wt = W.t()
             for name, fn in (("bi_gemm", lambda: bi.bi_gemm(A, W, out=C)),
-                             ("splitk", lambda: bi.bi_gemm_splitk(A, W, out=C, workspace=ws))):
+                             ("splitk", lambda: bi.bi_gemm_splitk(A, W, out=C, workspace=ws)),
+                             ("torch_mm", lambda: torch.mm(A, Wt, out=C))):
                 for _ in range(2):
                     fn()
                 t[name] = _time_calls(torch, fn, reps)
             out.append({"M": M, "N": N, "K": K, "bi_gemm_us": round(t["bi_gemm"] * 1e6, 2),
                         "splitk_us": round(t["splitk"] * 1e6, 2),
-                        "splitk_slices": int(need // (4 * M * N)) if need else 1,
-                        "invariant_slowdown": round(t["bi_gemm"] / t["splitk"], 3)})
+                        "splitk_workspace_slices": int(need // (4 * M * N)) if need else 0,
+                        "invariant_slowdown": round(t["bi_gemm"] / t["splitk"], 3),
+                        "vendor_torch_mm_us": round(t["torch_mm"] * 1e6, 2),
+                        "vs_vendor": round(t["bi_gemm"] / t["torch_mm"], 3)})
             log("invariance cost", out[-1])
             del A, C, ws
         del W

@@ -163,10 +163,11 @@ int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_t* tile_m, 
 /* Comparison variant, NOT batch-invariant ([DN], split-K matmul): same arguments as
  * bi_gemm with bf16 A and B_NK, on the same kernels, but K is split into slices whose number
  * grows as M shrinks (so that small batches fill the GPU): up to 4 rows (K in 512 .. 4096),
- * over the 4 waves of a workgroup, whose partials are added in LDS; otherwise into as many
- * slices (up to 16) as bring the launch to about two waves or tiles per CU, each slice's
- * fp32 partial in `workspace`, then added in ascending order by a second kernel.  The
- * association of a row's sums therefore depends on M.
+ * over the 4 waves of a workgroup, whose partials are added in LDS; otherwise, when the
+ * output grid has fewer waves or tiles than there are CUs, into as many slices (up to 16) as
+ * fill the CUs, each slice's fp32 partial in `workspace`, then added in ascending order by a
+ * second kernel (no split when the grid already fills the CUs).  The association of a row's
+ * sums therefore depends on M.
  * workspace >= bi_gemm_splitk_workspace_bytes(M, N, K) bytes (0 when none is used). */
 size_t bi_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,

@@ -1219,11 +1219,12 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ ws, void* __restr
   else static_cast<uint16_t*>(C)[row * ldc + col] = f32_to_bf16(s);
 }
 
-// Comparison variant: slices of K chosen from the size of the output grid -- as many as
-// bring the launch to about two waves (few-row kernel) or two tiles (LDS-staged tiles) per
-// CU, at most 16, each slice a whole number of 64-wide stages (at least 1024 columns for the
-// few-row kernel, whose prefetch needs 32 steps).  So the number of slices, and with it
-// every row's association of partial sums, changes with M.
+// Comparison variant: slices of K chosen from the size of the output grid -- when the grid
+// has fewer waves (few-row kernel) or tiles (LDS-staged tiles) than there are CUs, as many
+// slices as fill the CUs (at most 16; none when the grid already fills them), each slice a
+// whole number of 64-wide stages (at least 1024 columns for the few-row kernel, whose
+// prefetch needs 32 steps).  So the number of slices, and with it every row's association of
+// partial sums, changes with M.
 KSplit splitk_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t cus = cu_count();
   KSplit p;
@@ -1241,7 +1242,7 @@ KSplit splitk_plan(int64_t M, int64_t N, int64_t K) {
     }
     min_slice = 256;
   }
-  int64_t ks = (2 * cus + units - 1) / std::max<int64_t>(units, 1);
+  int64_t ks = cus / std::max<int64_t>(units, 1);
   ks = std::min<int64_t>(ks, 16);
   ks = std::min<int64_t>(ks, std::max<int64_t>(1, K / min_slice));
   for (; ks > 1; --ks) {   // slices of whole stages, the last one at least min_slice long

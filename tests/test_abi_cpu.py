@@ -95,7 +95,11 @@ def test_validation_rejects_before_launch(lib):
     bad_q = [P, 7] + [P] * 7          # an unknown q dtype
     assert lib.bi_attention(*bad_q, 2, 4, 32, 8, 128, 16, 4, 64, 0.088, P, 1, P, 1 << 20, None) == -3
     assert lib.bi_rope_qkv(P, 6144, 1, P, P, 5, P, P, 4, 32, 8, 128, 10000.0, None) == -3
-    assert lib.bi_gemm_splitk_workspace_bytes(2048, 2048, 2048) == 2 * 2048 * 2048 * 4
+    # the comparison variant splits K only when the grid leaves CUs idle (256 CUs assumed
+    # without a GPU): none for 2048^3 (256 tiles), four slices for 256 x 1024 (64 tiles)
+    assert lib.bi_gemm_splitk_workspace_bytes(2048, 2048, 2048) == 0
+    assert lib.bi_gemm_splitk_workspace_bytes(256, 1024, 8192) == 4 * 256 * 1024 * 4
+    assert lib.bi_gemm_splitk_workspace_bytes(2, 1024, 2048) == 0      # split over 4 waves
 
 
 def _fn_constants(src, name):
