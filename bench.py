@@ -570,9 +570,11 @@ def main():
                      "algorithmic_bytes": att["bytes"]},
         "kernel_time_ms": round(kernel_sum * 1e3, 4),
     }
-    # non-invariant comparison variants on the same inputs (the cost of invariance)
+    # non-invariant comparison variants on the same inputs (the cost of invariance): each pair
+    # timed the same way, back-to-back calls between two HIP events
     L = inp["L"]
     total_chunks = int(sum((int(l) - 1) // 256 + 1 for l in L))
+    ops_d = dict(ops)
     variants = [
         ("gemm", "bi_gemm_splitk", lambda: bi.bi_gemm_splitk(inp["A"], inp["B_nk"], out=inp["C"])),
         ("attention_decode", "bi_attention_batchdep_split", lambda: bi.bi_attention_batchdep_split(
@@ -582,18 +584,14 @@ def main():
     ]
     comp = {}
     for name, vname, fn in variants:
-        for _ in range(2):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(K):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / K * 1e-3
-        comp[name] = dict(variant=vname, ms=round(t * 1e3, 5),
-                          invariant_ms=round(per[name] * 1e3, 5),
-                          invariant_slowdown=round(per[name] / t, 4))
+        t = {}
+        for which, f in (("invariant", ops_d[name]), ("variant", fn)):
+            for _ in range(2):
+                f()
+            t[which] = _time_calls(torch, f, K)
+        comp[name] = dict(variant=vname, ms=round(t["variant"] * 1e3, 5),
+                          invariant_ms=round(t["invariant"] * 1e3, 5),
+                          invariant_slowdown=round(t["invariant"] / t["variant"], 4))
     res["nonbi_comparison"] = comp
     if not args.no_gemm_set:
         log("GEMM set 2' (Mistral shapes, M >= 1024)")
