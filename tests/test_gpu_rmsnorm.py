@@ -117,3 +117,18 @@ def test_add_rmsnorm_equals_two_calls(lib, dtype, ydtype):
         a2 = a.clone()
         s2, y2 = lib.bi_add_rmsnorm(a2, b, g, 1e-5, sum_out=a2, out_dtype=ydtype)
         assert same_bits(s2, s_ref) and same_bits(y2, y_ref), (m, d)
+
+
+@pytest.mark.parametrize("m,d", [(9001, 4096), (9001, 8192), (20011, 512), (17003, 104)])
+def test_many_rows_bit_exact(lib, m, d):
+    # thousands of rows (many more workgroups than can be resident, row counts that are not
+    # a multiple of anything): every row equals the oracle's tree replay, and the same row
+    # computed alone
+    say("rmsnorm many rows", m, d)
+    x = normal_bf16((m, d), 0.0, 1.0, 25, d)
+    g = normal_bf16((d,), 1.0, 0.02, 25, d + 1)
+    X, G = bf16(x), bf16(g)
+    y = lib.bi_rmsnorm(X, G, 1e-5)
+    assert np.array_equal(bits(y), rmsnorm_tree(x, g, 1e-5))
+    for r in (0, 1, m // 2, m - 1):
+        assert same_bits(lib.bi_rmsnorm(X[r:r + 1], G, 1e-5)[0], y[r])
