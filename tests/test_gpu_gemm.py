@@ -186,6 +186,42 @@ def test_b_kn_ragged_equals_b_nk(lib, m, n, k):
     assert same_bits(c32, lib.bi_gemm(af, Bnk, out_dtype=torch.float32))
 
 
+def _padded(x):
+    """bf16 copy of x whose rows have a stride of a multiple of 8 elements with zero padding
+    (every row readable in whole 16-byte pieces, the last one included)."""
+    r, c_ = x.shape
+    p = torch.zeros((r, (c_ + 7) // 8 * 8), dtype=torch.bfloat16, device="cuda")
+    p[:, :c_] = bf16(x)
+    return p[:, :c_]
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (1, 17, 1), (300, 3, 1), (3, 5, 7), (17, 1, 33),
+                                   (2, 3, 31), (64, 2, 8), (1, 1, 4100)])
+def test_degenerate_shapes(lib, m, n, k):
+    # one output row or column, K under one 8-element piece or one 32-wide step.  At K = 1
+    # every output is one product of two bf16 values (exact in fp32) rounded once, so bf16
+    # and fp32 outputs equal the fp64 oracle rounded once, bit for bit; otherwise the 1-ulp
+    # bar.  The [K, N] layout gives the [N, K] bits.
+    from invariant_amd import BI_B_KN
+    say("gemm degenerate", m, n, k)
+    a, b = gemm_inputs(m, n, k, cfg=38)
+    A, Bnk, Bkn = _padded(a), _padded(_nk(b)), _padded(b)
+    ref = gemm_f64(a, b)
+    c = lib.bi_gemm(A, Bnk)
+    cf = lib.bi_gemm(A, Bnk, out_dtype=torch.float32)
+    if k == 1:
+        assert np.array_equal(bits(c), fp.f64_to_bf16(ref))
+        assert np.array_equal(host(cf), ref.astype(np.float32))
+    else:
+        r = bf16_within_1ulp(bits(c), ref)
+        assert r["ok"], r
+        assert f32_within_rel(host(cf), ref)["ok"]
+    assert same_bits(lib.bi_gemm(A, Bkn, b_layout=BI_B_KN), c)
+    # each row alone: the same bits
+    for i in sorted({0, m - 1}):
+        assert same_bits(lib.bi_gemm(A[i:i + 1], Bnk), c[i:i + 1])
+
+
 def test_splitk_variant_is_not_invariant(lib):
     # the page's linspace example: row 0 of a [1, D] product vs of a [2048, D] product
     Bn, D = 2048, 4096

@@ -29,7 +29,7 @@ def test_cfg1_batch_sweep_bit_exact(lib):
 
 @pytest.mark.parametrize("m,d,eps", [(1, 4096, 1e-5), (7, 4096, 1e-5), (300, 4096, 1e-5),
                                      (5, 14336, 1e-5), (3, 1000, 1e-6), (4, 12, 1e-6),
-                                     (2, 9000, 1e-5), (9, 100, 0.5)])
+                                     (2, 9000, 1e-5), (9, 100, 0.5), (3, 1, 1e-6), (2, 8, 1e-6)])
 def test_shapes_bit_exact(lib, m, d, eps):
     say("rmsnorm", m, d)
     x = normal_bf16((m, d), 0.0, 1.0, 21, d)
