@@ -567,6 +567,10 @@ def main():
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(att["bytes"] / per["attention_decode"] / HBM_PEAK, 4),
                      "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),
+                     "traffic_source": "not measured in this run: rocprofv3 FETCH_SIZE + WRITE_SIZE "
+                                       "per call, scaled by a copy kernel of known size, from "
+                                       "profiles/attention_decode_traffic.json; null once "
+                                       "attention.hip differs from the profiled source",
                      "algorithmic_bytes": att["bytes"]},
         "kernel_time_ms": round(kernel_sum * 1e3, 4),
     }
