@@ -192,6 +192,8 @@ int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  *            scores see q at full fp32 precision; keys stay the cache's bf16)
  *   k_new    [num_tokens, Hkv, D] bf16 (keys already rotated), contiguous
  *   v_new    [num_tokens, Hkv, D] bf16, contiguous
+ *            k_new = v_new = NULL: the call's new keys and values are in their pages
+ *            already (written by bi_rope_kv_write); step 1 is skipped
  *   k_cache  [num_pages, Hkv, D/8, page_size, 8] bf16: per page and kv head, D is cut
  *            into 8-element groups; group j holds d = 8j..8j+7 of every slot.  Inside each
  *            aligned block of 16 slots the slot order is permuted by swapping bits 2 and 3
@@ -205,7 +207,8 @@ int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  *   seq_lens [batch] int32, query_start_loc [batch + 1] int32 (device)
  *   out      [num_tokens, Hq, D], dtype out_dtype (BI_BF16 | BI_F32)
  *   scale    softmax scale (1/sqrt(D) for the standard reading)
- * Step 1 writes k_new/v_new into their pages.  Step 2: token at position p of q head
+ * Step 1 writes k_new/v_new into their pages (unless both are NULL).  Step 2: token at
+ * position p of q head
  * h (kv head h / (Hq/Hkv)) computes, for each chunk c <= p/256, the partial
  * (m_c, l_c, o_c) over keys [256c, min(256c + 256, p + 1)) with fp32 scores, P kept
  * as an exact bf16 hi + lo pair, fp32 accumulation.  Step 3 merges in two fixed levels,
@@ -223,9 +226,9 @@ int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * 256-key chunk (bi_attention fills a quarter of it, one per 4-chunk group; the
  * comparison variant below may use all of it) and a 16-byte record per token; 0 for
  * longer calls (no workspace is used).
- * Errors: BI_ERR_NULL, BI_ERR_SHAPE (also when num_tokens * ceil(max_seq_len / 256) *
- * Hkv reaches 2^31 on the split path), BI_ERR_UNSUPPORTED, BI_ERR_WORKSPACE, BI_ERR_ALIGN
- * (16-byte alignment of every tensor).
+ * Errors: BI_ERR_NULL (also when exactly one of k_new, v_new is NULL), BI_ERR_SHAPE (also
+ * when num_tokens * ceil(max_seq_len / 256) * Hkv reaches 2^31 on the split path),
+ * BI_ERR_UNSUPPORTED, BI_ERR_WORKSPACE, BI_ERR_ALIGN (16-byte alignment of every tensor).
  */
 size_t bi_attention_workspace_bytes(int64_t num_tokens, int32_t num_q_heads, int32_t head_dim,
                                     int64_t max_seq_len);
@@ -315,6 +318,26 @@ int bi_embedding(const int32_t* ids, const void* table, int table_dtype, void* o
 int bi_rope_qkv(const void* qkv, int64_t ldqkv, int qkv_dtype, const int32_t* positions,
                 void* q, int q_dtype, void* k, void* v, int64_t T, int32_t num_q_heads,
                 int32_t num_kv_heads, int32_t head_dim, double base, void* stream);
+
+/* bi_rope_kv_write: bi_rope_qkv fused with step 1 of bi_attention (the fused neighbours
+ *   of "Defeating nondeterminism in LLM inference", section on making kernels
+ *   batch-invariant: pointwise work riding on the cache write).  q [num_tokens, Hq, D]
+ *   (dtype q_dtype) receives the rotated queries; the rotated keys and the values of qkv
+ *   go straight into k_cache / v_cache at each new token's page slot, in the layouts of
+ *   bi_attention, with no k or v tensor in between.  A token's rotation position is its
+ *   cache position p = seq_lens[b] - q_b + i (the batch description of bi_attention).
+ *   q, k_cache and v_cache then hold exactly the bits of bi_rope_qkv at those positions
+ *   followed by bi_attention's step 1; call bi_attention with k_new = v_new = NULL next.
+ *   qkv [num_tokens, (Hq + 2 Hkv) * D] (row stride ldqkv, qkv_dtype BI_BF16 | BI_F32).
+ *   Supported: D = 128, page_size a multiple of 16 dividing 256.
+ *   Errors: BI_ERR_DTYPE, BI_ERR_SHAPE, BI_ERR_UNSUPPORTED, BI_ERR_NULL, BI_ERR_ALIGN
+ *   (k_cache, v_cache not 16-byte aligned). */
+int bi_rope_kv_write(const void* qkv, int64_t ldqkv, int qkv_dtype, void* q, int q_dtype,
+                     void* k_cache, void* v_cache, const int32_t* block_table,
+                     const int32_t* seq_lens, const int32_t* query_start_loc, int32_t batch,
+                     int64_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t page_size, int32_t max_pages_per_seq, double base,
+                     void* stream);
 
 /* bi_swiglu: out[t, j] = silu(g) * u with g = gu[t, j], u = gu[t, F + j];
  *   silu(g) = g / (1 + 2^(-g log2 e)) in fp32 with the hardware base-2 exponential

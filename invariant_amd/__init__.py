@@ -42,6 +42,8 @@ _SIGS = {
     "bi_embedding": (_c.c_int, [_P, _P, _c.c_int, _P, _I64, _I64, _I64, _c.c_int, _P]),
     "bi_rope_qkv": (_c.c_int, [_P, _I64, _c.c_int, _P, _P, _c.c_int, _P, _P, _I64, _I32, _I32, _I32, _F64,
                                _P]),
+    "bi_rope_kv_write": (_c.c_int, [_P, _I64, _c.c_int, _P, _c.c_int, _P, _P, _P, _P, _P, _I32, _I64, _I32,
+                                    _I32, _I32, _I32, _I32, _F64, _P]),
     "bi_swiglu": (_c.c_int, [_P, _I64, _P, _I64, _I64, _P]),
     "bi_gemm_swiglu": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
     "bi_add_rmsnorm": (_c.c_int, [_P, _P, _P, _c.c_int, _P, _P, _c.c_int, _I64, _I64, _c.c_float, _P]),
@@ -172,11 +174,12 @@ def bi_attention_workspace_bytes(num_tokens, num_q_heads, head_dim, max_seq_len)
 
 def bi_attention(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start_loc,
                  max_seq_len: int, scale: float, out=None, out_dtype=torch.bfloat16, workspace=None):
-    """q [T, Hq, D], k_new/v_new [T, Hkv, D] bf16; k_cache [P, Hkv, D/8, page, 8];
+    """q [T, Hq, D], k_new/v_new [T, Hkv, D] bf16 (both None: the new keys and values are in
+    the cache already, written by bi_rope_kv_write); k_cache [P, Hkv, D/8, page, 8];
     v_cache [P, Hkv, D, page]; block_table [B, max_pages] int32; seq_lens [B] int32;
     query_start_loc [B + 1] int32 (all on the device)."""
     T, Hq, D = q.shape
-    Hkv = k_new.shape[1]
+    Hkv = k_cache.shape[1]
     page = v_cache.shape[3]
     B, max_pages = block_table.shape
     if out is None:
@@ -197,7 +200,7 @@ def bi_attention_noalloc(q, k_new, v_new, k_cache, v_cache, block_table, seq_len
     """bi_attention with the library's own per-device scratch instead of a workspace (no
     device allocation inside the call; pass `out` to allocate nothing at all)."""
     T, Hq, D = q.shape
-    Hkv = k_new.shape[1]
+    Hkv = k_cache.shape[1]
     page = v_cache.shape[3]
     B, max_pages = block_table.shape
     if out is None:
@@ -214,7 +217,7 @@ def bi_attention_batchdep_split(q, k_new, v_new, k_cache, v_cache, block_table, 
                                 out=None, out_dtype=torch.bfloat16, workspace=None):
     """Comparison variant (not batch-invariant), same layouts as bi_attention."""
     T, Hq, D = q.shape
-    Hkv = k_new.shape[1]
+    Hkv = k_cache.shape[1]
     page = v_cache.shape[3]
     B, max_pages = block_table.shape
     if out is None:
@@ -267,6 +270,23 @@ def bi_rope_qkv(qkv, positions, num_q_heads, num_kv_heads, head_dim, base=10000.
                                               _ptr(q), _code(q.dtype), _ptr(k), _ptr(v), T, num_q_heads,
                                               num_kv_heads, head_dim, float(base), _stream(qkv)))
     return q, k, v
+
+
+def bi_rope_kv_write(qkv, k_cache, v_cache, block_table, seq_lens, query_start_loc, num_q_heads,
+                     base=10000.0, q=None, q_dtype=torch.bfloat16):
+    """bi_rope_qkv fused with bi_attention's cache write: returns q [T, Hq, D]; the rotated
+    keys and the values go into k_cache / v_cache at each new token's slot (cache
+    positions from seq_lens and query_start_loc).  Follow with bi_attention(q, None, None,
+    ...)."""
+    T = qkv.shape[0]
+    Hkv, D, page = k_cache.shape[1], v_cache.shape[2], v_cache.shape[3]
+    B, max_pages = block_table.shape
+    q = q if q is not None else torch.empty((T, num_q_heads, D), dtype=q_dtype, device=qkv.device)
+    _check("bi_rope_kv_write", load().bi_rope_kv_write(
+        _ptr(qkv), _ld(qkv), _code(qkv.dtype), _ptr(q), _code(q.dtype), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_table), _ptr(seq_lens), _ptr(query_start_loc), B, T, num_q_heads, Hkv, D, page,
+        max_pages, float(base), _stream(qkv)))
+    return q
 
 
 def bi_swiglu(gu, out=None):

@@ -372,6 +372,8 @@ __device__ __forceinline__ void load_q(const void* q, int64_t token, int head, i
 }
 
 // ---------------------------------------------------------------- step 1: cache write
+// (k_new NULL: the call's keys and values were written by rope_kv_write_kernel; only the
+// per-token records are produced)
 __global__ __launch_bounds__(256) void kv_write_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
@@ -381,6 +383,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
   const int b = find_seq_wave(qsl, batch, t);
   const int pos = seq_lens[b] - (qsl[b + 1] - qsl[b]) + (t - qsl[b]);
   if (tok && threadIdx.x == 0) tok[t] = make_int4(b, pos, seq_lens[b], 0);
+  if (!k_new) return;   // the keys and values are in the cache already: records only
   const int phys = bt[static_cast<int64_t>(b) * max_pages + pos / ps];
   const int slot = pos % ps;
   const int nvec = hkv * HD / 8;
@@ -398,6 +401,118 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) vc[pg + static_cast<int64_t>(d0 + e) * ps + slot] = x[e];
     }
+  }
+}
+
+// ---------------------------------------------------------------- step 1 fused with RoPE
+// One workgroup per token: RoPE of its q and k heads, q stored to [T, Hq, D], the rotated k
+// and the v of the fused projection written straight into the token's page slot (no
+// [T, Hkv, D] k or v tensor is written and read back).  The rotation position is the
+// token's cache position (seq_len - new tokens of its sequence + its index among them);
+// cosines and sines come from rope_cos_sin, once per pair index, and every element is
+// rope_rotate's, so q and the cache hold the bits of bi_rope_qkv followed by the cache
+// write.  Item (h, g): head h, elements 8g .. 8g + 7 and D/2 + 8g .. + 7, which are
+// d-groups g and g + 8 of the K layout.
+__device__ __forceinline__ void load8_f32(const void* p, int64_t i, int f32, int vec, float (&x)[8]) {
+  if (f32) {
+    const float* f = static_cast<const float*>(p) + i;
+    if (vec) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(f), c = *reinterpret_cast<const floatx4*>(f + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = c[e]; }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = f[e];
+    }
+  } else {
+    const uint16_t* h = static_cast<const uint16_t*>(p) + i;
+    if (vec) {
+      const u16x8 a = *reinterpret_cast<const u16x8*>(h);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(a[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(h[e]);
+    }
+  }
+}
+
+__device__ __forceinline__ void store8_f32(void* p, int64_t i, int f32, int vec, const float (&y)[8]) {
+  if (f32) {
+    float* f = static_cast<float*>(p) + i;
+    if (vec) {
+      floatx4 a, c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { a[e] = y[e]; c[e] = y[4 + e]; }
+      *reinterpret_cast<floatx4*>(f) = a;
+      *reinterpret_cast<floatx4*>(f + 4) = c;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = y[e];
+    }
+  } else {
+    uint16_t* h = static_cast<uint16_t*>(p) + i;
+    u16x8 a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = f32_to_bf16(y[e]);
+    if (vec) {
+      *reinterpret_cast<u16x8*>(h) = a;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = a[e];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void rope_kv_write_kernel(
+    const void* __restrict__ qkv, int64_t ld, int qkv_f32, int qkv_vec, void* __restrict__ q, int q_f32,
+    int q_vec, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch, int max_pages,
+    int hq, int hkv, int ps, double base) {
+  constexpr int HALF = HD / 2;
+  const int t = blockIdx.x;
+  const int b = find_seq_wave(qsl, batch, t);
+  const int pos = seq_lens[b] - (qsl[b + 1] - qsl[b]) + (t - qsl[b]);
+  __shared__ float cs[2][HALF];
+  if (threadIdx.x < HALF) rope_cos_sin(pos, threadIdx.x, HD, base, cs[0][threadIdx.x], cs[1][threadIdx.x]);
+  __syncthreads();
+  const int phys = bt[static_cast<int64_t>(b) * max_pages + pos / ps];
+  const int slot = pos % ps;
+  const int64_t row = static_cast<int64_t>(t) * ld;
+  for (int it = threadIdx.x; it < (hq + 2 * hkv) * 8; it += blockDim.x) {
+    const int h = it >> 3, g = it & 7;
+    const int64_t src = row + static_cast<int64_t>(h) * HD + 8 * g;
+    float x1[8], x2[8];
+    load8_f32(qkv, src, qkv_f32, qkv_vec, x1);
+    load8_f32(qkv, src + HALF, qkv_f32, qkv_vec, x2);
+    if (h >= hq + hkv) {   // v: stored as it is (rounded to bf16), V layout [d][slot]
+      uint16_t* pv = vc + (static_cast<int64_t>(phys) * hkv + (h - hq - hkv)) * ps * HD;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[static_cast<int64_t>(8 * g + e) * ps + slot] = f32_to_bf16(x1[e]);
+        pv[static_cast<int64_t>(HALF + 8 * g + e) * ps + slot] = f32_to_bf16(x2[e]);
+      }
+      continue;
+    }
+    float y1[8], y2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rope_rotate(x1[e], x2[e], cs[0][8 * g + e], cs[1][8 * g + e], y1[e], y2[e]);
+    if (h < hq) {   // q: bf16, or fp32 (the FP32-activation variant)
+      const int64_t o = (static_cast<int64_t>(t) * hq + h) * HD + 8 * g;
+      store8_f32(q, o, q_f32, q_vec, y1);
+      store8_f32(q, o + HALF, q_f32, q_vec, y2);
+      continue;
+    }
+    // k: d-groups g and g + 8 of the token's slot
+    uint16_t* pk = kc + (static_cast<int64_t>(phys) * hkv + (h - hq)) * ps * HD;
+    u16x8 a, c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = f32_to_bf16(y1[e]);
+      c[e] = f32_to_bf16(y2[e]);
+    }
+    *reinterpret_cast<u16x8*>(pk + (static_cast<int64_t>(g) * ps + k_slot(slot)) * 8) = a;
+    *reinterpret_cast<u16x8*>(pk + (static_cast<int64_t>(g + HALF / 8) * ps + k_slot(slot)) * 8) = c;
   }
 }
 
@@ -877,11 +992,12 @@ int attention_check(const void* q, int q_dtype, const void* k_new, const void* v
       max_seq_len > (1 << 30))
     return BI_ERR_SHAPE;
   if (num_tokens == 0 || batch == 0) return BI_OK;
-  if (!q || !k_new || !v_new || !k_cache || !v_cache || !block_table || !seq_lens ||
+  // k_new and v_new both NULL: the keys and values are in the cache already
+  if (!q || (!k_new != !v_new) || !k_cache || !v_cache || !block_table || !seq_lens ||
       !query_start_loc || !out)
     return BI_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
-      !aligned16(v_cache) || !aligned16(out))
+  if (!aligned16(q) || (k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)) ||
+      !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return BI_ERR_ALIGN;
   // the split path indexes its work items (token, chunk, kv head) with 32-bit integers
   if (num_tokens <= SPLIT_MAX_TOKENS &&
@@ -910,10 +1026,13 @@ void attention_launch(const void* q, const void* k_new, const void* v_new, void*
   const int G = num_q_heads / num_kv_heads;
   const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   const int64_t maxc = chunks_for(max_seq_len);
-  kv_write_kernel<<<dim3(static_cast<unsigned>(num_tokens)), dim3(256), 0, s>>>(
-      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-      static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_table, seq_lens,
-      query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size, split ? ws_tok : nullptr);
+  // the cache write (or, with the keys and values in the cache already, the split path's
+  // token records alone)
+  if (k_new || split)
+    kv_write_kernel<<<dim3(static_cast<unsigned>(num_tokens)), dim3(256), 0, s>>>(
+        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_table, seq_lens,
+        query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size, split ? ws_tok : nullptr);
   const int of = out_dtype == BI_F32;
   if (split) {
     // Work units of GROUP chunks, whose partial is the group's in-register merge; when that
@@ -1073,11 +1192,11 @@ extern "C" int bi_attention_batchdep_split(
   if (max_seq_len > static_cast<int64_t>(max_pages_per_seq) * page_size) return BI_ERR_SHAPE;
   if (num_tokens == 0 || batch == 0) return BI_OK;
   if (num_tokens > SPLIT_MAX_TOKENS) return BI_ERR_UNSUPPORTED;
-  if (!q || !k_new || !v_new || !k_cache || !v_cache || !block_table || !seq_lens ||
+  if (!q || (!k_new != !v_new) || !k_cache || !v_cache || !block_table || !seq_lens ||
       !query_start_loc || !out)
     return BI_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
-      !aligned16(v_cache) || !aligned16(out))
+  if (!aligned16(q) || (k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)) ||
+      !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return BI_ERR_ALIGN;
   const size_t need = bi_attention_workspace_bytes(num_tokens, num_q_heads, head_dim, max_seq_len);
   if (!workspace || workspace_bytes < need) return BI_ERR_WORKSPACE;
@@ -1090,10 +1209,11 @@ extern "C" int bi_attention_batchdep_split(
   const int64_t maxg = (maxc + group - 1) / group;
   hipStream_t s = as_stream(stream);
   const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  kv_write_kernel<<<dim3(static_cast<unsigned>(num_tokens)), dim3(256), 0, s>>>(
-      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-      static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_table, seq_lens,
-      query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size, nullptr);
+  if (k_new)
+    kv_write_kernel<<<dim3(static_cast<unsigned>(num_tokens)), dim3(256), 0, s>>>(
+        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_table, seq_lens,
+        query_start_loc, batch, max_pages_per_seq, num_kv_heads, page_size, nullptr);
   float* ws_ml = static_cast<float*>(workspace);
   float* ws_o = ws_ml + ml_floats(num_tokens * num_q_heads * maxg);
   const dim3 ggrid(static_cast<unsigned>(num_tokens * maxg), num_kv_heads);
@@ -1111,5 +1231,33 @@ extern "C" int bi_attention_batchdep_split(
   attn_combine_kernel<<<dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s>>>(
       ws_ml, ws_o, seq_lens, query_start_loc, batch, num_q_heads, static_cast<int>(maxg), rows, out,
       out_dtype == BI_F32, static_cast<int>(group), 1);
+  return launch_status();
+}
+
+extern "C" int bi_rope_kv_write(const void* qkv, int64_t ldqkv, int qkv_dtype, void* q, int q_dtype,
+                                void* k_cache, void* v_cache, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* query_start_loc,
+                                int32_t batch, int64_t num_tokens, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                int32_t max_pages_per_seq, double base, void* stream) {
+  if ((qkv_dtype != BI_BF16 && qkv_dtype != BI_F32) || (q_dtype != BI_BF16 && q_dtype != BI_F32))
+    return BI_ERR_DTYPE;
+  if (batch < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+      page_size < 1 || max_pages_per_seq < 1)
+    return BI_ERR_SHAPE;
+  if (head_dim != HD) return BI_ERR_UNSUPPORTED;
+  if (page_size % 16 || CHUNK % page_size) return BI_ERR_UNSUPPORTED;
+  if (ldqkv < static_cast<int64_t>(num_q_heads + 2 * num_kv_heads) * HD || num_tokens > (1 << 30))
+    return BI_ERR_SHAPE;
+  if (num_tokens == 0 || batch == 0) return BI_OK;
+  if (!qkv || !q || !k_cache || !v_cache || !block_table || !seq_lens || !query_start_loc)
+    return BI_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return BI_ERR_ALIGN;
+  const int qkv_vec = aligned16(qkv) && (ldqkv % (qkv_dtype == BI_F32 ? 4 : 8)) == 0;
+  const int q_vec = aligned16(q);
+  rope_kv_write_kernel<<<dim3(static_cast<unsigned>(num_tokens)), dim3(256), 0, as_stream(stream)>>>(
+      qkv, ldqkv, qkv_dtype == BI_F32, qkv_vec, q, q_dtype == BI_F32, q_vec,
+      static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_table, seq_lens,
+      query_start_loc, batch, max_pages_per_seq, num_q_heads, num_kv_heads, page_size, base);
   return launch_status();
 }

@@ -59,6 +59,21 @@ __device__ __forceinline__ uint16_t swiglu_bf16(uint16_t gb, uint16_t ub) {
   return f32_to_bf16(silu * u);
 }
 
+// RoPE of the rotate-half pair (j, j + D/2) at position pos: the angle pos * base^(-2j/D)
+// in fp64, its cosine and sine each rounded to fp32, then y1 = x1 c - x2 s and
+// y2 = x2 c + x1 s from separately rounded fp32 products.  bi_rope_qkv and the fused
+// RoPE + cache write both call these, so their q and k share every bit.
+__device__ __forceinline__ void rope_cos_sin(int pos, int j, int hd, double base, float& c, float& s) {
+  const double inv = pow(base, -2.0 * j / hd);
+  const double ang = static_cast<double>(pos) * inv;
+  c = static_cast<float>(cos(ang));
+  s = static_cast<float>(sin(ang));
+}
+__device__ __forceinline__ void rope_rotate(float x1, float x2, float c, float s, float& y1, float& y2) {
+  y1 = x1 * c - x2 * s;
+  y2 = x2 * c + x1 * s;
+}
+
 __device__ __forceinline__ float wave_xor(float v, int off) { return __shfl_xor(v, off, kWave); }
 
 // Butterfly over the 64 lanes with offsets 1, 2, 4, 8, 16, 32.  fp32 addition is

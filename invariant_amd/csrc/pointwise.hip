@@ -52,12 +52,7 @@ __global__ void rope_qkv_kernel(const void* __restrict__ qkv, int64_t ld, int qk
   const int h1 = min(h0 + hpt, heads);
   const int64_t row = t * ld;
   float c = 1.f, s = 0.f;
-  if (h0 < hq + hkv) {
-    const double inv = pow(base, -2.0 * j / hd);
-    const double ang = static_cast<double>(positions[t]) * inv;
-    c = static_cast<float>(cos(ang));
-    s = static_cast<float>(sin(ang));
-  }
+  if (h0 < hq + hkv) rope_cos_sin(positions[t], j, hd, base, c, s);
   for (int h = h0; h < h1; ++h) {
     const int64_t src = row + static_cast<int64_t>(h) * hd;
     const float x1 = load_as_f32(qkv, src + j, qkv_f32);
@@ -68,8 +63,8 @@ __global__ void rope_qkv_kernel(const void* __restrict__ qkv, int64_t ld, int qk
       dst[j + half] = f32_to_bf16(x2);
       continue;
     }
-    const float y1 = x1 * c - x2 * s;
-    const float y2 = x2 * c + x1 * s;
+    float y1, y2;
+    rope_rotate(x1, x2, c, s, y1, y2);
     if (h < hq) {   // q: bf16, or fp32 (the FP32-activation variant)
       const int64_t o = (t * hq + h) * hd;
       store_from_f32(q, o + j, y1, q_f32);

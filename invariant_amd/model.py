@@ -5,8 +5,9 @@ Orchestration only: every arithmetic step is one of the library's entry points; 
 provides device memory and the stream.  Sources:
   * "Defeating nondeterminism in LLM inference": a request's output must not depend on
     the server's batch (batch invariance); the KV cache and page table are updated
-    before the attention kernel (bi_attention does that first); chunked prefill must
-    give the same numbers as an unsplit prefill.
+    before the attention kernel (bi_rope_kv_write does it with the rotation, or, when a
+    layer is traced, bi_attention does it first from k and v tensors); chunked prefill
+    must give the same numbers as an unsplit prefill.
   * "Does the same LLM give different outputs on different GPUs? Why?": greedy decoding
     of a Mistral-7B model on a ~1400-token prompt, token probabilities from the
     normalised scores.
@@ -30,8 +31,8 @@ import numpy as np
 import torch
 
 from . import (bi_attention, bi_attention_workspace_bytes, bi_embedding, bi_gemm,
-               bi_logsoftmax_argmax, bi_residual_add, bi_rmsnorm, bi_rope_qkv, bi_swiglu,
-               bi_gemm_swiglu, interleave_gate_up, bi_add_rmsnorm)
+               bi_logsoftmax_argmax, bi_residual_add, bi_rmsnorm, bi_rope_kv_write, bi_rope_qkv,
+               bi_swiglu, bi_gemm_swiglu, interleave_gate_up, bi_add_rmsnorm)
 
 BF16, F32 = torch.bfloat16, torch.float32
 
@@ -171,14 +172,22 @@ def decoder_layer(w, h, batch: Batch, k_cache, v_cache, dims: Dims, fp32_variant
     attention norm (the previous layer computed it with its residual add).  With next_norm the
     layer returns (h_out, rmsnorm(h_out) with next_norm), else h_out.  Every path gives the
     same bits as the separate calls.  trace, if a dict, receives the layer's intermediate
-    tensors by name (h, x, qkv, q, k, v, attn, o, h2, x2, mlp, dn, out, next_x)."""
+    tensors by name (h, x, qkv, q, k, v, attn, o, h2, x2, mlp, dn, out, next_x); a traced
+    layer keeps k and v as tensors (bi_rope_qkv, then bi_attention writes them into the
+    pages), an untraced one rotates straight into the pages (bi_rope_kv_write): the same
+    bits either way."""
     T = h.shape[0]
     act = F32 if fp32_variant else BF16
     if x is None:
         x = bi_rmsnorm(h, w["attn_norm"], dims.eps, out_dtype=act)
     qkv = bi_gemm(x, w["wqkv"], out_dtype=act)
-    q, k, v = bi_rope_qkv(qkv, batch.positions, dims.n_q_heads, dims.n_kv_heads, dims.head_dim,
-                          dims.rope_base, q_dtype=act)
+    if trace is None:   # RoPE writes the rotated keys and the values straight into the pages
+        q = bi_rope_kv_write(qkv, k_cache, v_cache, batch.block_table, batch.seq_lens, batch.qsl,
+                             dims.n_q_heads, dims.rope_base, q_dtype=act)
+        k = v = None
+    else:               # the same bits through k and v tensors, which the trace keeps
+        q, k, v = bi_rope_qkv(qkv, batch.positions, dims.n_q_heads, dims.n_kv_heads, dims.head_dim,
+                              dims.rope_base, q_dtype=act)
     a = bi_attention(q, k, v, k_cache, v_cache, batch.block_table, batch.seq_lens, batch.qsl,
                      batch.max_seq_len, 1.0 / float(np.sqrt(dims.head_dim)), out_dtype=act,
                      workspace=batch.workspace)

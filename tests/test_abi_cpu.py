@@ -95,6 +95,19 @@ def test_validation_rejects_before_launch(lib):
     bad_q = [P, 7] + [P] * 7          # an unknown q dtype
     assert lib.bi_attention(*bad_q, 2, 4, 32, 8, 128, 16, 4, 64, 0.088, P, 1, P, 1 << 20, None) == -3
     assert lib.bi_rope_qkv(P, 6144, 1, P, P, 5, P, P, 4, 32, 8, 128, 10000.0, None) == -3
+    # attention with exactly one of k_new, v_new NULL (both NULL means "in the cache already")
+    one_null = [P, 1, None, P] + [P] * 5
+    assert lib.bi_attention(*one_null, 2, 4, 32, 8, 128, 16, 4, 64, 0.088, P, 1, P, 1 << 20, None) == -1
+    # fused RoPE + cache write: dtype, head_dim, page size, row stride, null operands
+    def rkw(qd=1, ld=6144, d=128, ps=16, qkv=P, kc=P, T=4, B=2):
+        return lib.bi_rope_kv_write(qkv, ld, 1, P, qd, kc, P, P, P, P, B, T, 32, 8, d, ps, 4, 10000.0, None)
+    assert rkw(qd=5) == -3
+    assert rkw(d=64, ld=3072) == -6
+    assert rkw(ps=24) == -6
+    assert rkw(ld=6000) == -2
+    assert rkw(qkv=None) == -1
+    assert rkw(kc=ctypes.c_void_p(18)) == -4
+    assert rkw(T=0) == 0 and rkw(B=0) == 0
     # the comparison variant splits K only when the grid leaves CUs idle (256 CUs assumed
     # without a GPU): none for 2048^3 (256 tiles), four slices for 256 x 1024 (64 tiles)
     assert lib.bi_gemm_splitk_workspace_bytes(2048, 2048, 2048) == 0
