@@ -576,17 +576,40 @@ __device__ __forceinline__ void load_q_col(const void* q, int64_t token, int hea
   load_q_at<NQ>(q, token, head, hq, qop);
 }
 
+// tok NULL (the keys and values were written by rope_kv_write_kernel, which writes no
+// records): each workgroup derives the records itself from the batch description, exactly
+// as kv_write_kernel does (sequence = the last b with qsl[b] <= t, searched in LDS when the
+// offsets fit there).
 template <int NQ>
 __global__ __launch_bounds__(256) void attn_split_kernel(
     const void* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt, const int4* __restrict__ tok,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int batch,
     int num_tokens, int max_pages, int hq, int hkv, int ps, int max_groups, float sl2,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, int uc) {
   __shared__ ChunkLDS sh;
   __shared__ int4 s_tok[SPLIT_MAX_TOKENS];
   __shared__ int s_start[SPLIT_MAX_TOKENS + 1];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int t = threadIdx.x; t < num_tokens; t += 256) s_tok[t] = tok[t];
+  if (tok) {
+    for (int t = threadIdx.x; t < num_tokens; t += 256) s_tok[t] = tok[t];
+  } else {
+    const bool staged = batch <= SPLIT_MAX_TOKENS;   // s_start holds the offsets meanwhile
+    if (staged)
+      for (int i = threadIdx.x; i <= batch; i += 256) s_start[i] = qsl[i];
+    __syncthreads();
+    for (int t = threadIdx.x; t < num_tokens; t += 256) {
+      int lo = 0, hi = batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((staged ? s_start[mid] : qsl[mid]) <= t) lo = mid;
+        else hi = mid - 1;
+      }
+      const int q0 = staged ? s_start[lo] : qsl[lo], q1 = staged ? s_start[lo + 1] : qsl[lo + 1];
+      const int len = seq_lens[lo];
+      s_tok[t] = make_int4(lo, len - (q1 - q0) + (t - q0), len, 0);
+    }
+  }
   __syncthreads();
   if (w == 0) {   // s_start[t] = groups of tokens 0 .. t-1 (token t has pos / 1024 + 1)
     int carry = 0;
@@ -1026,9 +1049,9 @@ void attention_launch(const void* q, const void* k_new, const void* v_new, void*
   const int G = num_q_heads / num_kv_heads;
   const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   const int64_t maxc = chunks_for(max_seq_len);
-  // the cache write (or, with the keys and values in the cache already, the split path's
-  // token records alone)
-  if (k_new || split)
+  // the cache write and the split path's token records (with the keys and values in the
+  // cache already, nothing: the split kernel derives the records itself)
+  if (k_new)
     kv_write_kernel<<<dim3(static_cast<unsigned>(num_tokens)), dim3(256), 0, s>>>(
         static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
         static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_table, seq_lens,
@@ -1048,7 +1071,8 @@ void attention_launch(const void* q, const void* k_new, const void* v_new, void*
     const int64_t grid = std::min<int64_t>(units, static_cast<int64_t>(split_resident<NQ>()) * cu_count());
     attn_split_kernel<NQ><<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, s>>>(
         q, static_cast<const uint16_t*>(k_cache),
-        static_cast<const uint16_t*>(v_cache), block_table, ws_tok, static_cast<int>(num_tokens),
+        static_cast<const uint16_t*>(v_cache), block_table, k_new ? ws_tok : nullptr, seq_lens,
+        query_start_loc, batch, static_cast<int>(num_tokens),
         max_pages_per_seq, num_q_heads, num_kv_heads, page_size, static_cast<int>(slots), sl2,
         ws_ml, ps_o, uc);
     const int64_t rows = num_tokens * num_q_heads;
