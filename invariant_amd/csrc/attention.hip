@@ -372,8 +372,7 @@ __device__ __forceinline__ void load_q(const void* q, int64_t token, int head, i
 }
 
 // ---------------------------------------------------------------- step 1: cache write
-// (k_new NULL: the call's keys and values were written by rope_kv_write_kernel; only the
-// per-token records are produced)
+// (not launched when the call's keys and values were written by rope_kv_write_kernel)
 __global__ __launch_bounds__(256) void kv_write_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
@@ -383,7 +382,6 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
   const int b = find_seq_wave(qsl, batch, t);
   const int pos = seq_lens[b] - (qsl[b + 1] - qsl[b]) + (t - qsl[b]);
   if (tok && threadIdx.x == 0) tok[t] = make_int4(b, pos, seq_lens[b], 0);
-  if (!k_new) return;   // the keys and values are in the cache already: records only
   const int phys = bt[static_cast<int64_t>(b) * max_pages + pos / ps];
   const int slot = pos % ps;
   const int nvec = hkv * HD / 8;
@@ -521,8 +519,8 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(
 // token t for kv head h, ordered by (t, g, h); the unit's 16 columns are the token's G q
 // heads (the rest unused).  A persistent grid: workgroup w reduces units w, w + gridDim.x,
 // ... chunk by chunk, merging each unit's chunks in registers and writing one partial per
-// unit.  The token records (sequence, position, length) written by kv_write_kernel and the
-// running count of units per token sit in LDS.  Loads are software-pipelined across
+// unit.  The token records (sequence, position, length), written by kv_write_kernel or
+// derived in the prologue, and the running count of units per token sit in LDS.  Loads are software-pipelined across
 // chunks: the next chunk's q and K go out once this chunk's scores are done, the page ids
 // of the chunk three ahead and the next chunk's V once its values are done, so a
 // workgroup keeps loads in flight while it computes.  Which workgroup reduces a unit, and
