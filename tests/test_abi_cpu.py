@@ -145,3 +145,25 @@ def test_hip_constants_equal_oracle_derivation():
     log_want = [k["SQRT2"], *reversed(k["LOG_B"]), k["LN2_HI"], k["LN2_LO"]]
     assert _fn_constants(src, "exp_cw") == [_bits(v) for v in exp_want]
     assert _fn_constants(src, "log_at") == [_bits(v) for v in log_want]
+
+
+def test_missing_library_raises_no_fallback(tmp_path):
+    # the binding has no CPU path: with the library absent every call raises before doing
+    # anything (run in a fresh interpreter, since this process has loaded the library)
+    import subprocess
+    import sys
+    code = (
+        "import torch, invariant_amd as bi\n"
+        f"bi.LIB_PATH = {str(tmp_path / 'absent' / 'libbi.so')!r}\n"
+        "x = torch.zeros((2, 8), dtype=torch.bfloat16)\n"
+        "g = torch.ones(8, dtype=torch.bfloat16)\n"
+        "for f in (lambda: bi.bi_rmsnorm(x, g, 1e-5), lambda: bi.bi_gemm(x, x)):\n"
+        "    try:\n"
+        "        f()\n"
+        "    except RuntimeError as e:\n"
+        "        assert 'not built' in str(e), e\n"
+        "    else:\n"
+        "        raise SystemExit('a call returned without the library')\n"
+        "print('raised')\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "raised" in r.stdout, (r.stdout, r.stderr)
