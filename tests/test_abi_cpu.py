@@ -167,3 +167,22 @@ def test_missing_library_raises_no_fallback(tmp_path):
         "print('raised')\n")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and "raised" in r.stdout, (r.stdout, r.stderr)
+
+
+def test_abi_from_plain_c(lib, tmp_path):
+    # include/bi.h as C99 and libbi.so linked from a C program: configuration, status
+    # strings and validation (tests/c/abi_from_c.c; no GPU work)
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    exe = str(tmp_path / "abi_from_c")
+    libdir = os.path.dirname(bi.LIB_PATH)
+    build = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                            os.path.join(ROOT, "tests", "c", "abi_from_c.c"), "-o", exe,
+                            f"-L{libdir}", "-l:" + os.path.basename(bi.LIB_PATH), f"-Wl,-rpath,{libdir}"],
+                           capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0 and run.stdout.strip() == "ok", (run.stdout, run.stderr)
