@@ -356,10 +356,12 @@ def model_bench(torch, bi):
         return time.perf_counter() - t
 
     timed([prompt], 2)
-    # bytes a decode step reads: every weight except the gate-then-up copy of the MLP rows
-    # (decoding reads their interleaved copy)
-    weight_bytes = sum(t.numel() * t.element_size() for t in _tensors(model)) - sum(
-        w["wgate_up"].numel() * 2 for w in model["layers"])
+    # bytes a decode step reads: each layer's norms, QKV, O and down weights and one copy of
+    # the gate/up rows (the tiled one), the final norm and the LM head (its tiled copy)
+    nb = lambda t: t.numel() * t.element_size()
+    weight_bytes = sum(nb(w[k]) for w in model["layers"]
+                       for k in ("attn_norm", "wqkv", "wo", "ffn_norm", "wgate_up", "wdown"))
+    weight_bytes += nb(model["final_norm"]) + nb(model["lm_head"])
     out_layer = layer_bench(torch, model, dims)
     out = {"workload": "Mistral-7B-shaped 32-layer greedy decode, random bf16 weights",
            "weight_bytes": weight_bytes, "decoder_layer_decode": out_layer}
@@ -386,7 +388,8 @@ def layer_bench(torch, model, dims):
     layer = model["layers"][0]
     ctx = synth.ragged_lengths(256, 0, 4096, 3, 2)
     cache = PagedKVCache(dims, n_pages=int(ctx.sum()) // 16 + 2 * 256 + 16, seed=3, n_layers=1)
-    lw_bytes = sum(t.numel() * t.element_size() for t in _tensors(layer)) - layer["wgate_up"].numel() * 2
+    lw_bytes = sum(layer[k].numel() * layer[k].element_size()
+                   for k in ("attn_norm", "wqkv", "wo", "ffn_norm", "wgate_up", "wdown"))
     for B in (1, 8, 64, 256):
         sids = list(range(B))
         batch = make_batch(cache, sids, [int(c) for c in ctx[:B]],
@@ -410,21 +413,6 @@ def layer_bench(torch, model, dims):
         for sid in sids:
             cache.release(sid)
     return out
-
-
-def _tensors(obj):
-    import torch
-    if isinstance(obj, torch.Tensor):
-        yield obj
-    elif isinstance(obj, dict):
-        for v in obj.values():
-            yield from _tensors(v)
-    elif isinstance(obj, (list, tuple)):
-        for v in obj:
-            yield from _tensors(v)
-    elif hasattr(obj, "__dict__"):
-        for v in vars(obj).values():
-            yield from _tensors(v)
 
 
 def graph_step(torch, inp, ops, K):

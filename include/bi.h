@@ -60,7 +60,7 @@ typedef enum {
 } bi_status;
 
 enum { BI_BF16 = 1, BI_F32 = 2 };
-enum { BI_B_KN = 0, BI_B_NK = 1 };
+enum { BI_B_KN = 0, BI_B_NK = 1, BI_B_TILED = 2 };
 
 /* Compile-time constants of the reduction strategy.  They never vary at run time,
  * because a run-time choice would be a way to break invariance. */
@@ -118,7 +118,10 @@ int bi_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t D, 
  *         same fp32 accumulator: fp32-operand products at three times the work, the
  *         upcast of [XV]); row stride lda
  *   B     bf16; b_layout BI_B_NK: B is [N, K] (a Linear weight, C = A . B^T), row
- *         stride ldb;  BI_B_KN: B is [K, N] (torch.mm orientation), row stride ldb
+ *         stride ldb;  BI_B_KN: B is [K, N] (torch.mm orientation), row stride ldb;
+ *         BI_B_TILED: an [N, K] B as bi_pack_b wrote it (ldb unused), for calls of at most
+ *         16 rows with K a multiple of 8 and at least 1024 (the few-row kernel's calls;
+ *         other calls return BI_ERR_UNSUPPORTED) -- the same bits as BI_B_NK
  *   C     dtype c_dtype (BI_BF16: one RNE rounding of the fp32 sum; BI_F32), stride ldc
  * Every output element is produced by the same sequence of matrix instructions
  * (v_mfma_f32_16x16x32_bf16, one fp32 accumulator from +0, K in ascending 32-wide steps,
@@ -354,11 +357,27 @@ int bi_swiglu(const void* gu, int64_t ldgu, void* out, int64_t T, int64_t F, voi
  *   bf16, and the pair goes through bi_swiglu's arithmetic, so out equals
  *   bi_swiglu(bi_gemm(A, W_gate_up)) bit for bit without writing the [M, 2F] intermediate.
  *   A [M, K] bf16 (row stride lda), W row stride ldw, out row stride ldo (bf16).
- *   Errors: BI_ERR_NULL, BI_ERR_SHAPE (F not a multiple of 16, strides too small),
- *   BI_ERR_ALIGN (16-byte pointers, lda and ldw multiples of 8), BI_ERR_UNSUPPORTED
- *   (A or W spanning 4 GiB or more: use bi_gemm and bi_swiglu). */
+ *   w_layout BI_B_NK: W as above; BI_B_TILED: bi_pack_b of that [2F, K] W (ldw unused; at
+ *   most 16 rows, K a multiple of 8 and at least 1024), the same bits.
+ *   Errors: BI_ERR_DTYPE (w_layout), BI_ERR_NULL, BI_ERR_SHAPE (F not a multiple of 16,
+ *   strides too small), BI_ERR_ALIGN (16-byte pointers, lda and ldw multiples of 8),
+ *   BI_ERR_UNSUPPORTED (A or W spanning 4 GiB or more: use bi_gemm and bi_swiglu; a tiled W
+ *   outside its row and K range). */
 int bi_gemm_swiglu(const void* A, const void* W, void* out, int64_t M, int64_t F, int64_t K,
-                   int64_t lda, int64_t ldw, int64_t ldo, void* stream);
+                   int64_t lda, int64_t ldw, int64_t ldo, int w_layout, void* stream);
+
+/* bi_pack_b: B [N, K] bf16 (row stride ldb) rewritten in the tiled layout of BI_B_TILED,
+ *   for weights read by calls of a few rows (greedy decode): 16-row x 32-column tiles,
+ *   stored one after another (row block b, then the 32-wide K step t), each 1 KB tile in
+ *   the order the few-row kernel's 64 lanes take their matrix-instruction operands --
+ *   B[16 b + r][32 t + 8 g + e] at ((b * ceil(K/32) + t) * 64 + r + 16 g) * 8 + e, zero past
+ *   N and K -- so each of a wave's loads reads one contiguous kilobyte, not 64 bytes from
+ *   each of 16 rows (no bit changes: the same operands reach the same instruction).
+ *   out: bi_pack_b_bytes(N, K) bytes, 16-byte aligned.  Layout chosen for MI355X's HBM,
+ *   not taken from the pages.
+ *   Errors: BI_ERR_SHAPE, BI_ERR_NULL, BI_ERR_ALIGN. */
+size_t bi_pack_b_bytes(int64_t N, int64_t K);
+int bi_pack_b(const void* B, int64_t N, int64_t K, int64_t ldb, void* out, void* stream);
 
 /* bi_residual_add: out = a + b elementwise over n elements, each operand of its own
  *   dtype (BI_BF16 | BI_F32); out may alias a or b. */

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbi.so")
 
 BI_BF16, BI_F32 = 1, 2
-BI_B_KN, BI_B_NK = 0, 1
+BI_B_KN, BI_B_NK, BI_B_TILED = 0, 1, 2
 
 _c = ctypes
 _P, _I64, _I32, _F32, _F64, _SZ = _c.c_void_p, _c.c_int64, _c.c_int32, _c.c_float, _c.c_double, _c.c_size_t
@@ -45,7 +45,9 @@ _SIGS = {
     "bi_rope_kv_write": (_c.c_int, [_P, _I64, _c.c_int, _P, _c.c_int, _P, _P, _P, _P, _P, _I32, _I64, _I32,
                                     _I32, _I32, _I32, _I32, _F64, _P]),
     "bi_swiglu": (_c.c_int, [_P, _I64, _P, _I64, _I64, _P]),
-    "bi_gemm_swiglu": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
+    "bi_gemm_swiglu": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _c.c_int, _P]),
+    "bi_pack_b_bytes": (_SZ, [_I64, _I64]),
+    "bi_pack_b": (_c.c_int, [_P, _I64, _I64, _I64, _P, _P]),
     "bi_add_rmsnorm": (_c.c_int, [_P, _P, _P, _c.c_int, _P, _P, _c.c_int, _I64, _I64, _c.c_float, _P]),
     "bi_residual_add": (_c.c_int, [_P, _c.c_int, _P, _c.c_int, _P, _c.c_int, _I64, _P]),
 }
@@ -135,14 +137,28 @@ def bi_rmsnorm(x, gamma, eps: float, out=None, out_dtype=torch.bfloat16):
     return out
 
 
-def bi_gemm(a, b, out=None, b_layout: int = BI_B_NK, out_dtype=torch.bfloat16):
-    """C = a @ b^T for b_layout BI_B_NK (b is [N, K]), C = a @ b for BI_B_KN (b is [K, N])."""
+def bi_gemm(a, b, out=None, b_layout: int = BI_B_NK, out_dtype=torch.bfloat16, n=None):
+    """C = a @ b^T for b_layout BI_B_NK (b is [N, K]), C = a @ b for BI_B_KN (b is [K, N]);
+    BI_B_TILED: b is bi_pack_b of an [N, K] B (N = n, default 16 x its row blocks)."""
     M, K = a.shape
-    N = b.shape[0] if b_layout == BI_B_NK else b.shape[1]
+    if b_layout == BI_B_TILED:
+        N = n if n is not None else b.shape[0] * 16
+        ldb = 0
+    else:
+        N = b.shape[0] if b_layout == BI_B_NK else b.shape[1]
+        ldb = _ld(b)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
-    _check("bi_gemm", load().bi_gemm(_ptr(a), _ptr(b), _ptr(out), M, N, K, _ld(a), _ld(b), _ld(out),
+    _check("bi_gemm", load().bi_gemm(_ptr(a), _ptr(b), _ptr(out), M, N, K, _ld(a), ldb, _ld(out),
                                       b_layout, _code(a.dtype), _code(out.dtype), _stream(a)))
+    return out
+
+
+def bi_pack_b(b):
+    """B [N, K] bf16 in the tiled layout of BI_B_TILED: [ceil(N/16), ceil(K/32), 64, 8]."""
+    N, K = b.shape
+    out = torch.empty(((N + 15) // 16, (K + 31) // 32, 64, 8), dtype=torch.bfloat16, device=b.device)
+    _check("bi_pack_b", load().bi_pack_b(_ptr(b), N, K, _ld(b), _ptr(out), _stream(b)))
     return out
 
 
@@ -304,14 +320,20 @@ def interleave_gate_up(w):
     return w.view(2, F2 // 32, 16, K).permute(1, 0, 2, 3).reshape(F2, K).contiguous()
 
 
-def bi_gemm_swiglu(a, w_interleaved, out=None):
-    """swiglu(a @ W^T) with W given as interleave_gate_up(W) (out [M, F] bf16)."""
+def bi_gemm_swiglu(a, w_interleaved, out=None, w_layout: int = BI_B_NK):
+    """swiglu(a @ W^T) with W given as interleave_gate_up(W) (out [M, F] bf16); w_layout
+    BI_B_TILED: bi_pack_b(interleave_gate_up(W))."""
     M, K = a.shape
-    F = w_interleaved.shape[0] // 2
+    if w_layout == BI_B_TILED:
+        F = w_interleaved.shape[0] * 16 // 2
+        ldw = 0
+    else:
+        F = w_interleaved.shape[0] // 2
+        ldw = _ld(w_interleaved)
     if out is None:
         out = torch.empty((M, F), dtype=torch.bfloat16, device=a.device)
     _check("bi_gemm_swiglu", load().bi_gemm_swiglu(_ptr(a), _ptr(w_interleaved), _ptr(out), M, F, K,
-                                                    _ld(a), _ld(w_interleaved), _ld(out), _stream(a)))
+                                                    _ld(a), ldw, _ld(out), w_layout, _stream(a)))
     return out
 
 

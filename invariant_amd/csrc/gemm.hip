@@ -874,7 +874,11 @@ TileKind pick_tile(int64_t M, int64_t N, int cus) {
 // PAIR: two waves per workgroup, one 16-column block each (CB = 1, split = 1): for SwiGLU
 // the second wave's block (the up columns) reaches the first through LDS, so a wave streams
 // one block, as in the plain one-block kernel.
-template <int RB, int CB, int PF, bool PAIR = false>
+// PK: B in the tiled layout of bi_pack_b (tile (column block, 32-wide step) = 1 KB, the
+// 16-byte piece of lane l at offset 16 l, which is lane l's instruction operand): each load
+// of a wave reads one contiguous kilobyte instead of 64 bytes from each of 16 rows.  Only
+// the addresses change; the operands, the instruction sequence and so the bits do not.
+template <int RB, int CB, int PF, bool PAIR = false, bool PK = false>
 __global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
     int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int split, int k_split,
@@ -909,15 +913,17 @@ __global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)   // rows past M repeat the last row; they are never stored
     pa[rb] = A + static_cast<int64_t>(min(row0 + rb * 16 + (lane & 15), M - 1)) * lda + kl;
+  const int64_t nk32 = (K + 31) / 32;   // tiles per column block (PK)
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
-    pb[cb] = B + static_cast<int64_t>(min(col0 + cb * 16 + (lane & 15), N - 1)) * ldb + kl;
+  for (int cb = 0; cb < CB; ++cb)   // (PK: blocks past N repeat the last one; never stored)
+    pb[cb] = PK ? B + static_cast<int64_t>(min(cblk * CB + cb, (N - 1) / 16)) * nk32 * 512 + lane * 8
+                : B + static_cast<int64_t>(min(col0 + cb * 16 + (lane & 15), N - 1)) * ldb + kl;
   bf16x8 ra[PF][RB], rv[PF][CB];
   auto load = [&](int t, bf16x8 (&dst_a)[RB], bf16x8 (&dst_b)[CB]) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) dst_a[rb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pa[rb] + 32 * t));
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) dst_b[cb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pb[cb] + 32 * t));
+    for (int cb = 0; cb < CB; ++cb) dst_b[cb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pb[cb] + (PK ? 512 : 32) * t));
   };
   floatx4 acc[RB][CB];
 #pragma unroll
@@ -942,8 +948,11 @@ __global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
   bf16x8 ta[RB], tb[CB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) ta[rb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pa[rb] + tofs));
+  // (PK: the partial step's tile, index nsteps, exists only when K is not a multiple of 32;
+  // its pieces past K hold zeros)
+  const int64_t tofs_b = PK ? (ktail < K ? int64_t(512) * nsteps : 0) : tofs;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) tb[cb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pb[cb] + tofs));
+  for (int cb = 0; cb < CB; ++cb) tb[cb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pb[cb] + tofs_b));
 #pragma unroll
   for (int p = 0; p < PF; ++p) load(p, ra[p], rv[p]);
   // full rounds: step t multiplies slot t % PF and refills it with step t + PF (straight-line
@@ -1176,16 +1185,45 @@ struct KSplit {
   int64_t stride = 0;
 };
 
-template <int RB, int CB, int PF, bool PAIR = false>
+template <int RB, int CB, int PF, bool PAIR = false, bool PK = false>
 void launch_rows_t(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                    int64_t lda, int64_t ldb, int64_t ldc, int cf, int split, hipStream_t s,
                    KSplit sk = {}) {
   const int64_t ncb = (N + CB * 16 - 1) / (CB * 16);
   const unsigned wgs = static_cast<unsigned>(PAIR ? (ncb + 1) / 2 : split == 1 ? ncb : 8 * split * ((ncb + 7) / 8));
-  gemm_rows_kernel<RB, CB, PF, PAIR><<<dim3(wgs, sk.ks), dim3(PAIR ? 128 : 64), 0, s>>>(
+  gemm_rows_kernel<RB, CB, PF, PAIR, PK><<<dim3(wgs, sk.ks), dim3(PAIR ? 128 : 64), 0, s>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, int(M), int(N), int(K),
       lda, ldb, ldc, cf, split, sk.k_split ? sk.k_split : int(K), sk.stride);
 }
+
+// The few-row kernel on a tiled B (bi_pack_b): the configurations of up to 16 rows.
+void launch_rows_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldc, int cf, hipStream_t s) {
+  const RowsCfg c = rows_cfg(M, N, cf);
+  if (c.pair) launch_rows_t<1, 1, 16, true, true>(A, B, C, M, N, K, lda, 0, ldc, cf, 1, s);
+  else if (c.cb == 2) launch_rows_t<1, 2, 16, false, true>(A, B, C, M, N, K, lda, 0, ldc, cf, 1, s);
+  else launch_rows_t<1, 1, 16, false, true>(A, B, C, M, N, K, lda, 0, ldc, cf, 1, s);
+}
+
+// Tiled layout: tile (column block b, step t) holds B[16 b + r][32 t + 8 g + e] at
+// ((b * ceil(K/32) + t) * 64 + r + 16 g) * 8 + e, zero where 16 b + r >= N or k >= K.
+__global__ void pack_b_kernel(const uint16_t* __restrict__ B, int64_t N, int64_t K, int64_t ldb,
+                              uint16_t* __restrict__ out, int64_t nk32, int64_t pieces) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= pieces) return;
+  const int lane = static_cast<int>(i & 63);
+  const int64_t tile = i >> 6;
+  const int64_t b = tile / nk32, t = tile % nk32;
+  const int64_t n = 16 * b + (lane & 15), k0 = 32 * t + 8 * (lane >> 4);
+  u16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (n < N && k0 + e < K) ? B[n * ldb + k0 + e] : uint16_t(0);
+  *reinterpret_cast<u16x8*>(out + i * 8) = v;
+}
+
+// A tiled B goes with calls of at most 16 rows that the few-row kernel takes (K a multiple
+// of 8 with at least 32 whole 32-wide steps).
+bool tiled_ok(int64_t M, int64_t K) { return M <= 16 && K % 8 == 0 && K / 32 >= 32; }
 
 void launch_rows(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                  int64_t lda, int64_t ldb, int64_t ldc, int cf, hipStream_t s, KSplit sk = {}) {
@@ -1284,12 +1322,20 @@ extern "C" int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t
                        int64_t lda, int64_t ldb, int64_t ldc, int b_layout, int a_dtype,
                        int c_dtype, void* stream) {
   if ((a_dtype != BI_BF16 && a_dtype != BI_F32) || (c_dtype != BI_BF16 && c_dtype != BI_F32) ||
-      (b_layout != BI_B_NK && b_layout != BI_B_KN))
+      (b_layout != BI_B_NK && b_layout != BI_B_KN && b_layout != BI_B_TILED))
     return BI_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0) return BI_ERR_SHAPE;
   if (M == 0 || N == 0) return BI_OK;
   if (K < 1 || lda < K || ldc < N || M > (1 << 30) || N > (1 << 30) || K > (1 << 30))
     return BI_ERR_SHAPE;
+  if (b_layout == BI_B_TILED) {   // ldb unused: the tiles are contiguous
+    if (a_dtype != BI_BF16 || !tiled_ok(M, K)) return BI_ERR_UNSUPPORTED;
+    if (!A || !B || !C) return BI_ERR_NULL;
+    if (!aligned16(A) || !aligned16(B) || (lda % 8)) return BI_ERR_ALIGN;
+    if (M * lda * 2 >= (int64_t(1) << 32)) return BI_ERR_UNSUPPORTED;
+    launch_rows_tiled(A, B, C, M, N, K, lda, ldc, c_dtype == BI_F32, as_stream(stream));
+    return launch_status();
+  }
   if (b_layout == BI_B_NK ? ldb < K : ldb < N) return BI_ERR_SHAPE;
   if (!A || !B || !C) return BI_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || (lda % (a_dtype == BI_F32 ? 4 : 8)) || (ldb % 8))
@@ -1391,16 +1437,44 @@ extern "C" int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, 
 }
 
 extern "C" int bi_gemm_swiglu(const void* A, const void* W, void* out, int64_t M, int64_t F, int64_t K,
-                              int64_t lda, int64_t ldw, int64_t ldo, void* stream) {
+                              int64_t lda, int64_t ldw, int64_t ldo, int w_layout, void* stream) {
+  if (w_layout != BI_B_NK && w_layout != BI_B_TILED) return BI_ERR_DTYPE;
   if (M < 0 || F < 0 || K < 0) return BI_ERR_SHAPE;
   if (M == 0 || F == 0) return BI_OK;
-  if (K < 1 || F % 16 != 0 || lda < K || ldw < K || ldo < F || M > (1 << 30) || F > (1 << 29) ||
-      K > (1 << 30))
+  if (K < 1 || F % 16 != 0 || lda < K || ldo < F || M > (1 << 30) || F > (1 << 29) || K > (1 << 30) ||
+      (w_layout == BI_B_NK && ldw < K))
     return BI_ERR_SHAPE;
+  if (w_layout == BI_B_TILED) {   // the tiles of interleave(W); ldw unused
+    if (!tiled_ok(M, K)) return BI_ERR_UNSUPPORTED;
+    if (!A || !W || !out) return BI_ERR_NULL;
+    if (!aligned16(A) || !aligned16(W) || (lda % 8)) return BI_ERR_ALIGN;
+    if (M * lda * 2 >= (int64_t(1) << 32)) return BI_ERR_UNSUPPORTED;
+    launch_rows_tiled(A, W, out, M, 2 * F, K, lda, ldo, kOutSwiGLU, as_stream(stream));
+    return launch_status();
+  }
   if (!A || !W || !out) return BI_ERR_NULL;
   if (!aligned16(A) || !aligned16(W) || (lda % 8) || (ldw % 8)) return BI_ERR_ALIGN;
   const int64_t N = 2 * F;
   if (!(M * lda * 2 < (int64_t(1) << 32) && N * ldw * 2 < (int64_t(1) << 32))) return BI_ERR_UNSUPPORTED;
   launch_bf16(A, W, out, M, N, K, lda, ldw, ldo, kOutSwiGLU, as_stream(stream));
+  return launch_status();
+}
+
+extern "C" size_t bi_pack_b_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N > (1 << 30) || K > (1 << 30)) return 0;
+  return static_cast<size_t>((N + 15) / 16) * static_cast<size_t>((K + 31) / 32) * 1024;
+}
+
+extern "C" int bi_pack_b(const void* B, int64_t N, int64_t K, int64_t ldb, void* out, void* stream) {
+  if (N < 0 || K < 0) return BI_ERR_SHAPE;
+  if (N == 0 || K == 0) return BI_OK;
+  if (ldb < K || N > (1 << 30) || K > (1 << 30)) return BI_ERR_SHAPE;
+  if (!B || !out) return BI_ERR_NULL;
+  if (!aligned16(out)) return BI_ERR_ALIGN;
+  const int64_t nk32 = (K + 31) / 32;
+  const int64_t pieces = (N + 15) / 16 * nk32 * 64;
+  if ((pieces + 255) / 256 > 0x7fffffffLL) return BI_ERR_SHAPE;
+  pack_b_kernel<<<dim3(static_cast<unsigned>((pieces + 255) / 256)), dim3(256), 0, as_stream(stream)>>>(
+      static_cast<const uint16_t*>(B), N, K, ldb, static_cast<uint16_t*>(out), nk32, pieces);
   return launch_status();
 }

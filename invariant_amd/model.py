@@ -32,7 +32,8 @@ import torch
 
 from . import (bi_attention, bi_attention_workspace_bytes, bi_embedding, bi_gemm,
                bi_logsoftmax_argmax, bi_residual_add, bi_rmsnorm, bi_rope_kv_write, bi_rope_qkv,
-               bi_swiglu, bi_gemm_swiglu, interleave_gate_up, bi_add_rmsnorm)
+               bi_swiglu, bi_gemm_swiglu, interleave_gate_up, bi_add_rmsnorm, bi_pack_b,
+               BI_B_TILED)
 
 BF16, F32 = torch.bfloat16, torch.float32
 
@@ -72,8 +73,11 @@ def random_layer(dims: Dims, gen, device="cuda", sd=0.02):
         wdown=_normal((d, dims.ffn), 0.0, sd, gen, device),
     )
     # the same gate/up rows interleaved in blocks of 16 for the fused GEMM + SwiGLU call
-    # (wgate_up keeps the gate-then-up order the reference computations read)
+    # (wgate_up keeps the gate-then-up order the reference computations read), and that
+    # interleaved matrix tiled for calls of a few rows (decode): the same bits, contiguous
+    # kilobyte loads
     w["wgate_up_i"] = interleave_gate_up(w["wgate_up"])
+    w["wgate_up_t"] = bi_pack_b(w["wgate_up_i"])
     return w
 
 
@@ -81,12 +85,23 @@ def random_model(dims: Dims, seed: int, device="cuda", sd=0.02):
     """Random-init weights of the given shape (linear and embedding ~ N(0, sd), norm
     gammas ~ N(1, 0.02)), drawn by a seeded device generator."""
     gen = torch.Generator(device=device).manual_seed(seed)
-    return dict(
+    return _with_tiled_head(dict(
         embed=_normal((dims.vocab, dims.hidden), 0.0, sd, gen, device),
         layers=[random_layer(dims, gen, device, sd) for _ in range(dims.n_layers)],
         final_norm=_normal((dims.hidden,), 1.0, 0.02, gen, device),
         lm_head=_normal((dims.vocab, dims.hidden), 0.0, sd, gen, device),
-    )
+    ))
+
+
+def _with_tiled_head(model):
+    model["lm_head_t"] = bi_pack_b(model["lm_head"])
+    return model
+
+
+def _tiled_ok(rows: int, k: int, a: torch.Tensor) -> bool:
+    """The calls a tiled weight serves (include/bi.h, BI_B_TILED): at most 16 rows of bf16 A,
+    K a multiple of 8 and at least 1024."""
+    return rows <= 16 and k % 8 == 0 and k >= 1024 and a.dtype == BF16
 
 
 # ------------------------------------------------------------------------- KV cache
@@ -197,7 +212,9 @@ def decoder_layer(w, h, batch: Batch, k_cache, v_cache, dims: Dims, fp32_variant
     else:
         h2 = bi_residual_add(h, o, out_dtype=act)
         x2 = bi_rmsnorm(h2, w["ffn_norm"], dims.eps, out_dtype=BF16)
-    if "wgate_up_i" in w:   # fused: == bi_swiglu(bi_gemm(x2, wgate_up)) bit for bit
+    if "wgate_up_t" in w and _tiled_ok(T, x2.shape[1], x2):   # a few rows: the tiled copy
+        m = bi_gemm_swiglu(x2, w["wgate_up_t"], w_layout=BI_B_TILED)
+    elif "wgate_up_i" in w:   # fused: == bi_swiglu(bi_gemm(x2, wgate_up)) bit for bit
         m = bi_gemm_swiglu(x2, w["wgate_up_i"])
     else:
         m = bi_swiglu(bi_gemm(x2, w["wgate_up"]))
@@ -242,7 +259,11 @@ def head(model, h, rows: torch.Tensor, dims: Dims, fp32_variant=False):
     act = F32 if fp32_variant else BF16
     hl = bi_embedding(rows, h, out_dtype=h.dtype)
     x = bi_rmsnorm(hl, model["final_norm"], dims.eps, out_dtype=act)
-    logits = bi_gemm(x, model["lm_head"], out_dtype=F32)
+    if "lm_head_t" in model and _tiled_ok(x.shape[0], x.shape[1], x):
+        logits = bi_gemm(x, model["lm_head_t"], b_layout=BI_B_TILED, n=model["lm_head"].shape[0],
+                         out_dtype=F32)
+    else:
+        logits = bi_gemm(x, model["lm_head"], out_dtype=F32)
     _, ids = bi_logsoftmax_argmax(logits, want_logprobs=False)
     return logits, ids
 

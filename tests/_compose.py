@@ -48,9 +48,10 @@ def _near(got64, ref64, dtype, axis=-1):
 
 
 def host_weights(w: dict) -> dict:
-    """Layer weights (device bf16 tensors) as bf16 bit arrays."""
+    """Layer weights (device bf16 tensors) as bf16 bit arrays (the re-laid-out copies of the
+    gate/up matrix left out)."""
     return {k: v.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-            for k, v in w.items() if k != "wgate_up_i"}
+            for k, v in w.items() if k not in ("wgate_up_i", "wgate_up_t")}
 
 
 def take(trace: dict, rows) -> dict:

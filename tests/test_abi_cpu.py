@@ -62,11 +62,24 @@ def test_validation_rejects_before_launch(lib):
     assert lib.bi_gemm(P, P, P, 4, 4, 8, 9, 8, 4, 1, 1, 1, None) == -4
     assert lib.bi_gemm(None, P, P, 4, 4, 8, 8, 8, 4, 1, 1, 1, None) == -1
     # fused gate/up + SwiGLU: F must be a multiple of 16; null and misaligned operands
-    assert lib.bi_gemm_swiglu(P, P, P, 4, 24, 64, 64, 64, 24, None) == -2
-    assert lib.bi_gemm_swiglu(P, P, P, 4, 32, 64, 60, 64, 32, None) == -2
-    assert lib.bi_gemm_swiglu(None, P, P, 4, 32, 64, 64, 64, 32, None) == -1
-    assert lib.bi_gemm_swiglu(P, ctypes.c_void_p(18), P, 4, 32, 64, 64, 64, 32, None) == -4
-    assert lib.bi_gemm_swiglu(None, None, None, 0, 32, 64, 64, 64, 32, None) == 0
+    assert lib.bi_gemm_swiglu(P, P, P, 4, 24, 64, 64, 64, 24, 1, None) == -2
+    assert lib.bi_gemm_swiglu(P, P, P, 4, 32, 64, 60, 64, 32, 1, None) == -2
+    assert lib.bi_gemm_swiglu(None, P, P, 4, 32, 64, 64, 64, 32, 1, None) == -1
+    assert lib.bi_gemm_swiglu(P, ctypes.c_void_p(18), P, 4, 32, 64, 64, 64, 32, 1, None) == -4
+    assert lib.bi_gemm_swiglu(None, None, None, 0, 32, 64, 64, 64, 32, 1, None) == 0
+    assert lib.bi_gemm_swiglu(P, P, P, 4, 32, 64, 64, 64, 32, 7, None) == -3     # w_layout
+    # tiled B / W: at most 16 rows, K a multiple of 8 and >= 1024, bf16 A
+    assert lib.bi_gemm(P, P, P, 17, 64, 1024, 1024, 0, 64, 2, 1, 1, None) == -6
+    assert lib.bi_gemm(P, P, P, 16, 64, 512, 512, 0, 64, 2, 1, 1, None) == -6
+    assert lib.bi_gemm(P, P, P, 16, 64, 1028, 1032, 0, 64, 2, 1, 1, None) == -6
+    assert lib.bi_gemm(P, P, P, 4, 64, 1024, 1024, 0, 64, 2, 2, 1, None) == -6    # fp32 A
+    assert lib.bi_gemm(P, None, P, 4, 64, 1024, 1024, 0, 64, 2, 1, 1, None) == -1
+    assert lib.bi_gemm_swiglu(P, P, P, 17, 32, 1024, 1024, 0, 32, 2, None) == -6
+    assert lib.bi_pack_b_bytes(33, 1000) == 3 * 32 * 1024 and lib.bi_pack_b_bytes(0, 8) == 0
+    assert lib.bi_pack_b(P, 4, 64, 32, P, None) == -2
+    assert lib.bi_pack_b(P, 4, 64, 64, ctypes.c_void_p(18), None) == -4
+    assert lib.bi_pack_b(None, 4, 64, 64, P, None) == -1
+    assert lib.bi_pack_b(None, 0, 64, 64, None, None) == 0
     # fused residual add + RMSNorm: dtype, D a multiple of 8 up to 8192, null operands
     assert lib.bi_add_rmsnorm(P, P, P, 3, P, P, 1, 4, 64, 1e-5, None) == -3
     assert lib.bi_add_rmsnorm(P, P, P, 1, P, P, 1, 4, 60, 1e-5, None) == -6

@@ -392,3 +392,48 @@ def test_gemm_swiglu_equals_unfused(lib, f, k):
     lib.bi_gemm_swiglu(A[:300], Wi, out=big[:, 1:f + 1])
     assert same_bits(big[:, 1:f + 1].contiguous(), lib.bi_swiglu(lib.bi_gemm(A[:300], W)))
     assert bool((big[:, 0] == -3.0).all()) and bool((big[:, f + 1:] == -3.0).all())
+
+
+def _pack_host(b_nk):
+    """The tiled layout of bi_pack_b written out on the host (include/bi.h, BI_B_TILED)."""
+    n, k = b_nk.shape
+    nb, nt = -(-n // 16), -(-k // 32)
+    full = np.zeros((nb * 16, nt * 32), dtype=np.uint16)
+    full[:n, :k] = b_nk
+    # [b, r, t, g, e] -> [b, t, g, r, e]: lane = r + 16 g
+    return full.reshape(nb, 16, nt, 4, 8).transpose(0, 2, 3, 1, 4).reshape(nb, nt, 64, 8)
+
+
+@pytest.mark.parametrize("n,k", [(4096, 4096), (1000, 1032), (6144, 4096), (32000, 4096),
+                                 (4096, 14336), (33, 1024)])
+def test_tiled_b_equals_nk(lib, n, k):
+    # a tiled B (bi_pack_b) at the row counts the few-row kernel takes it for: the bits of the
+    # [N, K] call, bf16 and fp32 outputs; ragged N and K (a partial last block and step)
+    from invariant_amd import BI_B_TILED
+    say("gemm tiled B", n, k)
+    a, b = gemm_inputs(16, n, k, cfg=39)
+    A, W = bf16(a), bf16(_nk(b))
+    Wt = lib.bi_pack_b(W)
+    if n * k <= 6144 * 4096:
+        assert np.array_equal(bits(Wt), _pack_host(_nk(b)))
+    for m in (1, 3, 8, 9, 16):
+        for od in (torch.bfloat16, torch.float32):
+            got = lib.bi_gemm(A[:m], Wt, b_layout=BI_B_TILED, n=n, out_dtype=od)
+            assert same_bits(got, lib.bi_gemm(A[:m], W, out_dtype=od)), (m, od)
+    r = bf16_within_1ulp(bits(lib.bi_gemm(A[:1], Wt, b_layout=BI_B_TILED, n=n)), gemm_f64(a[:1], b))
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("f,k", [(14336, 4096), (1024, 1024), (3008, 1032)])
+def test_tiled_swiglu_equals_interleaved(lib, f, k):
+    # the fused gate/up + SwiGLU on the tiled interleaved weights: the bits of the [2F, K] call
+    # (paired one-block waves up to 8 rows, two-block waves above)
+    from invariant_amd import BI_B_TILED, interleave_gate_up
+    say("gemm_swiglu tiled", f, k)
+    a, b = gemm_inputs(16, 2 * f, k, cfg=40, sd=0.5)
+    A = bf16(a)
+    Wi = interleave_gate_up(bf16(np.ascontiguousarray(b.T)))
+    Wt = lib.bi_pack_b(Wi)
+    for m in (1, 5, 8, 9, 16):
+        got = lib.bi_gemm_swiglu(A[:m], Wt, w_layout=BI_B_TILED)
+        assert same_bits(got, lib.bi_gemm_swiglu(A[:m], Wi)), m
