@@ -73,11 +73,12 @@ def random_layer(dims: Dims, gen, device="cuda", sd=0.02):
         wdown=_normal((d, dims.ffn), 0.0, sd, gen, device),
     )
     # the same gate/up rows interleaved in blocks of 16 for the fused GEMM + SwiGLU call
-    # (wgate_up keeps the gate-then-up order the reference computations read), and that
-    # interleaved matrix tiled for calls of a few rows (decode): the same bits, contiguous
-    # kilobyte loads
+    # (wgate_up keeps the gate-then-up order the reference computations read); that
+    # interleaved matrix and the QKV weights also tiled for calls of a few rows (decode):
+    # the same bits, contiguous kilobyte loads
     w["wgate_up_i"] = interleave_gate_up(w["wgate_up"])
     w["wgate_up_t"] = bi_pack_b(w["wgate_up_i"])
+    w["wqkv_t"] = bi_pack_b(w["wqkv"])
     return w
 
 
@@ -195,7 +196,10 @@ def decoder_layer(w, h, batch: Batch, k_cache, v_cache, dims: Dims, fp32_variant
     act = F32 if fp32_variant else BF16
     if x is None:
         x = bi_rmsnorm(h, w["attn_norm"], dims.eps, out_dtype=act)
-    qkv = bi_gemm(x, w["wqkv"], out_dtype=act)
+    if "wqkv_t" in w and _tiled_ok(T, x.shape[1], x):
+        qkv = bi_gemm(x, w["wqkv_t"], b_layout=BI_B_TILED, n=w["wqkv"].shape[0], out_dtype=act)
+    else:
+        qkv = bi_gemm(x, w["wqkv"], out_dtype=act)
     if trace is None:   # RoPE writes the rotated keys and the values straight into the pages
         q = bi_rope_kv_write(qkv, k_cache, v_cache, batch.block_table, batch.seq_lens, batch.qsl,
                              dims.n_q_heads, dims.rope_base, q_dtype=act)

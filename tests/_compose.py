@@ -51,7 +51,7 @@ def host_weights(w: dict) -> dict:
     """Layer weights (device bf16 tensors) as bf16 bit arrays (the re-laid-out copies of the
     gate/up matrix left out)."""
     return {k: v.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-            for k, v in w.items() if k not in ("wgate_up_i", "wgate_up_t")}
+            for k, v in w.items() if k not in ("wgate_up_i", "wgate_up_t", "wqkv_t")}
 
 
 def take(trace: dict, rows) -> dict:
