@@ -21,7 +21,7 @@ Beside the step, the same line carries:
   cpu_baseline       the oracle timed on the host (all cores and one core).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemm-set]
-                    [--gemm-sweep] [--gemm-profile M,N,K] [--model]
+                    [--gemm-sweep] [--decode-gemm] [--gemm-profile M,N,K] [--model]
 """
 from __future__ import annotations
 
@@ -332,6 +332,56 @@ def gemm_sweep(torch, bi):
     return out
 
 
+def decode_gemm(torch, bi):
+    """Decode-sized GEMMs (M = 1 and 8) on the Mistral weight shapes with every call reading
+    new weights from HBM: enough distinct weight copies are cycled that the 256 MB MALL
+    cannot hold them.  bi_gemm on the [N, K] weights and on their tiled copy (bi_pack_b),
+    the fused gate/up + SwiGLU both ways, and torch.mm (the vendor library) on the same
+    buffers as context; GB/s of weights streamed."""
+    from invariant_amd import BI_B_TILED, interleave_gate_up
+    dev = "cuda:0"
+    out = []
+    for (name, N, K) in (("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 28672, 4096),
+                         ("down", 4096, 14336), ("lm_head", 32000, 4096)):
+        copies = max(3, int(1.2e9 // (N * K * 2)) + 1)
+        Ws = [torch.randn((N, K), device=dev).to(torch.bfloat16) for _ in range(copies)]
+        if name == "gate_up":
+            Ws = [interleave_gate_up(w) for w in Ws]
+        Wts = [bi.bi_pack_b(w) for w in Ws]
+        WTs = [w.t() for w in Ws]
+        for M in (1, 8):
+            A = torch.randn((M, K), device=dev).to(torch.bfloat16)
+            if name == "gate_up":
+                C = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
+                fns = {"nk": lambda i: bi.bi_gemm_swiglu(A, Ws[i], out=C),
+                       "tiled": lambda i: bi.bi_gemm_swiglu(A, Wts[i], out=C, w_layout=BI_B_TILED)}
+            else:
+                C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                fns = {"nk": lambda i: bi.bi_gemm(A, Ws[i], out=C),
+                       "tiled": lambda i: bi.bi_gemm(A, Wts[i], out=C, b_layout=BI_B_TILED, n=N)}
+            C2 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            fns["torch_mm"] = lambda i: torch.mm(A, WTs[i], out=C2)
+            res = {}
+            for key, fn in fns.items():
+                for i in range(copies):
+                    fn(i)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 4
+                e0.record()
+                for _ in range(reps):
+                    for i in range(copies):
+                        fn(i)
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+                res[key] = dict(us=round(us, 2), weight_GBps=round(N * K * 2 / us / 1e3, 1))
+            out.append(dict(gemm=name, N=N, K=K, M=M, copies=copies, **res))
+            print(json.dumps(out[-1]), flush=True)
+            del A, C, C2
+        del Ws, Wts, WTs
+    return out
+
+
 def model_bench(torch, bi):
     """The composition rows: 32-layer Mistral-7B-shaped greedy decoding (random bf16 weights,
     std 0.02) of a 1400-token prompt alone and inside a ragged batch of 49 prompts, as in the
@@ -465,6 +515,8 @@ def main():
     ap.add_argument("--gemm-profile", metavar="M,N,K",
                     help="run bi_gemm on one shape (5 warm-up + 20 timed calls) and print its "
                          "TFLOP/s, for rocprofv3 counter runs")
+    ap.add_argument("--decode-gemm", action="store_true",
+                    help="decode-sized GEMMs on fresh weights: [N, K] vs tiled vs torch.mm")
     ap.add_argument("--model", action="store_true",
                     help="time 32-layer greedy decoding alone and in a 49-prompt batch (reported)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -483,6 +535,9 @@ def main():
 
     if args.gemm_sweep:
         gemm_sweep(torch, bi)
+        return
+    if args.decode_gemm:
+        decode_gemm(torch, bi)
         return
     if args.model:
         model_bench(torch, bi)
