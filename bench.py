@@ -533,6 +533,13 @@ def main():
     import invariant_amd as bi
     bi.load()
 
+    if args.copy_calibration:
+        src = torch.ones((1 << 29,), dtype=torch.bfloat16, device="cuda:0")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.gemm_sweep:
         gemm_sweep(torch, bi)
         return
@@ -546,13 +553,6 @@ def main():
         gemm_profile(torch, bi, [int(v) for v in args.gemm_profile.split(",")])
         return
 
-    if args.copy_calibration:
-        src = torch.ones((1 << 29,), dtype=torch.bfloat16, device="cuda:0")   # 1 GiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     log("building inputs")
     inp = build_inputs(torch, bi)
     ops = step_ops(bi, inp)
