@@ -143,6 +143,7 @@ def bi_gemm(a, b, out=None, b_layout: int = BI_B_NK, out_dtype=torch.bfloat16, n
     M, K = a.shape
     if b_layout == BI_B_TILED:
         N = n if n is not None else b.shape[0] * 16
+        _check_packed("bi_gemm", b, N, K)
         ldb = 0
     else:
         N = b.shape[0] if b_layout == BI_B_NK else b.shape[1]
@@ -152,6 +153,15 @@ def bi_gemm(a, b, out=None, b_layout: int = BI_B_NK, out_dtype=torch.bfloat16, n
     _check("bi_gemm", load().bi_gemm(_ptr(a), _ptr(b), _ptr(out), M, N, K, _ld(a), ldb, _ld(out),
                                       b_layout, _code(a.dtype), _code(out.dtype), _stream(a)))
     return out
+
+
+def _check_packed(fn, b, N, K):
+    """The kernels read ceil(N/16) x ceil(K/32) whole 1 KB tiles of a packed B: refuse a
+    tensor of another shape rather than read past it."""
+    want = ((N + 15) // 16, (K + 31) // 32, 64, 8)
+    if tuple(b.shape) != want or b.dtype != torch.bfloat16 or not b.is_contiguous():
+        raise ValueError(f"{fn}: packed B must be a contiguous bf16 tensor of shape {want} "
+                         f"(bi_pack_b of an [N, K] B), got {tuple(b.shape)} {b.dtype}")
 
 
 def bi_pack_b(b):
@@ -297,7 +307,12 @@ def bi_rope_kv_write(qkv, k_cache, v_cache, block_table, seq_lens, query_start_l
     T = qkv.shape[0]
     Hkv, D, page = k_cache.shape[1], v_cache.shape[2], v_cache.shape[3]
     B, max_pages = block_table.shape
+    if qkv.shape[1] != (num_q_heads + 2 * Hkv) * D:
+        raise ValueError(f"bi_rope_kv_write: qkv rows hold {qkv.shape[1]} values, not "
+                         f"(num_q_heads + 2 Hkv) D = {(num_q_heads + 2 * Hkv) * D}")
     q = q if q is not None else torch.empty((T, num_q_heads, D), dtype=q_dtype, device=qkv.device)
+    if tuple(q.shape) != (T, num_q_heads, D) or not q.is_contiguous():
+        raise ValueError(f"bi_rope_kv_write: q must be a contiguous [{T}, {num_q_heads}, {D}] tensor")
     _check("bi_rope_kv_write", load().bi_rope_kv_write(
         _ptr(qkv), _ld(qkv), _code(qkv.dtype), _ptr(q), _code(q.dtype), _ptr(k_cache), _ptr(v_cache),
         _ptr(block_table), _ptr(seq_lens), _ptr(query_start_loc), B, T, num_q_heads, Hkv, D, page,
@@ -326,6 +341,7 @@ def bi_gemm_swiglu(a, w_interleaved, out=None, w_layout: int = BI_B_NK):
     M, K = a.shape
     if w_layout == BI_B_TILED:
         F = w_interleaved.shape[0] * 16 // 2
+        _check_packed("bi_gemm_swiglu", w_interleaved, 2 * F, K)
         ldw = 0
     else:
         F = w_interleaved.shape[0] // 2

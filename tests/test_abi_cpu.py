@@ -199,3 +199,31 @@ def test_abi_from_plain_c(lib, tmp_path):
     assert build.returncode == 0, build.stderr
     run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0 and run.stdout.strip() == "ok", (run.stdout, run.stderr)
+
+
+def test_binding_rejects_mismatched_shapes():
+    # host-side shape checks of the binding, raised before any pointer reaches the library:
+    # a packed B whose tile grid does not match (N, K), and a fused q/k/v row of the wrong
+    # width for bi_rope_kv_write
+    import torch
+    a = torch.zeros((2, 1024), dtype=torch.bfloat16)
+    good = torch.zeros((4, 32, 64, 8), dtype=torch.bfloat16)          # N = 64, K = 1024
+    for bad in (torch.zeros((4, 31, 64, 8), dtype=torch.bfloat16),    # too few K steps
+                torch.zeros((4, 32, 64, 8), dtype=torch.float32),
+                good.transpose(0, 1)):
+        with pytest.raises(ValueError, match="packed B"):
+            bi.bi_gemm(a, bad, b_layout=bi.BI_B_TILED, n=64)
+        with pytest.raises(ValueError, match="packed B"):
+            bi.bi_gemm_swiglu(a, bad, w_layout=bi.BI_B_TILED)
+    with pytest.raises(ValueError, match="packed B"):
+        bi.bi_gemm(a, good, b_layout=bi.BI_B_TILED, n=65)             # 5 row blocks needed
+    kc = torch.zeros((2, 2, 16, 16, 8), dtype=torch.bfloat16)         # [P, Hkv, D/8, page, 8]
+    vc = torch.zeros((2, 2, 128, 16), dtype=torch.bfloat16)           # [P, Hkv, D, page]
+    bt = torch.zeros((1, 2), dtype=torch.int32)
+    sl = torch.ones(1, dtype=torch.int32)
+    qsl = torch.tensor([0, 1], dtype=torch.int32)
+    with pytest.raises(ValueError, match="qkv rows"):
+        bi.bi_rope_kv_write(torch.zeros((1, 7 * 128), dtype=torch.bfloat16), kc, vc, bt, sl, qsl, 4)
+    with pytest.raises(ValueError, match="contiguous"):
+        bi.bi_rope_kv_write(torch.zeros((1, 8 * 128), dtype=torch.bfloat16), kc, vc, bt, sl, qsl, 4,
+                            q=torch.zeros((1, 4, 64), dtype=torch.bfloat16))
