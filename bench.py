@@ -333,7 +333,7 @@ def gemm_sweep(torch, bi):
 
 
 def decode_gemm(torch, bi):
-    """Decode-sized GEMMs (M = 1 and 8) on the Mistral weight shapes with every call reading
+    """Decode-sized GEMMs (M = 1, 8 and 49) on the Mistral weight shapes with every call reading
     new weights from HBM: enough distinct weight copies are cycled that the 256 MB MALL
     cannot hold them.  bi_gemm on the [N, K] weights and on their tiled copy (bi_pack_b),
     the fused gate/up + SwiGLU both ways, and torch.mm (the vendor library) on the same
@@ -349,7 +349,7 @@ def decode_gemm(torch, bi):
             Ws = [interleave_gate_up(w) for w in Ws]
         Wts = [bi.bi_pack_b(w) for w in Ws]
         WTs = [w.t() for w in Ws]
-        for M in (1, 8):
+        for M in (1, 8, 49):
             A = torch.randn((M, K), device=dev).to(torch.bfloat16)
             if name == "gate_up":
                 C = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)

@@ -120,8 +120,10 @@ int bi_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t D, 
  *   B     bf16; b_layout BI_B_NK: B is [N, K] (a Linear weight, C = A . B^T), row
  *         stride ldb;  BI_B_KN: B is [K, N] (torch.mm orientation), row stride ldb;
  *         BI_B_TILED: an [N, K] B as bi_pack_b wrote it (ldb unused), for calls of at most
- *         16 rows with K a multiple of 8 and at least 1024 (the few-row kernel's calls;
- *         other calls return BI_ERR_UNSUPPORTED) -- the same bits as BI_B_NK
+ *         64 rows with K a multiple of 8 and at least 1024 (the few-row kernel's calls;
+ *         other calls return BI_ERR_UNSUPPORTED) -- the same bits as BI_B_NK.  Above 32
+ *         rows with more 32-column blocks than the device has CUs the [N, K] call, which
+ *         takes the LDS-staged tiles there, is the faster one
  *   C     dtype c_dtype (BI_BF16: one RNE rounding of the fp32 sum; BI_F32), stride ldc
  * Every output element is produced by the same sequence of matrix instructions
  * (v_mfma_f32_16x16x32_bf16, one fp32 accumulator from +0, K in ascending 32-wide steps,
@@ -358,7 +360,7 @@ int bi_swiglu(const void* gu, int64_t ldgu, void* out, int64_t T, int64_t F, voi
  *   bi_swiglu(bi_gemm(A, W_gate_up)) bit for bit without writing the [M, 2F] intermediate.
  *   A [M, K] bf16 (row stride lda), W row stride ldw, out row stride ldo (bf16).
  *   w_layout BI_B_NK: W as above; BI_B_TILED: bi_pack_b of that [2F, K] W (ldw unused; at
- *   most 16 rows, K a multiple of 8 and at least 1024), the same bits.
+ *   most 64 rows, K a multiple of 8 and at least 1024), the same bits.
  *   Errors: BI_ERR_DTYPE (w_layout), BI_ERR_NULL, BI_ERR_SHAPE (F not a multiple of 16,
  *   strides too small), BI_ERR_ALIGN (16-byte pointers, lda and ldw multiples of 8),
  *   BI_ERR_UNSUPPORTED (A or W spanning 4 GiB or more: use bi_gemm and bi_swiglu; a tiled W

@@ -846,7 +846,12 @@ TileKind pick_tile(int64_t M, int64_t N, int cus) {
   const int64_t n256 = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t n128 = ((M + 127) / 128) * ((N + 127) / 128);
   if (n128 <= cus) {
-    // one round or less: the largest tile whose grid still covers three quarters of the CUs
+    // one round or less: the largest tile whose grid still covers three quarters of the CUs;
+    // up to 64 rows (which reach these tiles only when N is too wide for the few-row kernel)
+    // the 64 x 64 tile, whose grid of up to twice the CUs streams the weights faster
+    // (measured at 33..64 x 28672 x 4096 and x 32000 x 4096: 0.92-1.01 of the time of the
+    // 128 x 128 tile)
+    if (M <= 64) return TileKind::k64;
     const int64_t n64x128 = ((M + 63) / 64) * ((N + 127) / 128);
     if (4 * n128 >= 3 * cus) return TileKind::k128deep;
     if (4 * n64x128 >= 3 * cus) return TileKind::k64x128;
@@ -1196,11 +1201,16 @@ void launch_rows_t(const void* A, const void* B, void* C, int64_t M, int64_t N, 
       lda, ldb, ldc, cf, split, sk.k_split ? sk.k_split : int(K), sk.stride);
 }
 
-// The few-row kernel on a tiled B (bi_pack_b): the configurations of up to 16 rows.
+// The few-row kernel on a tiled B (bi_pack_b), in the configuration rows_cfg gives (for
+// 33..64 rows also on grids wider than the CUs, which on an [N, K] B go to the LDS-staged
+// tiles).
 void launch_rows_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                        int64_t lda, int64_t ldc, int cf, hipStream_t s) {
   const RowsCfg c = rows_cfg(M, N, cf);
   if (c.pair) launch_rows_t<1, 1, 16, true, true>(A, B, C, M, N, K, lda, 0, ldc, cf, 1, s);
+  else if (c.rb == 4) launch_rows_t<4, 2, 12, false, true>(A, B, C, M, N, K, lda, 0, ldc, cf, 1, s);
+  else if (c.rb == 2) launch_rows_t<2, 2, 12, false, true>(A, B, C, M, N, K, lda, 0, ldc, cf, c.split, s);
+  else if (c.split > 1) launch_rows_t<1, 2, 12, false, true>(A, B, C, M, N, K, lda, 0, ldc, cf, c.split, s);
   else if (c.cb == 2) launch_rows_t<1, 2, 16, false, true>(A, B, C, M, N, K, lda, 0, ldc, cf, 1, s);
   else launch_rows_t<1, 1, 16, false, true>(A, B, C, M, N, K, lda, 0, ldc, cf, 1, s);
 }
@@ -1221,9 +1231,9 @@ __global__ void pack_b_kernel(const uint16_t* __restrict__ B, int64_t N, int64_t
   *reinterpret_cast<u16x8*>(out + i * 8) = v;
 }
 
-// A tiled B goes with calls of at most 16 rows that the few-row kernel takes (K a multiple
-// of 8 with at least 32 whole 32-wide steps).
-bool tiled_ok(int64_t M, int64_t K) { return M <= 16 && K % 8 == 0 && K / 32 >= 32; }
+// A tiled B goes with calls of at most 64 rows that the few-row kernel takes (K a multiple
+// of 8 with at least 32 whole 32-wide steps, which covers every configuration's 2 PF).
+bool tiled_ok(int64_t M, int64_t K) { return M <= 64 && K % 8 == 0 && K / 32 >= 32; }
 
 void launch_rows(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                  int64_t lda, int64_t ldb, int64_t ldc, int cf, hipStream_t s, KSplit sk = {}) {

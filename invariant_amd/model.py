@@ -72,13 +72,21 @@ def random_layer(dims: Dims, gen, device="cuda", sd=0.02):
         wgate_up=_normal((2 * dims.ffn, d), 0.0, sd, gen, device),
         wdown=_normal((d, dims.ffn), 0.0, sd, gen, device),
     )
-    # the same gate/up rows interleaved in blocks of 16 for the fused GEMM + SwiGLU call
-    # (wgate_up keeps the gate-then-up order the reference computations read); that
-    # interleaved matrix and the QKV weights also tiled for calls of a few rows (decode):
-    # the same bits, contiguous kilobyte loads
+    return with_derived_weights(w)
+
+
+# Copies of a layer's weights in other layouts, made from its [N, K] matrices: the gate/up
+# rows interleaved in blocks of 16 for the fused GEMM + SwiGLU call (wgate_up keeps the
+# gate-then-up order the reference computations read), and every projection tiled
+# (bi_pack_b) for calls of a few rows -- the same bits, contiguous kilobyte loads.
+DERIVED = ("wgate_up_i", "wqkv_t", "wo_t", "wgate_up_t", "wdown_t")
+
+
+def with_derived_weights(w: dict) -> dict:
     w["wgate_up_i"] = interleave_gate_up(w["wgate_up"])
     w["wgate_up_t"] = bi_pack_b(w["wgate_up_i"])
-    w["wqkv_t"] = bi_pack_b(w["wqkv"])
+    for k in ("wqkv", "wo", "wdown"):
+        w[k + "_t"] = bi_pack_b(w[k])
     return w
 
 
@@ -99,10 +107,39 @@ def _with_tiled_head(model):
     return model
 
 
-def _tiled_ok(rows: int, k: int, a: torch.Tensor) -> bool:
-    """The calls a tiled weight serves (include/bi.h, BI_B_TILED): at most 16 rows of bf16 A,
-    K a multiple of 8 and at least 1024."""
-    return rows <= 16 and k % 8 == 0 and k >= 1024 and a.dtype == BF16
+_CUS = {}
+
+
+def _cus(dev) -> int:
+    if dev not in _CUS:
+        _CUS[dev] = torch.cuda.get_device_properties(dev).multi_processor_count
+    return _CUS[dev]
+
+
+def _tiled_ok(a: torch.Tensor, n: int) -> bool:
+    """Whether an [M, K] x [N, K]^T call reads the tiled copy of its weight.  A tiled B
+    serves the few-row kernel (include/bi.h, BI_B_TILED: at most 64 rows of bf16 A, K a
+    multiple of 8 and at least 1024); among those calls it is the faster operand except
+    (measured on MI355X with the weights streamed from HBM, Mistral-7B shapes, same bits
+    either way) above 32 rows on grids of more 32-column blocks than CUs, where the [N, K]
+    weight goes to the 128 x 128 tiles (gate/up, LM head at 49 rows: 51 and 61 us against
+    68 and 71), and up to 16 rows when one 16-column block per wave leaves at most one wave
+    per CU (O and down at 16 rows: 10.1 and 29.7 us against 11.3 and 31.7)."""
+    m, k = a.shape
+    if m > 64 or k % 8 or k < 1024 or a.dtype != BF16:
+        return False
+    cus = _cus(a.device)
+    if m > 32:
+        return (n + 31) // 32 <= cus
+    return m > 16 or (n + 15) // 16 > cus
+
+
+def _linear(x: torch.Tensor, w: dict, name: str, out_dtype) -> torch.Tensor:
+    """x @ w[name]^T, from the tiled copy w[name + "_t"] where there is one and it pays."""
+    n = w[name].shape[0]
+    if name + "_t" in w and _tiled_ok(x, n):
+        return bi_gemm(x, w[name + "_t"], b_layout=BI_B_TILED, n=n, out_dtype=out_dtype)
+    return bi_gemm(x, w[name], out_dtype=out_dtype)
 
 
 # ------------------------------------------------------------------------- KV cache
@@ -196,10 +233,7 @@ def decoder_layer(w, h, batch: Batch, k_cache, v_cache, dims: Dims, fp32_variant
     act = F32 if fp32_variant else BF16
     if x is None:
         x = bi_rmsnorm(h, w["attn_norm"], dims.eps, out_dtype=act)
-    if "wqkv_t" in w and _tiled_ok(T, x.shape[1], x):
-        qkv = bi_gemm(x, w["wqkv_t"], b_layout=BI_B_TILED, n=w["wqkv"].shape[0], out_dtype=act)
-    else:
-        qkv = bi_gemm(x, w["wqkv"], out_dtype=act)
+    qkv = _linear(x, w, "wqkv", act)
     if trace is None:   # RoPE writes the rotated keys and the values straight into the pages
         q = bi_rope_kv_write(qkv, k_cache, v_cache, batch.block_table, batch.seq_lens, batch.qsl,
                              dims.n_q_heads, dims.rope_base, q_dtype=act)
@@ -210,19 +244,19 @@ def decoder_layer(w, h, batch: Batch, k_cache, v_cache, dims: Dims, fp32_variant
     a = bi_attention(q, k, v, k_cache, v_cache, batch.block_table, batch.seq_lens, batch.qsl,
                      batch.max_seq_len, 1.0 / float(np.sqrt(dims.head_dim)), out_dtype=act,
                      workspace=batch.workspace)
-    o = bi_gemm(a.view(T, dims.n_q_heads * dims.head_dim), w["wo"], out_dtype=act)
+    o = _linear(a.view(T, dims.n_q_heads * dims.head_dim), w, "wo", act)
     if _fusable(h, o, dims):
         h2, x2 = bi_add_rmsnorm(h, o, w["ffn_norm"], dims.eps, out_dtype=BF16)
     else:
         h2 = bi_residual_add(h, o, out_dtype=act)
         x2 = bi_rmsnorm(h2, w["ffn_norm"], dims.eps, out_dtype=BF16)
-    if "wgate_up_t" in w and _tiled_ok(T, x2.shape[1], x2):   # a few rows: the tiled copy
+    if "wgate_up_t" in w and _tiled_ok(x2, w["wgate_up"].shape[0]):   # a few rows: the tiled copy
         m = bi_gemm_swiglu(x2, w["wgate_up_t"], w_layout=BI_B_TILED)
     elif "wgate_up_i" in w:   # fused: == bi_swiglu(bi_gemm(x2, wgate_up)) bit for bit
         m = bi_gemm_swiglu(x2, w["wgate_up_i"])
     else:
         m = bi_swiglu(bi_gemm(x2, w["wgate_up"]))
-    dn = bi_gemm(m, w["wdown"])
+    dn = _linear(m, w, "wdown", BF16)
     if next_norm is None:
         res = bi_residual_add(h2, dn, out_dtype=act)
         h3, x3 = res, None
@@ -263,11 +297,7 @@ def head(model, h, rows: torch.Tensor, dims: Dims, fp32_variant=False):
     act = F32 if fp32_variant else BF16
     hl = bi_embedding(rows, h, out_dtype=h.dtype)
     x = bi_rmsnorm(hl, model["final_norm"], dims.eps, out_dtype=act)
-    if "lm_head_t" in model and _tiled_ok(x.shape[0], x.shape[1], x):
-        logits = bi_gemm(x, model["lm_head_t"], b_layout=BI_B_TILED, n=model["lm_head"].shape[0],
-                         out_dtype=F32)
-    else:
-        logits = bi_gemm(x, model["lm_head"], out_dtype=F32)
+    logits = _linear(x, model, "lm_head", F32)
     _, ids = bi_logsoftmax_argmax(logits, want_logprobs=False)
     return logits, ids
 

@@ -17,6 +17,7 @@ inference", section on making kernels batch-invariant: the layer is its operatio
 import numpy as np
 import torch
 
+from invariant_amd.model import DERIVED
 from oracle import fp
 from oracle.check import bf16_within_1ulp, bits_equal, f32_within_rel, swiglu_interval_within
 from oracle.layer import Spec, op_attention, op_gemm, op_rmsnorm, op_rope_qkv, store, swiglu_f64
@@ -51,7 +52,7 @@ def host_weights(w: dict) -> dict:
     """Layer weights (device bf16 tensors) as bf16 bit arrays (the re-laid-out copies of the
     gate/up matrix left out)."""
     return {k: v.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-            for k, v in w.items() if k not in ("wgate_up_i", "wgate_up_t", "wqkv_t")}
+            for k, v in w.items() if k not in DERIVED}
 
 
 def take(trace: dict, rows) -> dict:

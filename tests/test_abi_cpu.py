@@ -68,13 +68,13 @@ def test_validation_rejects_before_launch(lib):
     assert lib.bi_gemm_swiglu(P, ctypes.c_void_p(18), P, 4, 32, 64, 64, 64, 32, 1, None) == -4
     assert lib.bi_gemm_swiglu(None, None, None, 0, 32, 64, 64, 64, 32, 1, None) == 0
     assert lib.bi_gemm_swiglu(P, P, P, 4, 32, 64, 64, 64, 32, 7, None) == -3     # w_layout
-    # tiled B / W: at most 16 rows, K a multiple of 8 and >= 1024, bf16 A
-    assert lib.bi_gemm(P, P, P, 17, 64, 1024, 1024, 0, 64, 2, 1, 1, None) == -6
+    # tiled B / W: at most 64 rows, K a multiple of 8 and >= 1024, bf16 A
+    assert lib.bi_gemm(P, P, P, 65, 64, 1024, 1024, 0, 64, 2, 1, 1, None) == -6
     assert lib.bi_gemm(P, P, P, 16, 64, 512, 512, 0, 64, 2, 1, 1, None) == -6
     assert lib.bi_gemm(P, P, P, 16, 64, 1028, 1032, 0, 64, 2, 1, 1, None) == -6
     assert lib.bi_gemm(P, P, P, 4, 64, 1024, 1024, 0, 64, 2, 2, 1, None) == -6    # fp32 A
     assert lib.bi_gemm(P, None, P, 4, 64, 1024, 1024, 0, 64, 2, 1, 1, None) == -1
-    assert lib.bi_gemm_swiglu(P, P, P, 17, 32, 1024, 1024, 0, 32, 2, None) == -6
+    assert lib.bi_gemm_swiglu(P, P, P, 65, 32, 1024, 1024, 0, 32, 2, None) == -6
     assert lib.bi_pack_b_bytes(33, 1000) == 3 * 32 * 1024 and lib.bi_pack_b_bytes(0, 8) == 0
     assert lib.bi_pack_b(P, 4, 64, 32, P, None) == -2
     assert lib.bi_pack_b(P, 4, 64, 64, ctypes.c_void_p(18), None) == -4

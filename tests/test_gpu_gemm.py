@@ -407,16 +407,20 @@ def _pack_host(b_nk):
 @pytest.mark.parametrize("n,k", [(4096, 4096), (1000, 1032), (6144, 4096), (32000, 4096),
                                  (4096, 14336), (33, 1024)])
 def test_tiled_b_equals_nk(lib, n, k):
-    # a tiled B (bi_pack_b) at the row counts the few-row kernel takes it for: the bits of the
-    # [N, K] call, bf16 and fp32 outputs; ragged N and K (a partial last block and step)
+    # a tiled B (bi_pack_b) at the row counts the few-row kernel takes it for (up to 64): the
+    # bits of the [N, K] call, bf16 and fp32 outputs; ragged N and K (a partial last block and
+    # step)
     from invariant_amd import BI_B_TILED
     say("gemm tiled B", n, k)
-    a, b = gemm_inputs(16, n, k, cfg=39)
+    a, b = gemm_inputs(64, n, k, cfg=39)
     A, W = bf16(a), bf16(_nk(b))
     Wt = lib.bi_pack_b(W)
     if n * k <= 6144 * 4096:
         assert np.array_equal(bits(Wt), _pack_host(_nk(b)))
-    for m in (1, 3, 8, 9, 16):
+    # every few-row configuration: one- and two-block waves, 16-row slices, 32 x 32 and
+    # 64 x 32 blocks (above 32 rows on grids wider than the CUs the [N, K] call takes the
+    # LDS-staged tiles instead: same bits)
+    for m in (1, 3, 8, 9, 16, 17, 24, 32, 33, 49, 64):
         for od in (torch.bfloat16, torch.float32):
             got = lib.bi_gemm(A[:m], Wt, b_layout=BI_B_TILED, n=n, out_dtype=od)
             assert same_bits(got, lib.bi_gemm(A[:m], W, out_dtype=od)), (m, od)
@@ -427,13 +431,14 @@ def test_tiled_b_equals_nk(lib, n, k):
 @pytest.mark.parametrize("f,k", [(14336, 4096), (1024, 1024), (3008, 1032)])
 def test_tiled_swiglu_equals_interleaved(lib, f, k):
     # the fused gate/up + SwiGLU on the tiled interleaved weights: the bits of the [2F, K] call
-    # (paired one-block waves up to 8 rows, two-block waves above)
+    # (paired one-block waves up to 8 rows, two-block waves above, 32 x 32 and 64 x 32 blocks
+    # from 17 rows)
     from invariant_amd import BI_B_TILED, interleave_gate_up
     say("gemm_swiglu tiled", f, k)
-    a, b = gemm_inputs(16, 2 * f, k, cfg=40, sd=0.5)
+    a, b = gemm_inputs(64, 2 * f, k, cfg=40, sd=0.5)
     A = bf16(a)
     Wi = interleave_gate_up(bf16(np.ascontiguousarray(b.T)))
     Wt = lib.bi_pack_b(Wi)
-    for m in (1, 5, 8, 9, 16):
+    for m in (1, 5, 8, 9, 16, 17, 32, 33, 49, 64):
         got = lib.bi_gemm_swiglu(A[:m], Wt, w_layout=BI_B_TILED)
         assert same_bits(got, lib.bi_gemm_swiglu(A[:m], Wi)), m

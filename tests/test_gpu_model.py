@@ -12,8 +12,8 @@ import pytest
 import torch
 
 import synth
-from invariant_amd.model import (Batch, Dims, PagedKVCache, decoder_layer, greedy_generate,
-                                 random_model)
+from invariant_amd.model import (DERIVED, Batch, Dims, PagedKVCache, decoder_layer, greedy_generate,
+                                 random_model, with_derived_weights)
 from oracle import fp
 from oracle.layer import model_ref_logits
 from tests._attn import k_slot
@@ -52,10 +52,7 @@ def _cfg3_setup():
     dims = Dims(n_layers=1)
     wb = synth.layer_weights(cfg=3)
     w = {k: bf16(v) for k, v in wb.items()}
-    from invariant_amd import bi_pack_b, interleave_gate_up
-    w["wgate_up_i"] = interleave_gate_up(w["wgate_up"])
-    w["wgate_up_t"] = bi_pack_b(w["wgate_up_i"])   # batches of up to 16 tokens read these
-    w["wqkv_t"] = bi_pack_b(w["wqkv"])
+    with_derived_weights(w)   # batches of up to 64 tokens read the tiled copies
     R = 256
     ctx = synth.ragged_lengths(R, 0, 4096, 3, 1)
     h = synth.normal_bf16((R, 4096), 0.0, 1.0, 3, 2)
@@ -184,7 +181,7 @@ def test_model_small_per_op_and_drift(lib, fp32_variant):
     forced = [int(np.argmax(g)) for g in got[:-1]]
     wts = dict(embed=bits(model["embed"]), final_norm=bits(model["final_norm"]),
                lm_head=bits(model["lm_head"]),
-               layers=[{k: bits(v) for k, v in L.items() if k not in ("wgate_up_i", "wgate_up_t", "wqkv_t")} for L in model["layers"]])
+               layers=[{k: bits(v) for k, v in L.items() if k not in DERIVED} for L in model["layers"]])
     ref = model_ref_logits(prompt, forced, wts, fp32_variant=fp32_variant)
     rep = logit_drift_report(got.astype(np.float64), ref)
     say("small model logit drift", fp32_variant, rep)
@@ -227,7 +224,7 @@ def test_cfg5_teacher_forced_drift_report(lib, fp32_variant):
     got = host(lg[0]).astype(np.float64)
     wts = dict(embed=bits(model["embed"]), final_norm=bits(model["final_norm"]),
                lm_head=bits(model["lm_head"]),
-               layers=[{k: bits(v) for k, v in L.items() if k not in ("wgate_up_i", "wgate_up_t", "wqkv_t")} for L in model["layers"]])
+               layers=[{k: bits(v) for k, v in L.items() if k not in DERIVED} for L in model["layers"]])
     del model
     t0 = time.time()
     ref = model_ref_logits(prompt, tok[0][:63], wts, fp32_variant=fp32_variant, one_pass=True)
