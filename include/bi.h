@@ -397,6 +397,34 @@ int bi_residual_add(const void* a, int a_dtype, const void* b, int b_dtype, void
 int bi_add_rmsnorm(const void* a, const void* b, void* sum, int dtype, const void* gamma, void* y,
                    int y_dtype, int64_t M, int64_t D, float eps, void* stream);
 
+/* bi_add_rmsnorm_gemm, bi_add_rmsnorm_gemm_swiglu: the residual add, the RMSNorm after it
+ *   and the projection that reads the normalised rows in one launch, for calls of a few rows
+ *   (greedy decode), where each launch costs more than its bytes ("Defeating nondeterminism
+ *   in LLM inference", section on batch-invariant RMSNorm: each row keeps its own fixed
+ *   reduction; pointwise work fused with its neighbours).  Every workgroup replays the row's
+ *   tree (bi_add_rmsnorm's, bf16) and multiplies the normalised bf16 rows from LDS, so
+ *     sum = a + b                         equals bi_add_rmsnorm's sum,
+ *     C   = rmsnorm(sum) . W^T            equals bi_gemm of bi_add_rmsnorm's y (c_dtype),
+ *     out = swiglu(rmsnorm(sum) . W^T)    equals bi_gemm_swiglu of that y,
+ *   bit for bit, without writing or re-reading y.
+ *   a, b, sum [M, K] bf16, rows contiguous (stride K); sum must not overlap a or b (one
+ *   workgroup writes it while the others read them); gamma bf16 [K]; W as in bi_gemm (N rows)
+ *   or bi_gemm_swiglu (2F interleaved rows): w_layout BI_B_NK with row stride ldw, or
+ *   BI_B_TILED (ldw unused); C [M, N] (c_dtype BI_BF16 | BI_F32), out [M, F] bf16, row
+ *   strides ldc / ldo.
+ *   Supported: 1 <= M <= 4, K a multiple of 8 with 1024 <= K <= 4096 (the normalised rows
+ *   sit in at most 32 KB of LDS); otherwise BI_ERR_UNSUPPORTED (use bi_add_rmsnorm and the
+ *   projection).
+ *   Errors: BI_ERR_DTYPE (w_layout, c_dtype), BI_ERR_SHAPE (strides too small, F not a
+ *   multiple of 16, sum overlapping a or b), BI_ERR_NULL, BI_ERR_ALIGN (16-byte pointers,
+ *   ldw a multiple of 8), BI_ERR_UNSUPPORTED. */
+int bi_add_rmsnorm_gemm(const void* a, const void* b, void* sum, const void* gamma, float eps,
+                        const void* W, void* C, int64_t M, int64_t N, int64_t K, int64_t ldw,
+                        int64_t ldc, int w_layout, int c_dtype, void* stream);
+int bi_add_rmsnorm_gemm_swiglu(const void* a, const void* b, void* sum, const void* gamma, float eps,
+                               const void* W, void* out, int64_t M, int64_t F, int64_t K,
+                               int64_t ldw, int64_t ldo, int w_layout, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

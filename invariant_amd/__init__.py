@@ -49,6 +49,10 @@ _SIGS = {
     "bi_pack_b_bytes": (_SZ, [_I64, _I64]),
     "bi_pack_b": (_c.c_int, [_P, _I64, _I64, _I64, _P, _P]),
     "bi_add_rmsnorm": (_c.c_int, [_P, _P, _P, _c.c_int, _P, _P, _c.c_int, _I64, _I64, _c.c_float, _P]),
+    "bi_add_rmsnorm_gemm": (_c.c_int, [_P, _P, _P, _P, _c.c_float, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                       _c.c_int, _c.c_int, _P]),
+    "bi_add_rmsnorm_gemm_swiglu": (_c.c_int, [_P, _P, _P, _P, _c.c_float, _P, _P, _I64, _I64, _I64, _I64,
+                                              _I64, _c.c_int, _P]),
     "bi_residual_add": (_c.c_int, [_P, _c.c_int, _P, _c.c_int, _P, _c.c_int, _I64, _P]),
 }
 EXPORTS = tuple(_SIGS)
@@ -359,6 +363,52 @@ def bi_residual_add(a, b, out=None, out_dtype=None):
     _check("bi_residual_add", load().bi_residual_add(_ptr(a), _code(a.dtype), _ptr(b), _code(b.dtype),
                                                       _ptr(out), _code(out.dtype), a.numel(), _stream(a)))
     return out
+
+
+def _norm_gemm_operands(fn, a, b, sum_out, w, w_layout, n_out, K):
+    M = a.shape[0]
+    if sum_out is None:
+        sum_out = torch.empty_like(a)
+    for t in (a, b, sum_out):
+        if t.shape != (M, K) or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{fn}: a, b and the sum must be contiguous bf16 [M, K]")
+    if w_layout == BI_B_TILED:
+        _check_packed(fn, w, n_out, K)
+        return sum_out, 0
+    return sum_out, _ld(w)
+
+
+def bi_add_rmsnorm_gemm(a, b, gamma, eps: float, w, w_layout: int = BI_B_NK, n=None,
+                        out_dtype=torch.bfloat16, sum_out=None, out=None):
+    """(s, C): s = a + b and C = rmsnorm(s) @ W^T in one call, the bits of bi_add_rmsnorm
+    followed by bi_gemm (at most 4 rows of contiguous bf16 a, b; W [N, K], or with
+    BI_B_TILED its bi_pack_b copy and N = n)."""
+    M, K = a.shape
+    N = (n if n is not None else w.shape[0] * 16) if w_layout == BI_B_TILED else w.shape[0]
+    sum_out, ldw = _norm_gemm_operands("bi_add_rmsnorm_gemm", a, b, sum_out, w, w_layout, N, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check("bi_add_rmsnorm_gemm", load().bi_add_rmsnorm_gemm(
+        _ptr(a), _ptr(b), _ptr(sum_out), _ptr(gamma), float(eps), _ptr(w), _ptr(out), M, N, K, ldw,
+        _ld(out), w_layout, _code(out.dtype), _stream(a)))
+    return sum_out, out
+
+
+def bi_add_rmsnorm_gemm_swiglu(a, b, gamma, eps: float, w_interleaved, w_layout: int = BI_B_NK,
+                               sum_out=None, out=None):
+    """(s, m): s = a + b and m = swiglu(rmsnorm(s) @ W^T) with W as interleave_gate_up(W) (or
+    its bi_pack_b copy), the bits of bi_add_rmsnorm followed by bi_gemm_swiglu (at most 4
+    rows)."""
+    M, K = a.shape
+    F = w_interleaved.shape[0] * (16 if w_layout == BI_B_TILED else 1) // 2
+    sum_out, ldw = _norm_gemm_operands("bi_add_rmsnorm_gemm_swiglu", a, b, sum_out, w_interleaved,
+                                       w_layout, 2 * F, K)
+    if out is None:
+        out = torch.empty((M, F), dtype=torch.bfloat16, device=a.device)
+    _check("bi_add_rmsnorm_gemm_swiglu", load().bi_add_rmsnorm_gemm_swiglu(
+        _ptr(a), _ptr(b), _ptr(sum_out), _ptr(gamma), float(eps), _ptr(w_interleaved), _ptr(out), M, F,
+        K, ldw, _ld(out), w_layout, _stream(a)))
+    return sum_out, out
 
 
 def bi_add_rmsnorm(a, b, gamma, eps: float, sum_out=None, out=None, out_dtype=torch.bfloat16):

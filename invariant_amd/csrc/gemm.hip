@@ -31,7 +31,7 @@
 // split exactly into bf16 hi + mid + lo (truncations, so hi + mid + lo == a for normal
 // numbers) and the three products are accumulated into the same fp32 accumulator in
 // the order hi, mid, lo for every 32-wide K step.
-#include "bi_common.h"
+#include "contract_fp.h"   // (includes bi_common.h) rms_scale of the fused RMSNorm
 
 namespace bi {
 namespace {
@@ -863,6 +863,97 @@ TileKind pick_tile(int64_t M, int64_t N, int cus) {
   return cost256 < cost128 ? TileKind::k256 : TileKind::k128;
 }
 
+// The residual add and RMSNorm in front of the few-row kernel (NORM): the kernel's A is the
+// first addend a [M, K] (rows contiguous), b the second, s = a + b goes to `sum` (workgroup 0
+// writes it), and the instruction's A operand is y = rmsnorm(s) with gamma, staged in LDS.
+constexpr int kNormRows = 4;   // rows of a NORM call (4 x 4096: 32 KB of LDS per workgroup)
+struct NormArgs {
+  const uint16_t* b = nullptr;
+  const uint16_t* gamma = nullptr;
+  uint16_t* sum = nullptr;
+  float eps = 0.f;
+};
+
+// The normalised rows of a NORM kernel, bf16 in LDS (row m at m Ks, zeros from K to Kp), with the
+// bits of bi_add_rmsnorm: s = bf16(a + b); thread t of the 256 is tree lane t (T = min(256,
+// K/8) lanes) and adds the squares of its 8-element vectors t, t + T (NV of them at most) in
+// ascending order from +0; each wave's butterfly gives its tree wave's sum, and the four are
+// combined as (w0 + w1) + (w2 + w3); r = rms_scale(sum, K, eps); y = (s r) g rounded once.
+// Workgroup 0 also writes s to the sum output.  norm_load issues every load of the rows and
+// of gamma (a slot past the row reads vector 0 and adds +0, which leaves a sum of squares
+// unchanged), so they are all in flight together; norm_store waits for them.
+template <int NV>
+struct NormRows {
+  int v[NV];
+  bool ok[NV];
+  u16x8 g[NV], a[kNormRows][NV], b[kNormRows][NV];
+  __device__ void load(const uint16_t* __restrict__ pa, const NormArgs& na, int M, int K) {
+    const int t = threadIdx.x, nvec = K / 8, T = min(256, nvec);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int vv = t + j * T;
+      ok[j] = t < T && vv < nvec;
+      v[j] = ok[j] ? vv : 0;
+      g[j] = *reinterpret_cast<const u16x8*>(na.gamma + 8 * v[j]);
+    }
+#pragma unroll
+    for (int m = 0; m < kNormRows; ++m)
+      if (m < M) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          a[m][j] = *reinterpret_cast<const u16x8*>(pa + static_cast<int64_t>(m) * K + 8 * v[j]);
+          b[m][j] = *reinterpret_cast<const u16x8*>(na.b + static_cast<int64_t>(m) * K + 8 * v[j]);
+        }
+      }
+  }
+  // row m of y at sy + m Ks (Ks = Kp + 32: rows 64 bytes apart in the banks, so the GEMM
+  // wave's 16 lanes of one step, on up to 4 rows and 4 k offsets, read 16 disjoint bank groups)
+  __device__ void store(const NormArgs& na, bool write_sum, int M, int K, int Kp, int Ks, uint16_t* sy,
+                        float* part) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < kNormRows; ++m)
+      if (m < M) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          u16x8 q;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) q[i] = f32_to_bf16(bf16_to_f32(a[m][j][i]) + bf16_to_f32(b[m][j][i]));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float x = bf16_to_f32(q[i]);
+            acc = acc + (ok[j] ? x * x : 0.f);
+          }
+          if (ok[j]) {
+            *reinterpret_cast<u16x8*>(sy + m * Ks + 8 * v[j]) = q;
+            if (write_sum) *reinterpret_cast<u16x8*>(na.sum + static_cast<int64_t>(m) * K + 8 * v[j]) = q;
+          }
+        }
+        const float ws = wave_tree_sum(acc);
+        if ((t & 63) == 0) part[m * 4 + (t >> 6)] = ws;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < kNormRows; ++m)
+      if (m < M) {
+        const float r = rms_scale((part[m * 4] + part[m * 4 + 1]) + (part[m * 4 + 2] + part[m * 4 + 3]), K, na.eps);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          if (!ok[j]) continue;
+          uint16_t* p = sy + m * Ks + 8 * v[j];
+          const u16x8 q = *reinterpret_cast<const u16x8*>(p);
+          u16x8 qy;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qy[i] = f32_to_bf16((bf16_to_f32(q[i]) * r) * bf16_to_f32(g[j][i]));
+          *reinterpret_cast<u16x8*>(p) = qy;
+        }
+        for (int vz = K / 8 + t; vz < Kp / 8; vz += 256) *reinterpret_cast<u16x8*>(sy + m * Ks + 8 * vz) = u16x8{};
+      }
+    __syncthreads();
+  }
+};
+
 // Few-row GEMM (M <= 64).  At decode sizes the weight stream bounds the call, and a
 // 128 x 128 grid leaves most CUs idle (N = 4096 gives 32 workgroups).  Here one wave owns CB
 // 16-column blocks and RB 16-row blocks (all M rows, or with `split` = 2 or 4 one of that many
@@ -883,12 +974,20 @@ TileKind pick_tile(int64_t M, int64_t N, int cus) {
 // 16-byte piece of lane l at offset 16 l, which is lane l's instruction operand): each load
 // of a wave reads one contiguous kilobyte instead of 64 bytes from each of 16 rows.  Only
 // the addresses change; the operands, the instruction sequence and so the bits do not.
-template <int RB, int CB, int PF, bool PAIR = false, bool PK = false>
-__global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
+// NORM > 0 (one row block, one wave's blocks, no split): A and na describe a residual add +
+// RMSNorm whose output is the A operand, staged in LDS by NormRows ([M][32 ceil(K/32) + 32]
+// bf16, dynamic; NORM vectors per tree lane: 1 for K <= 2048, 2 for K <= 4096).  The workgroup has
+// 256 threads, one per tree lane: wave 0 is the GEMM wave, waves 1..3 help normalise and
+// then leave (no barrier follows).  The rows' loads, then the weight prefetch, go out before
+// any of it is computed.
+template <int RB, int CB, int PF, bool PAIR = false, bool PK = false, int NORM = 0>
+__global__ __launch_bounds__(NORM > 0 ? 256 : (PAIR ? 128 : 64)) void gemm_rows_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
     int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int c_f32, int split, int k_split,
-    int64_t split_stride) {
+    int64_t split_stride, NormArgs na) {
   static_assert(!PAIR || CB == 1, "paired waves hold one block each");
+  static_assert(NORM == 0 || (RB == 1 && !PAIR), "the normalised rows are one row block of one wave");
+  extern __shared__ __attribute__((aligned(16))) uint16_t sy[];
   // K slice of blockIdx.y (as in gemm_dma_kernel; the split-K comparison variant only)
   if (blockIdx.y > 0) {
     const int kb = static_cast<int>(blockIdx.y) * k_split;
@@ -900,7 +999,7 @@ __global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
     K = min(k_split, K);
   }
   const int lane = threadIdx.x & 63;
-  const int wave = PAIR ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+  const int wave = PAIR || NORM > 0 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   // workgroup id -> (column block, row slice): ids 8 s + x, s = split c .. split c + split - 1
   // (one XCD) share column block 8 c + x; with split = 1 the id is the column block (the
   // pair's, for PAIR)
@@ -924,11 +1023,24 @@ __global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
     pb[cb] = PK ? B + static_cast<int64_t>(min(cblk * CB + cb, (N - 1) / 16)) * nk32 * 512 + lane * 8
                 : B + static_cast<int64_t>(min(col0 + cb * 16 + (lane & 15), N - 1)) * ldb + kl;
   bf16x8 ra[PF][RB], rv[PF][CB];
-  auto load = [&](int t, bf16x8 (&dst_a)[RB], bf16x8 (&dst_b)[CB]) {
+  // NORM: lane l's A operand row (clamped to M - 1 as above) in the staged rows
+  const int Kp = static_cast<int>(nk32) * 32, Ks = Kp + 32;
+  const int arow = NORM > 0 ? min(row0 + (lane & 15), M - 1) * Ks + kl : 0;
+  auto load_a = [&](int t, bf16x8 (&dst_a)[RB]) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) dst_a[rb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pa[rb] + 32 * t));
+    for (int rb = 0; rb < RB; ++rb)
+      dst_a[rb] = NORM > 0 ? as_bf16x8(*reinterpret_cast<const u16x8*>(sy + arow + 32 * t))
+                       : as_bf16x8(*reinterpret_cast<const u16x8*>(pa[rb] + 32 * t));
+  };
+  auto load_b = [&](int t, bf16x8 (&dst_b)[CB]) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) dst_b[cb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pb[cb] + (PK ? 512 : 32) * t));
+  };
+  // (NORM: the A operand is read from LDS at the step that uses it, see mma_at; only the
+  // weights ride the prefetch ring)
+  auto load = [&](int t, bf16x8 (&dst_a)[RB], bf16x8 (&dst_b)[CB]) {
+    if constexpr (NORM == 0) load_a(t, dst_a);
+    load_b(t, dst_b);
   };
   floatx4 acc[RB][CB];
 #pragma unroll
@@ -944,6 +1056,15 @@ __global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
       for (int cb = 0; cb < CB; ++cb)
         acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
   };
+  auto mma_at = [&](int t, const bf16x8 (&a)[RB], const bf16x8 (&b)[CB]) {
+    if constexpr (NORM > 0) {
+      bf16x8 an[RB];
+      load_a(t, an);
+      mma(an, b);
+    } else {
+      mma(a, b);
+    }
+  };
   const int nsteps = K / 32;   // whole steps, >= 2 PF (the host checks)
   // the partial last step (if any): a chunk at or past K re-reads k offset 0 of its row and
   // is zeroed once it has landed
@@ -951,22 +1072,40 @@ __global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
   const bool tin = ktail + kl < K;
   const int tofs = tin ? ktail : -kl;
   bf16x8 ta[RB], tb[CB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) ta[rb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pa[rb] + tofs));
   // (PK: the partial step's tile, index nsteps, exists only when K is not a multiple of 32;
   // its pieces past K hold zeros)
   const int64_t tofs_b = PK ? (ktail < K ? int64_t(512) * nsteps : 0) : tofs;
+  if constexpr (NORM > 0) {
+    // the rows and gamma, then (GEMM wave) the weights; the rows are normalised while the
+    // weights stream in (zeros past K in LDS, so the partial step needs no mask)
+    __shared__ float part[kNormRows * 4];
+    NormRows<NORM> rows;
+    rows.load(A, na, M, K);
+    if (wave == 0) {
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) tb[cb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pb[cb] + tofs_b));
+      for (int cb = 0; cb < CB; ++cb) tb[cb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pb[cb] + tofs_b));
 #pragma unroll
-  for (int p = 0; p < PF; ++p) load(p, ra[p], rv[p]);
+      for (int p = 0; p < PF; ++p) load_b(p, rv[p]);
+    }
+    rows.store(na, blockIdx.x == 0, M, K, Kp, Ks, sy, part);
+    if (wave != 0) return;   // the helpers' part is done
+    const bf16x8 z = {};
+    ta[0] = ktail < K ? as_bf16x8(*reinterpret_cast<const u16x8*>(sy + arow + ktail)) : z;
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) ta[rb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pa[rb] + tofs));
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) tb[cb] = as_bf16x8(*reinterpret_cast<const u16x8*>(pb[cb] + tofs_b));
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load(p, ra[p], rv[p]);
+  }
   // full rounds: step t multiplies slot t % PF and refills it with step t + PF (straight-line
   // code, so the compiler's load counters stay exact and PF steps stay in flight)
   int t0 = 0;
   for (; t0 + 2 * PF <= nsteps; t0 += PF) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      mma(ra[p], rv[p]);
+      mma_at(t0 + p, ra[p], rv[p]);
       load(t0 + PF + p, ra[p], rv[p]);
     }
   }
@@ -974,13 +1113,13 @@ __global__ __launch_bounds__(PAIR ? 128 : 64) void gemm_rows_kernel(
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
     if (t0 + p < nsteps) {
-      mma(ra[p], rv[p]);
+      mma_at(t0 + p, ra[p], rv[p]);
       if (t0 + PF + p < nsteps) load(t0 + PF + p, ra[p], rv[p]);
     }
   }
 #pragma unroll
   for (int p = 0; p < PF; ++p)
-    if (t0 + PF + p < nsteps) mma(ra[p], rv[p]);
+    if (t0 + PF + p < nsteps) mma_at(t0 + PF + p, ra[p], rv[p]);
   if (ktail < K) {
     const bf16x8 z = {};
 #pragma unroll
@@ -1198,7 +1337,39 @@ void launch_rows_t(const void* A, const void* B, void* C, int64_t M, int64_t N, 
   const unsigned wgs = static_cast<unsigned>(PAIR ? (ncb + 1) / 2 : split == 1 ? ncb : 8 * split * ((ncb + 7) / 8));
   gemm_rows_kernel<RB, CB, PF, PAIR, PK><<<dim3(wgs, sk.ks), dim3(PAIR ? 128 : 64), 0, s>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, int(M), int(N), int(K),
-      lda, ldb, ldc, cf, split, sk.k_split ? sk.k_split : int(K), sk.stride);
+      lda, ldb, ldc, cf, split, sk.k_split ? sk.k_split : int(K), sk.stride, NormArgs{});
+}
+
+// The residual add + RMSNorm fused in front of the few-row kernel (at most kNormRows rows):
+// the configurations rows_cfg gives those rows (one 16-column block per wave, paired waves
+// for SwiGLU), on an [N, K] or a tiled B.
+template <int CB, bool PK>
+void launch_rows_norm_t(const void* a, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                        int64_t ldb, int64_t ldc, int cf, NormArgs na, hipStream_t s) {
+  const unsigned wgs = static_cast<unsigned>((N + 16 * CB - 1) / (16 * CB));
+  const size_t lds = static_cast<size_t>(M) * ((K + 31) / 32 * 32 + 32) * sizeof(uint16_t);
+  const uint16_t *pa = static_cast<const uint16_t*>(a), *pb = static_cast<const uint16_t*>(B);
+  // K > 2048: two vectors per tree lane, and one-block waves prefetch 32 steps of weights
+  // (K / 32 >= 64), which keeps the stream going while the rows are normalised
+  if (K <= 2048)
+    gemm_rows_kernel<1, CB, 16, false, PK, 1><<<dim3(wgs), dim3(256), lds, s>>>(
+        pa, pb, C, int(M), int(N), int(K), K, ldb, ldc, cf, 1, int(K), 0, na);
+  else
+    gemm_rows_kernel<1, CB, CB == 1 ? 32 : 16, false, PK, 2><<<dim3(wgs), dim3(256), lds, s>>>(
+        pa, pb, C, int(M), int(N), int(K), K, ldb, ldc, cf, 1, int(K), 0, na);
+}
+
+// The residual add + RMSNorm fused in front of the few-row kernel (at most kNormRows rows): one
+// 16-column block per GEMM wave, two (the gate and up blocks) for SwiGLU.
+void launch_rows_norm(const void* a, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                      int64_t ldb, int64_t ldc, int cf, bool tiled, NormArgs na, hipStream_t s) {
+  if (cf == kOutSwiGLU) {
+    if (tiled) launch_rows_norm_t<2, true>(a, B, C, M, N, K, ldb, ldc, cf, na, s);
+    else launch_rows_norm_t<2, false>(a, B, C, M, N, K, ldb, ldc, cf, na, s);
+  } else {
+    if (tiled) launch_rows_norm_t<1, true>(a, B, C, M, N, K, ldb, ldc, cf, na, s);
+    else launch_rows_norm_t<1, false>(a, B, C, M, N, K, ldb, ldc, cf, na, s);
+  }
 }
 
 // The few-row kernel on a tiled B (bi_pack_b), in the configuration rows_cfg gives (for
@@ -1321,6 +1492,7 @@ void launch_bf16(const void* A, const void* B, void* C, int64_t M, int64_t N, in
     default: launch_dma<Tile128>(A, B, C, M, N, K, lda, ldb, ldc, mode, s, sk); break;
   }
 }
+
 
 }  // namespace
 }  // namespace bi
@@ -1467,6 +1639,60 @@ extern "C" int bi_gemm_swiglu(const void* A, const void* W, void* out, int64_t M
   const int64_t N = 2 * F;
   if (!(M * lda * 2 < (int64_t(1) << 32) && N * ldw * 2 < (int64_t(1) << 32))) return BI_ERR_UNSUPPORTED;
   launch_bf16(A, W, out, M, N, K, lda, ldw, ldo, kOutSwiGLU, as_stream(stream));
+  return launch_status();
+}
+
+namespace {
+// Checks shared by the two fused add + RMSNorm + GEMM calls (N = output columns of the
+// product: 2F for SwiGLU).
+int norm_gemm_check(const void* a, const void* b, const void* sum, const void* gamma, const void* W,
+                    const void* C, int64_t M, int64_t N, int64_t K, int64_t ldw, int64_t ldc,
+                    int64_t ldc_min, int w_layout) {
+  if (w_layout != BI_B_NK && w_layout != BI_B_TILED) return BI_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 1 || ldc < ldc_min || (w_layout == BI_B_NK && ldw < K) ||
+      N > (1 << 30) || K > (1 << 30))
+    return BI_ERR_SHAPE;
+  if (M == 0 || N == 0) return BI_OK;
+  if (M > kNormRows || K % 8 != 0 || K > 4096 || K / 32 < 32) return BI_ERR_UNSUPPORTED;
+  if (!a || !b || !sum || !gamma || !W || !C) return BI_ERR_NULL;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(sum) || !aligned16(gamma) || !aligned16(W) ||
+      (w_layout == BI_B_NK && ldw % 8))
+    return BI_ERR_ALIGN;
+  // sum is written by one workgroup while the others still read a and b
+  const char *pa = static_cast<const char*>(a), *pb = static_cast<const char*>(b),
+             *ps = static_cast<const char*>(sum);
+  const int64_t bytes = M * K * 2;
+  if ((ps < pa + bytes && pa < ps + bytes) || (ps < pb + bytes && pb < ps + bytes)) return BI_ERR_SHAPE;
+  if (w_layout == BI_B_NK && N * ldw * 2 >= (int64_t(1) << 32)) return BI_ERR_UNSUPPORTED;
+  return 1;   // go ahead
+}
+}  // namespace
+
+extern "C" int bi_add_rmsnorm_gemm(const void* a, const void* b, void* sum, const void* gamma, float eps,
+                                   const void* W, void* C, int64_t M, int64_t N, int64_t K, int64_t ldw,
+                                   int64_t ldc, int w_layout, int c_dtype, void* stream) {
+  if (c_dtype != BI_BF16 && c_dtype != BI_F32) return BI_ERR_DTYPE;
+  const int st = norm_gemm_check(a, b, sum, gamma, W, C, M, N, K, ldw, ldc, N, w_layout);
+  if (st != 1) return st;
+  const NormArgs na{static_cast<const uint16_t*>(b), static_cast<const uint16_t*>(gamma),
+                    static_cast<uint16_t*>(sum), eps};
+  launch_rows_norm(a, W, C, M, N, K, ldw, ldc, c_dtype == BI_F32, w_layout == BI_B_TILED, na,
+                   as_stream(stream));
+  return launch_status();
+}
+
+extern "C" int bi_add_rmsnorm_gemm_swiglu(const void* a, const void* b, void* sum, const void* gamma,
+                                          float eps, const void* W, void* out, int64_t M, int64_t F,
+                                          int64_t K, int64_t ldw, int64_t ldo, int w_layout,
+                                          void* stream) {
+  if (F < 0) return BI_ERR_SHAPE;
+  if (F % 16 != 0 || F > (1 << 29)) return BI_ERR_SHAPE;
+  const int st = norm_gemm_check(a, b, sum, gamma, W, out, M, 2 * F, K, ldw, ldo, F, w_layout);
+  if (st != 1) return st;
+  const NormArgs na{static_cast<const uint16_t*>(b), static_cast<const uint16_t*>(gamma),
+                    static_cast<uint16_t*>(sum), eps};
+  launch_rows_norm(a, W, out, M, 2 * F, K, ldw, ldo, kOutSwiGLU, w_layout == BI_B_TILED, na,
+                   as_stream(stream));
   return launch_status();
 }
 

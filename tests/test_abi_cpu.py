@@ -68,6 +68,28 @@ def test_validation_rejects_before_launch(lib):
     assert lib.bi_gemm_swiglu(P, ctypes.c_void_p(18), P, 4, 32, 64, 64, 64, 32, 1, None) == -4
     assert lib.bi_gemm_swiglu(None, None, None, 0, 32, 64, 64, 64, 32, 1, None) == 0
     assert lib.bi_gemm_swiglu(P, P, P, 4, 32, 64, 64, 64, 32, 7, None) == -3     # w_layout
+    # fused add + RMSNorm + projection: at most 4 rows, 1024 <= K <= 8192 (K % 8 == 0), the
+    # sum apart from a and b; a, b, sum, gamma, W, C at distinct (never dereferenced) addresses
+    a, b, sm, g, w, c = (ctypes.c_void_p(16 + (i << 24)) for i in range(6))
+    ng = lib.bi_add_rmsnorm_gemm
+    assert ng(a, b, sm, g, 1e-5, w, c, 1, 64, 1024, 1024, 64, 5, 1, None) == -3          # w_layout
+    assert ng(a, b, sm, g, 1e-5, w, c, 1, 64, 1024, 1024, 64, 1, 7, None) == -3          # c_dtype
+    assert ng(a, b, sm, g, 1e-5, w, c, 5, 64, 1024, 1024, 64, 1, 1, None) == -6          # 5 rows
+    for k in (1028, 512, 8200):
+        assert ng(a, b, sm, g, 1e-5, w, c, 1, 64, k, k, 64, 1, 1, None) == -6
+    assert ng(a, b, sm, g, 1e-5, w, c, 3, 64, 8192, 8192, 64, 1, 1, None) == -6        # 48 KB of rows
+    assert ng(a, b, sm, g, 1e-5, w, c, 1, 64, 1024, 1000, 64, 1, 1, None) == -2          # ldw < K
+    assert ng(a, b, sm, g, 1e-5, w, c, 1, 64, 1024, 1024, 60, 1, 1, None) == -2          # ldc < N
+    assert ng(None, b, sm, g, 1e-5, w, c, 1, 64, 1024, 1024, 64, 1, 1, None) == -1
+    assert ng(a, ctypes.c_void_p(18), sm, g, 1e-5, w, c, 1, 64, 1024, 1024, 64, 1, 1, None) == -4
+    assert ng(a, b, ctypes.c_void_p(16 + 1024), g, 1e-5, w, c, 1, 64, 1024, 1024, 64, 1, 1, None) == -2
+    assert ng(a, b, b, g, 1e-5, w, c, 2, 64, 1024, 1024, 64, 2, 1, None) == -2          # sum is b
+    assert ng(None, None, None, None, 1e-5, None, None, 0, 64, 1024, 1024, 64, 1, 1, None) == 0
+    ns = lib.bi_add_rmsnorm_gemm_swiglu
+    assert ns(a, b, sm, g, 1e-5, w, c, 1, 24, 1024, 1024, 24, 1, None) == -2             # F % 16
+    assert ns(a, b, sm, g, 1e-5, w, c, 5, 32, 1024, 1024, 32, 2, None) == -6
+    assert ns(a, b, sm, g, 1e-5, w, c, 1, 32, 1024, 1024, 32, 7, None) == -3
+    assert ns(a, b, sm, g, 1e-5, None, c, 1, 32, 1024, 1024, 32, 1, None) == -1
     # tiled B / W: at most 64 rows, K a multiple of 8 and >= 1024, bf16 A
     assert lib.bi_gemm(P, P, P, 65, 64, 1024, 1024, 0, 64, 2, 1, 1, None) == -6
     assert lib.bi_gemm(P, P, P, 16, 64, 512, 512, 0, 64, 2, 1, 1, None) == -6
