@@ -22,6 +22,7 @@ Beside the step, the same line carries:
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemm-set]
                     [--gemm-sweep] [--decode-gemm] [--gemm-profile M,N,K] [--model]
+                    [--decode-step B]
 """
 from __future__ import annotations
 
@@ -429,6 +430,39 @@ def model_bench(torch, bi):
     print(json.dumps(out), flush=True)
 
 
+def decode_step(torch, bi, B, K, W):
+    """One greedy decode step of the 32-layer Mistral-7B-shaped model (random bf16 weights,
+    std 0.02; forward + head) at batch B, issued eagerly: W warm-up and K timed steps on
+    a fixed batch whose contexts are those of the ragged batch test (B = 1: the 1400-token
+    prompt).  For kernel traces of the step; the token ids are not fed back."""
+    import synth
+    from invariant_amd.model import Dims, PagedKVCache, forward, head, make_batch, random_model
+    dims = Dims()
+    model = random_model(dims, seed=5)
+    ctx = [int(n) for n in (list(synth.ragged_lengths(48, 200, 4000, 5, 1)) + [1400])[-B:]]
+    cache = PagedKVCache(dims, n_pages=sum(ctx) // 16 + 4 * B + 16, seed=3)
+    batch = make_batch(cache, list(range(B)), ctx, [np.asarray([7 + i], np.int32) for i in range(B)],
+                       dims=dims)
+    rows = torch.arange(B, dtype=torch.int32, device="cuda")
+    step = lambda: head(model, forward(model, batch, cache, dims), rows, dims)
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t) / K * 1e3
+    out = dict(workload=f"32-layer Mistral-7B-shaped decode step, batch {B}, contexts {min(ctx)}-{max(ctx)}",
+               batch=B, steps=K, warmup=W, ms_per_step=round(ms, 3),
+               weight_GBps=round((sum(w[k].numel() * 2 for w in model["layers"]
+                                      for k in ("attn_norm", "wqkv", "wo", "ffn_norm", "wgate_up", "wdown"))
+                                  + model["lm_head"].numel() * 2 + model["final_norm"].numel() * 2)
+                                 / ms / 1e6, 1))
+    print(json.dumps(out), flush=True)
+    return out
+
+
 def layer_bench(torch, model, dims):
     """One decoder layer at decode: B requests with contexts L ~ U[0, 4096] (cache pages
     reserved, contents as they are), one new token each; time per layer call."""
@@ -519,6 +553,8 @@ def main():
                     help="decode-sized GEMMs on fresh weights: [N, K] vs tiled vs torch.mm")
     ap.add_argument("--model", action="store_true",
                     help="time 32-layer greedy decoding alone and in a 49-prompt batch (reported)")
+    ap.add_argument("--decode-step", type=int, metavar="B",
+                    help="time --steps eager 32-layer decode steps at batch B (for kernel traces)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (to scale rocprof byte counters)")
     args = ap.parse_args()
@@ -548,6 +584,9 @@ def main():
         return
     if args.model:
         model_bench(torch, bi)
+        return
+    if args.decode_step:
+        decode_step(torch, bi, args.decode_step, args.steps, args.warmup)
         return
     if args.gemm_profile:
         gemm_profile(torch, bi, [int(v) for v in args.gemm_profile.split(",")])
