@@ -18,6 +18,7 @@ Beside the step, the same line carries:
   nonbi_comparison   the non-invariant variants on the same inputs: split-K GEMM (2048^3 and
                      the Mistral shapes at M = 1, 64, 1024, 2048) and batch-dependent
                      split-KV attention -- the cost of invariance;
+  size_sweeps        reported (not graded) sizes: RMSNorm rows 1..65536, decode batches 1..64.
   cpu_baseline       the oracle timed on the host (all cores and one core).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemm-set]
@@ -499,6 +500,67 @@ def layer_bench(torch, model, dims):
     return out
 
 
+def _graph_time(torch, fns, reps=5):
+    """Seconds per call of the given calls (one round over them), captured once as a HIP graph
+    of 20 rounds and replayed, so that launches of a few microseconds are timed without the
+    host's gaps between them."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(20):
+            for f in fns:
+                f()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (reps * 20 * len(fns))
+
+
+def size_sweeps(torch, bi, inp):
+    """The reported (not graded) sizes of the GB/s rows: bi_rmsnorm on the first M rows of
+    x [65536, 4096], M = 1 .. 65536 (below ~16k rows the working set sits in the 256 MB MALL
+    and the call is launch-bound), and bi_attention decode on B = 1 .. 64 of the 64
+    sequences (contexts U[1400, 32768]): below 64, the call cycles over disjoint slices of B
+    sequences, so that together they read every cache page and the MALL cannot hold them."""
+    x, g, y = inp["x"], inp["gamma"], inp["y"]
+    D = x.shape[1]
+    rms = []
+    for M in (1, 64, 256, 1024, 4096, 16384, 65536):
+        t = _graph_time(torch, [lambda M=M: bi.bi_rmsnorm(x[:M], g, 1e-5, out=y[:M])])
+        b = 4 * M * D + 2 * D
+        rms.append(dict(M=M, us=round(t * 1e6, 2), GBps=round(b / t / 1e9, 1), frac=round(b / t / HBM_PEAK, 4)))
+    L = inp["L"]
+    hq, hd = inp["q"].shape[1], inp["q"].shape[2]
+    hkv = inp["k_new"].shape[1]
+    att = []
+    for B in (1, 2, 4, 8, 16, 32, 64):
+        fns, nbytes = [], 0
+        for s0 in range(0, 64, B):
+            sl = slice(s0, s0 + B)
+            Ls = L[sl]
+            qsl = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+            fns.append(lambda sl=sl, Ls=Ls, qsl=qsl: bi.bi_attention(
+                inp["q"][sl], inp["k_new"][sl], inp["v_new"][sl], inp["k_cache"], inp["v_cache"],
+                inp["bt"][sl], inp["seq_lens"][sl], qsl, max_seq_len=int(Ls.max()),
+                scale=1.0 / np.sqrt(128.0), out=inp["attn_out"][sl], workspace=inp["ws"]))
+            nbytes += 2 * 2 * hkv * hd * int(Ls.sum()) + 2 * 2 * B * hq * hd + 2 * 2 * B * hkv * hd
+        t = _graph_time(torch, fns)
+        b = nbytes / len(fns)
+        att.append(dict(B=B, us=round(t * 1e6, 2), GBps=round(b / t / 1e9, 1), frac=round(b / t / HBM_PEAK, 4)))
+    return {"rmsnorm_rows": rms, "attention_decode_batch": att}
+
+
 def graph_step(torch, inp, ops, K):
     """The same step captured once as a HIP graph (its kernel launches replayed as one) and
     timed over K replays.  Every output of a replay must equal the eager step's bit for bit;
@@ -679,6 +741,8 @@ def main():
                           invariant_ms=round(t["invariant"] * 1e3, 5),
                           invariant_slowdown=round(t["invariant"] / t["variant"], 4))
     res["nonbi_comparison"] = comp
+    log("reported sizes: RMSNorm rows, attention decode batches")
+    res["size_sweeps"] = size_sweeps(torch, bi, inp)
     if not args.no_gemm_set:
         log("GEMM set 2' (Mistral shapes, M >= 1024)")
         res["gemm_set2prime"] = gemm_set2(torch, bi)
