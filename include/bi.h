@@ -408,7 +408,8 @@ int bi_add_rmsnorm(const void* a, const void* b, void* sum, int dtype, const voi
  *     out = swiglu(rmsnorm(sum) . W^T)    equals bi_gemm_swiglu of that y,
  *   bit for bit, without writing or re-reading y.
  *   a, b, sum [M, K] bf16, rows contiguous (stride K); sum must not overlap a or b (one
- *   workgroup writes it while the others read them); gamma bf16 [K]; W as in bi_gemm (N rows)
+ *   workgroup writes it while the others read them), and C / out must overlap none of the
+ *   inputs (checked for sum only); gamma bf16 [K]; W as in bi_gemm (N rows)
  *   or bi_gemm_swiglu (2F interleaved rows): w_layout BI_B_NK with row stride ldw, or
  *   BI_B_TILED (ldw unused); C [M, N] (c_dtype BI_BF16 | BI_F32), out [M, F] bf16, row
  *   strides ldc / ldo.

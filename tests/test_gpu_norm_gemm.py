@@ -32,7 +32,7 @@ def _rows(k, seed):
     return a, b, g
 
 
-@pytest.mark.parametrize("n,k", [(6144, 4096), (1000, 1032), (4096, 8192), (48, 2048), (272, 1024)])
+@pytest.mark.parametrize("n,k", [(6144, 4096), (1000, 1032), (4096, 8192), (48, 2048), (272, 1024), (512, 3000)])
 def test_fused_norm_gemm_equals_unfused(lib, n, k):
     say("add_rmsnorm_gemm", n, k)
     from invariant_amd import BI_B_NK, BI_B_TILED, BIError
