@@ -18,7 +18,8 @@ Beside the step, the same line carries:
   nonbi_comparison   the non-invariant variants on the same inputs: split-K GEMM (2048^3 and
                      the Mistral shapes at M = 1, 64, 1024, 2048) and batch-dependent
                      split-KV attention -- the cost of invariance;
-  size_sweeps        reported (not graded) sizes: RMSNorm rows 1..65536, decode batches 1..64.
+  size_sweeps        reported (not graded) sizes: RMSNorm rows 1..65536, decode batches 1..64,
+                     RMSNorm + 512 x 512 linear at M = 1..32.
   cpu_baseline       the oracle timed on the host (all cores and one core).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemm-set]
@@ -558,7 +559,21 @@ def size_sweeps(torch, bi, inp):
         t = _graph_time(torch, fns)
         b = nbytes / len(fns)
         att.append(dict(B=B, us=round(t * 1e6, 2), GBps=round(b / t / 1e9, 1), frac=round(b / t / HBM_PEAK, 4)))
-    return {"rmsnorm_rows": rms, "attention_decode_batch": att}
+    # the RMSNorm + linear batch sweep (x [M, 512] ~ N(0, 1), gamma ~ N(1, 0.02), eps 1e-6,
+    # W [512, 512] std 1/512): both calls per M, launch-bound at these sizes
+    import synth
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    x1 = torch.randn((32, 512), generator=gen, device="cuda").to(torch.bfloat16)
+    g1 = torch.from_numpy(synth.normal_bf16((512,), 1.0, 0.02, 1, 1).view(np.int16)).cuda().view(torch.bfloat16)
+    w1 = (torch.randn((512, 512), generator=gen, device="cuda") / 512).to(torch.bfloat16)
+    y1 = torch.empty((32, 512), dtype=torch.bfloat16, device="cuda")
+    c1 = torch.empty((32, 512), dtype=torch.bfloat16, device="cuda")
+    lin = []
+    for M in (1, 2, 4, 8, 16, 32):
+        t = _graph_time(torch, [lambda M=M: bi.bi_rmsnorm(x1[:M], g1, 1e-6, out=y1[:M]),
+                                lambda M=M: bi.bi_gemm(y1[:M], w1, out=c1[:M])])
+        lin.append(dict(M=M, us_per_pair=round(2 * t * 1e6, 2)))
+    return {"rmsnorm_rows": rms, "attention_decode_batch": att, "rmsnorm_linear_512": lin}
 
 
 def graph_step(torch, inp, ops, K):
