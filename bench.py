@@ -23,6 +23,7 @@ Beside the step, the same line carries:
   cpu_baseline       the oracle timed on the host (all cores and one core).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemm-set]
+                    [--no-size-sweeps]
                     [--gemm-sweep] [--decode-gemm] [--gemm-profile M,N,K] [--model]
                     [--decode-step B]
 """
@@ -622,6 +623,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-set", action="store_true",
                     help="skip the Mistral-shape GEMM set and the split-K comparison on it")
+    ap.add_argument("--no-size-sweeps", action="store_true",
+                    help="skip the reported sizes (RMSNorm rows, decode batches), e.g. under a profiler")
     ap.add_argument("--gemm-sweep", action="store_true")
     ap.add_argument("--gemm-profile", metavar="M,N,K",
                     help="run bi_gemm on one shape (5 warm-up + 20 timed calls) and print its "
@@ -756,8 +759,9 @@ def main():
                           invariant_ms=round(t["invariant"] * 1e3, 5),
                           invariant_slowdown=round(t["invariant"] / t["variant"], 4))
     res["nonbi_comparison"] = comp
-    log("reported sizes: RMSNorm rows, attention decode batches")
-    res["size_sweeps"] = size_sweeps(torch, bi, inp)
+    if not args.no_size_sweeps:
+        log("reported sizes: RMSNorm rows, attention decode batches")
+        res["size_sweeps"] = size_sweeps(torch, bi, inp)
     if not args.no_gemm_set:
         log("GEMM set 2' (Mistral shapes, M >= 1024)")
         res["gemm_set2prime"] = gemm_set2(torch, bi)

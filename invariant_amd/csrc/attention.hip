@@ -840,8 +840,11 @@ __global__ __launch_bounds__(256) void attn_group_kernel(
 // chunk's K and V operands are loaded once and serve every group (chunk_scores and
 // chunk_values per group, the V masking depending on the sequence only), and each group
 // merges its chunks in registers (wave w keeps d-blocks 2w, 2w + 1).  A block that straddles
-// two sequences is processed once per sequence with the other sequence's columns off.
-constexpr int WALK_NG = 2;
+// two sequences is processed once per sequence with the other sequence's columns off.  Every
+// workgroup re-reads its sequence's K/V prefix from L2, so the more tokens a workgroup holds
+// the less of that traffic: four groups, whose q operands (the same in every wave) sit in
+// LDS so that the per-group state fits the registers.
+constexpr int WALK_NG = 4;
 
 template <int NQ>
 __global__ __launch_bounds__(256) void attn_walk_kernel(
@@ -851,6 +854,9 @@ __global__ __launch_bounds__(256) void attn_walk_kernel(
     int max_pages, int hq, int hkv, int ps, int64_t num_tokens, float sl2, void* __restrict__ out,
     int out_f32) {
   __shared__ ChunkLDS sh;
+  // the groups' q operands (lane l's of group gi, term j, d-step t at [gi][j][t][l]): the
+  // same in every wave, so they sit here rather than in each wave's registers
+  __shared__ u16x8 sqop[WALK_NG][NQ][4][64];
   const int G = hq / hkv;
   const int NT = 16 / G;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -875,16 +881,24 @@ __global__ __launch_bounds__(256) void attn_walk_kernel(
   const int b_last = find_seq(qsl, batch, static_cast<int>(tok_last));
   for (; b <= b_last; ++b) {
     if (qsl[b + 1] == qsl[b]) continue;
-    u16x8 qop[WALK_NG][NQ][4];
     int pcol[WALK_NG];
     int pmax = -1;
+    __syncthreads();   // the previous sequence's q operands are no longer read
 #pragma unroll
     for (int gi = 0; gi < WALK_NG; ++gi) {
       const bool mine = my_b[gi] == b;
       pcol[gi] = mine ? my_pos[gi] : -1;
-      load_q<NQ>(q, mine ? my_tok[gi] : 0, head, hq, mine, qop[gi]);
+      if (gi % 4 == w) {   // wave w stages group gi (WALK_NG is a multiple of 4 or below it)
+        u16x8 qtmp[NQ][4];
+        load_q<NQ>(q, mine ? my_tok[gi] : 0, head, hq, mine, qtmp);
+#pragma unroll
+        for (int j = 0; j < NQ; ++j)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) sqop[gi][j][t][lane] = qtmp[j][t];
+      }
       pmax = max(pmax, pcol[gi]);
     }
+    __syncthreads();
     const int L = seq_lens[b];
     Seq sq{kc, vc, bt + static_cast<int64_t>(b) * max_pages, ps, hkv, kvh, L, max_pages, __builtin_ctz(ps)};
     // highest position among this sequence's columns (the same in every wave)
@@ -906,9 +920,14 @@ __global__ __launch_bounds__(256) void attn_walk_kernel(
         float m_c, l_c;
         floatx4 oc[2];
         {
+          u16x8 qop[NQ][4];
+#pragma unroll
+          for (int j = 0; j < NQ; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) qop[j][t] = sqop[gi][j][t][lane];
           floatx4 sc[2][2];
           float mx, lsum;
-          chunk_scores<NQ>(c, kop, qop[gi], pcol[gi], sl2, sh, sc, mx, lsum);
+          chunk_scores<NQ>(c, kop, qop, pcol[gi], sl2, sh, sc, mx, lsum);
           chunk_values(sq, c, vop, sc, mx, lsum, sh, m_c, l_c, oc);
         }
         if (c * CHUNK > pcol[gi]) continue;
