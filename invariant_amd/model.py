@@ -350,11 +350,15 @@ def head(model, h, rows: torch.Tensor, dims: Dims, fp32_variant=False):
 
 def greedy_generate(model, prompts, n_new: int, cache: PagedKVCache, dims: Dims,
                     fp32_variant=False, max_chunk_tokens: int = 16384, keep_logits=None,
-                    sid_base: int = 0):
+                    sid_base: int = 0, timings: dict | None = None):
     """Greedy decoding of a ragged batch.  The prompts are prefilled in chunks of at most
     max_chunk_tokens tokens (a prompt may be split across chunks), then every sequence
     decodes one token per step.  Returns (tokens [B, n_new] int32 numpy, logits dict
-    {b: [n_new, V] fp32 tensor} for b in keep_logits)."""
+    {b: [n_new, V] fp32 tensor} for b in keep_logits).  timings, if a dict, receives the
+    wall-clock seconds of the prefill (up to the first tokens on the host) and of the decode
+    steps after it (up to the last tokens on the host)."""
+    import time
+    t_start = time.perf_counter()
     B = len(prompts)
     keep = set(range(B)) if keep_logits is None else set(keep_logits)
     sids = [sid_base + i for i in range(B)]
@@ -388,6 +392,7 @@ def greedy_generate(model, prompts, n_new: int, cache: PagedKVCache, dims: Dims,
                 if i in keep:
                     logits_out[i].append(lg[r].clone())
         del h
+    t_prefill = time.perf_counter()   # (the first tokens are on the host: the work is done)
     # decode: every sequence's pages for the whole generation are reserved up front, so the
     # block table stays fixed; each step's argmax is the next step's token on the device and
     # the positions and lengths advance in place, so the host issues step after step without
@@ -405,17 +410,26 @@ def greedy_generate(model, prompts, n_new: int, cache: PagedKVCache, dims: Dims,
                   qsl=torch.arange(B + 1, dtype=torch.int32, device=dev), max_seq_len=msl,
                   workspace=torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None)
     rows = torch.arange(B, dtype=torch.int32, device=dev)
-    ids_all = [batch.tokens]
+    keep_list = sorted(keep)
+    keep_idx = torch.tensor(keep_list, dtype=torch.int64, device=dev)
+    ids_all, kept = [batch.tokens], []
     for step in range(1, n_new):
         h = forward(model, batch, cache, dims, fp32_variant)
         lg, ids = head(model, h, rows, dims, fp32_variant)
         ids_all.append(ids)
-        for i in keep:
-            logits_out[i].append(lg[i].clone())
+        if keep_list:   # the kept rows in one gather per step
+            kept.append(lg.index_select(0, keep_idx))
         batch.tokens = ids
         batch.positions.add_(1)
         batch.seq_lens.add_(1)
+    if kept:
+        dec = torch.stack(kept, dim=1)   # [kept sequences, decode steps, V]
+        for r, i in enumerate(keep_list):
+            logits_out[i].extend(dec[r].unbind(0))
     tokens = torch.stack(ids_all, dim=1).cpu().numpy().astype(np.int32)
+    if timings is not None:
+        timings.update(prefill_s=t_prefill - t_start, decode_s=time.perf_counter() - t_prefill,
+                       decode_steps=n_new - 1)
     for s in sids:
         cache.release(s)
     return tokens, {i: torch.stack(v) for i, v in logits_out.items()}
