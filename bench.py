@@ -17,7 +17,8 @@ Beside the step, the same line carries:
                      set its >= 60 %-of-peak target is stated on;
   nonbi_comparison   the non-invariant variants on the same inputs: split-K GEMM (2048^3 and
                      the Mistral shapes at M = 1, 64, 1024, 2048) and batch-dependent
-                     split-KV attention -- the cost of invariance;
+                     split-KV attention -- the cost of invariance; beside the Mistral rows,
+                     the invariant fixed split of K (bi_gemm_fixed_split, 1024-column slices);
   size_sweeps        reported (not graded) sizes: RMSNorm rows 1..65536, decode batches 1..64,
                      RMSNorm + 512 x 512 linear at M = 1..32.
   cpu_baseline       the oracle timed on the host (all cores and one core).
@@ -270,12 +271,17 @@ def gemm_set2(torch, bi, ms=(1024, 2048, 4096, 8192, 16384), reps=10):
             "n_at_or_above_0.6": sum(f >= 0.6 for f in fr), "n": len(fr)}
 
 
+FIXED_K_SLICE = 1024
+
+
 def invariance_cost(torch, bi, ms=(1, 64, 1024, 2048), reps=10):
     """bi_gemm against the non-invariant split-K variant (slices of K chosen from the grid size,
     on the same few-row and LDS-staged kernels, then a fixed-order sum of the slices) on the
     Mistral shapes at decode- and prefill-sized M: the cost of keeping one reduction order.
-    The vendor library (torch.mm, hipBLASLt, not batch-invariant) on the same operands is
-    timed beside it as context."""
+    Beside them the batch-invariant fixed split (bi_gemm_fixed_split: K in slices of 1024
+    columns at every M, then the same fixed-order sum), the other invariant way to spread a
+    small batch over the GPU.  The vendor library (torch.mm, hipBLASLt, not batch-invariant)
+    on the same operands is timed as context."""
     dev = "cuda:0"
     g = torch.Generator(device=dev).manual_seed(22)
     out = []
@@ -286,10 +292,14 @@ def invariance_cost(torch, bi, ms=(1, 64, 1024, 2048), reps=10):
             C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             need = bi.load().bi_gemm_splitk_workspace_bytes(M, N, K)
             ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            need_f = bi.load().bi_gemm_fixed_split_workspace_bytes(M, N, K, FIXED_K_SLICE)
+            ws_f = torch.empty(max(need_f, 16), dtype=torch.uint8, device=dev)
             t = {}
             Wt = W.t()
             for name, fn in (("bi_gemm", lambda: bi.bi_gemm(A, W, out=C)),
                              ("splitk", lambda: bi.bi_gemm_splitk(A, W, out=C, workspace=ws)),
+                             ("fixed_split", lambda: bi.bi_gemm_fixed_split(A, W, FIXED_K_SLICE, out=C,
+                                                                            workspace=ws_f)),
                              ("torch_mm", lambda: torch.mm(A, Wt, out=C))):
                 for _ in range(2):
                     fn()
@@ -298,10 +308,13 @@ def invariance_cost(torch, bi, ms=(1, 64, 1024, 2048), reps=10):
                         "splitk_us": round(t["splitk"] * 1e6, 2),
                         "splitk_workspace_slices": int(need // (4 * M * N)) if need else 0,
                         "invariant_slowdown": round(t["bi_gemm"] / t["splitk"], 3),
+                        "fixed_split_us": round(t["fixed_split"] * 1e6, 2),
+                        "fixed_split_slices": -(-K // FIXED_K_SLICE),
+                        "fixed_split_vs_bi_gemm": round(t["fixed_split"] / t["bi_gemm"], 3),
                         "vendor_torch_mm_us": round(t["torch_mm"] * 1e6, 2),
                         "vs_vendor": round(t["bi_gemm"] / t["torch_mm"], 3)})
             log("invariance cost", out[-1])
-            del A, C, ws
+            del A, C, ws, ws_f
         del W
     return out
 

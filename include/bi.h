@@ -179,6 +179,26 @@ int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, 
                    int64_t lda, int64_t ldb, int64_t ldc, int c_dtype, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/* Batch-invariant split of K ([DN], batch-invariant RMSNorm, last paragraph: a reduction
+ * strategy with enough parallelism for tiny batches stays batch-invariant when it is used
+ * for every batch size; [DN], batch-invariant matmul: split-K for small M and N).  Same
+ * arguments as bi_gemm with bf16 A and B_NK, plus k_slice: K is cut into slices of k_slice
+ * columns at absolute offsets 0, k_slice, 2 k_slice, .. (the last one shorter when k_slice
+ * does not divide K), a function of K and k_slice alone, never of M.  Each slice's partial is
+ * bi_gemm's fp32 chain over the slice's columns (same instruction and ascending order, from
+ * +0), written to `workspace`; a second kernel adds the slices in ascending order from +0
+ * and rounds once to c_dtype.  For a fixed k_slice the bits of a row therefore do not depend
+ * on M or on the row's place in the batch (they differ from bi_gemm's when K > k_slice; with
+ * K <= k_slice the call is bi_gemm).  k_slice: a multiple of 64, at least 64 (BI_ERR_SHAPE
+ * otherwise); at most 65535 slices (BI_ERR_UNSUPPORTED).
+ * workspace >= bi_gemm_fixed_split_workspace_bytes(M, N, K, k_slice) = slices x M x N x 4
+ * bytes (0 with one slice), caller-owned, on the device (BI_ERR_WORKSPACE if smaller);
+ * the function returns 0 for invalid sizes. */
+size_t bi_gemm_fixed_split_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t k_slice);
+int bi_gemm_fixed_split(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc, int c_dtype, int64_t k_slice,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ attention
  * [DN] batch-invariant attention: the K/V cache and page table are updated BEFORE
  * the attention kernel runs, so that a query token reduces over the same keys in the

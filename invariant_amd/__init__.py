@@ -30,6 +30,9 @@ _SIGS = {
     "bi_gemm": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _c.c_int, _c.c_int, _c.c_int, _P]),
     "bi_gemm_splitk_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "bi_gemm_splitk": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _c.c_int, _P, _SZ, _P]),
+    "bi_gemm_fixed_split_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
+    "bi_gemm_fixed_split": (_c.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _c.c_int, _I64, _P,
+                                       _SZ, _P]),
     "bi_attention_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I64]),
     "bi_attention": (_c.c_int, [_P, _c.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32,
                                 _I32, _I32, _I64, _F32, _P, _c.c_int, _P, _SZ, _P]),
@@ -194,6 +197,22 @@ def bi_gemm_splitk(a, b, out=None, out_dtype=torch.bfloat16, workspace=None):
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
     _check("bi_gemm_splitk", load().bi_gemm_splitk(
         _ptr(a), _ptr(b), _ptr(out), M, N, K, _ld(a), _ld(b), _ld(out), _code(out.dtype),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(a)))
+    return out
+
+
+def bi_gemm_fixed_split(a, b, k_slice: int, out=None, out_dtype=torch.bfloat16, workspace=None):
+    """C = a b^T with K cut into slices of k_slice columns at absolute offsets, whatever M is
+    (a [M, K], b [N, K] bf16)."""
+    M, K = a.shape
+    N = b.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    need = load().bi_gemm_fixed_split_workspace_bytes(M, N, K, k_slice)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    _check("bi_gemm_fixed_split", load().bi_gemm_fixed_split(
+        _ptr(a), _ptr(b), _ptr(out), M, N, K, _ld(a), _ld(b), _ld(out), _code(out.dtype), int(k_slice),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(a)))
     return out
 

@@ -614,7 +614,7 @@ __device__ __forceinline__ void unrolled_steps(const DmaCtx<T>& d, const uint16_
 
 // k_split: K columns per blockIdx.y (K itself for bi_gemm, whose grid has one y); slice y
 // reads A and B from k = y k_split on and writes its fp32 result split_stride bytes further
-// into C (the split-K comparison variant only).
+// into C (the split-K comparison variant and the fixed split).
 template <class T>
 __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C, int M,
@@ -988,7 +988,7 @@ __global__ __launch_bounds__(NORM > 0 ? 256 : (PAIR ? 128 : 64)) void gemm_rows_
   static_assert(!PAIR || CB == 1, "paired waves hold one block each");
   static_assert(NORM == 0 || (RB == 1 && !PAIR), "the normalised rows are one row block of one wave");
   extern __shared__ __attribute__((aligned(16))) uint16_t sy[];
-  // K slice of blockIdx.y (as in gemm_dma_kernel; the split-K comparison variant only)
+  // K slice of blockIdx.y (as in gemm_dma_kernel; the split-K variant and the fixed split)
   if (blockIdx.y > 0) {
     const int kb = static_cast<int>(blockIdx.y) * k_split;
     A += kb;
@@ -1321,8 +1321,9 @@ bool use_rows(int64_t M, int64_t N, int64_t K, int mode) {
   return K / 32 >= 2 * rows_cfg(M, N, mode).pf;
 }
 
-// Split-K launches (comparison variant only): `ks` slices of k_split columns along grid y,
-// slice y's fp32 result split_stride bytes into C.  bi_gemm launches ks = 1, k_split = K.
+// K-slice launches (the split-K comparison variant and the fixed split): `ks` slices of
+// k_split columns along grid y, slice y's fp32 result split_stride bytes into C.  bi_gemm
+// launches ks = 1, k_split = K.
 struct KSplit {
   int ks = 1;
   int k_split = 0;   // 0: K
@@ -1426,7 +1427,8 @@ void launch_dma(const void* A, const void* B, void* C, int64_t M, int64_t N, int
       lda, ldb, ldc, cf, tm, tn, sk.k_split ? sk.k_split : int(K), sk.stride);
 }
 
-// Fixed-order sum of the split-K partials (comparison variant only).
+// Fixed-order sum of K-slice partials: slice 0 + slice 1 + .. from +0 (the split-K comparison
+// variant and the batch-invariant fixed split).
 __global__ void splitk_reduce_kernel(const float* __restrict__ ws, void* __restrict__ C, int M,
                                      int N, int64_t ldc, int c_f32, int splits) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -1480,7 +1482,9 @@ KSplit splitk_plan(int64_t M, int64_t N, int64_t K) {
 // bf16 A and B, both under 4 GiB: the few-row kernel or the LDS-staged tiles by grid size.
 void launch_bf16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                  int64_t lda, int64_t ldb, int64_t ldc, int mode, hipStream_t s, KSplit sk = {}) {
-  if (use_rows(M, N, K, mode)) {
+  // the few-row kernel's prefetch depth must fit the shortest K slice (the last one)
+  const int64_t k_short = sk.ks > 1 ? K - (sk.ks - 1) * static_cast<int64_t>(sk.k_split) : K;
+  if (use_rows(M, N, k_short, mode)) {
     launch_rows(A, B, C, M, N, K, lda, ldb, ldc, mode, s, sk);
     return;
   }
@@ -1611,6 +1615,59 @@ extern "C" int bi_gemm_splitk(const void* A, const void* B, void* C, int64_t M, 
   if (!workspace || workspace_bytes < bi_gemm_splitk_workspace_bytes(M, N, K)) return BI_ERR_WORKSPACE;
   // the few-row or LDS-staged kernels, each slice's fp32 result into the workspace, then the
   // slices added in ascending order
+  launch_bf16(A, B, workspace, M, N, K, lda, ldb, N, kOutF32, s, p);
+  const int64_t total = M * N;
+  splitk_reduce_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(
+      static_cast<const float*>(workspace), C, int(M), int(N), ldc, cf, p.ks);
+  return launch_status();
+}
+
+namespace bi {
+namespace {
+// Slices of a batch-invariant split: k_slice columns each at absolute offsets 0, k_slice, ..
+// (the last one shorter when k_slice does not divide K), a function of K and k_slice alone.
+int64_t fixed_slices(int64_t K, int64_t k_slice) { return (K + k_slice - 1) / k_slice; }
+}  // namespace
+}  // namespace bi
+
+extern "C" size_t bi_gemm_fixed_split_workspace_bytes(int64_t M, int64_t N, int64_t K,
+                                                      int64_t k_slice) {
+  if (M <= 0 || N <= 0 || K <= 0 || M > (1 << 30) || N > (1 << 30) || K > (1 << 30) ||
+      k_slice < 64 || k_slice % 64 != 0)
+    return 0;
+  const int64_t ks = fixed_slices(K, k_slice);
+  return ks > 1 ? static_cast<size_t>(ks) * M * N * sizeof(float) : 0;
+}
+
+extern "C" int bi_gemm_fixed_split(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                                   int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int c_dtype,
+                                   int64_t k_slice, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (c_dtype != BI_BF16 && c_dtype != BI_F32) return BI_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0) return BI_ERR_SHAPE;
+  if (M == 0 || N == 0) return BI_OK;
+  if (K < 1 || lda < K || ldb < K || ldc < N || M > (1 << 30) || N > (1 << 30) || K > (1 << 30) ||
+      k_slice < 64 || k_slice % 64 != 0)
+    return BI_ERR_SHAPE;
+  if (!A || !B || !C) return BI_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || (lda % 8) || (ldb % 8)) return BI_ERR_ALIGN;
+  if (!(M * lda * 2 < (int64_t(1) << 32) && N * ldb * 2 < (int64_t(1) << 32))) return BI_ERR_UNSUPPORTED;
+  const int64_t ks = fixed_slices(K, k_slice);
+  if (ks > 65535) return BI_ERR_UNSUPPORTED;   // one grid row per slice
+  hipStream_t s = as_stream(stream);
+  const int cf = c_dtype == BI_F32;
+  if (ks == 1) {   // one slice: bi_gemm itself
+    launch_bf16(A, B, C, M, N, K, lda, ldb, ldc, cf, s);
+    return launch_status();
+  }
+  if (!workspace || workspace_bytes < bi_gemm_fixed_split_workspace_bytes(M, N, K, k_slice))
+    return BI_ERR_WORKSPACE;
+  KSplit p;
+  p.ks = static_cast<int>(ks);
+  p.k_split = static_cast<int>(k_slice);
+  p.stride = M * N * static_cast<int64_t>(sizeof(float));
+  // each slice's fp32 chain (bi_gemm's instruction and order over the slice's columns) into
+  // the workspace, then the slices added in ascending order from +0
   launch_bf16(A, B, workspace, M, N, K, lda, ldb, N, kOutF32, s, p);
   const int64_t total = M * N;
   splitk_reduce_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(

@@ -98,6 +98,19 @@ def test_validation_rejects_before_launch(lib):
     assert lib.bi_gemm(P, None, P, 4, 64, 1024, 1024, 0, 64, 2, 1, 1, None) == -1
     assert lib.bi_gemm_swiglu(P, P, P, 65, 32, 1024, 1024, 0, 32, 2, None) == -6
     assert lib.bi_pack_b_bytes(33, 1000) == 3 * 32 * 1024 and lib.bi_pack_b_bytes(0, 8) == 0
+    # fixed split of K: k_slice a multiple of 64 and at least 64; the workspace holds one fp32
+    # M x N partial per slice (none with one slice), checked before any launch
+    fs, fsb = lib.bi_gemm_fixed_split, lib.bi_gemm_fixed_split_workspace_bytes
+    assert fsb(3, 5, 4096, 1024) == 4 * 3 * 5 * 4 and fsb(3, 5, 4097, 1024) == 5 * 3 * 5 * 4
+    assert fsb(3, 5, 1024, 1024) == 0 and fsb(3, 5, 4096, 100) == 0 and fsb(3, 5, 4096, 0) == 0
+    for ks in (0, 32, 100, -64):
+        assert fs(P, P, P, 4, 4, 4096, 4096, 4096, 4, 1, ks, P, 1 << 20, None) == -2
+    assert fs(P, P, P, 4, 4, 4096, 4096, 4096, 4, 1, 1024, P, 255, None) == -5        # workspace
+    assert fs(P, P, P, 4, 4, 4096, 4096, 4096, 4, 1, 1024, None, 1 << 20, None) == -5
+    assert fs(P, P, P, 4, 4, 4096, 4096, 4096, 4, 9, 1024, P, 1 << 20, None) == -3    # c_dtype
+    assert fs(None, P, P, 4, 4, 4096, 4096, 4096, 4, 1, 1024, P, 1 << 20, None) == -1
+    assert fs(P, P, P, 4, 4, 4096, 4096, 4000, 4, 1, 1024, P, 1 << 20, None) == -2    # ldb < K
+    assert fs(None, None, None, 0, 4, 4096, 4096, 4096, 4, 1, 1024, None, 0, None) == 0
     assert lib.bi_pack_b(P, 4, 64, 32, P, None) == -2
     assert lib.bi_pack_b(P, 4, 64, 64, ctypes.c_void_p(18), None) == -4
     assert lib.bi_pack_b(None, 4, 64, 64, P, None) == -1
