@@ -118,7 +118,7 @@ def test_chunked_prefill_matches_full_prefill(lib):
         start += piece
 
 
-def test_cfg4_decode_batch64(lib):
+def test_paged_decode_batch64_long_contexts(lib):
     B = 64
     L = ragged_lengths(B, 1400, 32768, 4, 0)
     case = attention_case(L, [1] * B, cfg=4)
@@ -134,7 +134,7 @@ def test_cfg4_decode_batch64(lib):
     assert f32_within_rel(host(of[0]), ref)["ok"]
 
 
-def test_cfg4_decode_equals_prefill_long(lib):
+def test_decode_equals_prefill_long_contexts(lib):
     L = [4000, 9000]
     pre = attention_case(L, L, cfg=44)
     kc, vc, bt = make_cache(pre, 16, [0, 0])

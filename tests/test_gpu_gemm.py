@@ -97,7 +97,7 @@ def test_integer_inputs_bit_exact(lib):
     assert np.array_equal(host(c).astype(np.float64), ref)
 
 
-def test_cfg1_rmsnorm_then_linear(lib):
+def test_rmsnorm_then_512_linear_batch_sweep(lib):
     x, gamma, w = rmsnorm_linear_inputs(32, 512, 512)
     X, G, W = bf16(x), bf16(gamma), bf16(w)
     row0 = None
@@ -112,7 +112,7 @@ def test_cfg1_rmsnorm_then_linear(lib):
         assert same_bits(z[0], row0), m
 
 
-def test_cfg2_repeats_prefixes_permutation(lib):
+def test_gemm_2048_repeats_prefixes_permutation(lib):
     a, b = gemm_inputs(2048, 2048, 2048, cfg=2)
     A, B = bf16(a), bf16(_nk(b))
     ref = lib.bi_gemm(A, B)
@@ -132,8 +132,8 @@ def test_cfg2_repeats_prefixes_permutation(lib):
     assert same_bits(cm[0], ref[100]) and same_bits(cm[41], ref[5])
 
 
-def test_cfg2_torch_mm_orientation(lib):
-    # configs[1] in the orientation of the page's torch.mm(A, B): B is [K, N] as drawn.  1000
+def test_gemm_2048_torch_mm_orientation(lib):
+    # the 2048^3 product in the orientation of the page's torch.mm(A, B): B is [K, N] as drawn.  1000
     # repeats are bitwise equal, prefix rows equal the full product's rows, and every bit
     # equals the [N, K] layout's result on the transposed copy of B (same instruction
     # sequence per element)

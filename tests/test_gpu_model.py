@@ -48,7 +48,7 @@ def _layer_batch(cache, sids, ctx):
                  workspace=torch.empty(max(ws, 16), dtype=torch.uint8, device="cuda"))
 
 
-def _cfg3_setup():
+def _mistral_layer_setup():
     dims = Dims(n_layers=1)
     wb = synth.layer_weights(cfg=3)
     w = {k: bf16(v) for k, v in wb.items()}
@@ -67,14 +67,14 @@ def _cfg3_setup():
 
 
 @pytest.mark.parametrize("fp32_variant", [False, True])
-def test_cfg3_layer_batch_invariance_and_per_op_oracle(lib, fp32_variant):
-    # configs[2]: each request's output is bitwise equal at token batches 1, 8, 64 and 256 and
-    # under a permuted batch; every operation of the layer matches the oracle on the GPU's own
-    # inputs to it (sampled requests of the 256-batch)
+def test_mistral_layer_batch_invariance_and_per_op_oracle(lib, fp32_variant):
+    # the Mistral-shaped layer: each request's output is bitwise equal at token batches 1, 8,
+    # 64 and 256 and under a permuted batch; every operation of the layer matches the oracle
+    # on the GPU's own inputs to it (sampled requests of the 256-batch)
     from invariant_amd.model import decoder_layer
     from oracle.layer import Spec
     from tests._compose import check_layer, host_weights, take
-    dims, wb, w, ctx, h, cache, pk, pv = _cfg3_setup()
+    dims, wb, w, ctx, h, cache, pk, pv = _mistral_layer_setup()
     R = 256
     H = bf16(h).float() if fp32_variant else bf16(h)
     tr = {}
@@ -97,7 +97,7 @@ def test_cfg3_layer_batch_invariance_and_per_op_oracle(lib, fp32_variant):
         return (np.concatenate([fp.bf16_to_f64(pk[r]), kn[i:i + 1]]),
                 np.concatenate([fp.bf16_to_f64(pv[r]), vn[i:i + 1]]))
     rep = check_layer(lib, rt, host_weights(w), w, ctx[rows], kv, Spec(variant=fp32_variant),
-                      tag=f"cfg3 layer variant={fp32_variant}")
+                      tag=f"mistral layer variant={fp32_variant}")
     assert all(v["ok"] for v in rep.values()), {k: v for k, v in rep.items() if not v["ok"]}
 
 
@@ -191,8 +191,8 @@ def test_model_small_per_op_and_drift(lib, fp32_variant):
 
 
 @pytest.mark.parametrize("fp32_variant", [False, True])
-def test_cfg5_per_op_prefill_and_decode(lib, fp32_variant):
-    # configs[4]'s model and 1400-token prompt: the prefill and one decode step, every op of
+def test_model32_per_op_prefill_and_decode(lib, fp32_variant):
+    # the 32-layer model and its 1400-token prompt: the prefill and one decode step, every op of
     # every one of the 32 layers against the oracle on the GPU's own inputs (sampled prefill
     # rows: the first, chunk and group boundaries, the last)
     dims = Dims()
@@ -200,12 +200,12 @@ def test_cfg5_per_op_prefill_and_decode(lib, fp32_variant):
     prompt = synth.uniform_ints(1400, 0, 31999, 5, 0)
     rows = [0, 255, 256, 1023, 1024, 1399]
     _model_per_op(lib, model, dims, fp32_variant, prompt, 1, rows, list(range(32)),
-                  tag=f"cfg5 variant={fp32_variant}")
+                  tag=f"32-layer model variant={fp32_variant}")
 
 
 @pytest.mark.parametrize("fp32_variant", [False, True])
-def test_cfg5_teacher_forced_drift_report(lib, fp32_variant):
-    # configs[4]: 64 greedy tokens of the 32-layer model on the 1400-token prompt; the oracle
+def test_model32_teacher_forced_drift_report(lib, fp32_variant):
+    # 64 greedy tokens of the 32-layer model on the 1400-token prompt; the oracle
     # model (fp64 inside every op, the model's own storage points) is teacher-forced on the
     # GPU's tokens and the logit mismatch at every step is REPORTED in the metric families of
     # the cross-vendor abstract (logit difference, top-k and token agreement) with the
@@ -232,10 +232,11 @@ def test_cfg5_teacher_forced_drift_report(lib, fp32_variant):
     rep = {"all_steps": logit_drift_report(got, ref), "step0": logit_drift_report(got[:1], ref[:1]),
            "step63": logit_drift_report(got[63:], ref[63:]),
            "oracle_greedy_tokens_agree": float(np.mean(np.argmax(ref, 1) == tok[0]))}
-    say("cfg5 logit drift", "fp32 variant" if fp32_variant else "bf16", json.dumps(rep))
-    if os.path.isdir("gpurun_out"):
-        name = "cfg5_drift_fp32variant.json" if fp32_variant else "cfg5_drift_bf16.json"
-        with open(os.path.join("gpurun_out", name), "w") as f:
+    say("32-layer model logit drift", "fp32 variant" if fp32_variant else "bf16", json.dumps(rep))
+    out_dir = os.environ.get("BI_REPORT_DIR")   # where to keep the report, if anywhere
+    if out_dir and os.path.isdir(out_dir):
+        name = "model32_drift_fp32variant.json" if fp32_variant else "model32_drift_bf16.json"
+        with open(os.path.join(out_dir, name), "w") as f:
             json.dump(rep, f, indent=1)
     assert np.all(np.isfinite(got)) and rep["all_steps"]["max_over_rms"] < 0.5
     clear = (np.sort(ref, 1)[:, -1] - np.sort(ref, 1)[:, -2]) > 4 * rep["all_steps"]["max_abs"]
@@ -243,7 +244,7 @@ def test_cfg5_teacher_forced_drift_report(lib, fp32_variant):
 
 
 @pytest.mark.parametrize("fp32_variant", [False, True])
-def test_cfg5_greedy_alone_vs_batched(lib, fp32_variant):
+def test_model32_greedy_alone_vs_batched(lib, fp32_variant):
     dims = Dims()
     model = random_model(dims, seed=5)
     prompt = synth.uniform_ints(1400, 0, 31999, 5, 0)
@@ -252,7 +253,7 @@ def test_cfg5_greedy_alone_vs_batched(lib, fp32_variant):
     prompts = others[:24] + [prompt] + others[24:]
     total = sum(len(p) + 64 for p in prompts)
     cache = PagedKVCache(dims, n_pages=total // 16 + 2 * len(prompts) + 16, seed=5)
-    say("cfg5 variant fp32" if fp32_variant else "cfg5 bf16", "batched tokens", sum(len(p) for p in prompts))
+    say("32-layer model fp32 variant" if fp32_variant else "32-layer model bf16", "batched tokens", sum(len(p) for p in prompts))
     tok_a, lg_a = greedy_generate(model, [prompt], 64, cache, dims, fp32_variant, keep_logits=[0])
     tok_b, lg_b = greedy_generate(model, prompts, 64, cache, dims, fp32_variant, keep_logits=[24])
     say("tokens", tok_a[0][:16])

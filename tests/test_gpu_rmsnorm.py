@@ -14,7 +14,7 @@ from tests._gpu import bf16, bits, f32, host, same_bits, say
 pytestmark = pytest.mark.gpu
 
 
-def test_cfg1_batch_sweep_bit_exact(lib):
+def test_rmsnorm_512_batch_sweep_bit_exact(lib):
     x, gamma, _ = rmsnorm_linear_inputs(32, 512, 512)
     ref = rmsnorm_tree(x, gamma, 1e-6)
     X, G = bf16(x), bf16(gamma)
