@@ -22,10 +22,13 @@ Beside the step, the same line carries:
                      (bi_gemm_fixed_split) and the cost is taken against the fastest split;
   size_sweeps        reported (not graded) sizes: RMSNorm rows 1..65536, decode batches 1..64,
                      RMSNorm + 512 x 512 linear at M = 1..32.
-  cpu_baseline       the oracle timed on the host (all cores and one core).
+  cpu_baseline       the oracle timed on the host (all cores and one core);
+  composition        reported, not graded: one Mistral-shaped decoder layer at decode (1, 8,
+                     64, 256 requests) and 32-layer greedy decoding alone and in a 49-prompt
+                     batch (the --model rows).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemm-set]
-                    [--no-size-sweeps]
+                    [--no-size-sweeps] [--no-composition]
                     [--gemm-sweep] [--decode-gemm] [--gemm-profile M,N,K] [--model]
                     [--decode-step B]
 """
@@ -450,7 +453,9 @@ def model_bench(torch, bi):
                          decode_tokens_per_s=round(len(ps) / step, 1),
                          decode_weight_GBps=round(weight_bytes / step / 1e9, 1))
         log(name, out[name])
-    print(json.dumps(out), flush=True)
+    del model, cache
+    torch.cuda.empty_cache()
+    return out
 
 
 def decode_step(torch, bi, B, K, W):
@@ -653,6 +658,8 @@ def main():
                     help="decode-sized GEMMs on fresh weights: [N, K] vs tiled vs torch.mm")
     ap.add_argument("--model", action="store_true",
                     help="time 32-layer greedy decoding alone and in a 49-prompt batch (reported)")
+    ap.add_argument("--no-composition", action="store_true",
+                    help="leave the --model rows out of the bench line")
     ap.add_argument("--decode-step", type=int, metavar="B",
                     help="time --steps eager 32-layer decode steps at batch B (for kernel traces)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -683,7 +690,7 @@ def main():
         decode_gemm(torch, bi)
         return
     if args.model:
-        model_bench(torch, bi)
+        print(json.dumps(model_bench(torch, bi)), flush=True)
         return
     if args.decode_step:
         decode_step(torch, bi, args.decode_step, args.steps, args.warmup)
@@ -790,6 +797,11 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the oracle on a sample")
         res["cpu_baseline"] = cpu_baseline(inp, torch, t_peak)
+    if not args.no_composition:
+        log("composition: one decoder layer at decode, 32-layer greedy decoding (reported)")
+        inp.clear()
+        torch.cuda.empty_cache()
+        res["composition"] = model_bench(torch, bi)
     print(json.dumps(res), flush=True)
 
 
