@@ -156,9 +156,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     b_off[i] = static_cast<int64_t>(b_ok[i] ? rb : 0) * ldb;
   }
 
-  // [K, N] staging: thread tid owns columns 8 (tid % 16) .. + 7 and k rows 4 (tid / 16) .. + 3
-  // of the 128 x 64 B stage
-  const int kn_n = tn * BN + (tid & 15) * 8, kn_k = (tid >> 4) * 4;
+  // [K, N] staging: thread tid owns columns 8 (tid / 16) .. + 7 and k rows 4 (tid % 16) .. + 3
+  // of the 128 x 64 B stage, so the 16 threads that share a column chunk write 16 adjacent
+  // 8-byte pieces of each transposed LDS row (no bank conflicts among them)
+  const int kn_n = tn * BN + (tid >> 4) * 8, kn_k = (tid & 15) * 4;
   auto load_stage = [&](Stage<AF32>& s, int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const u16x4 col = {s.b[0][e], s.b[1][e], s.b[2][e], s.b[3][e]};
-        *reinterpret_cast<u16x4*>(&sB[buf][((tid & 15) * 8 + e) * LDS_LD + kn_k]) = col;
+        *reinterpret_cast<u16x4*>(&sB[buf][((tid >> 4) * 8 + e) * LDS_LD + kn_k]) = col;
       }
     }
   };
