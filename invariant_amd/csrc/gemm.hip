@@ -284,6 +284,7 @@ struct Tile {
   // operands of the next K step read in place (see advance) rather than into a second set
   static constexpr bool INPLACE = BLK_M * BLK_N >= 32;
   static constexpr bool OTF = INPLACE;   // load offsets computed per load (see DmaCtx)
+  static constexpr bool BKN = false;     // B as [N, K]
   static_assert(TM % (DW * RPI) == 0 && TN % (DW * RPI) == 0 && DW <= NW, "tile rows per wave");
   static_assert(STAGES >= 2, "unsupported staging");
 };
@@ -298,6 +299,24 @@ using Tile128Deep = Tile<2, 4, 4, 2, 3, 2, 4>;
 using Tile64x128 = Tile<2, 4, 2, 2, 3, 2, 4>;
 using Tile64 = Tile<2, 2, 2, 2, 3>;
 using Tile256 = Tile<2, 4, 8, 4, 2, 2, 4>;
+
+// The same tile reading B as [K, N] (torch.mm orientation).  A B stage then holds DBK k rows
+// of TN columns: a wave-wide 1 KB load fills RPK whole k rows, lane l taking 16-byte chunk
+// position l % CPRN of its row.  Chunk c of k row r sits at position c ^ swzk(r), so that
+// the transposing operand reads below (4 k rows x 32 bytes per group of 16 lanes, two groups
+// per half-wave 8 rows apart) fall on distinct banks.  The operand values, and so the
+// instruction sequence and every output bit, are those of the [N, K] tile.
+template <class T>
+struct KnTile : T {
+  static constexpr bool BKN = true;
+  static constexpr int CPRN = T::TN / 8;   // 16-byte chunks per k row
+  static constexpr int RPK = 64 / CPRN;    // k rows per wave-wide load
+  static_assert(!T::INPLACE && T::TN % 64 == 0 && (DBK / T::DW) == T::NJB * RPK, "[K, N] stage");
+};
+template <int CPRN>
+__device__ __forceinline__ int swzk(int r) {
+  return CPRN >= 16 ? (((r & 3) << 1) | (((r >> 3) & 1) << 3)) : ((r & 3) << 1);
+}
 
 // Chunk c of LDS row r (128 bytes) sits at position c ^ swz(r), swz(r) = (r / 2) % 8: the
 // 16-byte reads of 16 consecutive rows at one chunk index (a quarter of the wave's lanes)
@@ -366,6 +385,8 @@ struct DmaCtx {
   // registers the accumulators fill, computed per load from the row of load 0 (load j is
   // RPI j rows further, clamped to the last row) and the row pitch in bytes
   uint32_t aoff[T::OTF ? 1 : T::NJA], boff[T::OTF ? 1 : T::NJB];
+  int knrow[T::BKN ? T::NJB : 1];        // [K, N] B: k row (in the stage) of load j
+  int64_t ldb;                           // [K, N] B: elements per k row
   int ra_share, rb_share;   // first tile row of this wave's A and B share (wave-uniform)
   int a_last, b_last;
   uint32_t lda2, ldb2;
@@ -429,15 +450,29 @@ __device__ __forceinline__ void dma_stage_at(const DmaCtx<T>& d, uint32_t buf, i
       const uint32_t adv = (k0 + kc < d.K) ? static_cast<uint32_t>(k0) * 2 : static_cast<uint32_t>(-2 * kc);
       dma16(d.A, a_off<T>(d, lo, j) + adv, la + j * 1024);
     }
+    if constexpr (T::BKN) {
+      // [K, N] B: a k row at or past K reads the stage's first row instead (zeroed after
+      // landing)
+      const uint16_t* bk = d.B + static_cast<int64_t>(k0) * d.ldb;
 #pragma unroll
-    for (int j = 0; j < T::NJB; ++j) {
-      const int kc = (j & 1) ? lo.kc1 : lo.kc0;
-      const uint32_t adv = (k0 + kc < d.K) ? static_cast<uint32_t>(k0) * 2 : static_cast<uint32_t>(-2 * kc);
-      dma16(d.B, b_off<T>(d, lo, j) + adv, lb + j * 1024);
+      for (int j = 0; j < T::NJB; ++j) {
+        const uint32_t off = (k0 + d.knrow[j] < d.K) ? d.boff[j] : d.boff[j] - static_cast<uint32_t>(d.knrow[j]) * d.ldb2;
+        dma16(bk, off, lb + j * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < T::NJB; ++j) {
+        const int kc = (j & 1) ? lo.kc1 : lo.kc0;
+        const uint32_t adv = (k0 + kc < d.K) ? static_cast<uint32_t>(k0) * 2 : static_cast<uint32_t>(-2 * kc);
+        dma16(d.B, b_off<T>(d, lo, j) + adv, lb + j * 1024);
+      }
     }
   } else {
     dma16_run<0, T::NJA>(d.A + k0, [&](int j) { return a_off<T>(d, lo, j); }, la);
-    dma16_run<0, T::NJB>(d.B + k0, [&](int j) { return b_off<T>(d, lo, j); }, lb);
+    if constexpr (T::BKN)
+      dma16_run<0, T::NJB>(d.B + static_cast<int64_t>(k0) * d.ldb, [&](int j) { return d.boff[j]; }, lb);
+    else
+      dma16_run<0, T::NJB>(d.B + k0, [&](int j) { return b_off<T>(d, lo, j); }, lb);
   }
 }
 
@@ -464,6 +499,30 @@ struct Ops {
   bf16x8 a[T::BLK_M], b[T::BLK_N];
 };
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// [K, N] B operand of block j for one 32-wide K step whose k row 0 starts at `rows` (LDS):
+// two transposing reads, each giving lane l rows k .. k + 3 (k = 8 (l / 16) + 4 h) of column
+// 16 j + l % 16 of the wave's columns; lane l addresses row k + (l % 16) / 4 at column
+// 4 (l % 4) of that block, which is how the read distributes a 16-lane group's 4 x 16
+// elements (checked on the GPU).
+template <class T>
+__device__ __forceinline__ bf16x8 kn_operand(const char* rows, int wn, int j) {
+  const int l = static_cast<int>(threadIdx.x & 63);
+  u16x8 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * (l >> 4) + 4 * h + ((l & 15) >> 2);
+    const int col = wn * T::BLK_N * 16 + 16 * j + 4 * (l & 3);
+    const int off = row * T::TN * 2 + 16 * ((col >> 3) ^ swzk<T::CPRN>(row)) + 8 * ((col >> 2) & 1);
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rows + off));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[4 * h + e] = static_cast<uint16_t>(v[e]);
+  }
+  return as_bf16x8(r);
+}
+
 template <class T>
 __device__ __forceinline__ void load_ops(const uint16_t* sA, uint32_t buf, int ks, const Frag& f,
                                          Ops<T>& o) {
@@ -472,8 +531,16 @@ __device__ __forceinline__ void load_ops(const uint16_t* sA, uint32_t buf, int k
   // in the order the MFMAs consume them: A0, every B, then A1 .. (the first MFMAs can
   // start after 1 + BLK_N reads)
   o.a[0] = as_bf16x8(*reinterpret_cast<const u16x8*>(a));
+  if constexpr (T::BKN) {
+    const int wn = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) % T::WAVES_N;
+    const char* rows = reinterpret_cast<const char*>(sA) + T::STAGES * T::SA * 2 + buf * (T::SB * 2) +
+                       ks * 32 * T::TN * 2;
 #pragma unroll
-  for (int j = 0; j < T::BLK_N; ++j) o.b[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(b + j * kBlkBytes));
+    for (int j = 0; j < T::BLK_N; ++j) o.b[j] = kn_operand<T>(rows, wn, j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < T::BLK_N; ++j) o.b[j] = as_bf16x8(*reinterpret_cast<const u16x8*>(b + j * kBlkBytes));
+  }
 #pragma unroll
   for (int i = 1; i < T::BLK_M; ++i) o.a[i] = as_bf16x8(*reinterpret_cast<const u16x8*>(a + i * kBlkBytes));
 }
@@ -501,12 +568,24 @@ __device__ __forceinline__ void zero_k_tail(const DmaCtx<T>& d, uint16_t* sA, ui
     for (int e = 0; e < 8; ++e)
       if (k0 + ((j & 1) ? lo.kc1 : lo.kc0) + e >= d.K) sA[pos + e] = 0;
   }
+  if constexpr (T::BKN) {
+    // [K, N] B: load j's 16 bytes are one k row's chunk; clear it when that row is at or past K
 #pragma unroll
-  for (int j = 0; j < T::NJB; ++j) {
-    const int pos = buf * T::SB + ((T::TN / T::DW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
+    for (int j = 0; j < T::NJB; ++j) {
+      const int pos = buf * T::SB + (DBK / T::DW) * wave * T::TN + j * 512 + lane * 8;
+      if (k0 + d.knrow[j] >= d.K) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (k0 + ((j & 1) ? lo.kc1 : lo.kc0) + e >= d.K) sB[pos + e] = 0;
+        for (int e = 0; e < 8; ++e) sB[pos + e] = 0;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < T::NJB; ++j) {
+      const int pos = buf * T::SB + ((T::TN / T::DW) * wave + RPI * j + lane / CPR) * DBK + (lane % CPR) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k0 + ((j & 1) ? lo.kc1 : lo.kc0) + e >= d.K) sB[pos + e] = 0;
+    }
   }
 }
 
@@ -683,12 +762,27 @@ __global__ __launch_bounds__(T::THREADS, T::WAVES_PER_SIMD) void gemm_dma_kernel
       const int ra = min(d.ra_share + lane / CPR + RPI * j, M - 1);
       d.aoff[j] = static_cast<uint32_t>((static_cast<int64_t>(ra) * lda + d.kc[j & 1]) * 2);
     }
+    if constexpr (T::BKN) {
+      // load j of issuing wave dw: k row (DBK / DW) dw + RPK j + l / CPRN of the stage, the
+      // chunk of 8 columns that lands at position l % CPRN; a chunk past N reads columns 0..7
+      // instead (those outputs are not stored)
 #pragma unroll
-    for (int j = 0; j < T::NJB; ++j) {
-      const int rb = min(d.rb_share + lane / CPR + RPI * j, N - 1);
-      d.boff[j] = static_cast<uint32_t>((static_cast<int64_t>(rb) * ldb + d.kc[j & 1]) * 2);
+      for (int j = 0; j < T::NJB; ++j) {
+        const int row = (DBK / T::DW) * dw + T::RPK * j + lane / T::CPRN;
+        int n = tn * T::TN + 8 * ((lane % T::CPRN) ^ swzk<T::CPRN>(row));
+        if (n >= N) n = 0;
+        d.knrow[j] = row;
+        d.boff[j] = static_cast<uint32_t>((static_cast<int64_t>(row) * ldb + n) * 2);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < T::NJB; ++j) {
+        const int rb = min(d.rb_share + lane / CPR + RPI * j, N - 1);
+        d.boff[j] = static_cast<uint32_t>((static_cast<int64_t>(rb) * ldb + d.kc[j & 1]) * 2);
+      }
     }
   }
+  d.ldb = ldb;
   // operand reads: lane holds row (lane % 16) of each 16-row block and k-chunk
   // 4 ks + lane / 16 of each 32-wide K step (swz(row) = swz(lane % 16) in every block)
   Frag f;
@@ -1499,6 +1593,20 @@ void launch_bf16(const void* A, const void* B, void* C, int64_t M, int64_t N, in
 }
 
 
+// bf16 A and [K, N] B, both under 4 GiB: the LDS-staged tiles with B landed as k rows and
+// read transposed (the 256 x 256 tile, whose operands are read in place, is replaced by
+// 128 x 128; the few-row kernel, which loads its operands straight into registers, has no
+// [K, N] form).
+void launch_bf16_kn(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                    int64_t lda, int64_t ldb, int64_t ldc, int mode, hipStream_t s) {
+  switch (pick_tile(M, N, cu_count())) {
+    case TileKind::k128deep: launch_dma<KnTile<Tile128Deep>>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
+    case TileKind::k64x128: launch_dma<KnTile<Tile64x128>>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
+    case TileKind::k64: launch_dma<KnTile<Tile64>>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
+    default: launch_dma<KnTile<Tile128>>(A, B, C, M, N, K, lda, ldb, ldc, mode, s); break;
+  }
+}
+
 }  // namespace
 }  // namespace bi
 
@@ -1532,7 +1640,10 @@ extern "C" int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t
   if (nwg > 0x7fffffffLL) return BI_ERR_SHAPE;
   hipStream_t s = as_stream(stream);
   const int cf = c_dtype == BI_F32;
-  if (b_layout == BI_B_KN) {   // [K, N] B: register-staged kernel, transposed into LDS
+  if (b_layout == BI_B_KN && a_dtype == BI_BF16 && M * lda * 2 < (int64_t(1) << 32) &&
+      K * ldb * 2 < (int64_t(1) << 32)) {
+    launch_bf16_kn(A, B, C, M, N, K, lda, ldb, ldc, cf, s);
+  } else if (b_layout == BI_B_KN) {   // fp32 A or 4 GiB operands: register-staged, transposed into LDS
     if (a_dtype == BI_F32)
       gemm_kernel<true, true><<<dim3(static_cast<unsigned>(nwg), 1), dim3(kThreads), 0, s>>>(
           A, static_cast<const uint16_t*>(B), C, int(M), int(N), int(K), lda, ldb, ldc, cf, tm, tn,

@@ -154,11 +154,13 @@ def test_gemm_2048_torch_mm_orientation(lib):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1003, 77), (33, 200, 1000), (300, 8, 4096), (130, 4100, 64),
-                                   (3000, 700, 300)])
+                                   (3000, 700, 300), (1, 512, 4096), (600, 4096, 1000),
+                                   (4096, 4096, 256), (2048, 2048, 2048)])
 def test_b_kn_ragged_equals_b_nk(lib, m, n, k):
     # [K, N] B with N off a multiple of 8 (row stride padded to one, the padding NaN: nothing
     # past column N may be read into a stored output) and ragged K: bits of the [N, K] layout,
-    # within 1 ulp of the oracle, for bf16 and fp32 A
+    # within 1 ulp of the oracle, for bf16 and fp32 A; with bf16 A the shapes reach every
+    # tile the [K, N] form takes (64 x 64, 64 x 128, 128 x 128 one and two per CU)
     from invariant_amd import BI_B_KN
     say("gemm B [K, N]", m, n, k)
     a, b = gemm_inputs(m, n, k, cfg=46)
