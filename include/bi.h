@@ -134,10 +134,15 @@ int bi_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t D, 
  * Rows are read in 16-byte pieces: row i of A (of a [N, K] B) must be readable up to
  * element round_up(K, 8) (round_up(K, 4) for fp32 A), which lda (ldb) >= that guarantees
  * for every row but the last.
- * BI_B_KN runs a register-staged 128 x 128 tile that transposes each 4 x 8 block of B on
- * its way into on-chip memory; every output element then sees the same operands, lanes and
- * instruction sequence as with the [N, K] copy of B, so C is bit for bit the BI_B_NK result
- * (at a lower rate than the [N, K] kernels).  A [K, N] B is read only inside its N columns.
+ * BI_B_KN with bf16 A (operands under 4 GiB) runs the LDS-staged tiles below, B landing in
+ * on-chip memory as k rows and each instruction's B operand read with two transposing LDS
+ * reads; the few-row grids and the 256 x 256 tile are replaced by the tile the grid would
+ * otherwise take (64 x 64 .. 128 x 128).  With fp32 A (or 4 GiB operands) a register-staged
+ * 128 x 128 tile transposes each 4 x 8 block of B on its way into on-chip memory.  Either
+ * way every output element sees the same operands, lanes and instruction sequence as with
+ * the [N, K] copy of B, so C is bit for bit the BI_B_NK result.  A [K, N] B is read only
+ * inside its N columns (a 16-byte piece that starts inside reads up to the next multiple of
+ * 8 columns, within ldb) and its K rows.
  * Errors: BI_ERR_NULL, BI_ERR_SHAPE (negative sizes, K < 1 with M*N > 0, strides too
  * small), BI_ERR_DTYPE, BI_ERR_ALIGN.
  */
@@ -159,7 +164,9 @@ int bi_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
  * 128 x 128, with a 3-stage ring when the grid has no more tiles than CUs and a 2-stage
  * ring (two workgroups per CU) otherwise; when fewer than three quarters of the CUs would
  * get a 128 x 128 tile, 64 x 128 or (fewer still) 64 x 64 with a 3-stage ring; fp32 A:
- * 128 x 128, register staged.
+ * 128 x 128, register staged.  (For a [K, N] B bi_gemm takes the same choice among the
+ * LDS-staged tiles without the few-row and 256 x 256 forms; this call reports the [N, K]
+ * choice.)
  * Informational: the bits of C do not depend on it.  Errors: BI_ERR_NULL, BI_ERR_SHAPE
  * (negative sizes), BI_ERR_DTYPE. */
 int bi_gemm_tile(int64_t M, int64_t N, int64_t K, int a_dtype, int32_t* tile_m, int32_t* tile_n,
