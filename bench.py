@@ -21,7 +21,8 @@ Beside the step, the same line carries:
                      splits also include fixed slice lengths of 512, 1024 and 2048 columns
                      (bi_gemm_fixed_split) and the cost is taken against the fastest split;
   size_sweeps        reported (not graded) sizes: RMSNorm rows 1..65536, decode batches 1..64,
-                     RMSNorm + 512 x 512 linear at M = 1..32.
+                     RMSNorm + 512 x 512 linear at M = 1..32, the 2048^3 GEMM with B as
+                     [N, K] and as [K, N] (torch.mm orientation).
   cpu_baseline       the oracle timed on the host (all cores and one core);
   composition        reported, not graded: one Mistral-shaped decoder layer at decode (1, 8,
                      64, 256 requests) and 32-layer greedy decoding alone and in a 49-prompt
@@ -599,7 +600,23 @@ def size_sweeps(torch, bi, inp):
         t = _graph_time(torch, [lambda M=M: bi.bi_rmsnorm(x1[:M], g1, 1e-6, out=y1[:M]),
                                 lambda M=M: bi.bi_gemm(y1[:M], w1, out=c1[:M])])
         lin.append(dict(M=M, us_per_pair=round(2 * t * 1e6, 2)))
-    return {"rmsnorm_rows": rms, "attention_decode_batch": att, "rmsnorm_linear_512": lin}
+    # the 2048^3 product in both B orientations: [N, K] (the step's) and [K, N] as in the
+    # page's torch.mm(A, B) (the same bits), with the vendor library on the [K, N] B as context
+    from invariant_amd import BI_B_KN
+    A, Bnk, C = inp["A"], inp["B_nk"], inp["C"]
+    Bkn = Bnk.t().contiguous()
+    orient = {}
+    for name, fn in (("B_NK", lambda: bi.bi_gemm(A, Bnk, out=C)),
+                     ("B_KN", lambda: bi.bi_gemm(A, Bkn, out=C, b_layout=BI_B_KN)),
+                     ("torch_mm_KN", lambda: torch.mm(A, Bkn, out=C))):
+        for _ in range(3):
+            fn()
+        t = _time_calls(torch, fn, 20)   # back-to-back calls (the vendor call is not captured)
+        f = 2.0 * A.shape[0] * Bnk.shape[0] * A.shape[1]
+        orient[name] = dict(us=round(t * 1e6, 2), TFLOPs=round(f / t / 1e12, 1), frac=round(f / t / BF16_PEAK, 4))
+    del Bkn
+    return {"rmsnorm_rows": rms, "attention_decode_batch": att, "rmsnorm_linear_512": lin,
+            "gemm_2048_orientations": orient}
 
 
 def graph_step(torch, inp, ops, K):
